@@ -1,0 +1,250 @@
+"""Gated delta rule on MI355X (gfx950): thin Python binding over libgdn.so.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor properties, allocates outputs and workspaces with PyTorch
+and passes raw pointers plus the current HIP stream through the C ABI
+declared in include/gdn.h. There is no fallback: if libgdn.so is missing the
+calls raise.
+
+    o, hT, cs = fwd(q, k, v, g, beta, A_log, h0=None, save_chunk_states=True)
+    grads     = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, chunk_states=cs)
+    o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
+    o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["fwd", "bwd", "step", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
+           "chunk_states_size", "bwd_workspace_size"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
+           "gdn_chunk_states_size", "gdn_status_string", "gdn_last_error_detail"]
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_FLAG_ADDITIVE = 1
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, func, status, detail):
+        super().__init__(f"{func} failed with status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_delta_rule_74_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, Z = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_size_t
+        I32, U32 = ctypes.c_int32, ctypes.c_uint32
+        L.gdn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.gdn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
+        for f in (L.gdn_fwd, L.gdn_bwd, L.gdn_step):
+            f.restype = ctypes.c_int
+        for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_chunk_states_size):
+            f.argtypes = [S]
+            f.restype = Z
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error_detail.argtypes = []
+        L.gdn_last_error_detail.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(func, status):
+    if status != 0:
+        raise GdnError(func, status, lib().gdn_last_error_detail().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a HIP device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _shape(q, v, additive):
+    B, T, H, dk = q.shape
+    return Shape(B, T, H, dk, v.shape[-1], _dtype_code(q), 64, GDN_FLAG_ADDITIVE if additive else 0)
+
+
+def _check_seq(q, k, v, g, beta, A_log, h0=None):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype, (B, T, H, dk))
+    _need(k, "k", q.dtype, (B, T, H, dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
+    return B, T, H, dk, dv
+
+
+def chunk_states_size(q, v, additive=False):
+    s = _shape(q, v, additive)
+    return int(lib().gdn_chunk_states_size(ctypes.byref(s)))
+
+
+def bwd_workspace_size(q, v, additive=False):
+    s = _shape(q, v, additive)
+    return int(lib().gdn_bwd_workspace_size(ctypes.byref(s)))
+
+
+def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_chunk_states=False,
+        want_hT=True, o=None, hT=None, chunk_states=None):
+    """Chunked forward. Returns (o, hT or None, chunk_states or None)."""
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
+    s = _shape(q, v, additive)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, T, H, dv), dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(hT, "hT", torch.float32, (B, H, dk, dv), dev)
+    if chunk_states is None and save_chunk_states:
+        NC = (T + 63) // 64
+        chunk_states = torch.empty((B, H, NC, dk, dv), dtype=q.dtype, device=dev)
+    _need(chunk_states, "chunk_states", q.dtype, None, dev)
+    L = lib()
+    st = L.gdn_fwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0), _p(o),
+                   _p(hT), _p(chunk_states), None, 0, _stream(dev))
+    _check("gdn_fwd", st)
+    return o, hT, chunk_states
+
+
+def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, chunk_states=None, additive=False,
+        want_dh0=True, want_hT=False, workspace=None, out=None):
+    """Backward of sum(do * o) + sum(dhT * hT). Returns a dict with dq, dk,
+    dv, dg, dbeta, dA_log, dh0 (or None) and hT (when want_hT)."""
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
+    dev = q.device
+    _need(do, "do", q.dtype, (B, T, H, dv), dev)
+    _need(dhT, "dhT", torch.float32, (B, H, dk, dv), dev)
+    _need(chunk_states, "chunk_states", q.dtype, None, dev)
+    s = _shape(q, v, additive)
+    L = lib()
+    need = int(L.gdn_bwd_workspace_size(ctypes.byref(s)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    r = out if out is not None else {}
+    r.setdefault("dq", torch.empty_like(q))
+    r.setdefault("dk", torch.empty_like(k))
+    r.setdefault("dv", torch.empty_like(v))
+    r.setdefault("dg", torch.empty_like(g))
+    r.setdefault("dbeta", torch.empty_like(beta))
+    r.setdefault("dA_log", torch.empty_like(A_log))
+    if want_dh0:
+        r.setdefault("dh0", torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+    else:
+        r["dh0"] = None
+    if want_hT:
+        r.setdefault("hT", torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+    else:
+        r["hT"] = None
+    st = L.gdn_bwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0),
+                   _p(chunk_states), _p(do), _p(dhT), _p(r["dq"]), _p(r["dk"]), _p(r["dv"]),
+                   _p(r["dg"]), _p(r["dbeta"]), _p(r["dA_log"]), _p(r["dh0"]), _p(r["hT"]),
+                   _p(workspace), workspace.numel(), _stream(dev))
+    _check("gdn_bwd", st)
+    return r
+
+
+def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=None):
+    """One decode token per sequence. q, k [N,H,dk]; v [N,H,dv]; g, beta
+    [N,H]; h_in [N,H,dk,dv] fp32 or None. h_out may be h_in (in place).
+    Returns (o, h_out)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype, (N, H, dk))
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(g, "g", torch.float32, (N, H), dev)
+    _need(beta, "beta", torch.float32, (N, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    _need(h_in, "h_in", torch.float32, (N, H, dk, dv), dev)
+    if h_out is None:
+        h_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(h_out, "h_out", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, H, dv), dev)
+    st = lib().gdn_step(N, H, dk, dv, _dtype_code(q), GDN_FLAG_ADDITIVE if additive else 0, _p(q),
+                        _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out), _p(o),
+                        _stream(dev))
+    _check("gdn_step", st)
+    return o, h_out
+
+
+class GatedDeltaRule(torch.autograd.Function):
+    """Autograd wrapper: forward saves the per-chunk states, backward reads
+    them instead of recomputing."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False):
+        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_chunk_states=True)
+        ctx.save_for_backward(q, k, v, g, beta, A_log, h0, cs)
+        ctx.additive = additive
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, do, dhT):
+        q, k, v, g, beta, A_log, h0, cs = ctx.saved_tensors
+        if do is None:
+            do = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+        r = bwd(q, k, v, g, beta, A_log, do.contiguous(), h0,
+                None if dhT is None else dhT.contiguous(), chunk_states=cs,
+                additive=ctx.additive, want_dh0=h0 is not None)
+        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None

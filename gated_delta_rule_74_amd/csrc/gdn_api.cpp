@@ -1,0 +1,316 @@
+// C ABI of libgdn.so: argument validation, workspace layout and kernel
+// launches. The operation itself is described in include/gdn.h.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+gdn_status_t fail(gdn_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gdn_status_t ok() {
+    g_detail[0] = 0;
+    return GDN_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t esize(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+struct Range {
+    const void *p;
+    size_t n;
+    const char *name;
+};
+
+bool overlap(const Range &a, const Range &b) {
+    if (!a.p || !b.p || !a.n || !b.n) return false;
+    const char *pa = (const char *)a.p, *pb = (const char *)b.p;
+    return pa < pb + b.n && pb < pa + a.n;
+}
+
+gdn_status_t check_aliasing(const Range *in, int nin, const Range *out, int nout) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(out[i], in[j]))
+                return fail(GDN_EINVAL, "output %s overlaps input %s", out[i].name, in[j].name);
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j]))
+                return fail(GDN_EINVAL, "output %s overlaps output %s", out[i].name, out[j].name);
+    }
+    return GDN_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+gdn_status_t check_shape(const gdn_shape_t *s) {
+    if (!s) return fail(GDN_EINVAL, "shape is NULL");
+    if (s->B < 1 || s->T < 1 || s->H < 1) return fail(GDN_EINVAL, "B, T, H must be >= 1");
+    if (s->dk < 1 || s->dv < 1 || s->dk > 128 || s->dv > 128)
+        return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
+    if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", s->dtype);
+    if (s->chunk != 0 && s->chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 0 or 64");
+    if (s->flags & ~GDN_FLAG_ADDITIVE) return fail(GDN_EINVAL, "unknown flag bits 0x%x", s->flags);
+    if (s->dtype == GDN_F32 && (s->dk > 64 || s->dv > 64))
+        return fail(GDN_EUNSUPPORTED, "fp32 supports dk, dv <= 64");
+    const double elems = (double)s->B * s->T * s->H * (s->dk > s->dv ? s->dk : s->dv);
+    if (elems >= 2147483648.0 || (double)s->B * s->H >= 2147483648.0)
+        return fail(GDN_EINVAL, "tensor too large");
+    return GDN_OK;
+}
+
+int nchunks(const gdn_shape_t *s) { return (s->T + 63) / 64; }
+
+size_t states_bytes(const gdn_shape_t *s) {
+    return (size_t)s->B * s->H * nchunks(s) * s->dk * s->dv * esize(s->dtype);
+}
+
+gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *A_log, const float *h0) {
+    gdn::SeqArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.A_log = A_log;
+    a.h0 = h0;
+    a.B = s->B;
+    a.T = s->T;
+    a.H = s->H;
+    a.dk = s->dk;
+    a.dv = s->dv;
+    a.NC = nchunks(s);
+    a.additive = (s->flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
+    return a;
+}
+
+int pad_of(const gdn_shape_t *s) {
+    return gdn::pad_dim(s->dk > s->dv ? s->dk : s->dv, s->dtype == GDN_BF16);
+}
+
+gdn_status_t hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(GDN_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+} // namespace
+
+namespace gdn {
+int bwd_chain_vblock(bool bf16, int D);
+}
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status_t st) {
+    switch (st) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_EUNSUPPORTED: return "unsupported configuration";
+    case GDN_EWORKSPACE: return "workspace missing or too small";
+    case GDN_EHIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error_detail(void) { return g_detail; }
+
+size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
+    (void)s;
+    return 0;
+}
+
+size_t gdn_chunk_states_size(const gdn_shape_t *s) {
+    if (check_shape(s) != GDN_OK) return 0;
+    return states_bytes(s);
+}
+
+size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
+    if (check_shape(s) != GDN_OK) return 0;
+    const size_t st = align_up(states_bytes(s));
+    const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
+    return st /* recomputed chunk states */ + st /* dh per chunk */ + part;
+}
+
+gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const float *A_log, const float *h0, void *o, float *hT,
+                     void *chunk_states, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    gdn_status_t st = check_shape(s);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !g || !beta || !A_log || !o)
+        return fail(GDN_EINVAL, "q, k, v, g, beta, A_log and o must not be NULL");
+    const void *vec[] = {q, k, v, o, chunk_states};
+    for (const void *p : vec)
+        if (p && !aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, o, chunk_states must be 16-byte aligned");
+    const void *f32[] = {g, beta, A_log, h0, hT};
+    for (const void *p : f32)
+        if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    const size_t e = esize(s->dtype), BTH = (size_t)s->B * s->T * s->H;
+    const size_t sb = (size_t)s->B * s->H * s->dk * s->dv * 4;
+    const Range in[] = {{q, BTH * s->dk * e, "q"},     {k, BTH * s->dk * e, "k"}, {v, BTH * s->dv * e, "v"},
+                        {g, BTH * 4, "g"},             {beta, BTH * 4, "beta"},   {A_log, (size_t)s->H * 4, "A_log"},
+                        {h0, h0 ? sb : 0, "h0"}};
+    const Range out[] = {{o, BTH * s->dv * e, "o"}, {hT, hT ? sb : 0, "hT"},
+                         {chunk_states, chunk_states ? states_bytes(s) : 0, "chunk_states"}};
+    st = check_aliasing(in, 7, out, 3);
+    if (st != GDN_OK) return st;
+    gdn::FwdArgs a;
+    a.s = seq(s, q, k, v, g, beta, A_log, h0);
+    a.o = o;
+    a.hT = hT;
+    a.cs = chunk_states;
+    const int D = pad_of(s);
+    const int BV = gdn::fwd_vblock(D);
+    a.NVB = (s->dv + BV - 1) / BV;
+    return hip_status(gdn::launch_fwd(a, s->dtype == GDN_BF16, D, (hipStream_t)stream), "gdn_fwd launch");
+}
+
+gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const float *A_log, const float *h0, const void *chunk_states,
+                     const void *dout, const float *dhT, void *dq, void *dk, void *dv, float *dg,
+                     float *dbeta, float *dA_log, float *dh0, float *hT, void *ws, size_t ws_bytes,
+                     void *stream) {
+    gdn_status_t st = check_shape(s);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !g || !beta || !A_log || !dout || !dq || !dk || !dv || !dg || !dbeta || !dA_log)
+        return fail(GDN_EINVAL, "a required pointer is NULL");
+    if (chunk_states && hT) return fail(GDN_EINVAL, "hT can only be recomputed when chunk_states is NULL");
+    const bool bf = s->dtype == GDN_BF16;
+    const int D = pad_of(s);
+    if (!gdn::bwd_supported(bf, D))
+        return fail(GDN_EUNSUPPORTED, "backward not built for %s with head dim %d", bf ? "bf16" : "fp32",
+                    s->dk > s->dv ? s->dk : s->dv);
+    const void *vec[] = {q, k, v, dout, dq, dk, dv, chunk_states};
+    for (const void *p : vec)
+        if (p && !aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, do, dq, dk, dv must be 16-byte aligned");
+    const void *f32[] = {g, beta, A_log, h0, dhT, dg, dbeta, dA_log, dh0, hT};
+    for (const void *p : f32)
+        if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    const size_t need = gdn_bwd_workspace_size(s);
+    if (!ws || ws_bytes < need)
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    const size_t e = esize(s->dtype), BTH = (size_t)s->B * s->T * s->H;
+    const size_t sb = (size_t)s->B * s->H * s->dk * s->dv * 4;
+    const Range in[] = {{q, BTH * s->dk * e, "q"},
+                        {k, BTH * s->dk * e, "k"},
+                        {v, BTH * s->dv * e, "v"},
+                        {g, BTH * 4, "g"},
+                        {beta, BTH * 4, "beta"},
+                        {A_log, (size_t)s->H * 4, "A_log"},
+                        {h0, h0 ? sb : 0, "h0"},
+                        {chunk_states, chunk_states ? states_bytes(s) : 0, "chunk_states"},
+                        {dout, BTH * s->dv * e, "do"},
+                        {dhT, dhT ? sb : 0, "dhT"},
+                        {ws, need, "workspace"}};
+    const Range out[] = {{dq, BTH * s->dk * e, "dq"},       {dk, BTH * s->dk * e, "dk"},
+                         {dv, BTH * s->dv * e, "dv"},       {dg, BTH * 4, "dg"},
+                         {dbeta, BTH * 4, "dbeta"},         {dA_log, (size_t)s->H * 4, "dA_log"},
+                         {dh0, dh0 ? sb : 0, "dh0"},        {hT, hT ? sb : 0, "hT"}};
+    st = check_aliasing(in, 11, out, 8);
+    if (st != GDN_OK) return st;
+
+    hipStream_t strm = (hipStream_t)stream;
+    const size_t stb = align_up(states_bytes(s));
+    char *w = (char *)ws;
+    void *cs_ws = w;
+    void *dhs = w + stb;
+    float *part = (float *)(w + 2 * stb);
+    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
+    hipError_t he;
+    if (!chunk_states) {
+        gdn::FwdArgs fa;
+        fa.s = sa;
+        fa.o = nullptr;
+        fa.hT = hT;
+        fa.cs = cs_ws;
+        const int BV = gdn::fwd_vblock(D);
+        fa.NVB = (s->dv + BV - 1) / BV;
+        he = gdn::launch_fwd(fa, bf, D, strm);
+        if (he != hipSuccess) return hip_status(he, "gdn_bwd state recompute launch");
+        chunk_states = cs_ws;
+    }
+    gdn::BwdChainArgs ca;
+    ca.s = sa;
+    ca.dout = dout;
+    ca.dhT = dhT;
+    ca.dhs = dhs;
+    ca.dh0 = dh0;
+    const int BVc = gdn::bwd_chain_vblock(bf, D);
+    ca.NVB = (s->dv + BVc - 1) / BVc;
+    he = gdn::launch_bwd_chain(ca, bf, D, strm);
+    if (he != hipSuccess) return hip_status(he, "gdn_bwd chain launch");
+    gdn::BwdLocalArgs la;
+    la.s = sa;
+    la.dout = dout;
+    la.cs = chunk_states;
+    la.dhs = dhs;
+    la.dq = dq;
+    la.dk = dk;
+    la.dv = dv;
+    la.dg = dg;
+    la.dbeta = dbeta;
+    la.dA_part = part;
+    he = gdn::launch_bwd_local(la, bf, D, strm);
+    if (he != hipSuccess) return hip_status(he, "gdn_bwd local launch");
+    he = gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm);
+    return hip_status(he, "gdn_bwd dA_log launch");
+}
+
+gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
+                      const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *A_log, const float *h_in, float *h_out, void *o, void *stream) {
+    if (N < 1 || H < 1) return fail(GDN_EINVAL, "N and H must be >= 1");
+    if (dk < 1 || dv < 1 || dk > 128 || dv > 128) return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", dtype);
+    if (flags & ~GDN_FLAG_ADDITIVE) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
+    if ((double)N * H * dk * dv >= 2147483648.0) return fail(GDN_EINVAL, "state too large");
+    if (!q || !k || !v || !g || !beta || !A_log || !h_out || !o)
+        return fail(GDN_EINVAL, "a required pointer is NULL");
+    const void *all[] = {q, k, v, o, g, beta, A_log, h_in, h_out};
+    for (const void *p : all)
+        if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "pointers must be 4-byte aligned");
+    const size_t e = esize(dtype), NH = (size_t)N * H, sb = NH * dk * dv * 4;
+    const Range in[] = {{q, NH * dk * e, "q"},        {k, NH * dk * e, "k"},     {v, NH * dv * e, "v"},
+                        {g, NH * 4, "g"},             {beta, NH * 4, "beta"},    {A_log, (size_t)H * 4, "A_log"},
+                        {h_in == h_out ? nullptr : h_in, sb, "h_in"}};
+    const Range out[] = {{h_out, sb, "h_out"}, {o, NH * dv * e, "o"}};
+    gdn_status_t st = check_aliasing(in, 7, out, 2);
+    if (st != GDN_OK) return st;
+    if (h_in && h_in != h_out && overlap(Range{h_in, sb, "h_in"}, Range{h_out, sb, "h_out"}))
+        return fail(GDN_EINVAL, "h_in and h_out overlap without being equal");
+    gdn::StepArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.A_log = A_log;
+    a.h_in = h_in;
+    a.h_out = h_out;
+    a.o = o;
+    a.N = N;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
+    return hip_status(gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream), "gdn_step launch");
+}
+
+} // extern "C"

@@ -1,0 +1,653 @@
+// Reverse-chunk backward of the chunked gated delta rule.
+//
+// The forward per chunk (chunk-local cumulative log-decay gam, Gam_ij =
+// exp(gam_i - gam_j) for i >= j; see gdn_fwd.hip) is
+//   L = strict_lower(diag(beta)(K K^T o Gam)), Tm = (I + L)^{-1}
+//   U = Tm diag(beta) V,  Kw = Tm diag(beta e^gam) K,  W = U - Kw h
+//   O = diag(e^gam) Q h + P W,  P = (Q K^T) o Gam (lower, diagonal included)
+//   h' = e^{gam_n} h + Kt^T W,  Kt = diag(e^{gam_n - gam}) K
+// Its reverse, given dO and dh' (gradient with respect to h'):
+//   dW  = P^T dO + Kt dh'
+//   dh  = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW          (serial chain)
+//   dQ  = diag(e^gam) dO h^T + (dP o Gam) K,   dP = dO W^T
+//   dKw = -dW h^T,  dV' = Tm^T dW,  dK' = Tm^T dKw,  dV = diag(beta) dV'
+//   dL  = -(dV' U^T + dK' Kw^T) (strictly lower part)
+//   dK  = (dP o Gam)^T Q + diag(e^{gam_n - gam}) W dh'^T + diag(beta e^gam) dK'
+//         + dS K + dS^T K,  dS = diag(beta)(dL o Gam)
+//   dbeta_i = v_i . dV'_i + e^{gam_i} k_i . dK'_i + sum_j dL_ij (K K^T o Gam)_ij
+//   dgam from every place gam enters (e^gam, e^{gam_n}, e^{gam_n - gam}, Gam);
+//   dlam_r = sum_{i >= r} dgam_i;  dg = A dlam;  dA_log = sum_{b,t} g dg.
+//
+// Kernels: bwd_chain walks the chunks backwards per (batch, head, value
+// block) carrying dh and stores dh' of every chunk; bwd_local recomputes a
+// chunk's intermediates from the saved chunk-start state h and dh' and forms
+// all local gradients, one workgroup per (batch, head, chunk); dA_reduce sums
+// the per-chunk dA_log parts in a fixed order.
+#include "gdn_common.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// --------------------------------------------------------------- chain
+
+template <bool BF, int D, int BV> struct ChainSmem {
+    using S = typename Op<BF>::S;
+    static constexpr int LDD = D + Op<BF>::PAD;
+    static constexpr int LDC = C + Op<BF>::PAD;
+    static constexpr int szCD = C * LDD * (int)sizeof(S);
+    static constexpr int szDC = D * LDC * (int)sizeof(S);
+    static constexpr int oK = 0;                                  // Ks [C][LDD]
+    static constexpr int oKT = oK + szCD;                         // KT [D][LDC] (scaled beta e^gam)
+    static constexpr int oQ = oKT + szDC;                         // Qs [C][LDD] -> dWT [BV][LDC]
+    static constexpr int oQT = oQ + szCD;                         // QT [D][LDC] (scaled e^gam) -> -KwT
+    static constexpr int oDOT = oQT + szDC;                       // dOT [BV][LDC]
+    static constexpr int oR1 = oDOT + BV * LDC * (int)sizeof(S);  // L fp32 -> Tm as S
+    static constexpr int szR1 = (C * LDF * 4 > szCD) ? C * LDF * 4 : szCD;
+    static constexpr int oR2 = oR1 + szR1;                        // Tm fp32
+    static constexpr int oPT = oR2 + C * LDF * 4;                 // PT [C][LDC]
+    static constexpr int oDHT = oPT + C * LDC * (int)sizeof(S);   // dhT [BV][LDD]
+    static constexpr int oX = oDHT + BV * LDD * (int)sizeof(S);
+    static constexpr int oGam = oX + 4 * 16 * 17 * 4;
+    static constexpr int oEg = oGam + C * 8;
+    static constexpr int oEgn = oEg + C * 4;
+    static constexpr int oBet = oEgn + C * 4;
+    static constexpr int oG = oBet + C * 4;
+    static constexpr int oMisc = oG + C * 4;
+    static constexpr int SIZE = oMisc + 16;
+    static_assert(BV * LDC <= C * LDD, "dWT must fit in Qs");
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+template <bool BF, int D, int BV>
+__global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
+    using O = Op<BF>;
+    using S = typename O::S;
+    using L = ChainSmem<BF, D, BV>;
+    constexpr int LDD = L::LDD, LDC = L::LDC;
+    constexpr int DT = D / 16, VT = BV / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    S *Ks = (S *)(smem + L::oK);
+    S *KT = (S *)(smem + L::oKT);
+    S *Qs = (S *)(smem + L::oQ);
+    S *dWT = (S *)(smem + L::oQ);
+    S *QT = (S *)(smem + L::oQT);
+    S *KwT = (S *)(smem + L::oQT);
+    S *dOT = (S *)(smem + L::oDOT);
+    float *Lm = (float *)(smem + L::oR1);
+    S *TS = (S *)(smem + L::oR1);
+    float *Tm = (float *)(smem + L::oR2);
+    S *PT = (S *)(smem + L::oPT);
+    S *dHT = (S *)(smem + L::oDHT);
+    float *xs = (float *)(smem + L::oX);
+    double *gam = (double *)(smem + L::oGam);
+    float *eg = (float *)(smem + L::oEg);
+    float *egn = (float *)(smem + L::oEgn);
+    float *bet = (float *)(smem + L::oBet);
+    float *gch = (float *)(smem + L::oG);
+    float *misc = (float *)(smem + L::oMisc);
+
+    const SeqArgs &s = a.s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int vb = lid % a.NVB, bh = lid / a.NVB;
+    const int b = bh / s.H, h = bh % s.H;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
+    const int v0 = vb * BV, nvc = min(BV, dv - v0);
+    const double A = -exp((double)s.A_log[h]);
+    const S *q = (const S *)s.q;
+    const S *k = (const S *)s.k;
+    const S *dO = (const S *)a.dout;
+    S *dhs = (S *)a.dhs;
+    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
+
+    f32x4 accDH[Tiles<DT, VT>::PW];
+    for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+        accDH[i][e] = (a.dhT && row < dk && col < nvc) ? a.dhT[((size_t)bh * dk + row) * dv + v0 + col] : 0.f;
+    });
+    store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
+
+    for (int c = s.NC - 1; c >= 0; --c) {
+        const int t0 = c * C, n = min(C, T - t0);
+        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < dk && col < nvc)
+                dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
+        });
+        if (tid < C) {
+            const size_t gi = ((size_t)b * T + t0 + tid) * H + h;
+            gch[tid] = (tid < n) ? s.g[gi] : 0.f;
+            bet[tid] = (tid < n) ? s.beta[gi] : 0.f;
+        }
+        const size_t row0 = (size_t)b * T + t0;
+        load_chunk<BF, D>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Ks, LDD, KT, LDC, tid);
+        load_chunk<BF, D>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Qs, LDD, QT, LDC, tid);
+        load_chunk<BF, BV>(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, vecv, nullptr, 0, dOT,
+                           LDC, tid);
+        __syncthreads();
+        if (wave == 0) decay_prep(gch, A, n, lane, gam, eg, egn, misc);
+        __syncthreads();
+        // KT <- K^T diag(beta e^gam), QT <- Q^T diag(e^gam)
+        for (int e = tid; e < D * C; e += NTHR) {
+            const int d = e / C, j = e % C;
+            KT[d * LDC + j] = from_f<BF>(to_f(KT[d * LDC + j]) * bet[j] * eg[j]);
+            QT[d * LDC + j] = from_f<BF>(to_f(QT[d * LDC + j]) * eg[j]);
+        }
+        // Grams and decay mask; P stored transposed
+        {
+            f32x4 sk[4], sq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sk[i] = sq[i] = zero4();
+            if (!s.additive) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
+            gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
+            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+                const float G = (row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f;
+                Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * G : 0.f;
+                PT[col * LDC + row] = from_f<BF>(sq[i][e] * G);
+            });
+        }
+        __syncthreads();
+        // Q^T diag(e^gam) dO: independent of the chain
+        f32x4 accQD[Tiles<DT, VT>::PW];
+#pragma unroll
+        for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accQD[i] = zero4();
+        gemm<BF, DT, VT, C>(QT, LDC, dOT, LDC, accQD, wave, lane);
+        if (!s.additive) {
+            tri_inverse(Lm, Tm, xs, wave, lane); // ends with a barrier
+            for (int e = tid; e < C * C; e += NTHR) {
+                const int row = e / C, col = e % C;
+                TS[row * LDC + col] = from_f<BF>(Tm[row * LDF + col]);
+            }
+            __syncthreads();
+            // -Kw^T = -(K^T diag(beta e^gam)) Tm^T  -> over QT (QT reads done)
+            f32x4 accKw[Tiles<DT, 4>::PW];
+#pragma unroll
+            for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accKw[i] = zero4();
+            gemm<BF, DT, 4, C>(KT, LDC, TS, LDC, accKw, wave, lane);
+#pragma unroll
+            for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accKw[i] = -accKw[i];
+            store_N<BF, DT, 4>(accKw, KwT, LDC, wave, lane);
+        }
+        __syncthreads();
+        // ---- chain: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
+        {
+            f32x4 accW[Tiles<4, VT>::PW], accX[Tiles<4, VT>::PW];
+#pragma unroll
+            for (int i = 0; i < Tiles<4, VT>::PW; ++i) accW[i] = accX[i] = zero4();
+            gemm<BF, 4, VT, D>(Ks, LDD, dHT, LDD, accX, wave, lane);
+            gemm<BF, 4, VT, C>(PT, LDC, dOT, LDC, accW, wave, lane);
+            for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] += egn[row] * accX[i][e]; });
+            store_T<BF, 4, VT>(accW, dWT, LDC, wave, lane);
+        }
+        __syncthreads();
+        // ---- dh = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW
+        {
+            const float el = misc[0];
+#pragma unroll
+            for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accDH[i] = accDH[i] * el + accQD[i];
+            if (!s.additive) gemm<BF, DT, VT, C>(KwT, LDC, dWT, LDC, accDH, wave, lane);
+        }
+        __syncthreads();
+        store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
+    }
+    if (a.dh0) {
+        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < dk && col < nvc) a.dh0[((size_t)bh * dk + row) * dv + v0 + col] = accDH[i][e];
+        });
+    }
+}
+
+// --------------------------------------------------------------- local
+
+template <bool BF, int D> struct LocalSmem {
+    using S = typename Op<BF>::S;
+    static constexpr int LDD = D + Op<BF>::PAD;
+    static constexpr int LDC = C + Op<BF>::PAD;
+    static constexpr int sCD = C * LDD * (int)sizeof(S);
+    static constexpr int sDC = D * LDC * (int)sizeof(S);
+    static constexpr int sCC = C * LDC * (int)sizeof(S);
+    static constexpr int sDD = D * LDD * (int)sizeof(S);
+    static constexpr int sF = C * LDF * 4;
+    static constexpr int mx(int x, int y) { return x > y ? x : y; }
+    static constexpr int h1 = mx(mx(sDC, sDD), sCD);
+    static constexpr int oKs = 0;                        // Ks
+    static constexpr int oKT = oKs + sCD;                // KT
+    static constexpr int oPT = oKT + sDC;                // PT
+    static constexpr int oKKG = oPT + sCC;               // K K^T o Gam
+    static constexpr int oRa = oKKG + sCC;               // Qs -> TT -> dS -> dPG
+    static constexpr int szRa = mx(sCD, sCC);
+    static constexpr int oF1 = oRa + szRa;               // L | dOT,dHT | Hs,dHs | dVs,dKps | QT
+    static constexpr int szF1 = mx(sF, 2 * h1);
+    static constexpr int oF2 = oF1 + szF1;               // Tm | VT, HT -> dWs -> dKwT
+    static constexpr int szF2 = mx(sF, sDC + h1);
+    static constexpr int oRb = oF2 + szF2;               // Us
+    static constexpr int oRc = oRb + sCD;                // Kws
+    static constexpr int oRd = oRc + sCD;                // Ws
+    static constexpr int oRe = oRd + sCD;                // Tb -> dWT -> dST -> dPGT
+    static constexpr int szRe = mx(sCC, sDC);
+    static constexpr int oRf = oRe + szRe;               // Tk -> dOs
+    static constexpr int szRf = mx(sCC, sCD);
+    static constexpr int oX = oRf + szRf;                // solve scratch
+    static constexpr int oGam = oX + 4 * 16 * 17 * 4;    // double[C]
+    static constexpr int oEg = oGam + C * 8;
+    static constexpr int oEgn = oEg + C * 4;
+    static constexpr int oBet = oEgn + C * 4;
+    static constexpr int oG = oBet + C * 4;
+    static constexpr int oDgam = oG + C * 4;
+    static constexpr int oDbet = oDgam + C * 4;
+    static constexpr int oSv = oDbet + C * 4;
+    static constexpr int oPart = oSv + C * 4;            // [C][4] row/col partials
+    static constexpr int oMisc = oPart + C * 4 * 4;
+    static constexpr int SIZE = oMisc + 64;
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+// dst[row] (+)= sign * sum over the row of x, in a fixed order.
+template <int MT, int NT>
+__device__ __forceinline__ void add_rows(const f32x4 *x, float *part, float *dst, float sign, int tid,
+                                         int wave, int lane) {
+    row_partials<MT, NT>(x, part, wave, lane);
+    __syncthreads();
+    if (tid < MT * 16) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc += part[tid * NT + t];
+        dst[tid] += sign * acc;
+    }
+    __syncthreads();
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void add_cols(const f32x4 *x, float *part, float *dst, float sign, int tid,
+                                         int wave, int lane) {
+    col_partials<MT, NT>(x, part, wave, lane);
+    __syncthreads();
+    if (tid < NT * 16) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc += part[tid * MT + t];
+        dst[tid] += sign * acc;
+    }
+    __syncthreads();
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
+    using O = Op<BF>;
+    using S = typename O::S;
+    using L = LocalSmem<BF, D>;
+    constexpr int LDD = L::LDD, LDC = L::LDC;
+    constexpr int DT = D / 16;
+    constexpr int PWC = Tiles<4, 4>::PW, PWD = Tiles<4, DT>::PW;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    S *Ks = (S *)(smem + L::oKs);
+    S *KT = (S *)(smem + L::oKT);
+    S *PT = (S *)(smem + L::oPT);
+    S *KKG = (S *)(smem + L::oKKG);
+    S *Qs = (S *)(smem + L::oRa);
+    S *TT = (S *)(smem + L::oRa);
+    S *dSs = (S *)(smem + L::oRa);
+    S *dPG = (S *)(smem + L::oRa);
+    float *Lm = (float *)(smem + L::oF1);
+    S *F1a = (S *)(smem + L::oF1);
+    S *F1b = (S *)(smem + L::oF1 + L::h1);
+    float *Tm = (float *)(smem + L::oF2);
+    S *VT = (S *)(smem + L::oF2);
+    S *F2b = (S *)(smem + L::oF2 + L::sDC);
+    S *Us = (S *)(smem + L::oRb);
+    S *Kws = (S *)(smem + L::oRc);
+    S *Ws = (S *)(smem + L::oRd);
+    S *Re = (S *)(smem + L::oRe);
+    S *Rf = (S *)(smem + L::oRf);
+    float *xs = (float *)(smem + L::oX);
+    double *gam = (double *)(smem + L::oGam);
+    float *eg = (float *)(smem + L::oEg);
+    float *egn = (float *)(smem + L::oEgn);
+    float *bet = (float *)(smem + L::oBet);
+    float *gch = (float *)(smem + L::oG);
+    float *dgam = (float *)(smem + L::oDgam);
+    float *dbet = (float *)(smem + L::oDbet);
+    float *sv = (float *)(smem + L::oSv);
+    float *part = (float *)(smem + L::oPart);
+    float *misc = (float *)(smem + L::oMisc);
+
+    const SeqArgs &s = a.s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int c = lid % s.NC, bh = lid / s.NC;
+    const int b = bh / s.H, h = bh % s.H;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
+    const int t0 = c * C, n = min(C, T - t0);
+    const double A = -exp((double)s.A_log[h]);
+    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
+    const size_t row0 = (size_t)b * T + t0;
+    const S *q = (const S *)s.q + (row0 * H + h) * dk;
+    const S *k = (const S *)s.k + (row0 * H + h) * dk;
+    const S *v = (const S *)s.v + (row0 * H + h) * dv;
+    const S *dO = (const S *)a.dout + (row0 * H + h) * dv;
+    const S *hc = (const S *)a.cs + ((size_t)bh * s.NC + c) * dk * dv;
+    const S *dhc = (const S *)a.dhs + ((size_t)bh * s.NC + c) * dk * dv;
+    const bool add = s.additive != 0;
+
+    // ---- P1: K, Q, gates; Grams
+    if (tid < C) {
+        const size_t gi = (row0 + tid) * H + h;
+        gch[tid] = (tid < n) ? s.g[gi] : 0.f;
+        bet[tid] = (tid < n) ? s.beta[gi] : 0.f;
+        dgam[tid] = 0.f;
+        dbet[tid] = 0.f;
+    }
+    load_chunk<BF, D>(k, (size_t)H * dk, n, dk, veck, Ks, LDD, KT, LDC, tid);
+    load_chunk<BF, D>(q, (size_t)H * dk, n, dk, veck, Qs, LDD, nullptr, 0, tid);
+    __syncthreads();
+    if (wave == 0) decay_prep(gch, A, n, lane, gam, eg, egn, misc);
+    __syncthreads();
+    {
+        f32x4 sk[PWC], sq[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) sk[i] = sq[i] = zero4();
+        if (!add) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
+        gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
+        for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+            const float G = (row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f;
+            const float kkg = (row > col) ? sk[i][e] * G : 0.f;
+            Lm[row * LDF + col] = bet[row] * kkg;
+            KKG[row * LDC + col] = from_f<BF>(kkg);
+            PT[col * LDC + row] = from_f<BF>(sq[i][e] * G);
+        });
+    }
+    __syncthreads();
+    // ---- P2: Tm, then Tb (Re), Tk (Rf), TT (Ra)
+    if (!add) {
+        tri_inverse(Lm, Tm, xs, wave, lane);
+    } else {
+        for (int e = tid; e < C * C; e += NTHR) Tm[(e / C) * LDF + e % C] = (e / C == e % C) ? 1.f : 0.f;
+        __syncthreads();
+    }
+    for (int e = tid; e < C * C; e += NTHR) {
+        const int row = e / C, col = e % C;
+        const float t = Tm[row * LDF + col];
+        Re[row * LDC + col] = from_f<BF>(t * bet[col]);
+        Rf[row * LDC + col] = from_f<BF>(t * bet[col] * eg[col]);
+        TT[col * LDC + row] = from_f<BF>(t);
+    }
+    __syncthreads();
+    // ---- P3: U, Kw, W
+    load_chunk<BF, D>(v, (size_t)H * dv, n, dv, vecv, nullptr, 0, VT, LDC, tid);
+    load_state<BF, D>(hc, dk, dv, nullptr, F2b, LDD, tid); // h^T
+    __syncthreads();
+    f32x4 accW[PWD];
+    {
+        f32x4 accK[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accW[i] = accK[i] = zero4();
+        gemm<BF, 4, DT, C>(Re, LDC, VT, LDC, accW, wave, lane); // U
+        store_N<BF, 4, DT>(accW, Us, LDD, wave, lane);
+        if (!add) {
+            gemm<BF, 4, DT, C>(Rf, LDC, KT, LDC, accK, wave, lane); // Kw
+            store_N<BF, 4, DT>(accK, Kws, LDD, wave, lane);
+        }
+    }
+    __syncthreads();
+    if (!add) {
+        f32x4 accX[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accX[i] = zero4();
+        gemm<BF, 4, DT, D>(Kws, LDD, F2b, LDD, accX, wave, lane);
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accW[i] -= accX[i];
+    }
+    store_N<BF, 4, DT>(accW, Ws, LDD, wave, lane);
+    // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
+    load_chunk<BF, D>(dO, (size_t)H * dv, n, dv, vecv, nullptr, 0, F1a, LDC, tid); // dO^T
+    load_state<BF, D>(dhc, dk, dv, nullptr, F1b, LDD, tid);                          // dh'^T
+    __syncthreads();
+    {
+        f32x4 accdW[PWD], accX[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
+        gemm<BF, 4, DT, C>(PT, LDC, F1a, LDC, accdW, wave, lane);
+        gemm<BF, 4, DT, D>(Ks, LDD, F1b, LDD, accX, wave, lane);
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
+        store_N<BF, 4, DT>(accdW, F2b, LDD, wave, lane); // dWs over h^T (read before the barrier)
+        store_T<BF, 4, DT>(accdW, Re, LDC, wave, lane);  // dWT over Tb
+    }
+    __syncthreads();
+    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
+    load_state<BF, D>(hc, dk, dv, F1a, nullptr, LDD, tid);  // h
+    load_state<BF, D>(dhc, dk, dv, F1b, nullptr, LDD, tid); // dh'
+    load_chunk<BF, D>(dO, (size_t)H * dv, n, dv, vecv, Rf, LDD, nullptr, 0, tid); // dO
+    __syncthreads();
+    f32x4 accQ[PWD], accKd[PWD];
+#pragma unroll
+    for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
+    gemm<BF, 4, DT, D>(Rf, LDD, F1a, LDD, accQ, wave, lane); // dO h^T
+    f32x4 accM[Tiles<DT, 4>::PW];
+#pragma unroll
+    for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = zero4();
+    if (!add) gemm<BF, DT, 4, D>(F1a, LDD, F2b, LDD, accM, wave, lane); // h dW^T
+    {
+        f32x4 accKt[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
+        gemm<BF, 4, DT, D>(Ws, LDD, F1b, LDD, accKt, wave, lane); // W dh'^T
+        // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
+        f32x4 sx[PWD];
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
+            const float x = egn[row] * accKt[i][e];
+            accKd[i][e] = x;
+            sx[i][e] = x * to_f(Ks[row * LDD + col]);
+        });
+        // <h, dh'> partial sums per thread, then a fixed-order wave/workgroup sum
+        float hd = 0.f;
+        for (int e = tid; e < D * D; e += NTHR) {
+            const int i = e / D, j = e % D;
+            hd += to_f(F1a[i * LDD + j]) * to_f(F1b[i * LDD + j]);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
+        if (lane == 0) misc[4 + wave] = hd;
+        if (tid < C) sv[tid] = 0.f;
+        add_rows<4, DT>(sx, part, sv, 1.f, tid, wave, lane);
+        if (tid == 0) {
+            const float hds = (misc[4] + misc[5]) + (misc[6] + misc[7]);
+            float ssum = 0.f;
+            for (int j = 0; j < C; ++j) ssum += sv[j];
+            misc[8] = misc[0] * hds + ssum; // dgam_n contribution
+        }
+        __syncthreads();
+        if (tid < C) dgam[tid] -= sv[tid];
+        __syncthreads();
+        if (tid == 0) dgam[C - 1] += misc[8];
+    }
+    if (!add) {
+#pragma unroll
+        for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = -accM[i];
+        store_N<BF, DT, 4>(accM, F2b, LDC, wave, lane); // dKw^T over dWs
+    }
+    __syncthreads();
+    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw
+    {
+        f32x4 accV[PWD], accKp[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
+        gemm<BF, 4, DT, C>(TT, LDC, Re, LDC, accV, wave, lane);
+        if (!add) gemm<BF, 4, DT, C>(TT, LDC, F2b, LDC, accKp, wave, lane);
+        S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+        f32x4 x1[PWD], x2[PWD];
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < n && col < dv) dv_out[(size_t)row * H * dv + col] = from_f<BF>(bet[row] * accV[i][e]);
+            x1[i][e] = to_f(VT[col * LDC + row]) * accV[i][e];          // v_i . dV'_i
+            const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e];  // k_i . dK'_i
+            x2[i][e] = kk;
+            accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
+        });
+        add_rows<4, DT>(x1, part, dbet, 1.f, tid, wave, lane);
+        if (!add) {
+            row_partials<4, DT>(x2, part, wave, lane);
+            __syncthreads();
+            if (tid < C) {
+                float acc = 0.f;
+                for (int t = 0; t < DT; ++t) acc += part[tid * DT + t];
+                dbet[tid] += eg[tid] * acc;
+                dgam[tid] += bet[tid] * eg[tid] * acc;
+            }
+            __syncthreads();
+            store_N<BF, 4, DT>(accV, F1a, LDD, wave, lane);  // dV'
+            store_N<BF, 4, DT>(accKp, F1b, LDD, wave, lane); // dK'
+        }
+    }
+    __syncthreads();
+    // ---- P7: dL = -(dV' U^T + dK' Kw^T), dS
+    if (!add) {
+        f32x4 accL[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) accL[i] = zero4();
+        gemm<BF, 4, 4, D>(F1a, LDD, Us, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D>(F1b, LDD, Kws, LDD, accL, wave, lane);
+        f32x4 xb[PWC], xg[PWC];
+        for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+            const float dl = (row > col) ? -accL[i][e] : 0.f;
+            const float kkg = to_f(KKG[row * LDC + col]);
+            xb[i][e] = dl * kkg;
+            xg[i][e] = dl * bet[row] * kkg; // dL o L
+            accL[i][e] = bet[row] * dl * ((row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f);
+        });
+        add_rows<4, 4>(xb, part, dbet, 1.f, tid, wave, lane);
+        add_rows<4, 4>(xg, part, dgam, 1.f, tid, wave, lane);
+        add_cols<4, 4>(xg, part, dgam, -1.f, tid, wave, lane);
+        store_N<BF, 4, 4>(accL, dSs, LDC, wave, lane);
+        store_T<BF, 4, 4>(accL, Re, LDC, wave, lane);
+        __syncthreads();
+        // ---- P8: dK += dS K + dS^T K
+        gemm<BF, 4, DT, C>(dSs, LDC, KT, LDC, accKd, wave, lane);
+        gemm<BF, 4, DT, C>(Re, LDC, KT, LDC, accKd, wave, lane);
+        __syncthreads();
+    }
+    // ---- P9: dP = dO W^T (lower incl. diagonal), dP o Gam
+    {
+        f32x4 accP[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) accP[i] = zero4();
+        gemm<BF, 4, 4, D>(Rf, LDD, Ws, LDD, accP, wave, lane);
+        f32x4 xm[PWC];
+        for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+            const bool low = row >= col;
+            const float dp = low ? accP[i][e] : 0.f;
+            xm[i][e] = dp * to_f(PT[col * LDC + row]);
+            accP[i][e] = low ? dp * expf((float)(gam[row] - gam[col])) : 0.f;
+        });
+        add_rows<4, 4>(xm, part, dgam, 1.f, tid, wave, lane);
+        add_cols<4, 4>(xm, part, dgam, -1.f, tid, wave, lane);
+        store_N<BF, 4, 4>(accP, dPG, LDC, wave, lane);
+        store_T<BF, 4, 4>(accP, Re, LDC, wave, lane);
+        load_chunk<BF, D>(q, (size_t)H * dk, n, dk, veck, nullptr, 0, F1a, LDC, tid); // Q^T
+    }
+    __syncthreads();
+    // ---- P10: dQ, dK
+    {
+        f32x4 xq[PWD];
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
+            accQ[i][e] *= eg[row];
+            xq[i][e] = accQ[i][e] * to_f(F1a[col * LDC + row]);
+        });
+        add_rows<4, DT>(xq, part, dgam, 1.f, tid, wave, lane);
+        gemm<BF, 4, DT, C>(dPG, LDC, KT, LDC, accQ, wave, lane);
+        gemm<BF, 4, DT, C>(Re, LDC, F1a, LDC, accKd, wave, lane);
+        S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+        S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < n && col < dk) {
+                dq_out[(size_t)row * H * dk + col] = from_f<BF>(accQ[i][e]);
+                dk_out[(size_t)row * H * dk + col] = from_f<BF>(accKd[i][e]);
+            }
+        });
+    }
+    // ---- P11: dlam = reverse cumsum of dgam; dg = A dlam; dbeta; dA_log part
+    if (wave == 0) {
+        float x = dgam[lane];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_down(x, off, 64);
+            if (lane + off < 64) x += o;
+        }
+        const float dg = (float)A * x;
+        float p = (lane < n) ? gch[lane] * dg : 0.f;
+        if (lane < n) {
+            const size_t gi = (row0 + lane) * H + h;
+            a.dg[gi] = dg;
+            a.dbeta[gi] = dbet[lane];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+        if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
+    }
+}
+
+__global__ void dA_reduce_kernel(const float *__restrict__ part, float *__restrict__ dA, int B, int H,
+                                 int NC) {
+    const int h = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < NC; ++c) acc += part[((size_t)b * H + h) * NC + c];
+    dA[h] = acc;
+}
+
+// --------------------------------------------------------------- launch
+
+static int chain_vblock(bool bf16, int D) {
+    if (!bf16 && D >= 64) return 16;
+    return D >= 64 ? 32 : 16;
+}
+
+template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
+    constexpr int BV = (!BF && D >= 64) ? 16 : (D >= 64 ? 32 : 16);
+    const int grid = a.s.B * a.s.H * a.NVB;
+    hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t st) {
+    if (chain_vblock(bf16, D) * a.NVB < a.s.dv) return hipErrorInvalidValue;
+    if (bf16) {
+        switch (D) {
+        case 32: return chain_inst<true, 32>(a, st);
+        case 64: return chain_inst<true, 64>(a, st);
+        }
+    } else {
+        switch (D) {
+        case 16: return chain_inst<false, 16>(a, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hipStream_t st) {
+    const int grid = a.s.B * a.s.H * a.s.NC;
+    hipLaunchKernelGGL((bwd_local_kernel<BF, D>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st) {
+    if (bf16) {
+        switch (D) {
+        case 32: return local_inst<true, 32>(a, st);
+        case 64: return local_inst<true, 64>(a, st);
+        }
+    } else {
+        switch (D) {
+        case 16: return local_inst<false, 16>(a, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st) {
+    hipLaunchKernelGGL(dA_reduce_kernel, dim3((H + 63) / 64), dim3(64), 0, st, part, dA_log, B, H, NC);
+    return hipGetLastError();
+}
+
+bool bwd_supported(bool bf16, int D) { return bf16 ? (D == 32 || D == 64) : (D == 16); }
+
+int bwd_chain_vblock(bool bf16, int D) { return chain_vblock(bf16, D); }
+
+} // namespace gdn

@@ -1,0 +1,64 @@
+// Host-side launch interface between the C ABI (gdn_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct SeqArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *A_log, *h0;
+    int B, T, H, dk, dv, NC;
+    int additive;
+};
+
+struct FwdArgs {
+    SeqArgs s;
+    void *o;          // may be null (state-only recompute)
+    float *hT;        // may be null
+    void *cs;         // chunk states [B,H,NC,dk,dv] in operand dtype, may be null
+    int NVB;          // value-column blocks
+};
+
+struct BwdChainArgs {
+    SeqArgs s;
+    const void *dout;
+    const float *dhT; // may be null
+    void *dhs;        // [B,H,NC,dk,dv] operand dtype: gradient wrt the state after each chunk
+    float *dh0;       // may be null
+    int NVB;
+};
+
+struct BwdLocalArgs {
+    SeqArgs s;
+    const void *dout;
+    const void *cs;   // chunk-start states
+    const void *dhs;  // gradient wrt chunk-end states
+    void *dq, *dk, *dv;
+    float *dg, *dbeta;
+    float *dA_part;   // [B*H*NC]
+};
+
+struct StepArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *A_log, *h_in;
+    float *h_out;
+    void *o;
+    int N, H, dk, dv, additive;
+};
+
+// Padded head dimension the kernels are instantiated for.
+int pad_dim(int d, bool bf16);
+int fwd_vblock(int D);
+
+hipError_t launch_fwd(const FwdArgs &a, bool bf16, int D, hipStream_t st);
+hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t st);
+hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st);
+hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st);
+hipError_t launch_step(const StepArgs &a, bool bf16, hipStream_t st);
+
+bool bwd_supported(bool bf16, int D);
+
+} // namespace gdn

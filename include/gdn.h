@@ -1,0 +1,145 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) gated delta rule library, libgdn.so.
+ *
+ * What is computed. Per batch b and head h the library carries an fp32 state
+ * h in R^{dk x dv} through the gated delta rule
+ *
+ *     alpha_t = exp(g_t * A),  A = -exp(A_log[h])
+ *     h_t     = alpha_t (h_{t-1} - beta_t k_t (k_t^T h_{t-1})) + beta_t k_t v_t^T
+ *     o_t     = h_t^T q_t
+ *
+ * The recurrence is the one of "GDN & MLA Mechanism Deep-Dive" (Intuition and
+ * Math derivation, Step 4: per-head decay alpha_t = exp(g_t A) in (0,1), A kept
+ * in log space as A_log, read o_t after the write) and of "HyMo-434M
+ * documentation portal" (FIG. A0 probe and 01 GDN RECURRENCE: the delta rule
+ * with gate beta_t), whose erase term is read with the key k_t. With
+ * GDN_FLAG_ADDITIVE the erase term is off and the write/read pair of Step 4
+ * remains: h_t = alpha_t h_{t-1} + beta_t k_t v_t^T. The forward runs the
+ * chunked algorithm of Step 5 (chunk of 64 tokens solved in closed form with
+ * 64 x 64 matrices, state carried serially between chunks); results equal the
+ * serial definition above up to floating-point rounding.
+ *
+ * Layouts (all contiguous, row-major, no padding in memory):
+ *   q, k, dq, dk        [B, T, H, dk]   dtype of the call (fp32 or bf16)
+ *   v, o, do, dv        [B, T, H, dv]   dtype of the call
+ *   g, beta, dg, dbeta  [B, T, H]       fp32; g and beta are the values the
+ *                                       recurrence uses (post-sigmoid gate,
+ *                                       no sigmoid is applied here)
+ *   A_log, dA_log       [H]             fp32
+ *   h0, hT, dhT, dh0    [B, H, dk, dv]  fp32 (row i = key index)
+ *   decode (gdn_step):  q,k [N,H,dk], v,o [N,H,dv], g,beta [N,H],
+ *                       states [N,H,dk,dv]
+ * bf16 outputs are rounded to nearest even. The library applies no scaling
+ * to q and no normalisation to k.
+ *
+ * Ownership. The caller allocates every buffer, including the workspaces
+ * sized by the *_workspace_size queries; the library never allocates, frees
+ * or synchronises. All device pointers are HIP device memory; `stream` is a
+ * hipStream_t (NULL = the default stream). Work is enqueued on that stream and
+ * the call returns without waiting for it.
+ *
+ * Errors. Argument checks run before anything is enqueued; a failing call
+ * writes nothing and returns GDN_EINVAL / GDN_EUNSUPPORTED / GDN_EWORKSPACE.
+ * A failed launch returns GDN_EHIP. Faults inside kernels surface at the
+ * caller's next synchronisation. gdn_last_error_detail() gives a text for the
+ * last non-OK status of the calling thread. NaN/Inf inputs propagate.
+ * Results are bitwise reproducible for a given build, shape and device.
+ *
+ * Supported sizes: T >= 1 (a last chunk shorter than 64 is handled on chip),
+ * 1 <= dk, dv <= 128 for bf16 and <= 64 for fp32, chunk 0 or 64, base
+ * pointers 16-byte aligned, B*H < 2^31, tensors below 2^31 elements.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,       /* bad argument (size, null pointer, alignment, aliasing) */
+    GDN_EUNSUPPORTED = 2, /* valid request this build does not implement */
+    GDN_EWORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
+    GDN_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} gdn_status_t;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+/* Erase term off: h_t = alpha_t h_{t-1} + beta_t k_t v_t^T ("GDN & MLA
+ * Mechanism Deep-Dive", Step 4 write line, write key b_t = beta_t k_t). */
+#define GDN_FLAG_ADDITIVE 1u
+
+typedef struct {
+    int32_t B, T, H; /* batch, tokens, heads */
+    int32_t dk, dv;  /* key and value head dimensions */
+    int32_t dtype;   /* gdn_dtype_t of q, k, v, o, do, dq, dk, dv */
+    int32_t chunk;   /* 0 or 64 */
+    uint32_t flags;  /* 0 or GDN_FLAG_ADDITIVE */
+} gdn_shape_t;
+
+/* Bytes of device workspace gdn_fwd / gdn_bwd need for this shape (0 means
+ * ws may be NULL). Return 0 for an invalid shape as well; the call itself
+ * reports the error. */
+size_t gdn_fwd_workspace_size(const gdn_shape_t *s);
+size_t gdn_bwd_workspace_size(const gdn_shape_t *s);
+
+/* Bytes of the optional per-chunk state buffer: the state at the start of
+ * every 64-token chunk, [B, H, ceil(T/64), dk, dv] in the call's dtype.
+ * gdn_fwd fills it when given; gdn_bwd reads it instead of recomputing. */
+size_t gdn_chunk_states_size(const gdn_shape_t *s);
+
+/* Forward pass over a whole sequence ("GDN & MLA Mechanism Deep-Dive",
+ * Step 4 and Step 5).
+ *   q, k, v, g, beta, A_log  inputs (layouts above)
+ *   h0            initial state or NULL (zero state)
+ *   o             output [B,T,H,dv]
+ *   hT            final state or NULL (not written)
+ *   chunk_states  NULL, or gdn_chunk_states_size() bytes receiving the state
+ *                 at the start of every chunk (for gdn_bwd)
+ *   ws, ws_bytes  workspace of gdn_fwd_workspace_size() bytes */
+gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const float *A_log, const float *h0,
+                     void *o, float *hT, void *chunk_states, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Backward pass: gradients of sum(do * o) + sum(dhT * hT) with respect to q,
+ * k, v, g, beta, A_log and h0, by the reverse-chunk derivative of the chunked
+ * forward. Inputs are those of the gdn_fwd call; do is the upstream gradient of
+ * o, dhT that of the final state (NULL = zero).
+ *   chunk_states  NULL (recompute in the workspace) or the buffer gdn_fwd
+ *                 filled for the same inputs
+ *   dq, dk, dv    [B,T,H,*] in the call's dtype
+ *   dg, dbeta     [B,T,H] fp32
+ *   dA_log        [H] fp32, overwritten (sum over the batch)
+ *   dh0           [B,H,dk,dv] fp32 or NULL
+ *   hT            NULL, or receives the recomputed final state; only allowed
+ *                 when chunk_states is NULL
+ *   ws, ws_bytes  workspace of gdn_bwd_workspace_size() bytes */
+gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const float *A_log, const float *h0,
+                     const void *chunk_states, const void *dout, const float *dhT, void *dq,
+                     void *dk, void *dv, float *dg, float *dbeta, float *dA_log, float *dh0,
+                     float *hT, void *ws, size_t ws_bytes, void *stream);
+
+/* One decode token for each of N independent sequences: one step of the
+ * recurrence from a carried state (the O(1)-state read/write of "GDN & MLA
+ * Mechanism Deep-Dive", Intuition). h_in may be NULL (zero state) and may
+ * equal h_out (in-place update); no other aliasing is allowed. `dtype` is the
+ * gdn_dtype_t of q, k, v and o; `flags` is 0 or GDN_FLAG_ADDITIVE. */
+gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
+                      const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *A_log, const float *h_in, float *h_out,
+                      void *o, void *stream);
+
+const char *gdn_status_string(gdn_status_t st);
+const char *gdn_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

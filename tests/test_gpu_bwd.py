@@ -1,0 +1,153 @@
+"""Backward parity: HIP reverse-chunk backward vs the oracle's manual reverse
+pass of the serial loop, for every gradient, on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_74_amd as gdn
+import gdn_inputs as gi
+from gpu_util import TOL, assert_close, dev, f64, host, say
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+
+
+def _oracle():
+    import oracle
+
+    return oracle
+
+
+def with_dhT(x, seed):
+    B, _, H, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    rng = np.random.default_rng(seed)
+    x = dict(x)
+    x["dhT"] = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    if x["h0"] is None:
+        x["h0"] = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    return x
+
+
+def run_bwd(x, additive=False, use_saved=True, want_hT=False):
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log = dev(x["g"]), dev(x["beta"]), dev(x["A_log"])
+    h0, do, dhT = dev(x["h0"]), dev(x["do"]), dev(x.get("dhT"))
+    cs = None
+    if use_saved:
+        _, _, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_chunk_states=True,
+                           want_hT=False)
+    r = gdn.bwd(q, k, v, g, beta, A_log, do, h0, dhT, chunk_states=cs, additive=additive,
+                want_hT=want_hT)
+    torch.cuda.synchronize()
+    return r
+
+
+def check_bwd(x, dtype, additive=False, units=None, tol=None, use_saved=True):
+    tol = tol or TOL[dtype]
+    r = run_bwd(x, additive, use_saved)
+    ref = _oracle().bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                        f64(x["A_log"]), f64(x["h0"]), f64(x["do"]), f64(x.get("dhT")),
+                        delta=not additive, units=units)
+    got = {kk: host(vv) for kk, vv in r.items() if vv is not None}
+    if units is None:
+        for name in GRADS:
+            assert_close(name, got[name], ref[name], tol)
+        assert_close("dA_log", got["dA_log"], ref["dA_log"], tol)
+    else:
+        H = got["dq"].shape[2]
+        for u in units:
+            b, h = divmod(u, H)
+            for name in ["dq", "dk", "dv", "dg", "dbeta"]:
+                assert_close(f"{name}[{b},:,{h}]", got[name][b, :, h], ref[name][b, :, h], tol)
+            assert_close(f"dh0[{b},{h}]", got["dh0"][b, h], ref["dh0"][b, h], tol)
+        # dA_log[h] = sum_{b,t} g dg holds for any size; check it on the GPU outputs
+        ident = np.sum(f64(x["g"]) * got["dg"], axis=(0, 1))
+        assert_close("dA_log vs sum g*dg", got["dA_log"], ident, 1e-3)
+    return r
+
+
+def test_pr1_shape_fp32():
+    say("bwd fp32 B1 H2 T128 d16")
+    x = gi.gen_config("pr1_ref", decay="weak", h0="randn", with_do=True)
+    check_bwd(with_dhT(x, 1), "f32")
+
+
+@pytest.mark.parametrize("decay", ["normal", "weak", "zero"])
+def test_fp32_decays(decay):
+    say(f"bwd fp32 d16 decay={decay}")
+    x = gi.gen_seq(2, 150, 2, 16, 16, "f32", seed=1001, h0="randn", with_do=True, decay=decay)
+    check_bwd(with_dhT(x, 2), "f32")
+
+
+@pytest.mark.parametrize("decay", ["normal", "weak", "zero"])
+def test_model_shape_reduced_bf16(decay):
+    say(f"bwd bf16 B2 T200 H3 d56 decay={decay}")
+    x = gi.gen_seq(2, 200, 3, 56, 56, "bf16", seed=1002, h0="randn", with_do=True, decay=decay)
+    check_bwd(with_dhT(x, 3), "bf16")
+
+
+def test_additive_fp32_and_bf16():
+    x = gi.gen_seq(1, 140, 2, 16, 16, "f32", seed=1003, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 4), "f32", additive=True)
+    x = gi.gen_seq(1, 140, 2, 56, 56, "bf16", seed=1004, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 5), "bf16", additive=True)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+def test_ragged_lengths_bf16(T):
+    say(f"bwd bf16 T={T}")
+    x = gi.gen_seq(1, T, 2, 56, 56, "bf16", seed=1100 + T, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 6), "bf16")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 64), (48, 24), (5, 9)])
+def test_head_dims_bf16(dk, dv):
+    say(f"bwd bf16 dk={dk} dv={dv}")
+    x = gi.gen_seq(1, 130, 2, dk, dv, "bf16", seed=1200 + dk, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 7), "bf16")
+
+
+def test_recompute_path_equals_saved_states_path():
+    x = with_dhT(gi.gen_seq(2, 200, 2, 56, 56, "bf16", seed=1300, h0="randn", with_do=True,
+                            decay="weak"), 8)
+    a = run_bwd(x, use_saved=True)
+    b = run_bwd(x, use_saved=False, want_hT=True)
+    for name in GRADS + ["dA_log"]:
+        assert torch.equal(a[name], b[name]), name
+    _, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                          f64(x["A_log"]), f64(x["h0"]))
+    assert_close("recomputed hT", host(b["hT"]), rh, TOL["bf16"])
+
+
+def test_bitwise_deterministic():
+    x = with_dhT(gi.gen_seq(2, 300, 3, 56, 56, "bf16", seed=1301, h0="randn", with_do=True,
+                            decay="weak"), 9)
+    a = run_bwd(x)
+    b = run_bwd(x)
+    for name in GRADS + ["dA_log"]:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_autograd_function():
+    x = gi.gen_seq(1, 100, 2, 56, 56, "bf16", seed=1302, h0="randn", with_do=True, decay="weak")
+    ts = {kk: dev(x[kk]).requires_grad_(kk not in ("do",)) for kk in
+          ("q", "k", "v", "g", "beta", "A_log", "h0")}
+    o, hT = gdn.GatedDeltaRule.apply(ts["q"], ts["k"], ts["v"], ts["g"], ts["beta"], ts["A_log"],
+                                     ts["h0"])
+    o.backward(dev(x["do"]))
+    ref = _oracle().bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                        f64(x["A_log"]), f64(x["h0"]), f64(x["do"]), None)
+    for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
+                      ("A_log", "dA_log"), ("h0", "dh0")]:
+        assert_close(f"autograd {key}", host(ts[name].grad), ref[key], TOL["bf16"])
+
+
+@pytest.mark.parametrize("decay", ["normal", "weak"])
+def test_full_size_fwdbwd_sampled(decay):
+    """B8 H16 T4096 d56 bf16 at full size with the launch configuration the
+    benchmark times (saved chunk states); oracle on sampled (b, h) units."""
+    say(f"bwd full fwdbwd_model decay={decay}")
+    x = gi.gen_config("fwdbwd_model", decay=decay)
+    check_bwd(x, "bf16", units=[0, 45, 90, 127])

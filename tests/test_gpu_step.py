@@ -1,0 +1,90 @@
+"""Decode-step parity: chains of HIP single-token steps vs the oracle's step
+chain on the same seeded tokens and initial state."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_74_amd as gdn
+import gdn_inputs as gi
+from gpu_util import TOL, assert_close, dev, f64, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle():
+    import oracle
+
+    return oracle
+
+
+def run_chain(x, steps, additive=False, inplace=True, zero_start=False):
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log = dev(x["g"]), dev(x["beta"]), dev(x["A_log"])
+    h = None if zero_start else dev(x["h0"]).clone()
+    outs = []
+    for t in range(steps):
+        if inplace and h is not None:
+            o, h = gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, h, additive=additive)
+        else:
+            o, h = gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, None, additive=additive)
+        outs.append(o)
+    torch.cuda.synchronize()
+    return [host(o) for o in outs], host(h)
+
+
+def check_chain(x, steps, dtype, additive=False, inplace=True, zero_start=False):
+    got_o, got_h = run_chain(x, steps, additive, inplace, zero_start)
+    h = None if zero_start else f64(x["h0"])
+    tol = TOL[dtype]
+    for t in range(steps):
+        ro, h = _oracle().step(f64(x["q"])[t], f64(x["k"])[t], f64(x["v"])[t], f64(x["g"])[t],
+                               f64(x["beta"])[t], f64(x["A_log"]), h, delta=not additive)
+        if t in (0, steps // 2, steps - 1):
+            assert_close(f"o step {t}", got_o[t], ro, tol)
+    assert_close("final state", got_h, h, tol)
+
+
+@pytest.mark.parametrize("decay", ["normal", "weak", "zero"])
+def test_decode_reduced_bf16(decay):
+    say(f"step bf16 N8 H16 d56 decay={decay}")
+    x = gi.gen_decode(8, 16, 56, 56, 32, "bf16", decay=decay)
+    check_chain(x, 32, "bf16")
+
+
+def test_decode_full_width_bf16():
+    """The decode workload's full width (256 sequences x 16 heads x d56)."""
+    say("step bf16 N256 H16 d56, 8 steps")
+    x = gi.gen_decode(256, 16, 56, 56, 8, "bf16")
+    check_chain(x, 8, "bf16")
+
+
+@pytest.mark.parametrize("inplace", [True, False])
+def test_decode_fp32(inplace):
+    x = gi.gen_decode(4, 3, 16, 16, 20, "f32", decay="weak")
+    check_chain(x, 20, "f32", inplace=inplace)
+
+
+def test_decode_additive_and_zero_start():
+    x = gi.gen_decode(4, 3, 56, 56, 10, "bf16", decay="weak")
+    check_chain(x, 10, "bf16", additive=True)
+    check_chain(x, 10, "bf16", zero_start=True)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (100, 70), (64, 128), (5, 3)])
+def test_decode_head_dims(dk, dv):
+    say(f"step bf16 dk={dk} dv={dv}")
+    x = gi.gen_decode(4, 2, dk, dv, 6, "bf16", decay="weak")
+    check_chain(x, 6, "bf16")
+
+
+def test_decode_chain_matches_forward():
+    """1024 consecutive steps equal one forward pass over the same 1024 tokens
+    (checked against the oracle forward on one sequence)."""
+    x = gi.gen_decode(2, 2, 56, 56, 256, "bf16", decay="weak")
+    got_o, got_h = run_chain(x, 256)
+    # rearrange [steps, N, H, .] -> [N, steps, H, .]
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))
+    ro, rh = _oracle().fwd(tr(f64(x["q"])), tr(f64(x["k"])), tr(f64(x["v"])), tr(f64(x["g"])),
+                           tr(f64(x["beta"])), f64(x["A_log"]), f64(x["h0"]))
+    assert_close("o chain vs forward", tr(np.stack(got_o)), ro, TOL["bf16"])
+    assert_close("state chain vs forward", got_h, rh, TOL["bf16"])
