@@ -6,8 +6,8 @@ and passes raw pointers plus the current HIP stream through the C ABI
 declared in include/gdn.h. There is no fallback: if libgdn.so is missing the
 calls raise.
 
-    o, hT, cs = fwd(q, k, v, g, beta, A_log, h0=None, save_chunk_states=True)
-    grads     = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, chunk_states=cs)
+    o, hT, ctx = fwd(q, k, v, g, beta, A_log, h0=None, save_context=True)
+    grads      = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, context=ctx)
     o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
     o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0)
 """
@@ -19,12 +19,12 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "step", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
-           "chunk_states_size", "bwd_workspace_size"]
+           "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
-           "gdn_chunk_states_size", "gdn_status_string", "gdn_last_error_detail"]
+           "gdn_fwd_context_size", "gdn_status_string", "gdn_last_error_detail"]
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_ADDITIVE = 1
@@ -59,7 +59,7 @@ def lib():
         L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
         for f in (L.gdn_fwd, L.gdn_bwd, L.gdn_step):
             f.restype = ctypes.c_int
-        for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_chunk_states_size):
+        for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_fwd_context_size):
             f.argtypes = [S]
             f.restype = Z
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -129,9 +129,28 @@ def _check_seq(q, k, v, g, beta, A_log, h0=None):
     return B, T, H, dk, dv
 
 
-def chunk_states_size(q, v, additive=False):
+def context_size(q, v, additive=False):
     s = _shape(q, v, additive)
-    return int(lib().gdn_chunk_states_size(ctypes.byref(s)))
+    return int(lib().gdn_fwd_context_size(ctypes.byref(s)))
+
+
+def fwd_workspace_size(q, v, additive=False):
+    s = _shape(q, v, additive)
+    return int(lib().gdn_fwd_workspace_size(ctypes.byref(s)))
+
+
+def _bytes(n, dev):
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
+
+
+def context_states(context, q, v):
+    """View of the chunk-start states inside a forward context:
+    [B, H, ceil(T/64), dk, dv] in the dtype of q (for inspection/tests)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    NC = (T + 63) // 64
+    n = B * H * NC * dk * dv * q.element_size()
+    return context[:n].view(q.dtype).view(B, H, NC, dk, dv)
 
 
 def bwd_workspace_size(q, v, additive=False):
@@ -139,9 +158,10 @@ def bwd_workspace_size(q, v, additive=False):
     return int(lib().gdn_bwd_workspace_size(ctypes.byref(s)))
 
 
-def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_chunk_states=False,
-        want_hT=True, o=None, hT=None, chunk_states=None):
-    """Chunked forward. Returns (o, hT or None, chunk_states or None)."""
+def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_context=False,
+        want_hT=True, o=None, hT=None, context=None, workspace=None):
+    """Chunked forward. Returns (o, hT or None, context or None); the context
+    (a byte tensor) lets bwd() skip recomputing the forward."""
     B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
     s = _shape(q, v, additive)
     dev = q.device
@@ -151,18 +171,22 @@ def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_chunk_states=F
     if hT is None and want_hT:
         hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(hT, "hT", torch.float32, (B, H, dk, dv), dev)
-    if chunk_states is None and save_chunk_states:
-        NC = (T + 63) // 64
-        chunk_states = torch.empty((B, H, NC, dk, dv), dtype=q.dtype, device=dev)
-    _need(chunk_states, "chunk_states", q.dtype, None, dev)
     L = lib()
+    if context is None and save_context:
+        context = _bytes(L.gdn_fwd_context_size(ctypes.byref(s)), dev)
+    _need(context, "context", torch.uint8, None, dev)
+    if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
+        raise ValueError("context is smaller than gdn_fwd_context_size()")
+    need = int(L.gdn_fwd_workspace_size(ctypes.byref(s)))
+    if workspace is None or workspace.numel() < need:
+        workspace = _bytes(need, dev)
     st = L.gdn_fwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0), _p(o),
-                   _p(hT), _p(chunk_states), None, 0, _stream(dev))
+                   _p(hT), _p(context), _p(workspace), workspace.numel(), _stream(dev))
     _check("gdn_fwd", st)
-    return o, hT, chunk_states
+    return o, hT, context
 
 
-def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, chunk_states=None, additive=False,
+def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additive=False,
         want_dh0=True, want_hT=False, workspace=None, out=None):
     """Backward of sum(do * o) + sum(dhT * hT). Returns a dict with dq, dk,
     dv, dg, dbeta, dA_log, dh0 (or None) and hT (when want_hT)."""
@@ -170,12 +194,14 @@ def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, chunk_states=None, ad
     dev = q.device
     _need(do, "do", q.dtype, (B, T, H, dv), dev)
     _need(dhT, "dhT", torch.float32, (B, H, dk, dv), dev)
-    _need(chunk_states, "chunk_states", q.dtype, None, dev)
+    _need(context, "context", torch.uint8, None, dev)
     s = _shape(q, v, additive)
     L = lib()
+    if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
+        raise ValueError("context is smaller than gdn_fwd_context_size()")
     need = int(L.gdn_bwd_workspace_size(ctypes.byref(s)))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _bytes(need, dev)
     r = out if out is not None else {}
     r.setdefault("dq", torch.empty_like(q))
     r.setdefault("dk", torch.empty_like(k))
@@ -192,7 +218,7 @@ def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, chunk_states=None, ad
     else:
         r["hT"] = None
     st = L.gdn_bwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0),
-                   _p(chunk_states), _p(do), _p(dhT), _p(r["dq"]), _p(r["dk"]), _p(r["dv"]),
+                   _p(context), _p(do), _p(dhT), _p(r["dq"]), _p(r["dk"]), _p(r["dv"]),
                    _p(r["dg"]), _p(r["dbeta"]), _p(r["dA_log"]), _p(r["dh0"]), _p(r["hT"]),
                    _p(workspace), workspace.numel(), _stream(dev))
     _check("gdn_bwd", st)
@@ -229,12 +255,12 @@ def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=No
 
 
 class GatedDeltaRule(torch.autograd.Function):
-    """Autograd wrapper: forward saves the per-chunk states, backward reads
-    them instead of recomputing."""
+    """Autograd wrapper: forward saves its context (chunk-start states and
+    per-chunk key blocks), backward reads it instead of recomputing."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False):
-        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_chunk_states=True)
+        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_context=True)
         ctx.save_for_backward(q, k, v, g, beta, A_log, h0, cs)
         ctx.additive = additive
         return o, hT
@@ -245,6 +271,6 @@ class GatedDeltaRule(torch.autograd.Function):
         if do is None:
             do = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
         r = bwd(q, k, v, g, beta, A_log, do.contiguous(), h0,
-                None if dhT is None else dhT.contiguous(), chunk_states=cs,
+                None if dhT is None else dhT.contiguous(), context=cs,
                 additive=ctx.additive, want_dh0=h0 is not None)
         return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None

@@ -79,6 +79,14 @@ size_t states_bytes(const gdn_shape_t *s) {
     return (size_t)s->B * s->H * nchunks(s) * s->dk * s->dv * esize(s->dtype);
 }
 
+// per-chunk 64 x d blocks of U (d = dv) or NK (d = dk)
+size_t blocks_bytes(const gdn_shape_t *s, int d) {
+    return (size_t)s->B * s->H * nchunks(s) * 64 * d * esize(s->dtype);
+}
+
+// forward context = [chunk-start states | NK], each 256-byte aligned
+size_t ctx_bytes(const gdn_shape_t *s) { return align_up(states_bytes(s)) + align_up(blocks_bytes(s, s->dk)); }
+
 gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *A_log, const float *h0) {
     gdn::SeqArgs a;
@@ -110,10 +118,6 @@ gdn_status_t hip_status(hipError_t e, const char *what) {
 
 } // namespace
 
-namespace gdn {
-int bwd_chain_vblock(bool bf16, int D);
-}
-
 extern "C" {
 
 const char *gdn_status_string(gdn_status_t st) {
@@ -130,59 +134,88 @@ const char *gdn_status_string(gdn_status_t st) {
 const char *gdn_last_error_detail(void) { return g_detail; }
 
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
-    (void)s;
-    return 0;
+    if (check_shape(s) != GDN_OK) return 0;
+    return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk));
 }
 
-size_t gdn_chunk_states_size(const gdn_shape_t *s) {
+size_t gdn_fwd_context_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
-    return states_bytes(s);
+    return ctx_bytes(s);
 }
 
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
-    const size_t st = align_up(states_bytes(s));
     const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
-    return st /* recomputed chunk states */ + st /* dh per chunk */ + part;
+    return ctx_bytes(s) /* recomputed forward context */ + align_up(blocks_bytes(s, s->dv)) /* U */ +
+           align_up(states_bytes(s)) /* dh per chunk */ + part;
 }
 
+namespace {
+
+// Forward pass into caller-provided buffers: U and NK of every chunk, then
+// the serial state pass (o may be null: states only).
+hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
+                       void *o, float *hT, void *cs, hipStream_t strm) {
+    gdn::PrepArgs pa;
+    pa.s = sa;
+    pa.U = U;
+    pa.NK = NK;
+    hipError_t he = gdn::launch_fwd_prep(pa, bf, D, strm);
+    if (he != hipSuccess) return he;
+    gdn::FwdChainArgs fa;
+    fa.s = sa;
+    fa.U = U;
+    fa.NK = NK;
+    fa.o = o;
+    fa.hT = hT;
+    fa.cs = cs;
+    const int BV = gdn::fwd_vblock(D);
+    fa.NVB = (s->dv + BV - 1) / BV;
+    return gdn::launch_fwd_chain(fa, bf, D, strm);
+}
+
+} // namespace
+
 gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *A_log, const float *h0, void *o, float *hT,
-                     void *chunk_states, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
+                     const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                     void *ws, size_t ws_bytes, void *stream) {
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !g || !beta || !A_log || !o)
         return fail(GDN_EINVAL, "q, k, v, g, beta, A_log and o must not be NULL");
-    const void *vec[] = {q, k, v, o, chunk_states};
+    const void *vec[] = {q, k, v, o};
     for (const void *p : vec)
-        if (p && !aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, o, chunk_states must be 16-byte aligned");
+        if (!aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, o must be 16-byte aligned");
     const void *f32[] = {g, beta, A_log, h0, hT};
     for (const void *p : f32)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    if (ctx && !aligned(ctx, 256)) return fail(GDN_EINVAL, "ctx must be 256-byte aligned");
+    const size_t need = gdn_fwd_workspace_size(s);
+    if (!ws || ws_bytes < need)
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
     const size_t e = esize(s->dtype), BTH = (size_t)s->B * s->T * s->H;
     const size_t sb = (size_t)s->B * s->H * s->dk * s->dv * 4;
     const Range in[] = {{q, BTH * s->dk * e, "q"},     {k, BTH * s->dk * e, "k"}, {v, BTH * s->dv * e, "v"},
                         {g, BTH * 4, "g"},             {beta, BTH * 4, "beta"},   {A_log, (size_t)s->H * 4, "A_log"},
                         {h0, h0 ? sb : 0, "h0"}};
-    const Range out[] = {{o, BTH * s->dv * e, "o"}, {hT, hT ? sb : 0, "hT"},
-                         {chunk_states, chunk_states ? states_bytes(s) : 0, "chunk_states"}};
-    st = check_aliasing(in, 7, out, 3);
+    const Range out[] = {{o, BTH * s->dv * e, "o"},
+                         {hT, hT ? sb : 0, "hT"},
+                         {ctx, ctx ? ctx_bytes(s) : 0, "ctx"},
+                         {ws, need, "workspace"}};
+    st = check_aliasing(in, 7, out, 4);
     if (st != GDN_OK) return st;
-    gdn::FwdArgs a;
-    a.s = seq(s, q, k, v, g, beta, A_log, h0);
-    a.o = o;
-    a.hT = hT;
-    a.cs = chunk_states;
+    const bool bf = s->dtype == GDN_BF16;
     const int D = pad_of(s);
-    const int BV = gdn::fwd_vblock(D);
-    a.NVB = (s->dv + BV - 1) / BV;
-    return hip_status(gdn::launch_fwd(a, s->dtype == GDN_BF16, D, (hipStream_t)stream), "gdn_fwd launch");
+    char *w = (char *)ws;
+    void *U = w;
+    void *NK = ctx ? (char *)ctx + align_up(states_bytes(s)) : w + align_up(blocks_bytes(s, s->dv));
+    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
+    return hip_status(run_forward(s, sa, bf, D, U, NK, o, hT, ctx, (hipStream_t)stream), "gdn_fwd launch");
 }
 
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *A_log, const float *h0, const void *chunk_states,
+                     const float *beta, const float *A_log, const float *h0, const void *ctx,
                      const void *dout, const float *dhT, void *dq, void *dk, void *dv, float *dg,
                      float *dbeta, float *dA_log, float *dh0, float *hT, void *ws, size_t ws_bytes,
                      void *stream) {
@@ -190,18 +223,19 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !g || !beta || !A_log || !dout || !dq || !dk || !dv || !dg || !dbeta || !dA_log)
         return fail(GDN_EINVAL, "a required pointer is NULL");
-    if (chunk_states && hT) return fail(GDN_EINVAL, "hT can only be recomputed when chunk_states is NULL");
+    if (ctx && hT) return fail(GDN_EINVAL, "hT can only be recomputed when ctx is NULL");
     const bool bf = s->dtype == GDN_BF16;
     const int D = pad_of(s);
     if (!gdn::bwd_supported(bf, D))
         return fail(GDN_EUNSUPPORTED, "backward not built for %s with head dim %d", bf ? "bf16" : "fp32",
                     s->dk > s->dv ? s->dk : s->dv);
-    const void *vec[] = {q, k, v, dout, dq, dk, dv, chunk_states};
+    const void *vec[] = {q, k, v, dout, dq, dk, dv};
     for (const void *p : vec)
-        if (p && !aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, do, dq, dk, dv must be 16-byte aligned");
+        if (!aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, do, dq, dk, dv must be 16-byte aligned");
     const void *f32[] = {g, beta, A_log, h0, dhT, dg, dbeta, dA_log, dh0, hT};
     for (const void *p : f32)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    if (ctx && !aligned(ctx, 256)) return fail(GDN_EINVAL, "ctx must be 256-byte aligned");
     const size_t need = gdn_bwd_workspace_size(s);
     if (!ws || ws_bytes < need)
         return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
@@ -215,7 +249,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
                         {beta, BTH * 4, "beta"},
                         {A_log, (size_t)s->H * 4, "A_log"},
                         {h0, h0 ? sb : 0, "h0"},
-                        {chunk_states, chunk_states ? states_bytes(s) : 0, "chunk_states"},
+                        {ctx, ctx ? ctx_bytes(s) : 0, "ctx"},
                         {dout, BTH * s->dv * e, "do"},
                         {dhT, dhT ? sb : 0, "dhT"},
                         {ws, need, "workspace"}};
@@ -227,29 +261,25 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     if (st != GDN_OK) return st;
 
     hipStream_t strm = (hipStream_t)stream;
-    const size_t stb = align_up(states_bytes(s));
     char *w = (char *)ws;
-    void *cs_ws = w;
-    void *dhs = w + stb;
-    float *part = (float *)(w + 2 * stb);
+    char *wctx = w;
+    char *wU = wctx + ctx_bytes(s);
+    char *dhs = wU + align_up(blocks_bytes(s, s->dv));
+    float *part = (float *)(dhs + align_up(states_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     hipError_t he;
-    if (!chunk_states) {
-        gdn::FwdArgs fa;
-        fa.s = sa;
-        fa.o = nullptr;
-        fa.hT = hT;
-        fa.cs = cs_ws;
-        const int BV = gdn::fwd_vblock(D);
-        fa.NVB = (s->dv + BV - 1) / BV;
-        he = gdn::launch_fwd(fa, bf, D, strm);
-        if (he != hipSuccess) return hip_status(he, "gdn_bwd state recompute launch");
-        chunk_states = cs_ws;
+    if (!ctx) {
+        he = run_forward(s, sa, bf, D, wU, wctx + align_up(states_bytes(s)), nullptr, hT, wctx, strm);
+        if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
+        ctx = wctx;
     }
+    const void *cs = ctx;
+    const void *NK = (const char *)ctx + align_up(states_bytes(s));
     gdn::BwdChainArgs ca;
     ca.s = sa;
     ca.dout = dout;
     ca.dhT = dhT;
+    ca.NK = NK;
     ca.dhs = dhs;
     ca.dh0 = dh0;
     const int BVc = gdn::bwd_chain_vblock(bf, D);
@@ -259,7 +289,8 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     gdn::BwdLocalArgs la;
     la.s = sa;
     la.dout = dout;
-    la.cs = chunk_states;
+    la.cs = cs;
+    la.NK = NK;
     la.dhs = dhs;
     la.dq = dq;
     la.dk = dk;

@@ -36,25 +36,18 @@ template <bool BF, int D, int BV> struct ChainSmem {
     static constexpr int LDC = C + Op<BF>::PAD;
     static constexpr int szCD = C * LDD * (int)sizeof(S);
     static constexpr int szDC = D * LDC * (int)sizeof(S);
-    static constexpr int oK = 0;                                  // Ks [C][LDD]
-    static constexpr int oKT = oK + szCD;                         // KT [D][LDC] (scaled beta e^gam)
-    static constexpr int oQ = oKT + szDC;                         // Qs [C][LDD] -> dWT [BV][LDC]
-    static constexpr int oQT = oQ + szCD;                         // QT [D][LDC] (scaled e^gam) -> -KwT
-    static constexpr int oDOT = oQT + szDC;                       // dOT [BV][LDC]
-    static constexpr int oR1 = oDOT + BV * LDC * (int)sizeof(S);  // L fp32 -> Tm as S
-    static constexpr int szR1 = (C * LDF * 4 > szCD) ? C * LDF * 4 : szCD;
-    static constexpr int oR2 = oR1 + szR1;                        // Tm fp32
-    static constexpr int oPT = oR2 + C * LDF * 4;                 // PT [C][LDC]
+    static constexpr int oK = 0;                                  // Ks  [C][LDD]
+    static constexpr int oQ = oK + szCD;                          // Qs  [C][LDD]
+    static constexpr int oQT = oQ + szCD;                         // QT  [D][LDC] (columns * e^gam)
+    static constexpr int oNKT = oQT + szDC;                       // NKT [D][LDC] (-Kw^T)
+    static constexpr int oDOT = oNKT + szDC;                      // dOT [BV][LDC]
+    static constexpr int oPT = oDOT + BV * LDC * (int)sizeof(S);  // PT  [C][LDC]
     static constexpr int oDHT = oPT + C * LDC * (int)sizeof(S);   // dhT [BV][LDD]
-    static constexpr int oX = oDHT + BV * LDD * (int)sizeof(S);
-    static constexpr int oGam = oX + 4 * 16 * 17 * 4;
-    static constexpr int oEg = oGam + C * 8;
-    static constexpr int oEgn = oEg + C * 4;
-    static constexpr int oBet = oEgn + C * 4;
-    static constexpr int oG = oBet + C * 4;
-    static constexpr int oMisc = oG + C * 4;
+    static constexpr int oDWT = oDHT + BV * LDD * (int)sizeof(S); // dWT [BV][LDC]
+    static constexpr int oGam = oDWT + BV * LDC * (int)sizeof(S);
+    static constexpr int oEgn = oGam + C * 8;
+    static constexpr int oMisc = oEgn + C * 4;
     static constexpr int SIZE = oMisc + 16;
-    static_assert(BV * LDC <= C * LDD, "dWT must fit in Qs");
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -67,23 +60,15 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     constexpr int DT = D / 16, VT = BV / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
-    S *KT = (S *)(smem + L::oKT);
     S *Qs = (S *)(smem + L::oQ);
-    S *dWT = (S *)(smem + L::oQ);
     S *QT = (S *)(smem + L::oQT);
-    S *KwT = (S *)(smem + L::oQT);
+    S *NKT = (S *)(smem + L::oNKT);
     S *dOT = (S *)(smem + L::oDOT);
-    float *Lm = (float *)(smem + L::oR1);
-    S *TS = (S *)(smem + L::oR1);
-    float *Tm = (float *)(smem + L::oR2);
     S *PT = (S *)(smem + L::oPT);
     S *dHT = (S *)(smem + L::oDHT);
-    float *xs = (float *)(smem + L::oX);
-    double *gam = (double *)(smem + L::oGam);
-    float *eg = (float *)(smem + L::oEg);
+    S *dWT = (S *)(smem + L::oDWT);
+    double *gam2 = (double *)(smem + L::oGam);
     float *egn = (float *)(smem + L::oEgn);
-    float *bet = (float *)(smem + L::oBet);
-    float *gch = (float *)(smem + L::oG);
     float *misc = (float *)(smem + L::oMisc);
 
     const SeqArgs &s = a.s;
@@ -93,10 +78,11 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     const int b = bh / s.H, h = bh % s.H;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int v0 = vb * BV, nvc = min(BV, dv - v0);
-    const double A = -exp((double)s.A_log[h]);
+    const double A2 = -exp((double)s.A_log[h]) * LOG2E;
     const S *q = (const S *)s.q;
     const S *k = (const S *)s.k;
     const S *dO = (const S *)a.dout;
+    const S *NK = (const S *)a.NK;
     S *dhs = (S *)a.dhs;
     const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
 
@@ -106,84 +92,70 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     });
     store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
 
-    for (int c = s.NC - 1; c >= 0; --c) {
+    ChunkFrag<BF, D> fk, fq, fn;
+    ChunkFrag<BF, BV> fo;
+    float pg = 0.f;
+    auto fetch = [&](int c) {
         const int t0 = c * C, n = min(C, T - t0);
+        const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
+        fk.fetch(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
+        fq.fetch(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
+        fo.fetch(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, vecv, tid);
+        if (!s.additive) fn.fetch(NK + cb * C * dk, (size_t)dk, n, dk, veck, tid);
+        pg = lane < n ? s.g[(row0 + lane) * H + h] : 0.f;
+    };
+    fetch(s.NC - 1);
+
+    for (int c = s.NC - 1; c >= 0; --c) {
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc)
                 dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
         });
-        if (tid < C) {
-            const size_t gi = ((size_t)b * T + t0 + tid) * H + h;
-            gch[tid] = (tid < n) ? s.g[gi] : 0.f;
-            bet[tid] = (tid < n) ? s.beta[gi] : 0.f;
+        // every wave computes the decay of its lane's row: the transposed
+        // copy of Q (row j = lane) is scaled by e^{gam_j} while it is stored
+        const Decay dc = decay_lane(pg, A2, lane);
+        if (wave == 0) {
+            gam2[lane] = dc.gam2;
+            egn[lane] = dc.egn;
+            if (lane == 0) misc[0] = dc.eglast;
         }
-        const size_t row0 = (size_t)b * T + t0;
-        load_chunk<BF, D>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Ks, LDD, KT, LDC, tid);
-        load_chunk<BF, D>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Qs, LDD, QT, LDC, tid);
-        load_chunk<BF, BV>(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, vecv, nullptr, 0, dOT,
-                           LDC, tid);
+        fk.stash(Ks, LDD, nullptr, 0, tid);
+        fq.stash_scaled(Qs, LDD, QT, LDC, tid, dc.eg);
+        fo.stash(nullptr, 0, dOT, LDC, tid);
+        if (!s.additive) fn.stash(nullptr, 0, NKT, LDC, tid);
+        if (c > 0) fetch(c - 1);
         __syncthreads();
-        if (wave == 0) decay_prep(gch, A, n, lane, gam, eg, egn, misc);
-        __syncthreads();
-        // KT <- K^T diag(beta e^gam), QT <- Q^T diag(e^gam)
-        for (int e = tid; e < D * C; e += NTHR) {
-            const int d = e / C, j = e % C;
-            KT[d * LDC + j] = from_f<BF>(to_f(KT[d * LDC + j]) * bet[j] * eg[j]);
-            QT[d * LDC + j] = from_f<BF>(to_f(QT[d * LDC + j]) * eg[j]);
-        }
-        // Grams and decay mask; P stored transposed
+
+        // P^T and Q^T diag(e^gam) dO: independent of the chain
         {
-            f32x4 sk[4], sq[4];
+            f32x4 sq[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sk[i] = sq[i] = zero4();
-            if (!s.additive) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
+            for (int i = 0; i < 4; ++i) sq[i] = zero4();
             gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
             for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-                const float G = (row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f;
-                Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * G : 0.f;
-                PT[col * LDC + row] = from_f<BF>(sq[i][e] * G);
+                PT[col * LDC + row] = from_f<BF>(sq[i][e] * gamma_ij(gam2, row, col));
             });
         }
-        __syncthreads();
-        // Q^T diag(e^gam) dO: independent of the chain
         f32x4 accQD[Tiles<DT, VT>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accQD[i] = zero4();
         gemm<BF, DT, VT, C>(QT, LDC, dOT, LDC, accQD, wave, lane);
-        if (!s.additive) {
-            tri_inverse(Lm, Tm, xs, wave, lane); // ends with a barrier
-            for (int e = tid; e < C * C; e += NTHR) {
-                const int row = e / C, col = e % C;
-                TS[row * LDC + col] = from_f<BF>(Tm[row * LDF + col]);
-            }
-            __syncthreads();
-            // -Kw^T = -(K^T diag(beta e^gam)) Tm^T  -> over QT (QT reads done)
-            f32x4 accKw[Tiles<DT, 4>::PW];
+        // dW = diag(e^{gam_n - gam}) K dh' + P^T dO (P^T is read after the barrier)
+        f32x4 accW[Tiles<4, VT>::PW];
 #pragma unroll
-            for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accKw[i] = zero4();
-            gemm<BF, DT, 4, C>(KT, LDC, TS, LDC, accKw, wave, lane);
-#pragma unroll
-            for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accKw[i] = -accKw[i];
-            store_N<BF, DT, 4>(accKw, KwT, LDC, wave, lane);
-        }
+        for (int i = 0; i < Tiles<4, VT>::PW; ++i) accW[i] = zero4();
+        gemm<BF, 4, VT, D>(Ks, LDD, dHT, LDD, accW, wave, lane);
+        for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] *= egn[row]; });
         __syncthreads();
-        // ---- chain: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-        {
-            f32x4 accW[Tiles<4, VT>::PW], accX[Tiles<4, VT>::PW];
-#pragma unroll
-            for (int i = 0; i < Tiles<4, VT>::PW; ++i) accW[i] = accX[i] = zero4();
-            gemm<BF, 4, VT, D>(Ks, LDD, dHT, LDD, accX, wave, lane);
-            gemm<BF, 4, VT, C>(PT, LDC, dOT, LDC, accW, wave, lane);
-            for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] += egn[row] * accX[i][e]; });
-            store_T<BF, 4, VT>(accW, dWT, LDC, wave, lane);
-        }
+        gemm<BF, 4, VT, C>(PT, LDC, dOT, LDC, accW, wave, lane);
+        store_T<BF, 4, VT>(accW, dWT, LDC, wave, lane);
         __syncthreads();
-        // ---- dh = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW
+        // dh = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW
         {
             const float el = misc[0];
 #pragma unroll
             for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accDH[i] = accDH[i] * el + accQD[i];
-            if (!s.additive) gemm<BF, DT, VT, C>(KwT, LDC, dWT, LDC, accDH, wave, lane);
+            if (!s.additive) gemm<BF, DT, VT, C>(NKT, LDC, dWT, LDC, accDH, wave, lane);
         }
         __syncthreads();
         store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
@@ -219,12 +191,12 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int oF2 = oF1 + szF1;               // Tm | VT, HT -> dWs -> dKwT
     static constexpr int szF2 = mx(sF, sDC + h1);
     static constexpr int oRb = oF2 + szF2;               // Us
-    static constexpr int oRc = oRb + sCD;                // Kws
+    static constexpr int oRc = oRb + sCD;                // -Kw
     static constexpr int oRd = oRc + sCD;                // Ws
     static constexpr int oRe = oRd + sCD;                // Tb -> dWT -> dST -> dPGT
     static constexpr int szRe = mx(sCC, sDC);
-    static constexpr int oRf = oRe + szRe;               // Tk -> dOs
-    static constexpr int szRf = mx(sCC, sCD);
+    static constexpr int oRf = oRe + szRe;               // dOs
+    static constexpr int szRf = sCD;
     static constexpr int oX = oRf + szRf;                // solve scratch
     static constexpr int oGam = oX + 4 * 16 * 17 * 4;    // double[C]
     static constexpr int oEg = oGam + C * 8;
@@ -325,7 +297,19 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     const S *dO = (const S *)a.dout + (row0 * H + h) * dv;
     const S *hc = (const S *)a.cs + ((size_t)bh * s.NC + c) * dk * dv;
     const S *dhc = (const S *)a.dhs + ((size_t)bh * s.NC + c) * dk * dv;
+    const S *nk = (const S *)a.NK + ((size_t)bh * s.NC + c) * C * dk;
     const bool add = s.additive != 0;
+
+    // all global inputs of the chunk are requested up front
+    ChunkFrag<BF, D> fk, fq, fv, fo, fn;
+    ChunkFrag<BF, D, D> fh, fd;
+    fk.fetch(k, (size_t)H * dk, n, dk, veck, tid);
+    fq.fetch(q, (size_t)H * dk, n, dk, veck, tid);
+    fv.fetch(v, (size_t)H * dv, n, dv, vecv, tid);
+    fo.fetch(dO, (size_t)H * dv, n, dv, vecv, tid);
+    if (!add) fn.fetch(nk, (size_t)dk, n, dk, veck, tid);
+    fh.fetch(hc, (size_t)dv, dk, dv, vecv, tid);
+    fd.fetch(dhc, (size_t)dv, dk, dv, vecv, tid);
 
     // ---- P1: K, Q, gates; Grams
     if (tid < C) {
@@ -335,10 +319,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         dgam[tid] = 0.f;
         dbet[tid] = 0.f;
     }
-    load_chunk<BF, D>(k, (size_t)H * dk, n, dk, veck, Ks, LDD, KT, LDC, tid);
-    load_chunk<BF, D>(q, (size_t)H * dk, n, dk, veck, Qs, LDD, nullptr, 0, tid);
-    __syncthreads();
-    if (wave == 0) decay_prep(gch, A, n, lane, gam, eg, egn, misc);
+    if (wave == 0) {
+        const Decay dc = decay_lane(gch[lane], A * LOG2E, lane);
+        gam[lane] = dc.gam2;
+        eg[lane] = dc.eg;
+        egn[lane] = dc.egn;
+        if (lane == 0) misc[0] = dc.eglast;
+    }
+    fk.stash(Ks, LDD, KT, LDC, tid);
+    fq.stash(Qs, LDD, nullptr, 0, tid);
     __syncthreads();
     {
         f32x4 sk[PWC], sq[PWC];
@@ -347,7 +336,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         if (!add) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
         gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            const float G = (row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f;
+            const float G = gamma_ij(gam, row, col);
             const float kkg = (row > col) ? sk[i][e] * G : 0.f;
             Lm[row * LDF + col] = bet[row] * kkg;
             KKG[row * LDC + col] = from_f<BF>(kkg);
@@ -355,50 +344,32 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         });
     }
     __syncthreads();
-    // ---- P2: Tm, then Tb (Re), Tk (Rf), TT (Ra)
+    // ---- P2: Tm with Tb = Tm diag(beta) (Re) and TT = Tm^T (Ra)
     if (!add) {
-        tri_inverse(Lm, Tm, xs, wave, lane);
+        tri_inverse<BF>(Lm, Tm, xs, wave, lane, Re, nullptr, TT, LDC, bet, nullptr);
     } else {
-        for (int e = tid; e < C * C; e += NTHR) Tm[(e / C) * LDF + e % C] = (e / C == e % C) ? 1.f : 0.f;
+        for (int e = tid; e < C * C; e += NTHR) {
+            const int row = e / C, col = e % C;
+            Re[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
+            TT[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
+        }
         __syncthreads();
     }
-    for (int e = tid; e < C * C; e += NTHR) {
-        const int row = e / C, col = e % C;
-        const float t = Tm[row * LDF + col];
-        Re[row * LDC + col] = from_f<BF>(t * bet[col]);
-        Rf[row * LDC + col] = from_f<BF>(t * bet[col] * eg[col]);
-        TT[col * LDC + row] = from_f<BF>(t);
-    }
-    __syncthreads();
     // ---- P3: U, Kw, W
-    load_chunk<BF, D>(v, (size_t)H * dv, n, dv, vecv, nullptr, 0, VT, LDC, tid);
-    load_state<BF, D>(hc, dk, dv, nullptr, F2b, LDD, tid); // h^T
+    fv.stash(nullptr, 0, VT, LDC, tid);
+    fh.stash(nullptr, 0, F2b, LDD, tid); // h^T
+    if (!add) fn.stash(Kws, LDD, nullptr, 0, tid); // -Kw
     __syncthreads();
     f32x4 accW[PWD];
-    {
-        f32x4 accK[PWD];
 #pragma unroll
-        for (int i = 0; i < PWD; ++i) accW[i] = accK[i] = zero4();
-        gemm<BF, 4, DT, C>(Re, LDC, VT, LDC, accW, wave, lane); // U
-        store_N<BF, 4, DT>(accW, Us, LDD, wave, lane);
-        if (!add) {
-            gemm<BF, 4, DT, C>(Rf, LDC, KT, LDC, accK, wave, lane); // Kw
-            store_N<BF, 4, DT>(accK, Kws, LDD, wave, lane);
-        }
-    }
-    __syncthreads();
-    if (!add) {
-        f32x4 accX[PWD];
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accX[i] = zero4();
-        gemm<BF, 4, DT, D>(Kws, LDD, F2b, LDD, accX, wave, lane);
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accW[i] -= accX[i];
-    }
+    for (int i = 0; i < PWD; ++i) accW[i] = zero4();
+    gemm<BF, 4, DT, C>(Re, LDC, VT, LDC, accW, wave, lane); // U
+    store_N<BF, 4, DT>(accW, Us, LDD, wave, lane);
+    if (!add) gemm<BF, 4, DT, D>(Kws, LDD, F2b, LDD, accW, wave, lane); // W = U - Kw h
     store_N<BF, 4, DT>(accW, Ws, LDD, wave, lane);
     // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-    load_chunk<BF, D>(dO, (size_t)H * dv, n, dv, vecv, nullptr, 0, F1a, LDC, tid); // dO^T
-    load_state<BF, D>(dhc, dk, dv, nullptr, F1b, LDD, tid);                          // dh'^T
+    fo.stash(nullptr, 0, F1a, LDC, tid); // dO^T
+    fd.stash(nullptr, 0, F1b, LDD, tid); // dh'^T
     __syncthreads();
     {
         f32x4 accdW[PWD], accX[PWD];
@@ -412,9 +383,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     }
     __syncthreads();
     // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
-    load_state<BF, D>(hc, dk, dv, F1a, nullptr, LDD, tid);  // h
-    load_state<BF, D>(dhc, dk, dv, F1b, nullptr, LDD, tid); // dh'
-    load_chunk<BF, D>(dO, (size_t)H * dv, n, dv, vecv, Rf, LDD, nullptr, 0, tid); // dO
+    fh.stash(F1a, LDD, nullptr, 0, tid); // h
+    fd.stash(F1b, LDD, nullptr, 0, tid); // dh'
+    fo.stash(Rf, LDD, nullptr, 0, tid);  // dO
     __syncthreads();
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
@@ -491,12 +462,14 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                 dgam[tid] += bet[tid] * eg[tid] * acc;
             }
             __syncthreads();
-            store_N<BF, 4, DT>(accV, F1a, LDD, wave, lane);  // dV'
+#pragma unroll
+            for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
+            store_N<BF, 4, DT>(accV, F1a, LDD, wave, lane);  // -dV'
             store_N<BF, 4, DT>(accKp, F1b, LDD, wave, lane); // dK'
         }
     }
     __syncthreads();
-    // ---- P7: dL = -(dV' U^T + dK' Kw^T), dS
+    // ---- P7: dL = -(dV' U^T + dK' Kw^T) = (-dV') U^T + dK' (-Kw)^T, dS
     if (!add) {
         f32x4 accL[PWC];
 #pragma unroll
@@ -505,11 +478,11 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, 4, D>(F1b, LDD, Kws, LDD, accL, wave, lane);
         f32x4 xb[PWC], xg[PWC];
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            const float dl = (row > col) ? -accL[i][e] : 0.f;
+            const float dl = (row > col) ? accL[i][e] : 0.f;
             const float kkg = to_f(KKG[row * LDC + col]);
             xb[i][e] = dl * kkg;
             xg[i][e] = dl * bet[row] * kkg; // dL o L
-            accL[i][e] = bet[row] * dl * ((row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f);
+            accL[i][e] = bet[row] * dl * gamma_ij(gam, row, col);
         });
         add_rows<4, 4>(xb, part, dbet, 1.f, tid, wave, lane);
         add_rows<4, 4>(xg, part, dgam, 1.f, tid, wave, lane);
@@ -533,13 +506,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             const bool low = row >= col;
             const float dp = low ? accP[i][e] : 0.f;
             xm[i][e] = dp * to_f(PT[col * LDC + row]);
-            accP[i][e] = low ? dp * expf((float)(gam[row] - gam[col])) : 0.f;
+            accP[i][e] = low ? dp * gamma_ij(gam, row, col) : 0.f;
         });
         add_rows<4, 4>(xm, part, dgam, 1.f, tid, wave, lane);
         add_cols<4, 4>(xm, part, dgam, -1.f, tid, wave, lane);
         store_N<BF, 4, 4>(accP, dPG, LDC, wave, lane);
         store_T<BF, 4, 4>(accP, Re, LDC, wave, lane);
-        load_chunk<BF, D>(q, (size_t)H * dk, n, dk, veck, nullptr, 0, F1a, LDC, tid); // Q^T
+        fq.stash(nullptr, 0, F1a, LDC, tid); // Q^T
     }
     __syncthreads();
     // ---- P10: dQ, dK
@@ -582,14 +555,25 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     }
 }
 
-__global__ void dA_reduce_kernel(const float *__restrict__ part, float *__restrict__ dA, int B, int H,
-                                 int NC) {
-    const int h = blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= H) return;
+// dA_log[h] = sum over (b, c) of part[b, h, c]: one workgroup per head,
+// per-thread strided sums, then a fixed tree, so the order never changes.
+__global__ __launch_bounds__(NTHR) void dA_reduce_kernel(const float *__restrict__ part,
+                                                         float *__restrict__ dA, int B, int H, int NC) {
+    __shared__ float red[NTHR];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int n = B * NC;
     float acc = 0.f;
-    for (int b = 0; b < B; ++b)
-        for (int c = 0; c < NC; ++c) acc += part[((size_t)b * H + h) * NC + c];
-    dA[h] = acc;
+    for (int i = tid; i < n; i += NTHR) {
+        const int b = i / NC, c = i % NC;
+        acc += part[((size_t)b * H + h) * NC + c];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int w = NTHR / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) dA[h] = red[0];
 }
 
 // --------------------------------------------------------------- launch
@@ -642,7 +626,7 @@ hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t
 }
 
 hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st) {
-    hipLaunchKernelGGL(dA_reduce_kernel, dim3((H + 63) / 64), dim3(64), 0, st, part, dA_log, B, H, NC);
+    hipLaunchKernelGGL(dA_reduce_kernel, dim3(H), dim3(NTHR), 0, st, part, dA_log, B, H, NC);
     return hipGetLastError();
 }
 

@@ -30,13 +30,19 @@ typedef uint16_t u16;
 
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ u16 f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) return (u16)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 with the hardware conversion (round to nearest even).
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
+
+// 2^x on the hardware exp unit (x <= 0 here; results below 2^-126 may flush
+// to zero, far below any tolerance).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr double LOG2E = 1.4426950408889634;
 
 // Operand storage: bf16 bit patterns or fp32.
 template <bool BF> struct Op;
@@ -116,12 +122,31 @@ __device__ __forceinline__ void for_tiles(int wave, int lane, F &&f) {
 
 // Store the tiles of this wave transposed: dst[col][row] (4 consecutive rows
 // per lane become 4 consecutive elements).
+// (optionally scaled per row by rs[row]).
 template <bool BF, int MT, int NT>
 __device__ __forceinline__ void store_T(const f32x4 *acc, typename Op<BF>::S *dst, int ld, int wave,
-                                        int lane) {
-    for_tiles<MT, NT>(wave, lane, [&](int i, int e, int row, int col) {
-        dst[col * ld + row] = from_f<BF>(acc[i][e]);
-    });
+                                        int lane, const float *rs = nullptr) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
+        const int t = wave + NWAVE * i;
+        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+        const int tm = t / NT, tn = t % NT;
+        const int row = tm * 16 + 4 * kq, col = tn * 16 + r;
+        f32x4 x = acc[i];
+        if (rs) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= rs[row + e];
+        }
+        if constexpr (BF) {
+            uint2 w;
+            w.x = f2bf2(x[0], x[1]);
+            w.y = f2bf2(x[2], x[3]);
+            *reinterpret_cast<uint2 *>(dst + col * ld + row) = w;
+        } else {
+            *reinterpret_cast<f32x4 *>(dst + col * ld + row) = x;
+        }
+    }
 }
 
 template <bool BF, int MT, int NT>
@@ -132,98 +157,170 @@ __device__ __forceinline__ void store_N(const f32x4 *acc, typename Op<BF>::S *ds
     });
 }
 
-// Load a C-row chunk of a [B,T,H,*] tensor (rows t0 .. t0+n-1 of one (b,h);
-// `x` points at column 0 of row t0, `rs` elements between rows, d valid
-// columns) into LDS, zero filled to C rows and DP columns. dst ([C][ldd])
-// receives it as stored, dstT ([DP][ldt]) transposed; either may be null.
-// When tscale is given the transposed copy gets row j multiplied by
-// tscale[j]. `vec` selects 16-byte global loads; the caller sets it only when
-// every row start and d are multiples of 16 bytes.
-template <bool BF, int DP>
-__device__ __forceinline__ void load_chunk(const typename Op<BF>::S *__restrict__ x, size_t rs,
-                                           int n, int d, bool vec, typename Op<BF>::S *dst,
-                                           int ldd, typename Op<BF>::S *dstT, int ldt, int tid,
-                                           const float *tscale = nullptr) {
-    using O = Op<BF>;
-    using S = typename O::S;
-    constexpr int V = O::VEC;
-    if (vec) {
-        constexpr int NG = DP / V; // vector groups per row
-        for (int it = tid; it < C * NG; it += NTHR) {
-            const int j = it / NG, cg = it % NG;
-            union {
-                uint4 u;
-                S s[V];
-            } val;
-            if (j < n && cg * V < d)
-                val.u = *reinterpret_cast<const uint4 *>(x + (size_t)j * rs + cg * V);
-            else
-                val.u = uint4{0u, 0u, 0u, 0u};
-            if (dst) *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = val.u;
+// Register fragment of an NR-row tile [NR][DP] (a chunk of a [B,T,H,*]
+// tensor, or a state matrix) in row-major global memory.
+// fetch() issues the global loads (16-byte vectors; one item = one vector of
+// one row), stash() writes the fragment to LDS straight and/or transposed.
+// Items are numbered so that consecutive lanes hold consecutive rows of the
+// same vector group: transposed LDS stores of a wave then hit consecutive
+// addresses, and straight 16-byte stores of 16 lanes cover all banks once.
+template <bool BF, int DP, int NR = C> struct ChunkFrag {
+    using S = typename Op<BF>::S;
+    static constexpr int V = Op<BF>::VEC;
+    static constexpr int NG = DP / V;
+    static constexpr int NIT = (NR * NG + NTHR - 1) / NTHR;
+    union U {
+        uint4 u;
+        S s[V];
+    };
+    U r[NIT];
+
+    // x: column 0 of row 0 of the chunk, rs: elements between rows, n valid
+    // rows, d valid columns. vec: rows start on 16-byte boundaries and d % V == 0.
+    __device__ __forceinline__ void fetch(const S *__restrict__ x, size_t rs, int n, int d, bool vec,
+                                          int tid) {
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            r[m].u = uint4{0u, 0u, 0u, 0u};
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if (j < n) {
+                if (vec) {
+                    if (cg * V < d) r[m].u = *reinterpret_cast<const uint4 *>(x + (size_t)j * rs + cg * V);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        if (cg * V + e < d) r[m].s[e] = x[(size_t)j * rs + cg * V + e];
+                }
+            }
+        }
+    }
+
+    // Like stash(), with the transposed copy scaled by `sc`; requires that
+    // every item of this thread lies in row j == lane (NR == 64).
+    __device__ __forceinline__ void stash_scaled(S *dst, int ldd, S *dstT, int ldt, int tid,
+                                                 float sc) const {
+        static_assert(NR == 64 && NTHR % 64 == 0, "row of an item must equal the lane");
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if (dst) *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = r[m].u;
+#pragma unroll
+            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = from_f<BF>(to_f(r[m].s[e]) * sc);
+        }
+    }
+
+    // dst [C][ldd] straight, dstT [DP][ldt] transposed (either may be null);
+    // the transposed copy's row j is multiplied by tscale[j] when given.
+    __device__ __forceinline__ void stash(S *dst, int ldd, S *dstT, int ldt, int tid,
+                                          const float *tscale = nullptr) const {
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if (dst) *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = r[m].u;
             if (dstT) {
                 const float sc = tscale ? tscale[j] : 1.f;
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    dstT[(cg * V + e) * ldt + j] = tscale ? from_f<BF>(to_f(val.s[e]) * sc) : val.s[e];
+                    dstT[(cg * V + e) * ldt + j] = tscale ? from_f<BF>(to_f(r[m].s[e]) * sc) : r[m].s[e];
             }
         }
-    } else {
-        for (int it = tid; it < C * DP; it += NTHR) {
-            const int j = it / DP, c = it % DP;
-            const S val = (j < n && c < d) ? x[(size_t)j * rs + c] : S(0);
-            if (dst) dst[j * ldd + c] = val;
-            if (dstT) dstT[c * ldt + j] = tscale ? from_f<BF>(to_f(val) * tscale[j]) : val;
-        }
+    }
+};
+
+// Zero the padding of a [D][ld] LDS matrix outside [d0][d1].
+template <bool BF, int D>
+__device__ __forceinline__ void zero_pad(typename Op<BF>::S *m, int ld, int d0, int d1, int tid) {
+    using S = typename Op<BF>::S;
+    if (d0 == D && d1 == D) return;
+    for (int e = tid; e < D * D; e += NTHR) {
+        const int i = e / D, j = e % D;
+        if (i >= d0 || j >= d1) m[i * ld + j] = S(0);
     }
 }
 
-// Per-chunk decay factors. lam_r = g_r * A (A = -exp(A_log)), gam_i = sum of
-// lam over the chunk up to i (fp64). Rows >= n get lam = 0, so gam stays at
-// its last valid value. Writes gam (fp64), eg = exp(gam), egn = exp(gam_last -
-// gam) and *eglast = exp(gam_last). Run by wave 0 only.
-__device__ __forceinline__ void decay_prep(const float *__restrict__ gch, double A, int n, int lane,
-                                           double *gam, float *eg, float *egn, float *eglast) {
-    double s = (lane < n) ? (double)gch[lane] * A : 0.0;
+// Per-chunk decay factors of row `lane` of a chunk. lam_r = g_r * A with
+// A = -exp(A_log); the cumulative in-chunk log-decay is kept in the log2
+// domain, gam2_i = log2(e) * sum_{r <= i} lam_r, summed in fp64 so that the
+// difference of two prefix sums keeps its precision. Rows past the end of
+// the sequence pass g = 0, so gam2 stays at its last valid value there.
+// Every wave can run this on its own copy of the gates.
+struct Decay {
+    double gam2;  // log2 of the cumulative decay up to this row
+    float eg;     // exp(gam_i)
+    float egn;    // exp(gam_last - gam_i)
+    float eglast; // exp(gam_last)
+};
+
+__device__ __forceinline__ Decay decay_lane(float g, double A2, int lane) {
+    double s = (double)g * A2;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const double o = __shfl_up(s, off, 64);
         if (lane >= off) s += o;
     }
     const double last = __shfl(s, 63, 64);
-    gam[lane] = s;
-    eg[lane] = expf((float)s);
-    egn[lane] = expf((float)(last - s));
-    if (lane == 0) *eglast = expf((float)last);
+    return Decay{s, exp2_fast((float)s), exp2_fast((float)(last - s)), exp2_fast((float)last)};
+}
+
+// Gam_ij = exp(gam_i - gam_j) for i >= j, else 0 (gam2 in LDS, log2 domain).
+__device__ __forceinline__ float gamma_ij(const double *gam2, int i, int j) {
+    return (i >= j) ? exp2_fast((float)(gam2[i] - gam2[j])) : 0.f;
 }
 
 constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 
 // T = (I + L)^{-1} for a strictly lower triangular 64 x 64 L (fp32, [C][LDF]),
-// written to Tm ([C][LDF]). Diagonal 16 x 16 blocks by forward substitution
-// (one wave each), off-diagonal blocks by block forward substitution
+// written to Tm ([C][LDF], fp32). Diagonal 16 x 16 blocks by forward
+// substitution (one wave each), off-diagonal blocks by block forward
+// substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
 // level by level (i - j = 1, 2, 3) with fp32 MFMA. xs: 4 x 16 x 17 floats.
+// Optional operand copies, written as the blocks are produced ([C][ldt]):
+//   Tb = T diag(cb), Tk = T diag(ck) (column scales), TT = T^T.
 // Ends with a barrier.
-__device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs, int wave,
-                                            int lane) {
+template <bool BF>
+__device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs, int wave, int lane,
+                                            typename Op<BF>::S *Tb, typename Op<BF>::S *Tk,
+                                            typename Op<BF>::S *TT, int ldt, const float *cb,
+                                            const float *ck) {
+    using S = typename Op<BF>::S;
     {
+        // column c of the inverse of the diagonal block, right-looking
+        // substitution: once x_i is final, fold it into every later row
+        // (independent updates, dependency depth 16)
         const int c = lane & 15, o = 16 * wave;
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == c) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < i; ++j) s -= L[(o + i) * LDF + o + j] * x[j];
-            x[i] = s;
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int rr = i + 1; rr < 16; ++rr) x[rr] -= L[(o + rr) * LDF + o + i] * x[i];
         }
         if (lane < 16) {
+            const float sb = cb ? cb[o + c] : 0.f, sk = ck ? ck[o + c] : 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Tm[(o + i) * LDF + o + c] = x[i];
+            for (int i = 0; i < 16; ++i) {
+                Tm[(o + i) * LDF + o + c] = x[i];
+                if (Tb) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
+                if (Tk) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
+                if (TT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
+            }
         }
         // zero the blocks right of the diagonal in this block row
         for (int e = lane; e < 16 * 48; e += 64) {
             const int i = e / 48, cc = e % 48 + 16 * (wave + 1);
-            if (cc < C) Tm[(o + i) * LDF + cc] = 0.f;
+            if (cc < C) {
+                if (Tb) Tb[(o + i) * ldt + cc] = S(0);
+                if (Tk) Tk[(o + i) * ldt + cc] = S(0);
+                if (TT) TT[cc * ldt + o + i] = S(0);
+            }
         }
     }
     __syncthreads();
@@ -253,8 +350,17 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
                 const float b = X[(k0 + kq) * 17 + r];
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
             }
+            const int col = 16 * bj + r;
+            const float sb = cb ? cb[col] : 0.f, sk = ck ? ck[col] : 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * kq + e) * LDF + 16 * bj + r] = -acc[e];
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * bi + 4 * kq + e;
+                const float t = -acc[e];
+                Tm[row * LDF + col] = t;
+                if (Tb) Tb[row * ldt + col] = from_f<BF>(t * sb);
+                if (Tk) Tk[row * ldt + col] = from_f<BF>(t * sk);
+                if (TT) TT[col * ldt + row] = from_f<BF>(t);
+            }
         }
         __syncthreads();
     }
@@ -298,22 +404,6 @@ __device__ __forceinline__ void col_partials(const f32x4 *x, float *part, int wa
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
         if (lane < 16) part[(tn * 16 + r) * MT + tm] = s;
-    }
-}
-
-// Load a [d0][d1] state matrix (row-major in global, element type S) into
-// LDS zero-padded to [D][D]: straight into dst ([D][ld]) and/or transposed
-// into dstT ([D][ld]).
-template <bool BF, int D>
-__device__ __forceinline__ void load_state(const typename Op<BF>::S *__restrict__ x, int d0, int d1,
-                                           typename Op<BF>::S *dst, typename Op<BF>::S *dstT,
-                                           int ld, int tid) {
-    using S = typename Op<BF>::S;
-    for (int e = tid; e < D * D; e += NTHR) {
-        const int i = e / D, j = e % D;
-        const S val = (i < d0 && j < d1) ? x[(size_t)i * d1 + j] : S(0);
-        if (dst) dst[i * ld + j] = val;
-        if (dstT) dstT[j * ld + i] = val;
     }
 }
 

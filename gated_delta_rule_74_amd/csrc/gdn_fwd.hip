@@ -3,75 +3,180 @@
 // between chunks; the closed form is the WY/UT representation of the cited
 // Gated Delta Net paper).
 //
-// One workgroup owns one (batch, head, block of BV value columns) and walks
-// the chunks in order. Columns of the state are independent, so splitting
-// d_v over workgroups multiplies the number of serial chains. Per chunk, with
-// chunk-local cumulative log-decay gam and Gam_ij = exp(gam_i - gam_j), i >= j:
+// Per chunk, with chunk-local cumulative log-decay gam and
+// Gam_ij = exp(gam_i - gam_j) for i >= j:
 //   L  = strict_lower(diag(beta) (K K^T o Gam)),   Tm = (I + L)^{-1}
 //   U  = Tm diag(beta) V,   Kw = Tm diag(beta e^gam) K
 //   W  = U - Kw h
 //   O  = diag(e^gam) Q h + ((Q K^T) o Gam) W
-//   h <- e^{gam_last} h + (diag(e^{gam_last - gam}) K)^T W
+//   h <- e^{gam_last} h + K^T diag(e^{gam_last - gam}) W
 // With the erase term off (additive write), Tm = I and W = diag(beta) V.
+//
+// Two kernels. fwd_prep does everything that does not depend on the state,
+// one workgroup per (batch, head, chunk), all chunks in parallel, and writes
+// U and NK = -Kw. fwd_chain walks the chunks in order for one (batch, head,
+// block of value columns): per chunk only Q K^T, W, O and the state update
+// remain, so the serial path is short.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-template <bool BF, int D, int BV> struct FwdSmem {
+// ------------------------------------------------------------------ prep
+
+template <bool BF, int D> struct PrepSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
+    static constexpr int mx(int x, int y) { return x > y ? x : y; }
+    static constexpr int oK = 0;                                       // Ks [C][LDD] -> Tb [C][LDC]
+    static constexpr int oKT = oK + mx(C * LDD, C * LDC) * (int)sizeof(S); // KT [D][LDC]
+    static constexpr int oVT = oKT + D * LDC * (int)sizeof(S);        // VT [D][LDC]
+    static constexpr int oL = oVT + D * LDC * (int)sizeof(S);         // L fp32 [C][LDF]
+    static constexpr int oT = oL + C * LDF * 4;                       // Tm fp32 [C][LDF]
+    static constexpr int oTk = oT + C * LDF * 4;                      // Tk [C][LDC]
+    static constexpr int oX = oTk + C * LDC * (int)sizeof(S);         // solve scratch
+    static constexpr int oGam = oX + 4 * 16 * 17 * 4;                 // double[C]
+    static constexpr int oBet = oGam + C * 8;                         // float[C]
+    static constexpr int oCk = oBet + C * 4;                          // beta e^gam
+    static constexpr int SIZE = oCk + C * 4;
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+// Store this wave's tiles of an [MT*16][NT*16] accumulator grid to a
+// row-major global matrix (rows < nr, cols < nc), times `sign`.
+template <bool BF, int MT, int NT>
+__device__ __forceinline__ void store_global(const f32x4 *acc, typename Op<BF>::S *dst, int ld, int nr,
+                                             int nc, float sign, int wave, int lane) {
+    for_tiles<MT, NT>(wave, lane, [&](int i, int e, int row, int col) {
+        if (row < nr && col < nc) dst[(size_t)row * ld + col] = from_f<BF>(sign * acc[i][e]);
+    });
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
+    using O = Op<BF>;
+    using S = typename O::S;
+    using L = PrepSmem<BF, D>;
+    constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    S *Ks = (S *)(smem + L::oK);
+    S *Tb = (S *)(smem + L::oK);
+    S *KT = (S *)(smem + L::oKT);
+    S *VT = (S *)(smem + L::oVT);
+    float *Lm = (float *)(smem + L::oL);
+    float *Tm = (float *)(smem + L::oT);
+    S *Tk = (S *)(smem + L::oTk);
+    float *xs = (float *)(smem + L::oX);
+    double *gam2 = (double *)(smem + L::oGam);
+    float *bet = (float *)(smem + L::oBet);
+    float *ck = (float *)(smem + L::oCk);
+
+    const SeqArgs &s = a.s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int c = lid % s.NC, bh = lid / s.NC;
+    const int b = bh / s.H, h = bh % s.H;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
+    const int t0 = c * C, n = min(C, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
+
+    ChunkFrag<BF, D> fk, fv;
+    fk.fetch((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
+    fv.fetch((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, vecv, tid);
+    if (wave == 0) {
+        const size_t gi = (row0 + lane) * H + h;
+        const float g = lane < n ? s.g[gi] : 0.f, be = lane < n ? s.beta[gi] : 0.f;
+        const Decay dc = decay_lane(g, -exp((double)s.A_log[h]) * LOG2E, lane);
+        gam2[lane] = dc.gam2;
+        bet[lane] = be;
+        ck[lane] = be * dc.eg;
+    }
+    fk.stash(Ks, LDD, KT, LDC, tid);
+    fv.stash(nullptr, 0, VT, LDC, tid);
+    __syncthreads();
+
+    if (!s.additive) {
+        f32x4 sk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sk[i] = zero4();
+        gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
+        for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+            Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f;
+        });
+        __syncthreads(); // L complete, Ks no longer read
+        tri_inverse<BF>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
+    } else {
+        for (int e = tid; e < C * C; e += NTHR) {
+            const int row = e / C, col = e % C;
+            Tb[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
+        }
+        __syncthreads();
+    }
+
+    const size_t cbase = (size_t)bh * s.NC + c;
+    {
+        f32x4 acc[Tiles<4, DT>::PW];
+#pragma unroll
+        for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
+        gemm<BF, 4, DT, C>(Tb, LDC, VT, LDC, acc, wave, lane);
+        store_global<BF, 4, DT>(acc, (S *)a.U + cbase * C * dv, dv, C, dv, 1.f, wave, lane);
+    }
+    if (!s.additive) {
+        f32x4 acc[Tiles<4, DT>::PW];
+#pragma unroll
+        for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
+        gemm<BF, 4, DT, C>(Tk, LDC, KT, LDC, acc, wave, lane);
+        store_global<BF, 4, DT>(acc, (S *)a.NK + cbase * C * dk, dk, C, dk, -1.f, wave, lane);
+    }
+}
+
+// ----------------------------------------------------------------- chain
+
+template <bool BF, int D, int BV> struct FwdChainSmem {
+    using S = typename Op<BF>::S;
+    static constexpr int LDD = D + Op<BF>::PAD;
+    static constexpr int LDC = C + Op<BF>::PAD;
+    static constexpr int LDV = BV + Op<BF>::PAD;
     static constexpr int szCD = C * LDD * (int)sizeof(S);
-    static constexpr int oK = 0;                                   // Ks  [C][LDD]
-    static constexpr int oKT = oK + szCD;                          // KTs [D][LDC] (later scaled)
-    static constexpr int oQ = oKT + D * LDC * (int)sizeof(S);      // Qs  [C][LDD]
-    static constexpr int oVT = oQ + szCD;                          // VTs [BV][LDC]
-    static constexpr int oR1 = oVT + BV * LDC * (int)sizeof(S);    // L fp32 -> Tb -> Kw
-    static constexpr int szR1 = (C * LDF * 4 > szCD) ? C * LDF * 4 : szCD;
-    static constexpr int oR2 = oR1 + szR1;                         // Tm fp32 -> Tk
-    static constexpr int oP = oR2 + C * LDF * 4;                   // Ps  [C][LDC]
-    static constexpr int oHT = oP + C * LDC * (int)sizeof(S);      // hTs [BV][LDD]
-    static constexpr int oWT = oHT + BV * LDD * (int)sizeof(S);    // WTs [BV][LDC]
-    static constexpr int oX = oWT + BV * LDC * (int)sizeof(S);     // solve scratch
-    static constexpr int oGam = oX + 4 * 16 * 17 * 4;              // double[C]
-    static constexpr int oEg = oGam + C * 8;                       // float[C]
+    static constexpr int oK = 0;                                  // Ks  [C][LDD]
+    static constexpr int oKT = oK + szCD;                         // KT  [D][LDC]
+    static constexpr int oQ = oKT + D * LDC * (int)sizeof(S);     // Qs  [C][LDD]
+    static constexpr int oNK = oQ + szCD;                         // NKs [C][LDD]  (-Kw)
+    static constexpr int oU = oNK + szCD;                         // Us  [C][LDV]
+    static constexpr int oP = oU + C * LDV * (int)sizeof(S);      // Ps  [C][LDC]
+    static constexpr int oHT = oP + C * LDC * (int)sizeof(S);     // hTs [BV][LDD]
+    static constexpr int oWT = oHT + BV * LDD * (int)sizeof(S);   // WT  [BV][LDC]
+    static constexpr int oWTd = oWT + BV * LDC * (int)sizeof(S);  // WTd [BV][LDC] (rows * e^{gam_n-gam})
+    static constexpr int oGam = oWTd + BV * LDC * (int)sizeof(S); // double[C]
+    static constexpr int oEg = oGam + C * 8;
     static constexpr int oEgn = oEg + C * 4;
-    static constexpr int oBet = oEgn + C * 4;
-    static constexpr int oG = oBet + C * 4;
-    static constexpr int oMisc = oG + C * 4;
+    static constexpr int oMisc = oEgn + C * 4;
     static constexpr int SIZE = oMisc + 16;
-    static_assert(C * LDC * (int)sizeof(S) <= szR1, "Tb must fit in R1");
-    static_assert(C * LDC * (int)sizeof(S) <= C * LDF * 4, "Tk must fit in R2");
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
 template <bool BF, int D, int BV>
-__global__ __launch_bounds__(NTHR) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
-    using L = FwdSmem<BF, D, BV>;
-    constexpr int LDD = L::LDD, LDC = L::LDC;
+    using L = FwdChainSmem<BF, D, BV>;
+    constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
     constexpr int DT = D / 16, VT = BV / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
-    S *KTs = (S *)(smem + L::oKT);
+    S *KT = (S *)(smem + L::oKT);
     S *Qs = (S *)(smem + L::oQ);
-    S *VTs = (S *)(smem + L::oVT);
-    float *Lm = (float *)(smem + L::oR1);
-    S *Tb = (S *)(smem + L::oR1);
-    S *Kws = (S *)(smem + L::oR1);
-    float *Tm = (float *)(smem + L::oR2);
-    S *Tk = (S *)(smem + L::oR2);
+    S *NKs = (S *)(smem + L::oNK);
+    S *Us = (S *)(smem + L::oU);
     S *Ps = (S *)(smem + L::oP);
     S *hTs = (S *)(smem + L::oHT);
-    S *WTs = (S *)(smem + L::oWT);
-    float *xs = (float *)(smem + L::oX);
-    double *gam = (double *)(smem + L::oGam);
+    S *WT = (S *)(smem + L::oWT);
+    S *WTd = (S *)(smem + L::oWTd);
+    double *gam2 = (double *)(smem + L::oGam);
     float *eg = (float *)(smem + L::oEg);
     float *egn = (float *)(smem + L::oEgn);
-    float *bet = (float *)(smem + L::oBet);
-    float *gch = (float *)(smem + L::oG);
     float *misc = (float *)(smem + L::oMisc);
 
     const SeqArgs &s = a.s;
@@ -80,12 +185,12 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdArgs a) {
     const int vb = lid % a.NVB, bh = lid / a.NVB;
     const int b = bh / s.H, h = bh % s.H;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
-    const int v0 = vb * BV;
-    const int nvc = min(BV, dv - v0); // valid value columns of this block
-    const double A = -exp((double)s.A_log[h]);
+    const int v0 = vb * BV, nvc = min(BV, dv - v0);
+    const double A2 = -exp((double)s.A_log[h]) * LOG2E;
     const S *q = (const S *)s.q;
     const S *k = (const S *)s.k;
-    const S *v = (const S *)s.v;
+    const S *U = (const S *)a.U;
+    const S *NK = (const S *)a.NK;
     S *o = (S *)a.o;
     S *cs = (S *)a.cs;
     const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
@@ -93,127 +198,87 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdArgs a) {
     // state h[D][BV] (fp32) lives in the accumulators of the h-update product
     f32x4 accH[Tiles<DT, VT>::PW];
     for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-        accH[i][e] = (s.h0 && row < dk && col < nvc)
-                         ? s.h0[((size_t)bh * dk + row) * dv + v0 + col]
-                         : 0.f;
+        accH[i][e] = (s.h0 && row < dk && col < nvc) ? s.h0[((size_t)bh * dk + row) * dv + v0 + col] : 0.f;
     });
     store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
 
+    // inputs of the next chunk are fetched into registers during this one
+    ChunkFrag<BF, D> fk, fq, fn;
+    ChunkFrag<BF, BV> fu;
+    float pg = 0.f;
+    auto fetch = [&](int c) {
+        const int t0 = c * C, n = min(C, T - t0);
+        const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
+        fk.fetch(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
+        fq.fetch(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
+        if (!s.additive) fn.fetch(NK + cb * C * dk, (size_t)dk, n, dk, veck, tid);
+        fu.fetch(U + cb * C * dv + v0, (size_t)dv, n, nvc, vecv, tid);
+        if (wave == 0) pg = lane < n ? s.g[(row0 + lane) * H + h] : 0.f;
+    };
+    fetch(0);
+
     for (int c = 0; c < s.NC; ++c) {
         const int t0 = c * C, n = min(C, T - t0);
+        const size_t row0 = (size_t)b * T + t0;
         if (cs) {
             for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
                 if (row < dk && col < nvc)
                     cs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accH[i][e]);
             });
         }
-        // ---- load the chunk
-        if (tid < C) {
-            const size_t gi = ((size_t)b * T + t0 + tid) * H + h;
-            gch[tid] = (tid < n) ? s.g[gi] : 0.f;
-            bet[tid] = (tid < n) ? s.beta[gi] : 0.f;
+        if (wave == 0) {
+            const Decay dc = decay_lane(pg, A2, lane);
+            gam2[lane] = dc.gam2;
+            eg[lane] = dc.eg;
+            egn[lane] = dc.egn;
+            if (lane == 0) misc[0] = dc.eglast;
         }
-        const size_t row0 = (size_t)b * T + t0;
-        load_chunk<BF, D>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Ks, LDD, KTs, LDC, tid);
-        load_chunk<BF, D>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, Qs, LDD, nullptr, 0, tid);
-        load_chunk<BF, BV>(v + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, vecv, nullptr, 0, VTs,
-                           LDC, tid);
-        __syncthreads();
-        if (wave == 0) decay_prep(gch, A, n, lane, gam, eg, egn, misc);
+        fk.stash(Ks, LDD, KT, LDC, tid);
+        fq.stash(Qs, LDD, nullptr, 0, tid);
+        if (!s.additive) fn.stash(NKs, LDD, nullptr, 0, tid);
+        fu.stash(Us, LDV, nullptr, 0, tid);
+        if (c + 1 < s.NC) fetch(c + 1);
         __syncthreads();
 
-        // ---- Gram products, decay mask
+        // P = (Q K^T) o Gam (independent of the state)
         {
-            f32x4 sk[4], sq[4];
+            f32x4 sq[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sk[i] = sq[i] = zero4();
-            if (!s.additive) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
+            for (int i = 0; i < 4; ++i) sq[i] = zero4();
             gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
             for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-                const float G = (row >= col) ? expf((float)(gam[row] - gam[col])) : 0.f;
-                Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * G : 0.f;
-                Ps[row * LDC + col] = from_f<BF>(sq[i][e] * G);
+                Ps[row * LDC + col] = from_f<BF>(sq[i][e] * gamma_ij(gam2, row, col));
             });
         }
-        __syncthreads();
-
-        // ---- Tm = (I + L)^{-1}
-        if (!s.additive) {
-            tri_inverse(Lm, Tm, xs, wave, lane);
-        } else {
-            for (int e = tid; e < C * C; e += NTHR) Tm[(e / C) * LDF + e % C] = (e / C == e % C) ? 1.f : 0.f;
-            __syncthreads();
-        }
-        // Tb = Tm diag(beta) into R1, then Tk = Tm diag(beta e^gam) in place over Tm
+        // W = U - Kw h (serial chain, part 1)
         {
-            float tv[C * C / NTHR];
-#pragma unroll
-            for (int m = 0; m < C * C / NTHR; ++m) {
-                const int e = tid + m * NTHR, row = e / C, col = e % C;
-                tv[m] = Tm[row * LDF + col];
-                Tb[row * LDC + col] = from_f<BF>(tv[m] * bet[col]);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int m = 0; m < C * C / NTHR; ++m) {
-                const int e = tid + m * NTHR, row = e / C, col = e % C;
-                Tk[row * LDC + col] = from_f<BF>(tv[m] * bet[col] * eg[col]);
-            }
+            f32x4 accW[Tiles<4, VT>::PW];
+            for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(Us[row * LDV + col]); });
+            if (!s.additive) gemm<BF, 4, VT, D>(NKs, LDD, hTs, LDD, accW, wave, lane);
+            store_T<BF, 4, VT>(accW, WT, LDC, wave, lane);
+            store_T<BF, 4, VT>(accW, WTd, LDC, wave, lane, egn);
         }
         __syncthreads();
 
-        // ---- U = Tb V (kept in registers), Kw = Tk K (to LDS)
-        f32x4 accW[Tiles<4, VT>::PW];
-#pragma unroll
-        for (int i = 0; i < Tiles<4, VT>::PW; ++i) accW[i] = zero4();
-        gemm<BF, 4, VT, C>(Tb, LDC, VTs, LDC, accW, wave, lane);
-        if (!s.additive) {
-            f32x4 accK[Tiles<4, DT>::PW];
-#pragma unroll
-            for (int i = 0; i < Tiles<4, DT>::PW; ++i) accK[i] = zero4();
-            gemm<BF, 4, DT, C>(Tk, LDC, KTs, LDC, accK, wave, lane);
-            __syncthreads();
-            store_N<BF, 4, DT>(accK, Kws, LDD, wave, lane);
-        } else {
-            __syncthreads();
-        }
-        // KTs <- K^T diag(e^{gam_last - gam})
-        for (int e = tid; e < D * C; e += NTHR) {
-            const int d = e / C, j = e % C;
-            KTs[d * LDC + j] = from_f<BF>(to_f(KTs[d * LDC + j]) * egn[j]);
-        }
-        __syncthreads();
-
-        // ---- W = U - Kw h  (serial chain, part 1)
-        if (!s.additive) {
-            f32x4 accX[Tiles<4, VT>::PW];
-#pragma unroll
-            for (int i = 0; i < Tiles<4, VT>::PW; ++i) accX[i] = zero4();
-            gemm<BF, 4, VT, D>(Kws, LDD, hTs, LDD, accX, wave, lane);
-#pragma unroll
-            for (int i = 0; i < Tiles<4, VT>::PW; ++i) accW[i] -= accX[i];
-        }
-        store_T<BF, 4, VT>(accW, WTs, LDC, wave, lane);
-        __syncthreads();
-
-        // ---- O = diag(e^gam) Q h + P W
+        // O = diag(e^gam) Q h + P W
         if (o) {
             f32x4 accO[Tiles<4, VT>::PW];
 #pragma unroll
             for (int i = 0; i < Tiles<4, VT>::PW; ++i) accO[i] = zero4();
             gemm<BF, 4, VT, D>(Qs, LDD, hTs, LDD, accO, wave, lane);
             for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accO[i][e] *= eg[row]; });
-            gemm<BF, 4, VT, C>(Ps, LDC, WTs, LDC, accO, wave, lane);
+            gemm<BF, 4, VT, C>(Ps, LDC, WT, LDC, accO, wave, lane);
+            S *orow = o + (row0 * H + h) * dv + v0;
             for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
-                if (row < n && col < nvc) o[((row0 + row) * H + h) * dv + v0 + col] = from_f<BF>(accO[i][e]);
+                if (row < n && col < nvc) orow[(size_t)row * H * dv + col] = from_f<BF>(accO[i][e]);
             });
         }
-        // ---- h <- e^{gam_last} h + Ktilde^T W  (serial chain, part 2)
+        // h <- e^{gam_last} h + K^T diag(e^{gam_last - gam}) W (serial chain, part 2)
         {
             const float el = misc[0];
 #pragma unroll
             for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accH[i] *= el;
-            gemm<BF, DT, VT, C>(KTs, LDC, WTs, LDC, accH, wave, lane);
+            gemm<BF, DT, VT, C>(KT, LDC, WTd, LDC, accH, wave, lane);
         }
         __syncthreads();
         store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
@@ -225,6 +290,8 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- launch
+
 int pad_dim(int d, bool bf16) {
     int D = bf16 ? 32 : 16;
     while (D < d) D *= 2;
@@ -233,25 +300,49 @@ int pad_dim(int d, bool bf16) {
 
 int fwd_vblock(int D) { return D >= 64 ? 32 : 16; }
 
-template <bool BF, int D> static hipError_t fwd_inst(const FwdArgs &a, hipStream_t st) {
-    constexpr int BV = (D >= 64) ? 32 : 16;
-    const int grid = a.s.B * a.s.H * a.NVB;
-    hipLaunchKernelGGL((fwd_kernel<BF, D, BV>), dim3(grid), dim3(NTHR), 0, st, a);
+template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStream_t st) {
+    const int grid = a.s.B * a.s.H * a.s.NC;
+    hipLaunchKernelGGL((fwd_prep_kernel<BF, D>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs &a, bool bf16, int D, hipStream_t st) {
+template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
+    constexpr int BV = (D >= 64) ? 32 : 16;
+    const int grid = a.s.B * a.s.H * a.NVB;
+    hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st) {
     if (bf16) {
         switch (D) {
-        case 32: return fwd_inst<true, 32>(a, st);
-        case 64: return fwd_inst<true, 64>(a, st);
-        case 128: return fwd_inst<true, 128>(a, st);
+        case 32: return prep_inst<true, 32>(a, st);
+        case 64: return prep_inst<true, 64>(a, st);
+        case 128: return prep_inst<true, 128>(a, st);
         }
     } else {
         switch (D) {
-        case 16: return fwd_inst<false, 16>(a, st);
-        case 32: return fwd_inst<false, 32>(a, st);
-        case 64: return fwd_inst<false, 64>(a, st);
+        case 16: return prep_inst<false, 16>(a, st);
+        case 32: return prep_inst<false, 32>(a, st);
+        case 64: return prep_inst<false, 64>(a, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t st) {
+    if (fwd_vblock(D) * a.NVB < a.s.dv) return hipErrorInvalidValue;
+    if (bf16) {
+        switch (D) {
+        case 32: return chain_inst<true, 32>(a, st);
+        case 64: return chain_inst<true, 64>(a, st);
+        case 128: return chain_inst<true, 128>(a, st);
+        }
+    } else {
+        switch (D) {
+        case 16: return chain_inst<false, 16>(a, st);
+        case 32: return chain_inst<false, 32>(a, st);
+        case 64: return chain_inst<false, 64>(a, st);
         }
     }
     return hipErrorInvalidValue;

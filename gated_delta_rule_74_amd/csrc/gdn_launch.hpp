@@ -14,19 +14,28 @@ struct SeqArgs {
     int additive;
 };
 
-struct FwdArgs {
+// Per-chunk products that do not depend on the state:
+// U = Tm diag(beta) V  [B*H][NC][64][dv],  NK = -Tm diag(beta e^gam) K  [B*H][NC][64][dk]
+struct PrepArgs {
     SeqArgs s;
-    void *o;          // may be null (state-only recompute)
-    float *hT;        // may be null
-    void *cs;         // chunk states [B,H,NC,dk,dv] in operand dtype, may be null
-    int NVB;          // value-column blocks
+    void *U, *NK;
+};
+
+struct FwdChainArgs {
+    SeqArgs s;
+    const void *U, *NK;
+    void *o;   // may be null (state-only pass)
+    float *hT; // may be null
+    void *cs;  // chunk-start states [B,H,NC,dk,dv] in operand dtype, may be null
+    int NVB;   // value-column blocks
 };
 
 struct BwdChainArgs {
     SeqArgs s;
     const void *dout;
     const float *dhT; // may be null
-    void *dhs;        // [B,H,NC,dk,dv] operand dtype: gradient wrt the state after each chunk
+    const void *NK;
+    void *dhs;        // [B,H,NC,dk,dv]: gradient wrt the state after each chunk
     float *dh0;       // may be null
     int NVB;
 };
@@ -34,11 +43,12 @@ struct BwdChainArgs {
 struct BwdLocalArgs {
     SeqArgs s;
     const void *dout;
-    const void *cs;   // chunk-start states
-    const void *dhs;  // gradient wrt chunk-end states
+    const void *cs;  // chunk-start states
+    const void *NK;
+    const void *dhs; // gradient wrt chunk-end states
     void *dq, *dk, *dv;
     float *dg, *dbeta;
-    float *dA_part;   // [B*H*NC]
+    float *dA_part;  // [B*H*NC]
 };
 
 struct StepArgs {
@@ -52,13 +62,14 @@ struct StepArgs {
 // Padded head dimension the kernels are instantiated for.
 int pad_dim(int d, bool bf16);
 int fwd_vblock(int D);
+int bwd_chain_vblock(bool bf16, int D);
+bool bwd_supported(bool bf16, int D);
 
-hipError_t launch_fwd(const FwdArgs &a, bool bf16, int D, hipStream_t st);
+hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st);
+hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st);
 hipError_t launch_step(const StepArgs &a, bool bf16, hipStream_t st);
-
-bool bwd_supported(bool bf16, int D);
 
 } // namespace gdn

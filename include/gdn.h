@@ -81,16 +81,16 @@ typedef struct {
     uint32_t flags;  /* 0 or GDN_FLAG_ADDITIVE */
 } gdn_shape_t;
 
-/* Bytes of device workspace gdn_fwd / gdn_bwd need for this shape (0 means
- * ws may be NULL). Return 0 for an invalid shape as well; the call itself
- * reports the error. */
+/* Bytes of device workspace gdn_fwd / gdn_bwd need for this shape. Return 0
+ * for an invalid shape; the call itself then reports the error. */
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s);
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s);
 
-/* Bytes of the optional per-chunk state buffer: the state at the start of
- * every 64-token chunk, [B, H, ceil(T/64), dk, dv] in the call's dtype.
- * gdn_fwd fills it when given; gdn_bwd reads it instead of recomputing. */
-size_t gdn_chunk_states_size(const gdn_shape_t *s);
+/* Bytes of the optional forward context: what gdn_fwd can save for gdn_bwd
+ * so that the backward skips recomputing the forward. It holds the state at
+ * the start of every 64-token chunk and the chunk's -Tm diag(beta e^gam) K
+ * block, both in the call's dtype. Its layout is private to the library. */
+size_t gdn_fwd_context_size(const gdn_shape_t *s);
 
 /* Forward pass over a whole sequence ("GDN & MLA Mechanism Deep-Dive",
  * Step 4 and Step 5).
@@ -98,32 +98,35 @@ size_t gdn_chunk_states_size(const gdn_shape_t *s);
  *   h0            initial state or NULL (zero state)
  *   o             output [B,T,H,dv]
  *   hT            final state or NULL (not written)
- *   chunk_states  NULL, or gdn_chunk_states_size() bytes receiving the state
- *                 at the start of every chunk (for gdn_bwd)
- *   ws, ws_bytes  workspace of gdn_fwd_workspace_size() bytes */
+ *   ctx           NULL, or gdn_fwd_context_size() bytes (256-byte aligned)
+ *                 that receive the forward context for gdn_bwd
+ *   ws, ws_bytes  workspace of gdn_fwd_workspace_size() bytes, 256-byte
+ *                 aligned; its contents are scratch */
 gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
                      const float *g, const float *beta, const float *A_log, const float *h0,
-                     void *o, float *hT, void *chunk_states, void *ws, size_t ws_bytes,
-                     void *stream);
+                     void *o, float *hT, void *ctx, void *ws, size_t ws_bytes, void *stream);
 
 /* Backward pass: gradients of sum(do * o) + sum(dhT * hT) with respect to q,
  * k, v, g, beta, A_log and h0, by the reverse-chunk derivative of the chunked
  * forward. Inputs are those of the gdn_fwd call; do is the upstream gradient of
  * o, dhT that of the final state (NULL = zero).
- *   chunk_states  NULL (recompute in the workspace) or the buffer gdn_fwd
- *                 filled for the same inputs
+ *   ctx           NULL (the forward is recomputed in the workspace) or the
+ *                 context gdn_fwd saved for the same inputs
  *   dq, dk, dv    [B,T,H,*] in the call's dtype
  *   dg, dbeta     [B,T,H] fp32
  *   dA_log        [H] fp32, overwritten (sum over the batch)
  *   dh0           [B,H,dk,dv] fp32 or NULL
  *   hT            NULL, or receives the recomputed final state; only allowed
- *                 when chunk_states is NULL
- *   ws, ws_bytes  workspace of gdn_bwd_workspace_size() bytes */
+ *                 when ctx is NULL
+ *   ws, ws_bytes  workspace of gdn_bwd_workspace_size() bytes, 256-byte
+ *                 aligned
+ * Supported head dimensions: bf16 up to 64, fp32 up to 16 (others return
+ * GDN_EUNSUPPORTED). */
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
                      const float *g, const float *beta, const float *A_log, const float *h0,
-                     const void *chunk_states, const void *dout, const float *dhT, void *dq,
-                     void *dk, void *dv, float *dg, float *dbeta, float *dA_log, float *dh0,
-                     float *hT, void *ws, size_t ws_bytes, void *stream);
+                     const void *ctx, const void *dout, const float *dhT, void *dq, void *dk,
+                     void *dv, float *dg, float *dbeta, float *dA_log, float *dh0, float *hT,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* One decode token for each of N independent sequences: one step of the
  * recurrence from a carried state (the O(1)-state read/write of "GDN & MLA

@@ -46,10 +46,11 @@ def fake(i, size=1 << 30):
 
 def fwd_call(L, shape, **over):
     args = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), A_log=fake(6), h0=None,
-                o=fake(7), hT=None, cs=None)
+                o=fake(7), hT=None, cs=None, ws=fake(30), ws_bytes=1 << 30)
     args.update(over)
     return L.gdn_fwd(ctypes.byref(shape), args["q"], args["k"], args["v"], args["g"], args["beta"],
-                     args["A_log"], args["h0"], args["o"], args["hT"], args["cs"], None, 0, None)
+                     args["A_log"], args["h0"], args["o"], args["hT"], args["cs"], args["ws"],
+                     args["ws_bytes"], None)
 
 
 def test_fwd_rejects_bad_shapes(L):
@@ -64,6 +65,10 @@ def test_fwd_rejects_bad_shapes(L):
     s = gdn.Shape(1, 8, 2, 65, 16, 0, 64, 0)  # fp32 above 64
     assert fwd_call(L, s) == EUNSUPPORTED
     assert L.gdn_fwd(None, *[None] * 10, None, 0, None) == EINVAL
+    s = gdn.Shape(1, 8, 2, 16, 16, 1, 64, 0)
+    assert fwd_call(L, s, ws=None) == EWORKSPACE
+    assert fwd_call(L, s, ws_bytes=16) == EWORKSPACE
+    assert fwd_call(L, s, cs=ctypes.c_void_p(fake(8).value + 16)) == EINVAL  # ctx misaligned
 
 
 def test_fwd_rejects_null_misaligned_and_aliased(L):
@@ -94,18 +99,22 @@ def test_bwd_validation(L):
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need - 1) == EWORKSPACE
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dq=None) == EINVAL
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, cs=fake(15), hT=fake(16)) == EINVAL
+    assert bwd_call(L, gdn.Shape(1, 8, 2, 100, 100, 1, 64, 0), ws=fake(20), ws_bytes=need) == EUNSUPPORTED
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dq=fake(1)) == EINVAL  # dq aliases q
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dk=fake(20)) == EINVAL  # dk in workspace
 
 
-def test_workspace_and_state_sizes(L):
+def test_workspace_and_context_sizes(L):
     s = gdn.Shape(8, 4096, 16, 56, 56, 1, 64, 0)
-    st = L.gdn_chunk_states_size(ctypes.byref(s))
-    assert st == 8 * 16 * 64 * 56 * 56 * 2
-    assert L.gdn_bwd_workspace_size(ctypes.byref(s)) >= 2 * st + 8 * 16 * 64 * 4
-    assert L.gdn_fwd_workspace_size(ctypes.byref(s)) == 0
+    states = 8 * 16 * 64 * 56 * 56 * 2
+    blocks = 8 * 16 * 64 * 64 * 56 * 2
+    ctx = L.gdn_fwd_context_size(ctypes.byref(s))
+    assert ctx >= states + blocks and ctx < states + blocks + 1024
+    assert L.gdn_fwd_workspace_size(ctypes.byref(s)) >= 2 * blocks
+    assert L.gdn_bwd_workspace_size(ctypes.byref(s)) >= ctx + blocks + states + 8 * 16 * 64 * 4
     bad = gdn.Shape(0, 1, 1, 1, 1, 1, 64, 0)
-    assert L.gdn_chunk_states_size(ctypes.byref(bad)) == 0
+    assert L.gdn_fwd_context_size(ctypes.byref(bad)) == 0
+    assert L.gdn_fwd_workspace_size(ctypes.byref(bad)) == 0
 
 
 def test_step_validation(L):

@@ -36,9 +36,9 @@ def run_bwd(x, additive=False, use_saved=True, want_hT=False):
     h0, do, dhT = dev(x["h0"]), dev(x["do"]), dev(x.get("dhT"))
     cs = None
     if use_saved:
-        _, _, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_chunk_states=True,
+        _, _, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_context=True,
                            want_hT=False)
-    r = gdn.bwd(q, k, v, g, beta, A_log, do, h0, dhT, chunk_states=cs, additive=additive,
+    r = gdn.bwd(q, k, v, g, beta, A_log, do, h0, dhT, context=cs, additive=additive,
                 want_hT=want_hT)
     torch.cuda.synchronize()
     return r

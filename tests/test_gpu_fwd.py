@@ -15,7 +15,7 @@ def run_fwd(x, additive=False, with_h0=True):
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     g, beta, A_log = dev(x["g"]), dev(x["beta"]), dev(x["A_log"])
     h0 = dev(x["h0"]) if with_h0 else None
-    o, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_chunk_states=True)
+    o, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_context=True)
     torch.cuda.synchronize()
     return o, hT, cs
 
@@ -116,8 +116,8 @@ def test_chunk_states_match_oracle_prefix_states():
     """The saved state at the start of chunk c equals the oracle's final state
     after the first 64*c tokens."""
     x = gi.gen_seq(1, 200, 2, 56, 56, "bf16", seed=902, h0="randn", decay="weak")
-    _, _, cs = run_fwd(x)
-    cs = host(cs)
+    o, _, ctx = run_fwd(x)
+    cs = host(gdn.context_states(ctx, dev(x["q"]), dev(x["v"])))
     for c in range(4):
         t = 64 * c
         if t == 0:
