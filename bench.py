@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = one forward (saving its context) + one backward over one batch of
+the layer shape B=8, H=16, T=4096, d_k=d_v=56, bf16 q/k/v/do, fp32 gates and
+state, chunk 64, seeded synthetic inputs (gdn_inputs, workload
+"fwdbwd_model"), all resident in HBM before timing starts.
+
+Prints one JSON line with whole-step throughput (tokens/s), the roofline of
+the dominant kernel (per-kernel durations measured here with HIP events
+around every library launch) and the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+WORKLOAD = "fwdbwd_model"
+C = 64
+
+# Kernels in launch order within one step (forward with context, backward).
+KERNELS = ["fwd_prep", "fwd_chain", "bwd_chain", "bwd_local", "dA_reduce"]
+
+
+def kernel_bytes_per_token_head(d):
+    """Algorithmic HBM bytes per (token, head) of each kernel: the bytes of
+    the operation's own inputs it must read and outputs it must write (bf16
+    q/k/v/o/do/dq/dk/dv of d elements, fp32 g/beta/dg/dbeta); workspace and
+    context traffic is implementation cost and is not counted."""
+    e = 2 * d
+    return {
+        "fwd_prep": 2 * e + 8,          # k, v, g, beta
+        "fwd_chain": 2 * e + 4 + e,     # q, k, g -> o
+        "bwd_chain": 3 * e + 4,         # q, k, do, g
+        "bwd_local": 4 * e + 8 + 3 * e + 8,  # q, k, v, do, g, beta -> dq, dk, dv, dg, dbeta
+        "dA_reduce": 0,
+    }
+
+
+def step_model(B, T, H, d):
+    """Algorithmic FLOPs and HBM bytes of one forward + backward (chunk-form
+    FLOP count per chunk-head: fwd 10C^2d + 6Cd^2 + C^3/3, bwd 20C^2d +
+    12Cd^2 + 4C^3; bytes: read q,k,v,do,g,beta,h0 and write o,hT,dq,dk,dv,
+    dg,dbeta,dA_log,dh0 once each)."""
+    nch = B * H * ((T + C - 1) // C)
+    flops = nch * ((10 * C * C * d + 6 * C * d * d + C ** 3 / 3) + (20 * C * C * d + 12 * C * d * d + 4 * C ** 3))
+    th = B * T * H
+    e = 2 * d
+    fwd_bytes = th * (3 * e + 8 + e) + B * H * d * d * 4 * 2  # + h0 read, hT write
+    bwd_bytes = th * (4 * e + 8 + 3 * e + 8) + B * H * d * d * 4 * 2 + H * 4
+    return flops, fwd_bytes + bwd_bytes
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_74_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM traffic of a kernel from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{WORKLOAD}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("traffic_bytes")
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(x, B, T, H, budget_s):
+    """The fp64 oracle (forward + reverse pass) on a bounded sample of the
+    workload's (b, h) units, threaded over units."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build()
+    f = {k: (v.f64() if hasattr(v, "f64") else (None if v is None else np.asarray(v, np.float64)))
+         for k, v in x.items()}
+    cores = cpu_threads()
+    # size the sample from a one-unit probe so the timed run lasts about budget_s
+    t0 = time.perf_counter()
+    oracle.fwd(f["q"], f["k"], f["v"], f["g"], f["beta"], f["A_log"], f["h0"], units=[0], nthreads=1)
+    oracle.bwd(f["q"], f["k"], f["v"], f["g"], f["beta"], f["A_log"], f["h0"], f["do"], units=[0],
+               nthreads=1)
+    per_unit = time.perf_counter() - t0
+    n_units = int(min(B * H, max(cores, round(budget_s * cores / max(per_unit, 1e-6)))))
+    n_units = max(1, (n_units // cores) * cores) if n_units >= cores else n_units
+    units = list(range(n_units))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:  # repeat a small sample until the time budget is used
+        oracle.fwd(f["q"], f["k"], f["v"], f["g"], f["beta"], f["A_log"], f["h0"], units=units,
+                   nthreads=cores)
+        oracle.bwd(f["q"], f["k"], f["v"], f["g"], f["beta"], f["A_log"], f["h0"], f["do"],
+                   units=units, nthreads=cores)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= budget_s or reps >= 100:
+            break
+    tokens = reps * n_units * T / H  # one token carries H heads
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_units} of {B * H} (batch, head) units at full T={T}, fwd+bwd in fp64, "
+                      f"{reps} pass(es), {wall:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the gated delta rule path here is built and timed "
+              "on a single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_74_amd as gdn
+    import gdn_inputs as gi
+
+    cfg = gi.CONFIGS[WORKLOAD]
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    x = gi.gen_config(WORKLOAD)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if isinstance(a, gi.Tensor):
+            return torch.from_numpy(a.data.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: to_dev(v) for k, v in x.items()}
+    q, k, v, g, beta, A_log, h0, do = (t[n] for n in ("q", "k", "v", "g", "beta", "A_log", "h0", "do"))
+    o = torch.empty_like(v)
+    hT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    ctx = torch.empty(gdn.context_size(q, v), dtype=torch.uint8, device=dev)
+    fws = torch.empty(gdn.fwd_workspace_size(q, v), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gdn.bwd_workspace_size(q, v), dtype=torch.uint8, device=dev)
+    grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+             "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+             "dA_log": torch.empty_like(A_log),
+             "dh0": torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)}
+
+    def step():
+        gdn.fwd(q, k, v, g, beta, A_log, h0, o=o, hT=hT, context=ctx, workspace=fws)
+        gdn.bwd(q, k, v, g, beta, A_log, do, h0, None, context=ctx, workspace=bws, out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: the same steps again with every launch bracketed
+    nk = len(KERNELS)
+    timer = gdn.LaunchTimer(nk * args.steps)
+    with timer:
+        for _ in range(args.steps):
+            step()
+    d = timer.durations_ms()
+    if len(d) != nk * args.steps:
+        raise RuntimeError(f"expected {nk * args.steps} launches, bracketed {len(d)}")
+    per_kernel = {name: float(np.mean(d[i::nk])) for i, name in enumerate(KERNELS)}
+
+    tokens = B * T
+    flops, step_bytes = step_model(B, T, H, dk)
+    dom = max(per_kernel, key=per_kernel.get)
+    kb = kernel_bytes_per_token_head(dk)[dom] * B * T * H
+    dom_s = per_kernel[dom] * 1e-3
+    achieved = kb / dom_s / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(dom), "bytes_per_launch": kb,
+            "avg_launch_ms": round(per_kernel[dom], 4)}
+
+    out = {
+        "metric": "GDN fwd+bwd tokens/s at B8·H16·T4096·d56; % of MFMA/HBM roofline",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded gdn_inputs workload fwdbwd_model)",
+        "config": {"workload": WORKLOAD, "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": C,
+                   "global_batch": B, "seq_len": T, "parallelism": "none (one GPU)"},
+        "roofline": roof,
+        "step_roofline": {
+            "hbm_bytes": step_bytes, "flops": flops,
+            "hbm_frac": round(step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        },
+        "kernels_ms": {k2: round(v2, 4) for k2, v2 in per_kernel.items()},
+        "wall_s_timed": round(wall_s, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, B, T, H, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

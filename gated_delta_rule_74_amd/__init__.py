@@ -19,12 +19,14 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "step", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
-           "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size"]
+           "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size",
+           "LaunchTimer"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
-           "gdn_fwd_context_size", "gdn_status_string", "gdn_last_error_detail"]
+           "gdn_fwd_context_size", "gdn_time_launches", "gdn_status_string",
+           "gdn_last_error_detail"]
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_ADDITIVE = 1
@@ -62,6 +64,8 @@ def lib():
         for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_fwd_context_size):
             f.argtypes = [S]
             f.restype = Z
+        L.gdn_time_launches.argtypes = [P, I32]
+        L.gdn_time_launches.restype = I32
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error_detail.argtypes = []
@@ -252,6 +256,34 @@ def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=No
                         _stream(dev))
     _check("gdn_step", st)
     return o, h_out
+
+
+class LaunchTimer:
+    """Brackets every kernel the library launches (from this thread) with
+    HIP events, for per-kernel timings: `with LaunchTimer(n) as t: ...` then
+    t.durations_ms() gives one duration per launch, in launch order."""
+
+    def __init__(self, max_launches):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+        for e in self.events:  # torch creates the HIP event on first record
+            e.record()
+        torch.cuda.synchronize()
+        self._arr = (ctypes.c_void_p * len(self.events))(
+            *[ctypes.c_void_p(e.cuda_event) for e in self.events])
+        self.count = 0
+
+    def __enter__(self):
+        lib().gdn_time_launches(self._arr, len(self.events))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = int(lib().gdn_time_launches(None, 0))
+        return False
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        n = min(self.count, len(self.events) // 2)
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
 
 
 class GatedDeltaRule(torch.autograd.Function):

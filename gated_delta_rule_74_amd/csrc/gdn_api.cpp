@@ -111,6 +111,28 @@ int pad_of(const gdn_shape_t *s) {
     return gdn::pad_dim(s->dk > s->dv ? s->dk : s->dv, s->dtype == GDN_BF16);
 }
 
+// Launch bracketing for gdn_time_launches().
+thread_local void *const *g_events = nullptr;
+thread_local int g_nevents = 0;
+thread_local int g_launch = 0;
+
+template <class F> hipError_t timed(F &&launch, hipStream_t st) {
+    const int i = g_launch;
+    const bool on = g_events && 2 * i + 1 < g_nevents;
+    if (on) {
+        const hipError_t e = hipEventRecord((hipEvent_t)g_events[2 * i], st);
+        if (e != hipSuccess) return e;
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (on) {
+        const hipError_t e2 = hipEventRecord((hipEvent_t)g_events[2 * i + 1], st);
+        if (e2 != hipSuccess) return e2;
+    }
+    if (g_events) ++g_launch;
+    return hipSuccess;
+}
+
 gdn_status_t hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(GDN_EHIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -132,6 +154,14 @@ const char *gdn_status_string(gdn_status_t st) {
 }
 
 const char *gdn_last_error_detail(void) { return g_detail; }
+
+int32_t gdn_time_launches(void *const *events, int32_t n) {
+    const int32_t done = g_launch;
+    g_events = events;
+    g_nevents = events ? n : 0;
+    g_launch = 0;
+    return done;
+}
 
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
@@ -160,7 +190,7 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
     pa.s = sa;
     pa.U = U;
     pa.NK = NK;
-    hipError_t he = gdn::launch_fwd_prep(pa, bf, D, strm);
+    hipError_t he = timed([&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
     if (he != hipSuccess) return he;
     gdn::FwdChainArgs fa;
     fa.s = sa;
@@ -171,7 +201,7 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
     fa.cs = cs;
     const int BV = gdn::fwd_vblock(D);
     fa.NVB = (s->dv + BV - 1) / BV;
-    return gdn::launch_fwd_chain(fa, bf, D, strm);
+    return timed([&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
 }
 
 } // namespace
@@ -284,7 +314,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     ca.dh0 = dh0;
     const int BVc = gdn::bwd_chain_vblock(bf, D);
     ca.NVB = (s->dv + BVc - 1) / BVc;
-    he = gdn::launch_bwd_chain(ca, bf, D, strm);
+    he = timed([&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd chain launch");
     gdn::BwdLocalArgs la;
     la.s = sa;
@@ -298,9 +328,9 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     la.dg = dg;
     la.dbeta = dbeta;
     la.dA_part = part;
-    he = gdn::launch_bwd_local(la, bf, D, strm);
+    he = timed([&] { return gdn::launch_bwd_local(la, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd local launch");
-    he = gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm);
+    he = timed([&] { return gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm); }, strm);
     return hip_status(he, "gdn_bwd dA_log launch");
 }
 
@@ -341,7 +371,8 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
     a.dk = dk;
     a.dv = dv;
     a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
-    return hip_status(gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream), "gdn_step launch");
+    return hip_status(timed([&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
+                      "gdn_step launch");
 }
 
 } // extern "C"

@@ -51,7 +51,7 @@ template <bool BF, int D, int BV> struct ChainSmem {
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-template <bool BF, int D, int BV>
+template <bool BF, int D, int BV, bool VEC>
 __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -84,7 +84,6 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     const S *dO = (const S *)a.dout;
     const S *NK = (const S *)a.NK;
     S *dhs = (S *)a.dhs;
-    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
 
     f32x4 accDH[Tiles<DT, VT>::PW];
     for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
@@ -98,31 +97,33 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     auto fetch = [&](int c) {
         const int t0 = c * C, n = min(C, T - t0);
         const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
-        fk.fetch(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
-        fq.fetch(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
-        fo.fetch(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, vecv, tid);
-        if (!s.additive) fn.fetch(NK + cb * C * dk, (size_t)dk, n, dk, veck, tid);
-        pg = lane < n ? s.g[(row0 + lane) * H + h] : 0.f;
+        fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fo.template fetch<VEC>(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, tid);
+        if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
+        pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
     };
     fetch(s.NC - 1);
 
     for (int c = s.NC - 1; c >= 0; --c) {
+        const int n = min(C, T - c * C);
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc)
                 dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
         });
         // every wave computes the decay of its lane's row: the transposed
         // copy of Q (row j = lane) is scaled by e^{gam_j} while it is stored
-        const Decay dc = decay_lane(pg, A2, lane);
+        const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
         if (wave == 0) {
             gam2[lane] = dc.gam2;
             egn[lane] = dc.egn;
             if (lane == 0) misc[0] = dc.eglast;
         }
-        fk.stash(Ks, LDD, nullptr, 0, tid);
-        fq.stash_scaled(Qs, LDD, QT, LDC, tid, dc.eg);
-        fo.stash(nullptr, 0, dOT, LDC, tid);
-        if (!s.additive) fn.stash(nullptr, 0, NKT, LDC, tid);
+        fk.stash(Ks, LDD, tid);
+        fq.stash(Qs, LDD, tid);
+        fq.stash_T_scaled(QT, LDC, tid, dc.eg);
+        fo.stash_T(dOT, LDC, tid);
+        if (!s.additive) fn.stash_T(NKT, LDC, tid);
         if (c > 0) fetch(c - 1);
         __syncthreads();
 
@@ -241,7 +242,7 @@ __device__ __forceinline__ void add_cols(const f32x4 *x, float *part, float *dst
     __syncthreads();
 }
 
-template <bool BF, int D>
+template <bool BF, int D, bool VEC>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -289,7 +290,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int t0 = c * C, n = min(C, T - t0);
     const double A = -exp((double)s.A_log[h]);
-    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
     const size_t row0 = (size_t)b * T + t0;
     const S *q = (const S *)s.q + (row0 * H + h) * dk;
     const S *k = (const S *)s.k + (row0 * H + h) * dk;
@@ -303,31 +303,34 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     // all global inputs of the chunk are requested up front
     ChunkFrag<BF, D> fk, fq, fv, fo, fn;
     ChunkFrag<BF, D, D> fh, fd;
-    fk.fetch(k, (size_t)H * dk, n, dk, veck, tid);
-    fq.fetch(q, (size_t)H * dk, n, dk, veck, tid);
-    fv.fetch(v, (size_t)H * dv, n, dv, vecv, tid);
-    fo.fetch(dO, (size_t)H * dv, n, dv, vecv, tid);
-    if (!add) fn.fetch(nk, (size_t)dk, n, dk, veck, tid);
-    fh.fetch(hc, (size_t)dv, dk, dv, vecv, tid);
-    fd.fetch(dhc, (size_t)dv, dk, dv, vecv, tid);
+    fk.template fetch<VEC>(k, (size_t)H * dk, n, dk, tid);
+    fq.template fetch<VEC>(q, (size_t)H * dk, n, dk, tid);
+    fv.template fetch<VEC>(v, (size_t)H * dv, n, dv, tid);
+    fo.template fetch<VEC>(dO, (size_t)H * dv, n, dv, tid);
+    if (!add) fn.template fetch<VEC>(nk, (size_t)dk, n, dk, tid);
+    fh.template fetch<VEC>(hc, (size_t)dv, dk, dv, tid);
+    fd.template fetch<VEC>(dhc, (size_t)dv, dk, dv, tid);
 
     // ---- P1: K, Q, gates; Grams
-    if (tid < C) {
-        const size_t gi = (row0 + tid) * H + h;
-        gch[tid] = (tid < n) ? s.g[gi] : 0.f;
-        bet[tid] = (tid < n) ? s.beta[gi] : 0.f;
-        dgam[tid] = 0.f;
-        dbet[tid] = 0.f;
+    float gr = 0.f, br = 0.f;
+    if (wave == 0) {
+        gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
     }
     if (wave == 0) {
+        gch[lane] = lane < n ? gr : 0.f;
+        bet[lane] = lane < n ? br : 0.f;
+        dgam[lane] = 0.f;
+        dbet[lane] = 0.f;
         const Decay dc = decay_lane(gch[lane], A * LOG2E, lane);
         gam[lane] = dc.gam2;
         eg[lane] = dc.eg;
         egn[lane] = dc.egn;
         if (lane == 0) misc[0] = dc.eglast;
     }
-    fk.stash(Ks, LDD, KT, LDC, tid);
-    fq.stash(Qs, LDD, nullptr, 0, tid);
+    fk.stash(Ks, LDD, tid);
+    fk.stash_T(KT, LDC, tid);
+    fq.stash(Qs, LDD, tid);
     __syncthreads();
     {
         f32x4 sk[PWC], sq[PWC];
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     __syncthreads();
     // ---- P2: Tm with Tb = Tm diag(beta) (Re) and TT = Tm^T (Ra)
     if (!add) {
-        tri_inverse<BF>(Lm, Tm, xs, wave, lane, Re, nullptr, TT, LDC, bet, nullptr);
+        tri_inverse<BF, true, false, true>(Lm, Tm, xs, wave, lane, Re, nullptr, TT, LDC, bet, nullptr);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
             const int row = e / C, col = e % C;
@@ -356,9 +359,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         __syncthreads();
     }
     // ---- P3: U, Kw, W
-    fv.stash(nullptr, 0, VT, LDC, tid);
-    fh.stash(nullptr, 0, F2b, LDD, tid); // h^T
-    if (!add) fn.stash(Kws, LDD, nullptr, 0, tid); // -Kw
+    fv.stash_T(VT, LDC, tid);
+    fh.stash_T(F2b, LDD, tid); // h^T
+    if (!add) fn.stash(Kws, LDD, tid); // -Kw
     __syncthreads();
     f32x4 accW[PWD];
 #pragma unroll
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     if (!add) gemm<BF, 4, DT, D>(Kws, LDD, F2b, LDD, accW, wave, lane); // W = U - Kw h
     store_N<BF, 4, DT>(accW, Ws, LDD, wave, lane);
     // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-    fo.stash(nullptr, 0, F1a, LDC, tid); // dO^T
-    fd.stash(nullptr, 0, F1b, LDD, tid); // dh'^T
+    fo.stash_T(F1a, LDC, tid); // dO^T
+    fd.stash_T(F1b, LDD, tid); // dh'^T
     __syncthreads();
     {
         f32x4 accdW[PWD], accX[PWD];
@@ -383,9 +386,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     }
     __syncthreads();
     // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
-    fh.stash(F1a, LDD, nullptr, 0, tid); // h
-    fd.stash(F1b, LDD, nullptr, 0, tid); // dh'
-    fo.stash(Rf, LDD, nullptr, 0, tid);  // dO
+    fh.stash(F1a, LDD, tid); // h
+    fd.stash(F1b, LDD, tid); // dh'
+    fo.stash(Rf, LDD, tid);  // dO
     __syncthreads();
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         add_cols<4, 4>(xm, part, dgam, -1.f, tid, wave, lane);
         store_N<BF, 4, 4>(accP, dPG, LDC, wave, lane);
         store_T<BF, 4, 4>(accP, Re, LDC, wave, lane);
-        fq.stash(nullptr, 0, F1a, LDC, tid); // Q^T
+        fq.stash_T(F1a, LDC, tid); // Q^T
     }
     __syncthreads();
     // ---- P10: dQ, dK
@@ -586,7 +589,10 @@ static int chain_vblock(bool bf16, int D) {
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
     constexpr int BV = (!BF && D >= 64) ? 16 : (D >= 64 ? 32 : 16);
     const int grid = a.s.B * a.s.H * a.NVB;
-    hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV>), dim3(grid), dim3(NTHR), 0, st, a);
+    if (vec_ok<BF>(a.s))
+        hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, false>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 
@@ -607,7 +613,10 @@ hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t
 
 template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hipStream_t st) {
     const int grid = a.s.B * a.s.H * a.s.NC;
-    hipLaunchKernelGGL((bwd_local_kernel<BF, D>), dim3(grid), dim3(NTHR), 0, st, a);
+    if (vec_ok<BF>(a.s))
+        hipLaunchKernelGGL((bwd_local_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_local_kernel<BF, D, false>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 

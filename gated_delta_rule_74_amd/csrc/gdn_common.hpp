@@ -174,64 +174,96 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
         S s[V];
     };
     U r[NIT];
+    uint32_t ok; // bit m: item m lies inside the tensor (else it reads as zero)
 
-    // x: column 0 of row 0 of the chunk, rs: elements between rows, n valid
-    // rows, d valid columns. vec: rows start on 16-byte boundaries and d % V == 0.
-    __device__ __forceinline__ void fetch(const S *__restrict__ x, size_t rs, int n, int d, bool vec,
-                                          int tid) {
+    // x: column 0 of row 0 of the tile, rs: elements between rows, n valid
+    // rows (n >= 1), d valid columns. VEC: rows start on 16-byte boundaries
+    // and d % V == 0. The vector path issues its loads without any per-lane
+    // branch (out-of-range items read a clamped in-range address and are
+    // masked in stash()), so they stay in flight until the data is stashed.
+    template <bool VEC>
+    __device__ __forceinline__ void fetch(const S *__restrict__ x, size_t rs, int n, int d, int tid) {
+        ok = 0;
+        if constexpr (VEC) {
 #pragma unroll
-        for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
-            const int j = it % NR, cg = it / NR;
-            r[m].u = uint4{0u, 0u, 0u, 0u};
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
-            if (j < n) {
-                if (vec) {
-                    if (cg * V < d) r[m].u = *reinterpret_cast<const uint4 *>(x + (size_t)j * rs + cg * V);
-                } else {
+            for (int m = 0; m < NIT; ++m) {
+                const int it = tid + m * NTHR;
+                const int j = it % NR, cg = it / NR;
+                const bool in = ((NR * NG) % NTHR == 0 || cg < NG) && j < n && cg * V < d;
+                const int jj = min(j, n - 1), cc = min(cg * V, d - V);
+                r[m].u = *reinterpret_cast<const uint4 *>(x + (size_t)jj * rs + cc);
+                ok |= (in ? 1u : 0u) << m;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NIT; ++m) {
+                const int it = tid + m * NTHR;
+                const int j = it % NR, cg = it / NR;
+                r[m].u = uint4{0u, 0u, 0u, 0u};
+                if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+                if (j < n) {
 #pragma unroll
                     for (int e = 0; e < V; ++e)
                         if (cg * V + e < d) r[m].s[e] = x[(size_t)j * rs + cg * V + e];
                 }
+                ok |= 1u << m;
             }
         }
     }
 
-    // Like stash(), with the transposed copy scaled by `sc`; requires that
-    // every item of this thread lies in row j == lane (NR == 64).
-    __device__ __forceinline__ void stash_scaled(S *dst, int ldd, S *dstT, int ldt, int tid,
-                                                 float sc) const {
+    __device__ __forceinline__ uint4 item(int m) const {
+        return ((ok >> m) & 1u) ? r[m].u : uint4{0u, 0u, 0u, 0u};
+    }
+
+    // Straight copy to dst [NR][ldd].
+    __device__ __forceinline__ void stash(S *dst, int ldd, int tid) const {
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = item(m);
+        }
+    }
+
+    // Transposed copy to dstT [DP][ldt].
+    __device__ __forceinline__ void stash_T(S *dstT, int ldt, int tid) const {
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            U val;
+            val.u = item(m);
+#pragma unroll
+            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = val.s[e];
+        }
+    }
+
+    // Transposed copy scaled by `sc`; requires that every item of this
+    // thread lies in row j == lane (NR == 64).
+    __device__ __forceinline__ void stash_T_scaled(S *dstT, int ldt, int tid, float sc) const {
         static_assert(NR == 64 && NTHR % 64 == 0, "row of an item must equal the lane");
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
             const int it = tid + m * NTHR;
             const int j = it % NR, cg = it / NR;
             if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
-            if (dst) *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = r[m].u;
+            U val;
+            val.u = item(m);
 #pragma unroll
-            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = from_f<BF>(to_f(r[m].s[e]) * sc);
-        }
-    }
-
-    // dst [C][ldd] straight, dstT [DP][ldt] transposed (either may be null);
-    // the transposed copy's row j is multiplied by tscale[j] when given.
-    __device__ __forceinline__ void stash(S *dst, int ldd, S *dstT, int ldt, int tid,
-                                          const float *tscale = nullptr) const {
-#pragma unroll
-        for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
-            const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
-            if (dst) *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = r[m].u;
-            if (dstT) {
-                const float sc = tscale ? tscale[j] : 1.f;
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    dstT[(cg * V + e) * ldt + j] = tscale ? from_f<BF>(to_f(r[m].s[e]) * sc) : r[m].s[e];
-            }
+            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = from_f<BF>(to_f(val.s[e]) * sc);
         }
     }
 };
+
+// A per-lane scalar of a chunk (g or beta of row `lane`), loaded from a
+// clamped in-range address without a branch. The caller masks rows >= n
+// where it uses the value, so the load can stay in flight until then.
+__device__ __forceinline__ float load_row_scalar(const float *__restrict__ p, size_t stride, int lane,
+                                                 int n) {
+    return p[(size_t)min(lane, n - 1) * stride];
+}
 
 // Zero the padding of a [D][ld] LDS matrix outside [d0][d1].
 template <bool BF, int D>
@@ -281,10 +313,11 @@ constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 // substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
 // level by level (i - j = 1, 2, 3) with fp32 MFMA. xs: 4 x 16 x 17 floats.
-// Optional operand copies, written as the blocks are produced ([C][ldt]):
-//   Tb = T diag(cb), Tk = T diag(ck) (column scales), TT = T^T.
+// Operand copies written as the blocks are produced ([C][ldt]), each only
+// when its flag is set: Tb = T diag(cb) (WB), Tk = T diag(ck) (WK), both
+// column-scaled, and TT = T^T (WT).
 // Ends with a barrier.
-template <bool BF>
+template <bool BF, bool WB, bool WK, bool WT>
 __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs, int wave, int lane,
                                             typename Op<BF>::S *Tb, typename Op<BF>::S *Tk,
                                             typename Op<BF>::S *TT, int ldt, const float *cb,
@@ -304,22 +337,22 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
             for (int rr = i + 1; rr < 16; ++rr) x[rr] -= L[(o + rr) * LDF + o + i] * x[i];
         }
         if (lane < 16) {
-            const float sb = cb ? cb[o + c] : 0.f, sk = ck ? ck[o + c] : 0.f;
+            const float sb = WB ? cb[o + c] : 0.f, sk = WK ? ck[o + c] : 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 Tm[(o + i) * LDF + o + c] = x[i];
-                if (Tb) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
-                if (Tk) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
-                if (TT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
+                if constexpr (WB) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
+                if constexpr (WK) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
+                if constexpr (WT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
             }
         }
         // zero the blocks right of the diagonal in this block row
         for (int e = lane; e < 16 * 48; e += 64) {
             const int i = e / 48, cc = e % 48 + 16 * (wave + 1);
             if (cc < C) {
-                if (Tb) Tb[(o + i) * ldt + cc] = S(0);
-                if (Tk) Tk[(o + i) * ldt + cc] = S(0);
-                if (TT) TT[cc * ldt + o + i] = S(0);
+                if constexpr (WB) Tb[(o + i) * ldt + cc] = S(0);
+                if constexpr (WK) Tk[(o + i) * ldt + cc] = S(0);
+                if constexpr (WT) TT[cc * ldt + o + i] = S(0);
             }
         }
     }
@@ -351,15 +384,15 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
             }
             const int col = 16 * bj + r;
-            const float sb = cb ? cb[col] : 0.f, sk = ck ? ck[col] : 0.f;
+            const float sb = WB ? cb[col] : 0.f, sk = WK ? ck[col] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * bi + 4 * kq + e;
                 const float t = -acc[e];
                 Tm[row * LDF + col] = t;
-                if (Tb) Tb[row * ldt + col] = from_f<BF>(t * sb);
-                if (Tk) Tk[row * ldt + col] = from_f<BF>(t * sk);
-                if (TT) TT[col * ldt + row] = from_f<BF>(t);
+                if constexpr (WB) Tb[row * ldt + col] = from_f<BF>(t * sb);
+                if constexpr (WK) Tk[row * ldt + col] = from_f<BF>(t * sk);
+                if constexpr (WT) TT[col * ldt + row] = from_f<BF>(t);
             }
         }
         __syncthreads();

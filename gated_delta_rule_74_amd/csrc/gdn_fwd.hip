@@ -53,7 +53,7 @@ __device__ __forceinline__ void store_global(const f32x4 *acc, typename Op<BF>::
     });
 }
 
-template <bool BF, int D>
+template <bool BF, int D, bool VEC>
 __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -80,21 +80,22 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = (size_t)b * T + t0;
-    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
 
     ChunkFrag<BF, D> fk, fv;
-    fk.fetch((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
-    fv.fetch((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, vecv, tid);
+    fk.template fetch<VEC>((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+    fv.template fetch<VEC>((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
     if (wave == 0) {
-        const size_t gi = (row0 + lane) * H + h;
-        const float g = lane < n ? s.g[gi] : 0.f, be = lane < n ? s.beta[gi] : 0.f;
+        const float gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        const float br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
+        const float g = lane < n ? gr : 0.f, be = lane < n ? br : 0.f;
         const Decay dc = decay_lane(g, -exp((double)s.A_log[h]) * LOG2E, lane);
         gam2[lane] = dc.gam2;
         bet[lane] = be;
         ck[lane] = be * dc.eg;
     }
-    fk.stash(Ks, LDD, KT, LDC, tid);
-    fv.stash(nullptr, 0, VT, LDC, tid);
+    fk.stash(Ks, LDD, tid);
+    fk.stash_T(KT, LDC, tid);
+    fv.stash_T(VT, LDC, tid);
     __syncthreads();
 
     if (!s.additive) {
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
             Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f;
         });
         __syncthreads(); // L complete, Ks no longer read
-        tri_inverse<BF>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
+        tri_inverse<BF, true, true, false>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
             const int row = e / C, col = e % C;
@@ -157,7 +158,7 @@ template <bool BF, int D, int BV> struct FwdChainSmem {
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-template <bool BF, int D, int BV>
+template <bool BF, int D, int BV, bool VEC>
 __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -193,7 +194,6 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     const S *NK = (const S *)a.NK;
     S *o = (S *)a.o;
     S *cs = (S *)a.cs;
-    const bool veck = (dk % O::VEC) == 0, vecv = (dv % O::VEC) == 0;
 
     // state h[D][BV] (fp32) lives in the accumulators of the h-update product
     f32x4 accH[Tiles<DT, VT>::PW];
@@ -209,11 +209,11 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     auto fetch = [&](int c) {
         const int t0 = c * C, n = min(C, T - t0);
         const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
-        fk.fetch(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
-        fq.fetch(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, veck, tid);
-        if (!s.additive) fn.fetch(NK + cb * C * dk, (size_t)dk, n, dk, veck, tid);
-        fu.fetch(U + cb * C * dv + v0, (size_t)dv, n, nvc, vecv, tid);
-        if (wave == 0) pg = lane < n ? s.g[(row0 + lane) * H + h] : 0.f;
+        fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
+        fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
+        if (wave == 0) pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
     };
     fetch(0);
 
@@ -227,16 +227,17 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
             });
         }
         if (wave == 0) {
-            const Decay dc = decay_lane(pg, A2, lane);
+            const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
             gam2[lane] = dc.gam2;
             eg[lane] = dc.eg;
             egn[lane] = dc.egn;
             if (lane == 0) misc[0] = dc.eglast;
         }
-        fk.stash(Ks, LDD, KT, LDC, tid);
-        fq.stash(Qs, LDD, nullptr, 0, tid);
-        if (!s.additive) fn.stash(NKs, LDD, nullptr, 0, tid);
-        fu.stash(Us, LDV, nullptr, 0, tid);
+        fk.stash(Ks, LDD, tid);
+        fk.stash_T(KT, LDC, tid);
+        fq.stash(Qs, LDD, tid);
+        if (!s.additive) fn.stash(NKs, LDD, tid);
+        fu.stash(Us, LDV, tid);
         if (c + 1 < s.NC) fetch(c + 1);
         __syncthreads();
 
@@ -302,14 +303,20 @@ int fwd_vblock(int D) { return D >= 64 ? 32 : 16; }
 
 template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStream_t st) {
     const int grid = a.s.B * a.s.H * a.s.NC;
-    hipLaunchKernelGGL((fwd_prep_kernel<BF, D>), dim3(grid), dim3(NTHR), 0, st, a);
+    if (vec_ok<BF>(a.s))
+        hipLaunchKernelGGL((fwd_prep_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    else
+        hipLaunchKernelGGL((fwd_prep_kernel<BF, D, false>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 
 template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
     constexpr int BV = (D >= 64) ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
-    hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV>), dim3(grid), dim3(NTHR), 0, st, a);
+    if (vec_ok<BF>(a.s))
+        hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    else
+        hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, false>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 

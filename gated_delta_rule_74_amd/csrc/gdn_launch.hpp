@@ -59,6 +59,13 @@ struct StepArgs {
     int N, H, dk, dv, additive;
 };
 
+// 16-byte vector loads are possible when every row of q/k/v (and of the
+// per-chunk blocks) starts on a 16-byte boundary.
+template <bool BF> inline bool vec_ok(const SeqArgs &s) {
+    const int v = BF ? 8 : 4;
+    return s.dk % v == 0 && s.dv % v == 0;
+}
+
 // Padded head dimension the kernels are instantiated for.
 int pad_dim(int d, bool bf16);
 int fwd_vblock(int D);

@@ -138,6 +138,15 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
                       const float *beta, const float *A_log, const float *h_in, float *h_out,
                       void *o, void *stream);
 
+/* Timing aid for benchmarks (no effect on results). While `events` is
+ * non-NULL, every kernel the library launches from this thread is bracketed
+ * by hipEventRecord calls on the launch's stream: events[2i] before launch i
+ * and events[2i+1] after it, for the first n/2 launches counted from this
+ * call (later launches are not bracketed). `events` points to n hipEvent_t
+ * handles owned by the caller; NULL switches the aid off. Returns the number
+ * of launches bracketed since the previous call. */
+int32_t gdn_time_launches(void *const *events, int32_t n);
+
 const char *gdn_status_string(gdn_status_t st);
 const char *gdn_last_error_detail(void);
 
