@@ -209,7 +209,7 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int oSv = oDbet + C * 4;
     static constexpr int oPart = oSv + C * 4;            // [C][4] row/col partials
     static constexpr int oMisc = oPart + C * 4 * 4;
-    static constexpr int SIZE = oMisc + 64;
+    static constexpr int SIZE = oMisc + (16 + NWAVE) * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -418,11 +418,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
-        if (lane == 0) misc[4 + wave] = hd;
+        if (lane == 0) misc[16 + wave] = hd;
         if (tid < C) sv[tid] = 0.f;
         add_rows<4, DT>(sx, part, sv, 1.f, tid, wave, lane);
         if (tid == 0) {
-            const float hds = (misc[4] + misc[5]) + (misc[6] + misc[7]);
+            float hds = 0.f;
+            for (int w = 0; w < NWAVE; ++w) hds += misc[16 + w];
             float ssum = 0.f;
             for (int j = 0; j < C; ++j) ssum += sv[j];
             misc[8] = misc[0] * hds + ssum; // dgam_n contribution

@@ -2,11 +2,12 @@
 //
 // Conventions used by every kernel:
 //  * a chunk is C = 64 tokens ("GDN & MLA Mechanism Deep-Dive", Step 5 and
-//    the portal's "CHUNK 64"); a workgroup is 256 threads = 4 wave64s;
+//    the portal's "CHUNK 64"); a workgroup is 512 threads = 8 wave64s (two per SIMD,
+//    so one wave's latency is covered by the other's work);
 //  * matrices live in LDS row-major with a 16-byte row pad; a product
 //    C += A * B reads A as [M][K] and B as its transpose BT = [N][K] (both
 //    K-contiguous), so one 16-byte LDS read feeds one bf16 MFMA operand;
-//  * 16x16 output tiles are spread over the 4 waves (tile t -> wave t % 4);
+//  * 16x16 output tiles are spread over the 8 waves (tile t -> wave t % 8);
 //    inside a tile, lane l holds column (l % 16) and rows 4*(l/16) .. +3,
 //    the accumulator layout of v_mfma_f32_16x16x32_bf16 / _16x16x4_f32;
 //  * operands are bf16 (inputs in bf16) or fp32 (inputs in fp32); state,
@@ -21,8 +22,8 @@
 namespace gdn {
 
 constexpr int C = 64;
-constexpr int NTHR = 256;
-constexpr int NWAVE = 4;
+constexpr int NTHR = 512;
+constexpr int NWAVE = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -312,7 +313,8 @@ constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 // substitution (one wave each), off-diagonal blocks by block forward
 // substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
-// level by level (i - j = 1, 2, 3) with fp32 MFMA. xs: 4 x 16 x 17 floats.
+// level by level (i - j = 1, 2, 3) with fp32 MFMA; waves 0..3 do the work.
+// xs: 4 x 16 x 17 floats.
 // Operand copies written as the blocks are produced ([C][ldt]), each only
 // when its flag is set: Tb = T diag(cb) (WB), Tk = T diag(ck) (WK), both
 // column-scaled, and TT = T^T (WT).
@@ -323,7 +325,7 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
                                             typename Op<BF>::S *TT, int ldt, const float *cb,
                                             const float *ck) {
     using S = typename Op<BF>::S;
-    {
+    if (wave < 4) {
         // column c of the inverse of the diagonal block, right-looking
         // substitution: once x_i is final, fold it into every later row
         // (independent updates, dependency depth 16)
@@ -358,9 +360,9 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
     }
     __syncthreads();
     const int r = lane & 15, kq = lane >> 4;
-    float *X = xs + wave * 16 * 17;
+    float *X = xs + (wave & 3) * 16 * 17;
     for (int s = 1; s < 4; ++s) {
-        const int bi = s + wave, bj = wave; // block (bi, bj), bi - bj = s
+        const int bi = wave < 4 ? s + wave : 4, bj = wave; // block (bi, bj), bi - bj = s
         if (bi < 4) {
             f32x4 acc = zero4();
             for (int bk = bj; bk < bi; ++bk) {
