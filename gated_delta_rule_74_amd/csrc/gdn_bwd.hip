@@ -204,43 +204,12 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
     static constexpr int oG = oBet + C * 4;
-    static constexpr int oDgam = oG + C * 4;
-    static constexpr int oDbet = oDgam + C * 4;
-    static constexpr int oSv = oDbet + C * 4;
-    static constexpr int oPart = oSv + C * 4;            // [C][4] row/col partials
-    static constexpr int oMisc = oPart + C * 4 * 4;
+    static constexpr int oMisc = oG + C * 4;
     static constexpr int SIZE = oMisc + (16 + NWAVE) * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
+    // the final row/column partial sums reuse the U region
+    static_assert((3 * C * (D / 16) + 3 * C * 4) * 4 <= sCD, "partials must fit over U");
 };
-
-// dst[row] (+)= sign * sum over the row of x, in a fixed order.
-template <int MT, int NT>
-__device__ __forceinline__ void add_rows(const f32x4 *x, float *part, float *dst, float sign, int tid,
-                                         int wave, int lane) {
-    row_partials<MT, NT>(x, part, wave, lane);
-    __syncthreads();
-    if (tid < MT * 16) {
-        float acc = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc += part[tid * NT + t];
-        dst[tid] += sign * acc;
-    }
-    __syncthreads();
-}
-
-template <int MT, int NT>
-__device__ __forceinline__ void add_cols(const f32x4 *x, float *part, float *dst, float sign, int tid,
-                                         int wave, int lane) {
-    col_partials<MT, NT>(x, part, wave, lane);
-    __syncthreads();
-    if (tid < NT * 16) {
-        float acc = 0.f;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc += part[tid * MT + t];
-        dst[tid] += sign * acc;
-    }
-    __syncthreads();
-}
 
 template <bool BF, int D, bool VEC>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
@@ -276,10 +245,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     float *egn = (float *)(smem + L::oEgn);
     float *bet = (float *)(smem + L::oBet);
     float *gch = (float *)(smem + L::oG);
-    float *dgam = (float *)(smem + L::oDgam);
-    float *dbet = (float *)(smem + L::oDbet);
-    float *sv = (float *)(smem + L::oSv);
-    float *part = (float *)(smem + L::oPart);
     float *misc = (float *)(smem + L::oMisc);
 
     const SeqArgs &s = a.s;
@@ -320,8 +285,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     if (wave == 0) {
         gch[lane] = lane < n ? gr : 0.f;
         bet[lane] = lane < n ? br : 0.f;
-        dgam[lane] = 0.f;
-        dbet[lane] = 0.f;
         const Decay dc = decay_lane(gch[lane], A * LOG2E, lane);
         gam[lane] = dc.gam2;
         eg[lane] = dc.eg;
@@ -385,6 +348,16 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         store_T<BF, 4, DT>(accdW, Re, LDC, wave, lane);  // dWT over Tb
     }
     __syncthreads();
+    // Contributions to dbeta and dgam are accumulated per lane, at the
+    // (row, col) positions this lane owns, and reduced once at the end:
+    //   rbD/rgD/rsD: row sums over [C][D] grids (dbeta, dgam, s_j)
+    //   rbC/rgC: row sums and cgC: column sums over [C][C] grids
+    f32x4 rbD[PWD], rgD[PWD], rsD[PWD], rbC[PWC], rgC[PWC], cgC[PWC];
+#pragma unroll
+    for (int i = 0; i < PWD; ++i) rbD[i] = rgD[i] = rsD[i] = zero4();
+#pragma unroll
+    for (int i = 0; i < PWC; ++i) rbC[i] = rgC[i] = cgC[i] = zero4();
+
     // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
     fh.stash(F1a, LDD, tid); // h
     fd.stash(F1b, LDD, tid); // dh'
@@ -404,13 +377,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
         gemm<BF, 4, DT, D>(Ws, LDD, F1b, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
-        f32x4 sx[PWD];
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];
             accKd[i][e] = x;
-            sx[i][e] = x * to_f(Ks[row * LDD + col]);
+            rsD[i][e] = x * to_f(Ks[row * LDD + col]);
         });
-        // <h, dh'> partial sums per thread, then a fixed-order wave/workgroup sum
+        // <h, dh'>: per-thread partial sums, a wave butterfly, one slot per wave
         float hd = 0.f;
         for (int e = tid; e < D * D; e += NTHR) {
             const int i = e / D, j = e % D;
@@ -419,20 +391,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
         if (lane == 0) misc[16 + wave] = hd;
-        if (tid < C) sv[tid] = 0.f;
-        add_rows<4, DT>(sx, part, sv, 1.f, tid, wave, lane);
-        if (tid == 0) {
-            float hds = 0.f;
-            for (int w = 0; w < NWAVE; ++w) hds += misc[16 + w];
-            float ssum = 0.f;
-            for (int j = 0; j < C; ++j) ssum += sv[j];
-            misc[8] = misc[0] * hds + ssum; // dgam_n contribution
-        }
-        __syncthreads();
-        if (tid < C) dgam[tid] -= sv[tid];
-        __syncthreads();
-        if (tid == 0) dgam[C - 1] += misc[8];
     }
+    __syncthreads(); // F2b (dW) reads done
     if (!add) {
 #pragma unroll
         for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = -accM[i];
@@ -447,25 +407,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, DT, C>(TT, LDC, Re, LDC, accV, wave, lane);
         if (!add) gemm<BF, 4, DT, C>(TT, LDC, F2b, LDC, accKp, wave, lane);
         S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
-        f32x4 x1[PWD], x2[PWD];
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < n && col < dv) dv_out[(size_t)row * H * dv + col] = from_f<BF>(bet[row] * accV[i][e]);
-            x1[i][e] = to_f(VT[col * LDC + row]) * accV[i][e];          // v_i . dV'_i
-            const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e];  // k_i . dK'_i
-            x2[i][e] = kk;
+            const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
+            rbD[i][e] += to_f(VT[col * LDC + row]) * accV[i][e] + eg[row] * kk;
+            rgD[i][e] += bet[row] * eg[row] * kk;
             accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
         });
-        add_rows<4, DT>(x1, part, dbet, 1.f, tid, wave, lane);
         if (!add) {
-            row_partials<4, DT>(x2, part, wave, lane);
-            __syncthreads();
-            if (tid < C) {
-                float acc = 0.f;
-                for (int t = 0; t < DT; ++t) acc += part[tid * DT + t];
-                dbet[tid] += eg[tid] * acc;
-                dgam[tid] += bet[tid] * eg[tid] * acc;
-            }
-            __syncthreads();
+            __syncthreads(); // F1 (h, dh') reads done
 #pragma unroll
             for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
             store_N<BF, 4, DT>(accV, F1a, LDD, wave, lane);  // -dV'
@@ -480,17 +430,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWC; ++i) accL[i] = zero4();
         gemm<BF, 4, 4, D>(F1a, LDD, Us, LDD, accL, wave, lane);
         gemm<BF, 4, 4, D>(F1b, LDD, Kws, LDD, accL, wave, lane);
-        f32x4 xb[PWC], xg[PWC];
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
             const float kkg = to_f(KKG[row * LDC + col]);
-            xb[i][e] = dl * kkg;
-            xg[i][e] = dl * bet[row] * kkg; // dL o L
+            const float xl = dl * bet[row] * kkg; // dL o L
+            rbC[i][e] += dl * kkg;
+            rgC[i][e] += xl;
+            cgC[i][e] += xl;
             accL[i][e] = bet[row] * dl * gamma_ij(gam, row, col);
         });
-        add_rows<4, 4>(xb, part, dbet, 1.f, tid, wave, lane);
-        add_rows<4, 4>(xg, part, dgam, 1.f, tid, wave, lane);
-        add_cols<4, 4>(xg, part, dgam, -1.f, tid, wave, lane);
         store_N<BF, 4, 4>(accL, dSs, LDC, wave, lane);
         store_T<BF, 4, 4>(accL, Re, LDC, wave, lane);
         __syncthreads();
@@ -505,15 +453,14 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accP[i] = zero4();
         gemm<BF, 4, 4, D>(Rf, LDD, Ws, LDD, accP, wave, lane);
-        f32x4 xm[PWC];
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const bool low = row >= col;
             const float dp = low ? accP[i][e] : 0.f;
-            xm[i][e] = dp * to_f(PT[col * LDC + row]);
+            const float xm = dp * to_f(PT[col * LDC + row]); // dP o P
+            rgC[i][e] += xm;
+            cgC[i][e] += xm;
             accP[i][e] = low ? dp * gamma_ij(gam, row, col) : 0.f;
         });
-        add_rows<4, 4>(xm, part, dgam, 1.f, tid, wave, lane);
-        add_cols<4, 4>(xm, part, dgam, -1.f, tid, wave, lane);
         store_N<BF, 4, 4>(accP, dPG, LDC, wave, lane);
         store_T<BF, 4, 4>(accP, Re, LDC, wave, lane);
         fq.stash_T(F1a, LDC, tid); // Q^T
@@ -521,12 +468,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     __syncthreads();
     // ---- P10: dQ, dK
     {
-        f32x4 xq[PWD];
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             accQ[i][e] *= eg[row];
-            xq[i][e] = accQ[i][e] * to_f(F1a[col * LDC + row]);
+            rgD[i][e] += accQ[i][e] * to_f(F1a[col * LDC + row]); // e^{gam_i} q_i . dOh_i
         });
-        add_rows<4, DT>(xq, part, dgam, 1.f, tid, wave, lane);
         gemm<BF, 4, DT, C>(dPG, LDC, KT, LDC, accQ, wave, lane);
         gemm<BF, 4, DT, C>(Re, LDC, F1a, LDC, accKd, wave, lane);
         S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
@@ -538,24 +483,58 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             }
         });
     }
-    // ---- P11: dlam = reverse cumsum of dgam; dg = A dlam; dbeta; dA_log part
-    if (wave == 0) {
-        float x = dgam[lane];
+    // ---- P11: one fixed-order reduction of every dbeta / dgam contribution
+    {
+        float *pRbD = (float *)Us, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
+        float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
+        row_partials<4, DT>(rbD, pRbD, wave, lane);
+        row_partials<4, DT>(rgD, pRgD, wave, lane);
+        row_partials<4, DT>(rsD, pRsD, wave, lane);
+        row_partials<4, 4>(rbC, pRbC, wave, lane);
+        row_partials<4, 4>(rgC, pRgC, wave, lane);
+        col_partials<4, 4>(cgC, pCgC, wave, lane);
+        __syncthreads();
+        if (wave == 0) {
+            const int i = lane;
+            float db = 0.f, dgm = 0.f, sj = 0.f;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_down(x, off, 64);
-            if (lane + off < 64) x += o;
-        }
-        const float dg = (float)A * x;
-        float p = (lane < n) ? gch[lane] * dg : 0.f;
-        if (lane < n) {
-            const size_t gi = (row0 + lane) * H + h;
-            a.dg[gi] = dg;
-            a.dbeta[gi] = dbet[lane];
-        }
+            for (int t = 0; t < DT; ++t) {
+                db += pRbD[i * DT + t];
+                dgm += pRgD[i * DT + t];
+                sj += pRsD[i * DT + t];
+            }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
-        if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
+            for (int t = 0; t < 4; ++t) {
+                db += pRbC[i * 4 + t];
+                dgm += pRgC[i * 4 + t] - pCgC[i * 4 + t];
+            }
+            // gam_n enters through e^{gam_n} h and e^{gam_n - gam_j}: its gradient
+            // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row; -s_j to row j
+            float stot = sj;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) stot += __shfl_xor(stot, off, 64);
+            float hds = 0.f;
+            for (int w = 0; w < NWAVE; ++w) hds += misc[16 + w];
+            dgm -= sj;
+            if (i == C - 1) dgm += misc[0] * hds + stot;
+            // dlam_r = sum_{i >= r} dgam_i
+            float x = dgm;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += o;
+            }
+            const float dg = (float)A * x;
+            float p = (lane < n) ? gch[lane] * dg : 0.f;
+            if (lane < n) {
+                const size_t gi = (row0 + lane) * H + h;
+                a.dg[gi] = dg;
+                a.dbeta[gi] = db;
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+            if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
+        }
     }
 }
 

@@ -401,10 +401,26 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
     }
 }
 
+// x moved from lane (l ^ 1) / (l ^ 2) / mirrored within 8 / mirrored within
+// 16 lanes: data-parallel-primitive moves inside a 16-lane row.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF,
+                                                                 0xF, true));
+}
+
+// Sum over the 16 lanes of a row; every lane of the row gets the total.
+__device__ __forceinline__ float sum16(float x) {
+    x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x); // row_half_mirror
+    x += dpp_f<0x140>(x); // row_mirror
+    return x;
+}
+
 // Per-tile row sums of x (x[i][e] is this lane's value at (row, col) of tile
-// i): the 16 lanes of a row group are summed by a butterfly, and lane r == 0
-// writes part[row * NT + tn]. Every (row, tn) slot has exactly one writer, so
-// a later fixed-order sum over tn is deterministic.
+// i): the 16 lanes of a row group are summed inside their row, and lane
+// r == 0 writes part[row * NT + tn]. Every (row, tn) slot has exactly one
+// writer, so a later fixed-order sum over tn is deterministic.
 template <int MT, int NT>
 __device__ __forceinline__ void row_partials(const f32x4 *x, float *part, int wave, int lane) {
     const int r = lane & 15, kq = lane >> 4;
@@ -415,10 +431,7 @@ __device__ __forceinline__ void row_partials(const f32x4 *x, float *part, int wa
         const int tm = t / NT, tn = t % NT;
         f32x4 s = x[i];
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] += __shfl_xor(s[e], off, 64);
-        }
+        for (int e = 0; e < 4; ++e) s[e] = sum16(s[e]);
         if (r == 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) part[(tm * 16 + 4 * kq + e) * NT + tn] = s[e];
