@@ -169,46 +169,45 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 }
 
 // --------------------------------------------------------------- local
+//
+// Storage: inputs (K, Q, V, dO, -Kw, h, dh') are stashed once as they are in
+// memory (token rows, or state rows); every product result is stored once,
+// transposed with packed writes ("t" suffix: Xt[col][row] = X[row][col]).
+// Each product reads an operand straight or through the transposing LDS
+// read, whichever its storage needs (gemm<..., ATR, BTR>).
 
 template <bool BF, int D> struct LocalSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
-    static constexpr int sCD = C * LDD * (int)sizeof(S);
-    static constexpr int sDC = D * LDC * (int)sizeof(S);
-    static constexpr int sCC = C * LDC * (int)sizeof(S);
-    static constexpr int sDD = D * LDD * (int)sizeof(S);
-    static constexpr int sF = C * LDF * 4;
     static constexpr int mx(int x, int y) { return x > y ? x : y; }
-    static constexpr int h1 = mx(mx(sDC, sDD), sCD);
-    static constexpr int oKs = 0;                        // Ks
-    static constexpr int oKT = oKs + sCD;                // KT
-    static constexpr int oPT = oKT + sDC;                // PT
-    static constexpr int oKKG = oPT + sCC;               // K K^T o Gam
-    static constexpr int oRa = oKKG + sCC;               // Qs -> TT -> dS -> dPG
-    static constexpr int szRa = mx(sCD, sCC);
-    static constexpr int oF1 = oRa + szRa;               // L | dOT,dHT | Hs,dHs | dVs,dKps | QT
-    static constexpr int szF1 = mx(sF, 2 * h1);
-    static constexpr int oF2 = oF1 + szF1;               // Tm | VT, HT -> dWs -> dKwT
-    static constexpr int szF2 = mx(sF, sDC + h1);
-    static constexpr int oRb = oF2 + szF2;               // Us
-    static constexpr int oRc = oRb + sCD;                // -Kw
-    static constexpr int oRd = oRc + sCD;                // Ws
-    static constexpr int oRe = oRd + sCD;                // Tb -> dWT -> dST -> dPGT
-    static constexpr int szRe = mx(sCC, sDC);
-    static constexpr int oRf = oRe + szRe;               // dOs
-    static constexpr int szRf = sCD;
-    static constexpr int oX = oRf + szRf;                // solve scratch
-    static constexpr int oGam = oX + 4 * 16 * 17 * 4;    // double[C]
+    static constexpr int sCD = C * LDD * (int)sizeof(S); // token rows [C][D]
+    static constexpr int sDC = D * LDC * (int)sizeof(S); // [D][C]
+    static constexpr int sDD = D * LDD * (int)sizeof(S); // state [D][D]
+    static constexpr int sCC = C * LDC * (int)sizeof(S); // [C][C]
+    static constexpr int sF = C * LDF * 4;                // fp32 [C][C]
+    static constexpr int oK = 0;                           // K (all phases)
+    static constexpr int oA = oK + sCD;                    // Q -> Tt
+    static constexpr int oB = oA + mx(sCD, sCC);           // Pt -> dKw -> dSt -> dPGt
+    static constexpr int oTb = oB + mx(sCC, sCD);          // Tb -> dO -> final partials
+    static constexpr int oE = oTb + mx(sCC, sCD);          // L fp32 -> V | h
+    static constexpr int szE = mx(sF, sCD + sDD);
+    static constexpr int oG = oE + szE;                    // Tm fp32 -> -Kw | Ut
+    static constexpr int szG = mx(sF, sCD + sDC);
+    static constexpr int oW = oG + szG;                    // Wt
+    static constexpr int oH = oW + sDC;                    // dh' -> -dV't
+    static constexpr int oL = oH + mx(sDD, sDC);           // dWt -> dK't -> Q
+    static constexpr int oX = oL + mx(sDC, sCD);           // solve scratch
+    static constexpr int oGam = oX + 4 * 16 * 17 * 4;
     static constexpr int oEg = oGam + C * 8;
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
-    static constexpr int oG = oBet + C * 4;
-    static constexpr int oMisc = oG + C * 4;
+    static constexpr int oGch = oBet + C * 4;
+    static constexpr int oMisc = oGch + C * 4;
     static constexpr int SIZE = oMisc + (16 + NWAVE) * 4;
+    static constexpr int SLOT_E2 = sCD; // offset of the second half of E / G
     static_assert(SIZE <= 160 * 1024, "LDS budget");
-    // the final row/column partial sums reuse the U region
-    static_assert((3 * C * (D / 16) + 3 * C * 4) * 4 <= sCD, "partials must fit over U");
+    static_assert((3 * C * (D / 16) + 3 * C * 4) * 4 <= mx(sCC, sCD), "partials must fit over Tb");
 };
 
 template <bool BF, int D, bool VEC>
@@ -216,35 +215,30 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
     using L = LocalSmem<BF, D>;
-    constexpr int LDD = L::LDD, LDC = L::LDC;
-    constexpr int DT = D / 16;
+    constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
     constexpr int PWC = Tiles<4, 4>::PW, PWD = Tiles<4, DT>::PW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
-    S *Ks = (S *)(smem + L::oKs);
-    S *KT = (S *)(smem + L::oKT);
-    S *PT = (S *)(smem + L::oPT);
-    S *KKG = (S *)(smem + L::oKKG);
-    S *Qs = (S *)(smem + L::oRa);
-    S *TT = (S *)(smem + L::oRa);
-    S *dSs = (S *)(smem + L::oRa);
-    S *dPG = (S *)(smem + L::oRa);
-    float *Lm = (float *)(smem + L::oF1);
-    S *F1a = (S *)(smem + L::oF1);
-    S *F1b = (S *)(smem + L::oF1 + L::h1);
-    float *Tm = (float *)(smem + L::oF2);
-    S *VT = (S *)(smem + L::oF2);
-    S *F2b = (S *)(smem + L::oF2 + L::sDC);
-    S *Us = (S *)(smem + L::oRb);
-    S *Kws = (S *)(smem + L::oRc);
-    S *Ws = (S *)(smem + L::oRd);
-    S *Re = (S *)(smem + L::oRe);
-    S *Rf = (S *)(smem + L::oRf);
+    S *Ks = (S *)(smem + L::oK);
+    S *Qs = (S *)(smem + L::oA);
+    S *Tt = (S *)(smem + L::oA);
+    S *Rb = (S *)(smem + L::oB);
+    S *Tb = (S *)(smem + L::oTb);
+    S *dOs = (S *)(smem + L::oTb);
+    float *Lm = (float *)(smem + L::oE);
+    S *Vs = (S *)(smem + L::oE);
+    S *hs = (S *)(smem + L::oE + L::SLOT_E2);
+    float *Tm = (float *)(smem + L::oG);
+    S *NKs = (S *)(smem + L::oG);
+    S *Ut = (S *)(smem + L::oG + L::SLOT_E2);
+    S *Wt = (S *)(smem + L::oW);
+    S *Rh = (S *)(smem + L::oH);
+    S *Rl = (S *)(smem + L::oL);
     float *xs = (float *)(smem + L::oX);
     double *gam = (double *)(smem + L::oGam);
     float *eg = (float *)(smem + L::oEg);
     float *egn = (float *)(smem + L::oEgn);
     float *bet = (float *)(smem + L::oBet);
-    float *gch = (float *)(smem + L::oG);
+    float *gch = (float *)(smem + L::oGch);
     float *misc = (float *)(smem + L::oMisc);
 
     const SeqArgs &s = a.s;
@@ -275,13 +269,23 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     if (!add) fn.template fetch<VEC>(nk, (size_t)dk, n, dk, tid);
     fh.template fetch<VEC>(hc, (size_t)dv, dk, dv, tid);
     fd.template fetch<VEC>(dhc, (size_t)dv, dk, dv, tid);
-
-    // ---- P1: K, Q, gates; Grams
     float gr = 0.f, br = 0.f;
     if (wave == 0) {
         gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
         br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
     }
+
+    // Contributions to dbeta and dgam, accumulated per lane at the (row, col)
+    // positions this lane owns and reduced once at the end:
+    //   rbD / rgD / rsD: row sums over [C][D] grids (dbeta, dgam, s_j)
+    //   rbC: row sums, xgC: row sums minus column sums over [C][C] grids
+    f32x4 rbD[PWD], rgD[PWD], rsD[PWD], rbC[PWC], xgC[PWC];
+#pragma unroll
+    for (int i = 0; i < PWD; ++i) rbD[i] = rgD[i] = rsD[i] = zero4();
+#pragma unroll
+    for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
+
+    // ---- P1: gates, decay, K K^T and Q K^T
     if (wave == 0) {
         gch[lane] = lane < n ? gr : 0.f;
         bet[lane] = lane < n ? br : 0.f;
@@ -292,9 +296,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         if (lane == 0) misc[0] = dc.eglast;
     }
     fk.stash(Ks, LDD, tid);
-    fk.stash_T(KT, LDC, tid);
     fq.stash(Qs, LDD, tid);
     __syncthreads();
+    // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
+    f32x4 gC[PWC], kkg[PWC], pC[PWC];
     {
         f32x4 sk[PWC], sq[PWC];
 #pragma unroll
@@ -303,100 +308,93 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float G = gamma_ij(gam, row, col);
-            const float kkg = (row > col) ? sk[i][e] * G : 0.f;
-            Lm[row * LDF + col] = bet[row] * kkg;
-            KKG[row * LDC + col] = from_f<BF>(kkg);
-            PT[col * LDC + row] = from_f<BF>(sq[i][e] * G);
+            gC[i][e] = G;
+            kkg[i][e] = (row > col) ? sk[i][e] * G : 0.f;
+            Lm[row * LDF + col] = bet[row] * kkg[i][e];
+            pC[i][e] = sq[i][e] * G;
         });
+        store_T<BF, 4, 4>(pC, Rb, LDC, wave, lane); // Pt
     }
     __syncthreads();
-    // ---- P2: Tm with Tb = Tm diag(beta) (Re) and TT = Tm^T (Ra)
+    // ---- P2: Tm; Tb = Tm diag(beta) and Tt = Tm^T, both row-major
     if (!add) {
-        tri_inverse<BF, true, false, true>(Lm, Tm, xs, wave, lane, Re, nullptr, TT, LDC, bet, nullptr);
+        tri_inverse<BF, true, false, true>(Lm, Tm, xs, wave, lane, Tb, nullptr, Tt, LDC, bet, nullptr);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
             const int row = e / C, col = e % C;
-            Re[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
-            TT[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
+            Tb[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
+            Tt[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
         }
         __syncthreads();
     }
-    // ---- P3: U, Kw, W
-    fv.stash_T(VT, LDC, tid);
-    fh.stash_T(F2b, LDD, tid); // h^T
-    if (!add) fn.stash(Kws, LDD, tid); // -Kw
+    // ---- P3: U = Tb V, W = U - Kw h
+    fv.stash(Vs, LDD, tid);
+    fh.stash(hs, LDD, tid);
+    if (!add) fn.stash(NKs, LDD, tid);
     __syncthreads();
-    f32x4 accW[PWD];
+    {
+        f32x4 accW[PWD];
 #pragma unroll
-    for (int i = 0; i < PWD; ++i) accW[i] = zero4();
-    gemm<BF, 4, DT, C>(Re, LDC, VT, LDC, accW, wave, lane); // U
-    store_N<BF, 4, DT>(accW, Us, LDD, wave, lane);
-    if (!add) gemm<BF, 4, DT, D>(Kws, LDD, F2b, LDD, accW, wave, lane); // W = U - Kw h
-    store_N<BF, 4, DT>(accW, Ws, LDD, wave, lane);
+        for (int i = 0; i < PWD; ++i) accW[i] = zero4();
+        gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, accW, wave, lane); // U
+        store_T<BF, 4, DT>(accW, Ut, LDC, wave, lane);
+        if (!add) gemm<BF, 4, DT, D, false, true>(NKs, LDD, hs, LDD, accW, wave, lane); // + (-Kw) h
+        store_T<BF, 4, DT>(accW, Wt, LDC, wave, lane);
+    }
+    __syncthreads(); // Tb free
     // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-    fo.stash_T(F1a, LDC, tid); // dO^T
-    fd.stash_T(F1b, LDD, tid); // dh'^T
+    fo.stash(dOs, LDD, tid);
+    fd.stash(Rh, LDD, tid);
     __syncthreads();
     {
         f32x4 accdW[PWD], accX[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
-        gemm<BF, 4, DT, C>(PT, LDC, F1a, LDC, accdW, wave, lane);
-        gemm<BF, 4, DT, D>(Ks, LDD, F1b, LDD, accX, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(Rb, LDC, dOs, LDD, accdW, wave, lane); // P^T dO
+        gemm<BF, 4, DT, D, false, true>(Ks, LDD, Rh, LDD, accX, wave, lane);   // K dh'
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
-        store_N<BF, 4, DT>(accdW, F2b, LDD, wave, lane); // dWs over h^T (read before the barrier)
-        store_T<BF, 4, DT>(accdW, Re, LDC, wave, lane);  // dWT over Tb
+        store_T<BF, 4, DT>(accdW, Rl, LDC, wave, lane); // dWt
     }
     __syncthreads();
-    // Contributions to dbeta and dgam are accumulated per lane, at the
-    // (row, col) positions this lane owns, and reduced once at the end:
-    //   rbD/rgD/rsD: row sums over [C][D] grids (dbeta, dgam, s_j)
-    //   rbC/rgC: row sums and cgC: column sums over [C][C] grids
-    f32x4 rbD[PWD], rgD[PWD], rsD[PWD], rbC[PWC], rgC[PWC], cgC[PWC];
-#pragma unroll
-    for (int i = 0; i < PWD; ++i) rbD[i] = rgD[i] = rsD[i] = zero4();
-#pragma unroll
-    for (int i = 0; i < PWC; ++i) rbC[i] = rgC[i] = cgC[i] = zero4();
-
     // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
-    fh.stash(F1a, LDD, tid); // h
-    fd.stash(F1b, LDD, tid); // dh'
-    fo.stash(Rf, LDD, tid);  // dO
-    __syncthreads();
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
-    gemm<BF, 4, DT, D>(Rf, LDD, F1a, LDD, accQ, wave, lane); // dO h^T
+    gemm<BF, 4, DT, D>(dOs, LDD, hs, LDD, accQ, wave, lane); // dO h^T
     f32x4 accM[Tiles<DT, 4>::PW];
 #pragma unroll
     for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = zero4();
-    if (!add) gemm<BF, DT, 4, D>(F1a, LDD, F2b, LDD, accM, wave, lane); // h dW^T
+    if (!add) gemm<BF, DT, 4, D, false, true>(hs, LDD, Rl, LDC, accM, wave, lane); // h dW^T
     {
         f32x4 accKt[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
-        gemm<BF, 4, DT, D>(Ws, LDD, F1b, LDD, accKt, wave, lane); // W dh'^T
+        gemm<BF, 4, DT, D, true, false>(Wt, LDC, Rh, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];
             accKd[i][e] = x;
             rsD[i][e] = x * to_f(Ks[row * LDD + col]);
         });
-        // <h, dh'>: per-thread partial sums, a wave butterfly, one slot per wave
+        // <h, dh'> from the register fragments: one butterfly, one slot per wave
         float hd = 0.f;
-        for (int e = tid; e < D * D; e += NTHR) {
-            const int i = e / D, j = e % D;
-            hd += to_f(F1a[i * LDD + j]) * to_f(F1b[i * LDD + j]);
+#pragma unroll
+        for (int m = 0; m < fh.NIT; ++m) {
+            typename ChunkFrag<BF, D, D>::U x, y;
+            x.u = fh.item(m);
+            y.u = fd.item(m);
+#pragma unroll
+            for (int e = 0; e < O::VEC; ++e) hd += to_f(x.s[e]) * to_f(y.s[e]);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
         if (lane == 0) misc[16 + wave] = hd;
     }
-    __syncthreads(); // F2b (dW) reads done
+    __syncthreads(); // Pt, dh' no longer read
     if (!add) {
 #pragma unroll
         for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = -accM[i];
-        store_N<BF, DT, 4>(accM, F2b, LDC, wave, lane); // dKw^T over dWs
+        store_T<BF, DT, 4>(accM, Rb, LDD, wave, lane); // dKw, token rows [C][D]
     }
     __syncthreads();
     // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw
@@ -404,22 +402,22 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         f32x4 accV[PWD], accKp[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
-        gemm<BF, 4, DT, C>(TT, LDC, Re, LDC, accV, wave, lane);
-        if (!add) gemm<BF, 4, DT, C>(TT, LDC, F2b, LDC, accKp, wave, lane);
+        gemm<BF, 4, DT, C>(Tt, LDC, Rl, LDC, accV, wave, lane);
+        if (!add) gemm<BF, 4, DT, C, false, true>(Tt, LDC, Rb, LDD, accKp, wave, lane);
         S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < n && col < dv) dv_out[(size_t)row * H * dv + col] = from_f<BF>(bet[row] * accV[i][e]);
             const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
-            rbD[i][e] += to_f(VT[col * LDC + row]) * accV[i][e] + eg[row] * kk;
+            rbD[i][e] += to_f(Vs[row * LDD + col]) * accV[i][e] + eg[row] * kk;
             rgD[i][e] += bet[row] * eg[row] * kk;
             accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
         });
         if (!add) {
-            __syncthreads(); // F1 (h, dh') reads done
+            __syncthreads(); // dh', dWt reads done
 #pragma unroll
             for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-            store_N<BF, 4, DT>(accV, F1a, LDD, wave, lane);  // -dV'
-            store_N<BF, 4, DT>(accKp, F1b, LDD, wave, lane); // dK'
+            store_T<BF, 4, DT>(accV, Rh, LDC, wave, lane);  // -dV't
+            store_T<BF, 4, DT>(accKp, Rl, LDC, wave, lane); // dK't
         }
     }
     __syncthreads();
@@ -428,23 +426,19 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         f32x4 accL[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accL[i] = zero4();
-        gemm<BF, 4, 4, D>(F1a, LDD, Us, LDD, accL, wave, lane);
-        gemm<BF, 4, 4, D>(F1b, LDD, Kws, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, true>(Rh, LDC, Ut, LDC, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, false>(Rl, LDC, NKs, LDD, accL, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
-            const float kkg = to_f(KKG[row * LDC + col]);
-            const float xl = dl * bet[row] * kkg; // dL o L
-            rbC[i][e] += dl * kkg;
-            rgC[i][e] += xl;
-            cgC[i][e] += xl;
-            accL[i][e] = bet[row] * dl * gamma_ij(gam, row, col);
+            rbC[i][e] += dl * kkg[i][e];
+            xgC[i][e] += dl * bet[row] * kkg[i][e]; // dL o L
+            accL[i][e] = bet[row] * dl * gC[i][e];
         });
-        store_N<BF, 4, 4>(accL, dSs, LDC, wave, lane);
-        store_T<BF, 4, 4>(accL, Re, LDC, wave, lane);
+        store_T<BF, 4, 4>(accL, Rb, LDC, wave, lane); // dSt
         __syncthreads();
         // ---- P8: dK += dS K + dS^T K
-        gemm<BF, 4, DT, C>(dSs, LDC, KT, LDC, accKd, wave, lane);
-        gemm<BF, 4, DT, C>(Re, LDC, KT, LDC, accKd, wave, lane);
+        gemm<BF, 4, DT, C, true, true>(Rb, LDC, Ks, LDD, accKd, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(Rb, LDC, Ks, LDD, accKd, wave, lane);
         __syncthreads();
     }
     // ---- P9: dP = dO W^T (lower incl. diagonal), dP o Gam
@@ -452,28 +446,24 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         f32x4 accP[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accP[i] = zero4();
-        gemm<BF, 4, 4, D>(Rf, LDD, Ws, LDD, accP, wave, lane);
+        gemm<BF, 4, 4, D, false, true>(dOs, LDD, Wt, LDC, accP, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            const bool low = row >= col;
-            const float dp = low ? accP[i][e] : 0.f;
-            const float xm = dp * to_f(PT[col * LDC + row]); // dP o P
-            rgC[i][e] += xm;
-            cgC[i][e] += xm;
-            accP[i][e] = low ? dp * gamma_ij(gam, row, col) : 0.f;
+            const float dp = row >= col ? accP[i][e] : 0.f;
+            xgC[i][e] += dp * pC[i][e]; // dP o P
+            accP[i][e] = dp * gC[i][e];
         });
-        store_N<BF, 4, 4>(accP, dPG, LDC, wave, lane);
-        store_T<BF, 4, 4>(accP, Re, LDC, wave, lane);
-        fq.stash_T(F1a, LDC, tid); // Q^T
+        store_T<BF, 4, 4>(accP, Rb, LDC, wave, lane); // dPGt
+        fq.stash(Rl, LDD, tid);                     // Q again
     }
     __syncthreads();
-    // ---- P10: dQ, dK
+    // ---- P10: dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
     {
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             accQ[i][e] *= eg[row];
-            rgD[i][e] += accQ[i][e] * to_f(F1a[col * LDC + row]); // e^{gam_i} q_i . dOh_i
+            rgD[i][e] += accQ[i][e] * to_f(Rl[row * LDD + col]); // e^{gam_i} q_i . dOh_i
         });
-        gemm<BF, 4, DT, C>(dPG, LDC, KT, LDC, accQ, wave, lane);
-        gemm<BF, 4, DT, C>(Re, LDC, F1a, LDC, accKd, wave, lane);
+        gemm<BF, 4, DT, C, true, true>(Rb, LDC, Ks, LDD, accQ, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(Rb, LDC, Rl, LDD, accKd, wave, lane);
         S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
         S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
@@ -485,14 +475,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     }
     // ---- P11: one fixed-order reduction of every dbeta / dgam contribution
     {
-        float *pRbD = (float *)Us, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
+        float *pRbD = (float *)Tb, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
         float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
+        __syncthreads(); // dO (same slot) no longer read
         row_partials<4, DT>(rbD, pRbD, wave, lane);
         row_partials<4, DT>(rgD, pRgD, wave, lane);
         row_partials<4, DT>(rsD, pRsD, wave, lane);
         row_partials<4, 4>(rbC, pRbC, wave, lane);
-        row_partials<4, 4>(rgC, pRgC, wave, lane);
-        col_partials<4, 4>(cgC, pCgC, wave, lane);
+        row_partials<4, 4>(xgC, pRgC, wave, lane);
+        col_partials<4, 4>(xgC, pCgC, wave, lane);
         __syncthreads();
         if (wave == 0) {
             const int i = lane;

@@ -85,11 +85,33 @@ template <int MT, int NT> struct Tiles {
     static constexpr int PW = (N + NWAVE - 1) / NWAVE;
 };
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
+// One MFMA operand (8 consecutive K values for row/column r = lane % 16 of a
+// 16-wide block) read from an LDS matrix stored with K as its row index,
+// X[k][m] (row stride ld): two transposing 64-bit reads. Lane s of k-group g
+// points at X[k0 + 8g + s/4 (+4)][m0 + 4(s%4)]; the hardware hands lane
+// 16g + j the values X[k0 + 8g + e][m0 + j], e = 0..3 (then 4..7).
+__device__ __forceinline__ bf16x8 operand_tr(const u16 *X, int ld, int k0, int m0, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const u16 *p = X + (k0 + 8 * g + (sl >> 2)) * ld + m0 + 4 * (sl & 3);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(p));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(p + 4 * ld));
+    uint4 u;
+    u.x = __builtin_bit_cast(uint2, lo).x;
+    u.y = __builtin_bit_cast(uint2, lo).y;
+    u.z = __builtin_bit_cast(uint2, hi).x;
+    u.w = __builtin_bit_cast(uint2, hi).y;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 // acc[i] += A * B over K = KD for the tiles of this wave.
-// A: [M][lda] row-major, BT: [N][ldb] row-major (B transposed).
-template <bool BF, int MT, int NT, int KD>
+// A is stored [M][K] (ATR = false) or [K][M] (ATR = true); B is stored [N][K]
+// (BTR = false, i.e. B transposed) or [K][N] (BTR = true). Row strides lda, ldb.
+template <bool BF, int MT, int NT, int KD, bool ATR = false, bool BTR = false>
 __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
-                                     const typename Op<BF>::S *BT, int ldb, f32x4 *acc, int wave,
+                                     const typename Op<BF>::S *B, int ldb, f32x4 *acc, int wave,
                                      int lane) {
     using O = Op<BF>;
     static_assert(KD % O::KSTEP == 0, "contraction length must be a multiple of the MFMA K");
@@ -99,10 +121,21 @@ __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
         const int t = wave + NWAVE * i;
         if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
         const int tm = t / NT, tn = t % NT;
-        const typename O::S *a = A + (tm * 16 + r) * lda + kq * O::KSUB;
-        const typename O::S *b = BT + (tn * 16 + r) * ldb + kq * O::KSUB;
 #pragma unroll
-        for (int k0 = 0; k0 < KD; k0 += O::KSTEP) acc[i] = mma(a + k0, b + k0, acc[i]);
+        for (int k0 = 0; k0 < KD; k0 += O::KSTEP) {
+            if constexpr (BF) {
+                const bf16x8 av = ATR ? operand_tr(A, lda, k0, tm * 16, lane)
+                                      : *reinterpret_cast<const bf16x8 *>(A + (tm * 16 + r) * lda + k0 + kq * 8);
+                const bf16x8 bv = BTR ? operand_tr(B, ldb, k0, tn * 16, lane)
+                                      : *reinterpret_cast<const bf16x8 *>(B + (tn * 16 + r) * ldb + k0 + kq * 8);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+            } else {
+                const int k = k0 + kq;
+                const float av = ATR ? A[k * lda + tm * 16 + r] : A[(tm * 16 + r) * lda + k];
+                const float bv = BTR ? B[k * ldb + tn * 16 + r] : B[(tn * 16 + r) * ldb + k];
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
+            }
+        }
     }
 }
 
