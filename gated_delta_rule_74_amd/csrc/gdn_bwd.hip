@@ -34,14 +34,14 @@ template <bool BF, int D, int BV> struct ChainSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
+    static constexpr int LDV = BV + Op<BF>::PAD;
     static constexpr int szCD = C * LDD * (int)sizeof(S);
-    static constexpr int szDC = D * LDC * (int)sizeof(S);
     static constexpr int oK = 0;                                  // Ks  [C][LDD]
     static constexpr int oQ = oK + szCD;                          // Qs  [C][LDD]
-    static constexpr int oQT = oQ + szCD;                         // QT  [D][LDC] (columns * e^gam)
-    static constexpr int oNKT = oQT + szDC;                       // NKT [D][LDC] (-Kw^T)
-    static constexpr int oDOT = oNKT + szDC;                      // dOT [BV][LDC]
-    static constexpr int oPT = oDOT + BV * LDC * (int)sizeof(S);  // PT  [C][LDC]
+    static constexpr int oQE = oQ + szCD;                         // Qe  [C][LDD] (rows * e^gam)
+    static constexpr int oNK = oQE + szCD;                        // NKs [C][LDD] (-Kw)
+    static constexpr int oDO = oNK + szCD;                        // dOs [C][LDV]
+    static constexpr int oPT = oDO + C * LDV * (int)sizeof(S);    // Pt  [C][LDC] (P transposed)
     static constexpr int oDHT = oPT + C * LDC * (int)sizeof(S);   // dhT [BV][LDD]
     static constexpr int oDWT = oDHT + BV * LDD * (int)sizeof(S); // dWT [BV][LDC]
     static constexpr int oGam = oDWT + BV * LDC * (int)sizeof(S);
@@ -56,14 +56,14 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
     using L = ChainSmem<BF, D, BV>;
-    constexpr int LDD = L::LDD, LDC = L::LDC;
+    constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
     constexpr int DT = D / 16, VT = BV / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
     S *Qs = (S *)(smem + L::oQ);
-    S *QT = (S *)(smem + L::oQT);
-    S *NKT = (S *)(smem + L::oNKT);
-    S *dOT = (S *)(smem + L::oDOT);
+    S *Qe = (S *)(smem + L::oQE);
+    S *NKs = (S *)(smem + L::oNK);
+    S *dOs = (S *)(smem + L::oDO);
     S *PT = (S *)(smem + L::oPT);
     S *dHT = (S *)(smem + L::oDHT);
     S *dWT = (S *)(smem + L::oDWT);
@@ -107,12 +107,9 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 
     for (int c = s.NC - 1; c >= 0; --c) {
         const int n = min(C, T - c * C);
-        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < dk && col < nvc)
-                dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
-        });
-        // every wave computes the decay of its lane's row: the transposed
-        // copy of Q (row j = lane) is scaled by e^{gam_j} while it is stored
+        wait_vmem();
+        // every wave computes the decay of its lane's row: the copy of Q
+        // whose row j = lane is scaled by e^{gam_j} while it is stored
         const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
         if (wave == 0) {
             gam2[lane] = dc.gam2;
@@ -121,9 +118,15 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         }
         fk.stash(Ks, LDD, tid);
         fq.stash(Qs, LDD, tid);
-        fq.stash_T_scaled(QT, LDC, tid, dc.eg);
-        fo.stash_T(dOT, LDC, tid);
-        if (!s.additive) fn.stash_T(NKT, LDC, tid);
+        fq.stash_scaled(Qe, LDD, tid, dc.eg);
+        fo.stash(dOs, LDV, tid);
+        if (!s.additive) fn.stash(NKs, LDD, tid);
+        // stores go out between consuming one prefetch and issuing the next,
+        // so waiting for the inputs never waits for a store
+        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < dk && col < nvc)
+                dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
+        });
         if (c > 0) fetch(c - 1);
         __syncthreads();
 
@@ -133,14 +136,13 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq[i] = zero4();
             gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
-            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-                PT[col * LDC + row] = from_f<BF>(sq[i][e] * gamma_ij(gam2, row, col));
-            });
+            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) { sq[i][e] *= gamma_ij(gam2, row, col); });
+            store_T<BF, 4, 4>(sq, PT, LDC, wave, lane);
         }
         f32x4 accQD[Tiles<DT, VT>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accQD[i] = zero4();
-        gemm<BF, DT, VT, C>(QT, LDC, dOT, LDC, accQD, wave, lane);
+        gemm<BF, DT, VT, C, true, true>(Qe, LDD, dOs, LDV, accQD, wave, lane);
         // dW = diag(e^{gam_n - gam}) K dh' + P^T dO (P^T is read after the barrier)
         f32x4 accW[Tiles<4, VT>::PW];
 #pragma unroll
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         gemm<BF, 4, VT, D>(Ks, LDD, dHT, LDD, accW, wave, lane);
         for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] *= egn[row]; });
         __syncthreads();
-        gemm<BF, 4, VT, C>(PT, LDC, dOT, LDC, accW, wave, lane);
+        gemm<BF, 4, VT, C, false, true>(PT, LDC, dOs, LDV, accW, wave, lane);
         store_T<BF, 4, VT>(accW, dWT, LDC, wave, lane);
         __syncthreads();
         // dh = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
             const float el = misc[0];
 #pragma unroll
             for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accDH[i] = accDH[i] * el + accQD[i];
-            if (!s.additive) gemm<BF, DT, VT, C>(NKT, LDC, dWT, LDC, accDH, wave, lane);
+            if (!s.additive) gemm<BF, DT, VT, C, true, false>(NKs, LDD, dWT, LDC, accDH, wave, lane);
         }
         __syncthreads();
         store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
@@ -552,13 +554,10 @@ __global__ __launch_bounds__(NTHR) void dA_reduce_kernel(const float *__restrict
 
 // --------------------------------------------------------------- launch
 
-static int chain_vblock(bool bf16, int D) {
-    if (!bf16 && D >= 64) return 16;
-    return D >= 64 ? 32 : 16;
-}
+static int chain_vblock(bool, int D) { return D >= 64 ? 32 : 16; }
 
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
-    constexpr int BV = (!BF && D >= 64) ? 16 : (D >= 64 ? 32 : 16);
+    constexpr int BV = D >= 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);

@@ -260,6 +260,23 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
         }
     }
 
+    // Straight copy with every element scaled by `sc`; requires that every
+    // item of this thread lies in row j == lane (NR == 64).
+    __device__ __forceinline__ void stash_scaled(S *dst, int ldd, int tid, float sc) const {
+        static_assert(NR == 64 && NTHR % 64 == 0, "row of an item must equal the lane");
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            const int it = tid + m * NTHR;
+            const int j = it % NR, cg = it / NR;
+            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            U val, out;
+            val.u = item(m);
+#pragma unroll
+            for (int e = 0; e < V; ++e) out.s[e] = from_f<BF>(to_f(val.s[e]) * sc);
+            *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = out.u;
+        }
+    }
+
     // Transposed copy to dstT [DP][ldt].
     __device__ __forceinline__ void stash_T(S *dstT, int ldt, int tid) const {
 #pragma unroll
@@ -294,6 +311,13 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
 // A per-lane scalar of a chunk (g or beta of row `lane`), loaded from a
 // clamped in-range address without a branch. The caller masks rows >= n
 // where it uses the value, so the load can stay in flight until then.
+// Wait until every vector memory access this wave issued has completed
+// (s_waitcnt with vmcnt = 0 and the other counters left free). Placed where
+// all prefetched registers are needed anyway, it also tells the compiler's
+// wait tracking that no load into them is still outstanding, so later loads
+// into the same registers are not held back behind stores.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float load_row_scalar(const float *__restrict__ p, size_t stride, int lane,
                                                  int n) {
     return p[(size_t)min(lane, n - 1) * stride];

@@ -142,11 +142,10 @@ template <bool BF, int D, int BV> struct FwdChainSmem {
     static constexpr int LDV = BV + Op<BF>::PAD;
     static constexpr int szCD = C * LDD * (int)sizeof(S);
     static constexpr int oK = 0;                                  // Ks  [C][LDD]
-    static constexpr int oKT = oK + szCD;                         // KT  [D][LDC]
-    static constexpr int oQ = oKT + D * LDC * (int)sizeof(S);     // Qs  [C][LDD]
+    static constexpr int oQ = oK + szCD;                          // Qs  [C][LDD]
     static constexpr int oNK = oQ + szCD;                         // NKs [C][LDD]  (-Kw)
     static constexpr int oU = oNK + szCD;                         // Us  [C][LDV]
-    static constexpr int oP = oU + C * LDV * (int)sizeof(S);      // Ps  [C][LDC]
+    static constexpr int oP = oU + C * LDV * (int)sizeof(S);      // Pt  [C][LDC] (P transposed)
     static constexpr int oHT = oP + C * LDC * (int)sizeof(S);     // hTs [BV][LDD]
     static constexpr int oWT = oHT + BV * LDD * (int)sizeof(S);   // WT  [BV][LDC]
     static constexpr int oWTd = oWT + BV * LDC * (int)sizeof(S);  // WTd [BV][LDC] (rows * e^{gam_n-gam})
@@ -167,7 +166,6 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     constexpr int DT = D / 16, VT = BV / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
-    S *KT = (S *)(smem + L::oKT);
     S *Qs = (S *)(smem + L::oQ);
     S *NKs = (S *)(smem + L::oNK);
     S *Us = (S *)(smem + L::oU);
@@ -213,19 +211,25 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
         if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
         fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
-        if (wave == 0) pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+    };
+    // O of a chunk is held in registers and written out during the next
+    // chunk, after that chunk's inputs have arrived: stores are issued only
+    // between consuming one prefetch and issuing the next, so waiting for
+    // the inputs never waits for a store to complete
+    f32x4 accO[Tiles<4, VT>::PW];
+    auto store_o = [&](int c) {
+        const int n = min(C, T - c * C);
+        S *orow = o + (((size_t)b * T + c * C) * H + h) * dv + v0;
+        for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < n && col < nvc) orow[(size_t)row * H * dv + col] = from_f<BF>(accO[i][e]);
+        });
     };
     fetch(0);
 
     for (int c = 0; c < s.NC; ++c) {
         const int t0 = c * C, n = min(C, T - t0);
-        const size_t row0 = (size_t)b * T + t0;
-        if (cs) {
-            for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-                if (row < dk && col < nvc)
-                    cs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accH[i][e]);
-            });
-        }
+        wait_vmem();
         if (wave == 0) {
             const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
             gam2[lane] = dc.gam2;
@@ -234,10 +238,16 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
             if (lane == 0) misc[0] = dc.eglast;
         }
         fk.stash(Ks, LDD, tid);
-        fk.stash_T(KT, LDC, tid);
         fq.stash(Qs, LDD, tid);
         if (!s.additive) fn.stash(NKs, LDD, tid);
         fu.stash(Us, LDV, tid);
+        if (o && c > 0) store_o(c - 1);
+        if (cs) {
+            for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+                if (row < dk && col < nvc)
+                    cs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accH[i][e]);
+            });
+        }
         if (c + 1 < s.NC) fetch(c + 1);
         __syncthreads();
 
@@ -247,9 +257,8 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq[i] = zero4();
             gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
-            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-                Ps[row * LDC + col] = from_f<BF>(sq[i][e] * gamma_ij(gam2, row, col));
-            });
+            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) { sq[i][e] *= gamma_ij(gam2, row, col); });
+            store_T<BF, 4, 4>(sq, Ps, LDC, wave, lane);
         }
         // W = U - Kw h (serial chain, part 1)
         {
@@ -263,27 +272,23 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
 
         // O = diag(e^gam) Q h + P W
         if (o) {
-            f32x4 accO[Tiles<4, VT>::PW];
 #pragma unroll
             for (int i = 0; i < Tiles<4, VT>::PW; ++i) accO[i] = zero4();
             gemm<BF, 4, VT, D>(Qs, LDD, hTs, LDD, accO, wave, lane);
             for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accO[i][e] *= eg[row]; });
-            gemm<BF, 4, VT, C>(Ps, LDC, WT, LDC, accO, wave, lane);
-            S *orow = o + (row0 * H + h) * dv + v0;
-            for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
-                if (row < n && col < nvc) orow[(size_t)row * H * dv + col] = from_f<BF>(accO[i][e]);
-            });
+            gemm<BF, 4, VT, C, true, false>(Ps, LDC, WT, LDC, accO, wave, lane);
         }
         // h <- e^{gam_last} h + K^T diag(e^{gam_last - gam}) W (serial chain, part 2)
         {
             const float el = misc[0];
 #pragma unroll
             for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accH[i] *= el;
-            gemm<BF, DT, VT, C>(KT, LDC, WTd, LDC, accH, wave, lane);
+            gemm<BF, DT, VT, C, true, false>(Ks, LDD, WTd, LDC, accH, wave, lane);
         }
         __syncthreads();
         store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
     }
+    if (o) store_o(s.NC - 1);
     if (a.hT) {
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc) a.hT[((size_t)bh * dk + row) * dv + v0 + col] = accH[i][e];
@@ -311,7 +316,7 @@ template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStre
 }
 
 template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
-    constexpr int BV = (D >= 64) ? 32 : 16;
+    constexpr int BV = D >= 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
