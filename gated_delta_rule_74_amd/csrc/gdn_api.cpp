@@ -84,8 +84,19 @@ size_t blocks_bytes(const gdn_shape_t *s, int d) {
     return (size_t)s->B * s->H * nchunks(s) * 64 * d * esize(s->dtype);
 }
 
-// forward context = [chunk-start states | NK], each 256-byte aligned
-size_t ctx_bytes(const gdn_shape_t *s) { return align_up(states_bytes(s)) + align_up(blocks_bytes(s, s->dk)); }
+// forward context = [chunk-start states | NK | U | Tm], each 256-byte aligned
+struct CtxLayout {
+    size_t nk, u, t, total;
+};
+CtxLayout ctx_layout(const gdn_shape_t *s) {
+    CtxLayout l;
+    l.nk = align_up(states_bytes(s));
+    l.u = l.nk + align_up(blocks_bytes(s, s->dk));
+    l.t = l.u + align_up(blocks_bytes(s, s->dv));
+    l.total = l.t + align_up(blocks_bytes(s, 64));
+    return l;
+}
+size_t ctx_bytes(const gdn_shape_t *s) { return ctx_layout(s).total; }
 
 gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *A_log, const float *h0) {
@@ -176,8 +187,7 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s) {
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
     const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
-    return ctx_bytes(s) /* recomputed forward context */ + align_up(blocks_bytes(s, s->dv)) /* U */ +
-           align_up(states_bytes(s)) /* dh per chunk */ + part;
+    return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part;
 }
 
 namespace {
@@ -185,11 +195,12 @@ namespace {
 // Forward pass into caller-provided buffers: U and NK of every chunk, then
 // the serial state pass (o may be null: states only).
 hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
-                       void *o, float *hT, void *cs, hipStream_t strm) {
+                       void *Tsave, void *o, float *hT, void *cs, hipStream_t strm) {
     gdn::PrepArgs pa;
     pa.s = sa;
     pa.U = U;
     pa.NK = NK;
+    pa.Tsave = Tsave;
     hipError_t he = timed([&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
     if (he != hipSuccess) return he;
     gdn::FwdChainArgs fa;
@@ -237,11 +248,13 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     if (st != GDN_OK) return st;
     const bool bf = s->dtype == GDN_BF16;
     const int D = pad_of(s);
-    char *w = (char *)ws;
-    void *U = w;
-    void *NK = ctx ? (char *)ctx + align_up(states_bytes(s)) : w + align_up(blocks_bytes(s, s->dv));
+    char *w = (char *)ws, *c = (char *)ctx;
+    const CtxLayout cl = ctx_layout(s);
+    void *U = ctx ? c + cl.u : w;
+    void *NK = ctx ? c + cl.nk : w + align_up(blocks_bytes(s, s->dv));
+    void *Tsave = ctx ? c + cl.t : nullptr;
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
-    return hip_status(run_forward(s, sa, bf, D, U, NK, o, hT, ctx, (hipStream_t)stream), "gdn_fwd launch");
+    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, o, hT, ctx, (hipStream_t)stream), "gdn_fwd launch");
 }
 
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
@@ -293,18 +306,18 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     hipStream_t strm = (hipStream_t)stream;
     char *w = (char *)ws;
     char *wctx = w;
-    char *wU = wctx + ctx_bytes(s);
-    char *dhs = wU + align_up(blocks_bytes(s, s->dv));
+    char *dhs = wctx + ctx_bytes(s);
     float *part = (float *)(dhs + align_up(states_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
+    const CtxLayout cl = ctx_layout(s);
     hipError_t he;
     if (!ctx) {
-        he = run_forward(s, sa, bf, D, wU, wctx + align_up(states_bytes(s)), nullptr, hT, wctx, strm);
+        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, nullptr, hT, wctx, strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
         ctx = wctx;
     }
     const void *cs = ctx;
-    const void *NK = (const char *)ctx + align_up(states_bytes(s));
+    const void *NK = (const char *)ctx + cl.nk;
     gdn::BwdChainArgs ca;
     ca.s = sa;
     ca.dout = dout;
@@ -321,6 +334,8 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     la.dout = dout;
     la.cs = cs;
     la.NK = NK;
+    la.U = (const char *)ctx + cl.u;
+    la.Tm = (const char *)ctx + cl.t;
     la.dhs = dhs;
     la.dq = dq;
     la.dk = dk;

@@ -172,11 +172,20 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 
 // --------------------------------------------------------------- local
 //
-// Storage: inputs (K, Q, V, dO, -Kw, h, dh') are stashed once as they are in
-// memory (token rows, or state rows); every product result is stored once,
-// transposed with packed writes ("t" suffix: Xt[col][row] = X[row][col]).
-// Each product reads an operand straight or through the transposing LDS
-// read, whichever its storage needs (gemm<..., ATR, BTR>).
+// Storage: inputs (K, Q, V, dO, -Kw, U, Tm, h, dh') are stashed as they are
+// in memory (token rows, state rows, or Tm rows); every product result is
+// stored once, transposed with packed writes ("t" suffix: Xt[col][row] =
+// X[row][col]). Each product reads an operand straight or through the
+// transposing LDS read, whichever its storage needs (gemm<..., ATR, BTR>).
+// U and Tm come from the forward context, so no triangular solve runs here.
+// Eight LDS regions are reused phase by phase (Pn = phase n):
+//   R0 K                              R4 dh' (P4-5) -> -dV't (P6-7)
+//   R1 Q (P1) -> h (P3-5) -> V (P6) -> dSt (P7-8)
+//   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7) -> dPGt (P9-10)
+//   R3 U (P3) -> dO (P4-9) -> partial sums (P11)
+//   R5 Wt (P3-9)                      R6 dWt (P4-6) -> dK't (P6-7)
+//   R7 -Kw (P3) -> dKw (P5-6) -> U (P7) -> Q (P9-10)
+// Inputs needed in two phases stay in registers between their stashes.
 
 template <bool BF, int D> struct LocalSmem {
     using S = typename Op<BF>::S;
@@ -187,29 +196,23 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int sDC = D * LDC * (int)sizeof(S); // [D][C]
     static constexpr int sDD = D * LDD * (int)sizeof(S); // state [D][D]
     static constexpr int sCC = C * LDC * (int)sizeof(S); // [C][C]
-    static constexpr int sF = C * LDF * 4;                // fp32 [C][C]
-    static constexpr int oK = 0;                           // K (all phases)
-    static constexpr int oA = oK + sCD;                    // Q -> Tt
-    static constexpr int oB = oA + mx(sCD, sCC);           // Pt -> dKw -> dSt -> dPGt
-    static constexpr int oTb = oB + mx(sCC, sCD);          // Tb -> dO -> final partials
-    static constexpr int oE = oTb + mx(sCC, sCD);          // L fp32 -> V | h
-    static constexpr int szE = mx(sF, sCD + sDD);
-    static constexpr int oG = oE + szE;                    // Tm fp32 -> -Kw | Ut
-    static constexpr int szG = mx(sF, sCD + sDC);
-    static constexpr int oW = oG + szG;                    // Wt
-    static constexpr int oH = oW + sDC;                    // dh' -> -dV't
-    static constexpr int oL = oH + mx(sDD, sDC);           // dWt -> dK't -> Q
-    static constexpr int oX = oL + mx(sDC, sCD);           // solve scratch
-    static constexpr int oGam = oX + 4 * 16 * 17 * 4;
+    static constexpr int sPart = (3 * C * (D / 16) + 3 * C * 4) * 4;
+    static constexpr int o0 = 0;
+    static constexpr int o1 = o0 + sCD;
+    static constexpr int o2 = o1 + mx(mx(sCD, sDD), sCC);
+    static constexpr int o3 = o2 + mx(sCC, sCD);
+    static constexpr int o4 = o3 + mx(sCD, sPart);
+    static constexpr int o5 = o4 + mx(sDD, sDC);
+    static constexpr int o6 = o5 + sDC;
+    static constexpr int o7 = o6 + sDC;
+    static constexpr int oGam = o7 + mx(sCD, sCC);
     static constexpr int oEg = oGam + C * 8;
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
     static constexpr int oGch = oBet + C * 4;
     static constexpr int oMisc = oGch + C * 4;
     static constexpr int SIZE = oMisc + (16 + NWAVE) * 4;
-    static constexpr int SLOT_E2 = sCD; // offset of the second half of E / G
     static_assert(SIZE <= 160 * 1024, "LDS budget");
-    static_assert((3 * C * (D / 16) + 3 * C * 4) * 4 <= mx(sCC, sCD), "partials must fit over Tb");
 };
 
 template <bool BF, int D, bool VEC>
@@ -220,22 +223,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
     constexpr int PWC = Tiles<4, 4>::PW, PWD = Tiles<4, DT>::PW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
-    S *Ks = (S *)(smem + L::oK);
-    S *Qs = (S *)(smem + L::oA);
-    S *Tt = (S *)(smem + L::oA);
-    S *Rb = (S *)(smem + L::oB);
-    S *Tb = (S *)(smem + L::oTb);
-    S *dOs = (S *)(smem + L::oTb);
-    float *Lm = (float *)(smem + L::oE);
-    S *Vs = (S *)(smem + L::oE);
-    S *hs = (S *)(smem + L::oE + L::SLOT_E2);
-    float *Tm = (float *)(smem + L::oG);
-    S *NKs = (S *)(smem + L::oG);
-    S *Ut = (S *)(smem + L::oG + L::SLOT_E2);
-    S *Wt = (S *)(smem + L::oW);
-    S *Rh = (S *)(smem + L::oH);
-    S *Rl = (S *)(smem + L::oL);
-    float *xs = (float *)(smem + L::oX);
+    S *R0 = (S *)(smem + L::o0);
+    S *R1 = (S *)(smem + L::o1);
+    S *R2 = (S *)(smem + L::o2);
+    S *R3 = (S *)(smem + L::o3);
+    S *R4 = (S *)(smem + L::o4);
+    S *R5 = (S *)(smem + L::o5);
+    S *R6 = (S *)(smem + L::o6);
+    S *R7 = (S *)(smem + L::o7);
+    S *Ks = R0;
     double *gam = (double *)(smem + L::oGam);
     float *eg = (float *)(smem + L::oEg);
     float *egn = (float *)(smem + L::oEgn);
@@ -251,26 +247,31 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int t0 = c * C, n = min(C, T - t0);
     const double A = -exp((double)s.A_log[h]);
-    const size_t row0 = (size_t)b * T + t0;
+    const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
     const S *q = (const S *)s.q + (row0 * H + h) * dk;
     const S *k = (const S *)s.k + (row0 * H + h) * dk;
     const S *v = (const S *)s.v + (row0 * H + h) * dv;
     const S *dO = (const S *)a.dout + (row0 * H + h) * dv;
-    const S *hc = (const S *)a.cs + ((size_t)bh * s.NC + c) * dk * dv;
-    const S *dhc = (const S *)a.dhs + ((size_t)bh * s.NC + c) * dk * dv;
-    const S *nk = (const S *)a.NK + ((size_t)bh * s.NC + c) * C * dk;
+    const S *hc = (const S *)a.cs + cb * dk * dv;
+    const S *dhc = (const S *)a.dhs + cb * dk * dv;
+    const S *nk = (const S *)a.NK + cb * C * dk;
+    const S *uc = (const S *)a.U + cb * C * dv;
+    const S *tc = (const S *)a.Tm + cb * C * C;
     const bool add = s.additive != 0;
 
     // all global inputs of the chunk are requested up front
-    ChunkFrag<BF, D> fk, fq, fv, fo, fn;
+    ChunkFrag<BF, D> fk, fq, fv, fo, fn, fu;
     ChunkFrag<BF, D, D> fh, fd;
+    ChunkFrag<BF, C> ft;
     fk.template fetch<VEC>(k, (size_t)H * dk, n, dk, tid);
     fq.template fetch<VEC>(q, (size_t)H * dk, n, dk, tid);
-    fv.template fetch<VEC>(v, (size_t)H * dv, n, dv, tid);
-    fo.template fetch<VEC>(dO, (size_t)H * dv, n, dv, tid);
+    fu.template fetch<VEC>(uc, (size_t)dv, n, dv, tid);
     if (!add) fn.template fetch<VEC>(nk, (size_t)dk, n, dk, tid);
     fh.template fetch<VEC>(hc, (size_t)dv, dk, dv, tid);
+    fo.template fetch<VEC>(dO, (size_t)H * dv, n, dv, tid);
     fd.template fetch<VEC>(dhc, (size_t)dv, dk, dv, tid);
+    ft.template fetch<VEC>(tc, (size_t)C, C, C, tid);
+    fv.template fetch<VEC>(v, (size_t)H * dv, n, dv, tid);
     float gr = 0.f, br = 0.f;
     if (wave == 0) {
         gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         if (lane == 0) misc[0] = dc.eglast;
     }
     fk.stash(Ks, LDD, tid);
-    fq.stash(Qs, LDD, tid);
+    fq.stash(R1, LDD, tid);
     __syncthreads();
     // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
     f32x4 gC[PWC], kkg[PWC], pC[PWC];
@@ -307,71 +308,56 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int i = 0; i < PWC; ++i) sk[i] = sq[i] = zero4();
         if (!add) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
-        gemm<BF, 4, 4, D>(Qs, LDD, Ks, LDD, sq, wave, lane);
+        gemm<BF, 4, 4, D>(R1, LDD, Ks, LDD, sq, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float G = gamma_ij(gam, row, col);
             gC[i][e] = G;
             kkg[i][e] = (row > col) ? sk[i][e] * G : 0.f;
-            Lm[row * LDF + col] = bet[row] * kkg[i][e];
             pC[i][e] = sq[i][e] * G;
         });
-        store_T<BF, 4, 4>(pC, Rb, LDC, wave, lane); // Pt
+        store_T<BF, 4, 4>(pC, R2, LDC, wave, lane); // Pt
     }
-    __syncthreads();
-    // ---- P2: Tm; Tb = Tm diag(beta) and Tt = Tm^T, both row-major
-    if (!add) {
-        tri_inverse<BF, true, false, true>(Lm, Tm, xs, wave, lane, Tb, nullptr, Tt, LDC, bet, nullptr);
-    } else {
-        for (int e = tid; e < C * C; e += NTHR) {
-            const int row = e / C, col = e % C;
-            Tb[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
-            Tt[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
-        }
-        __syncthreads();
-    }
-    // ---- P3: U = Tb V, W = U - Kw h
-    fv.stash(Vs, LDD, tid);
-    fh.stash(hs, LDD, tid);
-    if (!add) fn.stash(NKs, LDD, tid);
+    __syncthreads(); // Q reads done
+    // ---- P3: W = U - Kw h
+    fh.stash(R1, LDD, tid);
+    fu.stash(R3, LDD, tid);
+    if (!add) fn.stash(R7, LDD, tid);
     __syncthreads();
     {
         f32x4 accW[PWD];
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accW[i] = zero4();
-        gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, accW, wave, lane); // U
-        store_T<BF, 4, DT>(accW, Ut, LDC, wave, lane);
-        if (!add) gemm<BF, 4, DT, D, false, true>(NKs, LDD, hs, LDD, accW, wave, lane); // + (-Kw) h
-        store_T<BF, 4, DT>(accW, Wt, LDC, wave, lane);
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(R3[row * LDD + col]); });
+        if (!add) gemm<BF, 4, DT, D, false, true>(R7, LDD, R1, LDD, accW, wave, lane); // + (-Kw) h
+        store_T<BF, 4, DT>(accW, R5, LDC, wave, lane);                               // Wt
     }
-    __syncthreads(); // Tb free
+    __syncthreads(); // U reads done
     // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-    fo.stash(dOs, LDD, tid);
-    fd.stash(Rh, LDD, tid);
+    fo.stash(R3, LDD, tid);
+    fd.stash(R4, LDD, tid);
     __syncthreads();
     {
         f32x4 accdW[PWD], accX[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
-        gemm<BF, 4, DT, C, false, true>(Rb, LDC, dOs, LDD, accdW, wave, lane); // P^T dO
-        gemm<BF, 4, DT, D, false, true>(Ks, LDD, Rh, LDD, accX, wave, lane);   // K dh'
+        gemm<BF, 4, DT, C, false, true>(R2, LDC, R3, LDD, accdW, wave, lane); // P^T dO
+        gemm<BF, 4, DT, D, false, true>(Ks, LDD, R4, LDD, accX, wave, lane);  // K dh'
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
-        store_T<BF, 4, DT>(accdW, Rl, LDC, wave, lane); // dWt
+        store_T<BF, 4, DT>(accdW, R6, LDC, wave, lane); // dWt
     }
     __syncthreads();
     // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
-    gemm<BF, 4, DT, D>(dOs, LDD, hs, LDD, accQ, wave, lane); // dO h^T
-    f32x4 accM[Tiles<DT, 4>::PW];
-#pragma unroll
-    for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = zero4();
-    if (!add) gemm<BF, DT, 4, D, false, true>(hs, LDD, Rl, LDC, accM, wave, lane); // h dW^T
+    gemm<BF, 4, DT, D>(R3, LDD, R1, LDD, accQ, wave, lane); // dO h^T
     {
+        f32x4 accM[Tiles<DT, 4>::PW];
+#pragma unroll
+        for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = zero4();
+        if (!add) gemm<BF, DT, 4, D, false, true>(R1, LDD, R6, LDC, accM, wave, lane); // h dW^T
         f32x4 accKt[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
-        gemm<BF, 4, DT, D, true, false>(Wt, LDC, Rh, LDD, accKt, wave, lane); // W dh'^T
+        gemm<BF, 4, DT, D, true, false>(R5, LDC, R4, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];
@@ -391,81 +377,84 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
         if (lane == 0) misc[16 + wave] = hd;
-    }
-    __syncthreads(); // Pt, dh' no longer read
-    if (!add) {
+        // R7 (-Kw) and R2 (Pt) are free: dKw (token rows) and Tm go there
+        if (!add) {
 #pragma unroll
-        for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = -accM[i];
-        store_T<BF, DT, 4>(accM, Rb, LDD, wave, lane); // dKw, token rows [C][D]
+            for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = -accM[i];
+            store_T<BF, DT, 4>(accM, R7, LDD, wave, lane); // dKw, token rows [C][D]
+        }
+        ft.stash(R2, LDC, tid);
     }
-    __syncthreads();
+    __syncthreads(); // h, dh' no longer read
     // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw
+    fv.stash(R1, LDD, tid);
     {
         f32x4 accV[PWD], accKp[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
-        gemm<BF, 4, DT, C>(Tt, LDC, Rl, LDC, accV, wave, lane);
-        if (!add) gemm<BF, 4, DT, C, false, true>(Tt, LDC, Rb, LDD, accKp, wave, lane);
+        gemm<BF, 4, DT, C, true, false>(R2, LDC, R6, LDC, accV, wave, lane);
+        if (!add) gemm<BF, 4, DT, C, true, true>(R2, LDC, R7, LDD, accKp, wave, lane);
+        __syncthreads(); // V visible; Tm, dWt, dKw reads done
         S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < n && col < dv) dv_out[(size_t)row * H * dv + col] = from_f<BF>(bet[row] * accV[i][e]);
             const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
-            rbD[i][e] += to_f(Vs[row * LDD + col]) * accV[i][e] + eg[row] * kk;
+            rbD[i][e] += to_f(R1[row * LDD + col]) * accV[i][e] + eg[row] * kk;
             rgD[i][e] += bet[row] * eg[row] * kk;
             accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
         });
         if (!add) {
-            __syncthreads(); // dh', dWt reads done
 #pragma unroll
             for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-            store_T<BF, 4, DT>(accV, Rh, LDC, wave, lane);  // -dV't
-            store_T<BF, 4, DT>(accKp, Rl, LDC, wave, lane); // dK't
+            store_T<BF, 4, DT>(accV, R4, LDC, wave, lane);  // -dV't
+            store_T<BF, 4, DT>(accKp, R6, LDC, wave, lane); // dK't
+            fn.stash(R2, LDD, tid);                         // -Kw again
+            fu.stash(R7, LDD, tid);                         // U again
         }
     }
-    __syncthreads();
+    __syncthreads(); // V reads done
     // ---- P7: dL = -(dV' U^T + dK' Kw^T) = (-dV') U^T + dK' (-Kw)^T, dS
     if (!add) {
         f32x4 accL[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accL[i] = zero4();
-        gemm<BF, 4, 4, D, true, true>(Rh, LDC, Ut, LDC, accL, wave, lane);
-        gemm<BF, 4, 4, D, true, false>(Rl, LDC, NKs, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, false>(R4, LDC, R7, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, false>(R6, LDC, R2, LDD, accL, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
             rbC[i][e] += dl * kkg[i][e];
             xgC[i][e] += dl * bet[row] * kkg[i][e]; // dL o L
             accL[i][e] = bet[row] * dl * gC[i][e];
         });
-        store_T<BF, 4, 4>(accL, Rb, LDC, wave, lane); // dSt
+        store_T<BF, 4, 4>(accL, R1, LDC, wave, lane); // dSt
         __syncthreads();
         // ---- P8: dK += dS K + dS^T K
-        gemm<BF, 4, DT, C, true, true>(Rb, LDC, Ks, LDD, accKd, wave, lane);
-        gemm<BF, 4, DT, C, false, true>(Rb, LDC, Ks, LDD, accKd, wave, lane);
-        __syncthreads();
+        gemm<BF, 4, DT, C, true, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
     }
     // ---- P9: dP = dO W^T (lower incl. diagonal), dP o Gam
     {
         f32x4 accP[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accP[i] = zero4();
-        gemm<BF, 4, 4, D, false, true>(dOs, LDD, Wt, LDC, accP, wave, lane);
+        gemm<BF, 4, 4, D, false, true>(R3, LDD, R5, LDC, accP, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float dp = row >= col ? accP[i][e] : 0.f;
             xgC[i][e] += dp * pC[i][e]; // dP o P
             accP[i][e] = dp * gC[i][e];
         });
-        store_T<BF, 4, 4>(accP, Rb, LDC, wave, lane); // dPGt
-        fq.stash(Rl, LDD, tid);                     // Q again
+        store_T<BF, 4, 4>(accP, R2, LDC, wave, lane); // dPGt
+        fq.stash(R7, LDD, tid);                     // Q again
     }
     __syncthreads();
     // ---- P10: dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
     {
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             accQ[i][e] *= eg[row];
-            rgD[i][e] += accQ[i][e] * to_f(Rl[row * LDD + col]); // e^{gam_i} q_i . dOh_i
+            rgD[i][e] += accQ[i][e] * to_f(R7[row * LDD + col]); // e^{gam_i} q_i . dOh_i
         });
-        gemm<BF, 4, DT, C, true, true>(Rb, LDC, Ks, LDD, accQ, wave, lane);
-        gemm<BF, 4, DT, C, false, true>(Rb, LDC, Rl, LDD, accKd, wave, lane);
+        gemm<BF, 4, DT, C, true, true>(R2, LDC, Ks, LDD, accQ, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(R2, LDC, R7, LDD, accKd, wave, lane);
         S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
         S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
@@ -477,9 +466,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     }
     // ---- P11: one fixed-order reduction of every dbeta / dgam contribution
     {
-        float *pRbD = (float *)Tb, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
+        // R3 (dO) was last read before the P9 barrier
+        float *pRbD = (float *)R3, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
         float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
-        __syncthreads(); // dO (same slot) no longer read
         row_partials<4, DT>(rbD, pRbD, wave, lane);
         row_partials<4, DT>(rgD, pRgD, wave, lane);
         row_partials<4, DT>(rsD, pRsD, wave, lane);

@@ -14,9 +14,9 @@
 //
 // Two kernels. fwd_prep does everything that does not depend on the state,
 // one workgroup per (batch, head, chunk), all chunks in parallel, and writes
-// U and NK = -Kw. fwd_chain walks the chunks in order for one (batch, head,
-// block of value columns): per chunk only Q K^T, W, O and the state update
-// remain, so the serial path is short.
+// U, NK = -Kw and (when the backward will need it) Tm. fwd_chain walks the
+// chunks in order for one (batch, head, block of value columns): per chunk
+// only Q K^T, W, O and the state update remain, so the serial path is short.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -117,6 +117,27 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     }
 
     const size_t cbase = (size_t)bh * s.NC + c;
+    // Tm of the chunk for the backward (row-major [64][64]; identity when
+    // the erase term is off), one 16-byte store per thread and step. The
+    // solve leaves the 16x16 blocks above the diagonal of Tm unwritten: they
+    // are zero.
+    if (a.Tsave) {
+        S *dst = (S *)a.Tsave + cbase * C * C;
+        constexpr int V = O::VEC;
+        for (int e = tid * V; e < C * C; e += NTHR * V) {
+            const int row = e / C, col = e % C;
+            const bool upper = (col >> 4) > (row >> 4);
+            union {
+                uint4 u;
+                S x[V];
+            } pk;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                pk.x[j] = from_f<BF>(s.additive ? (row == col + j ? 1.f : 0.f)
+                                                : (upper ? 0.f : Tm[row * LDF + col + j]));
+            *reinterpret_cast<uint4 *>(dst + e) = pk.u;
+        }
+    }
     {
         f32x4 acc[Tiles<4, DT>::PW];
 #pragma unroll

@@ -15,10 +15,12 @@ struct SeqArgs {
 };
 
 // Per-chunk products that do not depend on the state:
-// U = Tm diag(beta) V  [B*H][NC][64][dv],  NK = -Tm diag(beta e^gam) K  [B*H][NC][64][dk]
+// U = Tm diag(beta) V  [B*H][NC][64][dv],  NK = -Tm diag(beta e^gam) K  [B*H][NC][64][dk],
+// and (if Tsave is set) Tm itself [B*H][NC][64][64], row-major, for the backward.
 struct PrepArgs {
     SeqArgs s;
     void *U, *NK;
+    void *Tsave; // may be null
 };
 
 struct FwdChainArgs {
@@ -45,6 +47,8 @@ struct BwdLocalArgs {
     const void *dout;
     const void *cs;  // chunk-start states
     const void *NK;
+    const void *U;   // U of every chunk (forward context)
+    const void *Tm;  // (I + L)^{-1} of every chunk (forward context)
     const void *dhs; // gradient wrt chunk-end states
     void *dq, *dk, *dv;
     float *dg, *dbeta;

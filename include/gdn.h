@@ -87,9 +87,10 @@ size_t gdn_fwd_workspace_size(const gdn_shape_t *s);
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s);
 
 /* Bytes of the optional forward context: what gdn_fwd can save for gdn_bwd
- * so that the backward skips recomputing the forward. It holds the state at
- * the start of every 64-token chunk and the chunk's -Tm diag(beta e^gam) K
- * block, both in the call's dtype. Its layout is private to the library. */
+ * so that the backward skips recomputing the forward. It holds, in the
+ * call's dtype, the state at the start of every 64-token chunk and the
+ * chunk's -Tm diag(beta e^gam) K, Tm diag(beta) V and Tm = (I + L)^{-1}
+ * blocks. Its layout is private to the library. */
 size_t gdn_fwd_context_size(const gdn_shape_t *s);
 
 /* Forward pass over a whole sequence ("GDN & MLA Mechanism Deep-Dive",

@@ -108,10 +108,12 @@ def test_workspace_and_context_sizes(L):
     s = gdn.Shape(8, 4096, 16, 56, 56, 1, 64, 0)
     states = 8 * 16 * 64 * 56 * 56 * 2
     blocks = 8 * 16 * 64 * 64 * 56 * 2
+    tms = 8 * 16 * 64 * 64 * 64 * 2
     ctx = L.gdn_fwd_context_size(ctypes.byref(s))
-    assert ctx >= states + blocks and ctx < states + blocks + 1024
+    # chunk-start states, -Kw and U of every chunk, and (I + L)^{-1} per chunk
+    assert ctx >= states + 2 * blocks + tms and ctx < states + 2 * blocks + tms + 1024
     assert L.gdn_fwd_workspace_size(ctypes.byref(s)) >= 2 * blocks
-    assert L.gdn_bwd_workspace_size(ctypes.byref(s)) >= ctx + blocks + states + 8 * 16 * 64 * 4
+    assert L.gdn_bwd_workspace_size(ctypes.byref(s)) >= ctx + states + 8 * 16 * 64 * 4
     bad = gdn.Shape(0, 1, 1, 1, 1, 1, 64, 0)
     assert L.gdn_fwd_context_size(ctypes.byref(bad)) == 0
     assert L.gdn_fwd_workspace_size(ctypes.byref(bad)) == 0
