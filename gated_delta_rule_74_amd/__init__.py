@@ -149,12 +149,13 @@ def _bytes(n, dev):
 
 def context_states(context, q, v):
     """View of the chunk-start states inside a forward context:
-    [B, H, ceil(T/64), dk, dv] in the dtype of q (for inspection/tests)."""
+    [B, H, ceil(T/64), dk, dv] in the dtype of q (for inspection/tests; the
+    context stores each state transposed, so the view is not contiguous)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     NC = (T + 63) // 64
     n = B * H * NC * dk * dv * q.element_size()
-    return context[:n].view(q.dtype).view(B, H, NC, dk, dv)
+    return context[:n].view(q.dtype).view(B, H, NC, dv, dk).transpose(-1, -2)
 
 
 def bwd_workspace_size(q, v, additive=False):

@@ -174,9 +174,12 @@ int32_t gdn_time_launches(void *const *events, int32_t n) {
     return done;
 }
 
+// per-token log2-decay of every chunk (fp32), written by fwd_prep
+size_t gam_bytes(const gdn_shape_t *s) { return (size_t)s->B * s->H * nchunks(s) * 64 * sizeof(float); }
+
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
-    return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk));
+    return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)) + align_up(gam_bytes(s));
 }
 
 size_t gdn_fwd_context_size(const gdn_shape_t *s) {
@@ -187,7 +190,8 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s) {
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
     const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
-    return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part;
+    return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part +
+           align_up(gam_bytes(s)) /* forward decay */;
 }
 
 namespace {
@@ -195,18 +199,20 @@ namespace {
 // Forward pass into caller-provided buffers: U and NK of every chunk, then
 // the serial state pass (o may be null: states only).
 hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
-                       void *Tsave, void *o, float *hT, void *cs, hipStream_t strm) {
+                       void *Tsave, float *gam, void *o, float *hT, void *cs, hipStream_t strm) {
     gdn::PrepArgs pa;
     pa.s = sa;
     pa.U = U;
     pa.NK = NK;
     pa.Tsave = Tsave;
+    pa.gam = gam;
     hipError_t he = timed([&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
     if (he != hipSuccess) return he;
     gdn::FwdChainArgs fa;
     fa.s = sa;
     fa.U = U;
     fa.NK = NK;
+    fa.gam = gam;
     fa.o = o;
     fa.hT = hT;
     fa.cs = cs;
@@ -253,8 +259,10 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     void *U = ctx ? c + cl.u : w;
     void *NK = ctx ? c + cl.nk : w + align_up(blocks_bytes(s, s->dv));
     void *Tsave = ctx ? c + cl.t : nullptr;
+    float *gam = (float *)(w + align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
-    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, o, hT, ctx, (hipStream_t)stream), "gdn_fwd launch");
+    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, gam, o, hT, ctx, (hipStream_t)stream),
+                      "gdn_fwd launch");
 }
 
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
@@ -308,11 +316,12 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     char *wctx = w;
     char *dhs = wctx + ctx_bytes(s);
     float *part = (float *)(dhs + align_up(states_bytes(s)));
+    float *gam = (float *)((char *)part + align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     const CtxLayout cl = ctx_layout(s);
     hipError_t he;
     if (!ctx) {
-        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, nullptr, hT, wctx, strm);
+        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, nullptr, hT, wctx, strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
         ctx = wctx;
     }

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         // so waiting for the inputs never waits for a store
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc)
-                dhs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accDH[i][e]);
+                dhs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accDH[i][e]);
         });
         if (c > 0) fetch(c - 1);
         __syncthreads();
@@ -172,15 +172,15 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 
 // --------------------------------------------------------------- local
 //
-// Storage: inputs (K, Q, V, dO, -Kw, U, Tm, h, dh') are stashed as they are
-// in memory (token rows, state rows, or Tm rows); every product result is
+// Storage: inputs (K, Q, V, dO, -Kw, U, Tm, h^T, dh'^T) are stashed as they
+// are in memory (token rows, transposed states, Tm rows); every product is
 // stored once, transposed with packed writes ("t" suffix: Xt[col][row] =
 // X[row][col]). Each product reads an operand straight or through the
 // transposing LDS read, whichever its storage needs (gemm<..., ATR, BTR>).
 // U and Tm come from the forward context, so no triangular solve runs here.
 // Eight LDS regions are reused phase by phase (Pn = phase n):
-//   R0 K                              R4 dh' (P4-5) -> -dV't (P6-7)
-//   R1 Q (P1) -> h (P3-5) -> V (P6) -> dSt (P7-8)
+//   R0 K                              R4 dh'^T (P4-5) -> -dV't (P6-7)
+//   R1 Q (P1) -> h^T (P3-5) -> V (P6) -> dSt (P7-8)
 //   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7) -> dPGt (P9-10)
 //   R3 U (P3) -> dO (P4-9) -> partial sums (P11)
 //   R5 Wt (P3-9)                      R6 dWt (P4-6) -> dK't (P6-7)
@@ -267,9 +267,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     fq.template fetch<VEC>(q, (size_t)H * dk, n, dk, tid);
     fu.template fetch<VEC>(uc, (size_t)dv, n, dv, tid);
     if (!add) fn.template fetch<VEC>(nk, (size_t)dk, n, dk, tid);
-    fh.template fetch<VEC>(hc, (size_t)dv, dk, dv, tid);
+    fh.template fetch<VEC>(hc, (size_t)dk, dv, dk, tid);
     fo.template fetch<VEC>(dO, (size_t)H * dv, n, dv, tid);
-    fd.template fetch<VEC>(dhc, (size_t)dv, dk, dv, tid);
+    fd.template fetch<VEC>(dhc, (size_t)dk, dv, dk, tid);
     ft.template fetch<VEC>(tc, (size_t)C, C, C, tid);
     fv.template fetch<VEC>(v, (size_t)H * dv, n, dv, tid);
     float gr = 0.f, br = 0.f;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     {
         f32x4 accW[PWD];
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(R3[row * LDD + col]); });
-        if (!add) gemm<BF, 4, DT, D, false, true>(R7, LDD, R1, LDD, accW, wave, lane); // + (-Kw) h
+        if (!add) gemm<BF, 4, DT, D, false, false>(R7, LDD, R1, LDD, accW, wave, lane); // + (-Kw) h
         store_T<BF, 4, DT>(accW, R5, LDC, wave, lane);                               // Wt
     }
     __syncthreads(); // U reads done
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
         gemm<BF, 4, DT, C, false, true>(R2, LDC, R3, LDD, accdW, wave, lane); // P^T dO
-        gemm<BF, 4, DT, D, false, true>(Ks, LDD, R4, LDD, accX, wave, lane);  // K dh'
+        gemm<BF, 4, DT, D, false, false>(Ks, LDD, R4, LDD, accX, wave, lane); // K dh'
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
         store_T<BF, 4, DT>(accdW, R6, LDC, wave, lane); // dWt
     }
@@ -348,16 +348,16 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
-    gemm<BF, 4, DT, D>(R3, LDD, R1, LDD, accQ, wave, lane); // dO h^T
+    gemm<BF, 4, DT, D, false, true>(R3, LDD, R1, LDD, accQ, wave, lane); // dO h^T
     {
         f32x4 accM[Tiles<DT, 4>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<DT, 4>::PW; ++i) accM[i] = zero4();
-        if (!add) gemm<BF, DT, 4, D, false, true>(R1, LDD, R6, LDC, accM, wave, lane); // h dW^T
+        if (!add) gemm<BF, DT, 4, D, true, true>(R1, LDD, R6, LDC, accM, wave, lane); // h dW^T
         f32x4 accKt[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
-        gemm<BF, 4, DT, D, true, false>(R5, LDC, R4, LDD, accKt, wave, lane); // W dh'^T
+        gemm<BF, 4, DT, D, true, true>(R5, LDC, R4, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];

@@ -198,11 +198,11 @@ __device__ __forceinline__ void store_N(const f32x4 *acc, typename Op<BF>::S *ds
 // Items are numbered so that consecutive lanes hold consecutive rows of the
 // same vector group: transposed LDS stores of a wave then hit consecutive
 // addresses, and straight 16-byte stores of 16 lanes cover all banks once.
-template <bool BF, int DP, int NR = C> struct ChunkFrag {
+template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
     using S = typename Op<BF>::S;
     static constexpr int V = Op<BF>::VEC;
     static constexpr int NG = DP / V;
-    static constexpr int NIT = (NR * NG + NTHR - 1) / NTHR;
+    static constexpr int NIT = (NR * NG + NT - 1) / NT;
     union U {
         uint4 u;
         S s[V];
@@ -221,9 +221,9 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
         if constexpr (VEC) {
 #pragma unroll
             for (int m = 0; m < NIT; ++m) {
-                const int it = tid + m * NTHR;
+                const int it = tid + m * NT;
                 const int j = it % NR, cg = it / NR;
-                const bool in = ((NR * NG) % NTHR == 0 || cg < NG) && j < n && cg * V < d;
+                const bool in = ((NR * NG) % NT == 0 || cg < NG) && j < n && cg * V < d;
                 const int jj = min(j, n - 1), cc = min(cg * V, d - V);
                 r[m].u = *reinterpret_cast<const uint4 *>(x + (size_t)jj * rs + cc);
                 ok |= (in ? 1u : 0u) << m;
@@ -231,10 +231,10 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
         } else {
 #pragma unroll
             for (int m = 0; m < NIT; ++m) {
-                const int it = tid + m * NTHR;
+                const int it = tid + m * NT;
                 const int j = it % NR, cg = it / NR;
                 r[m].u = uint4{0u, 0u, 0u, 0u};
-                if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+                if ((NR * NG) % NT != 0 && cg >= NG) continue;
                 if (j < n) {
 #pragma unroll
                     for (int e = 0; e < V; ++e)
@@ -253,9 +253,9 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
     __device__ __forceinline__ void stash(S *dst, int ldd, int tid) const {
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
+            const int it = tid + m * NT;
             const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if ((NR * NG) % NT != 0 && cg >= NG) continue;
             *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = item(m);
         }
     }
@@ -263,12 +263,12 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
     // Straight copy with every element scaled by `sc`; requires that every
     // item of this thread lies in row j == lane (NR == 64).
     __device__ __forceinline__ void stash_scaled(S *dst, int ldd, int tid, float sc) const {
-        static_assert(NR == 64 && NTHR % 64 == 0, "row of an item must equal the lane");
+        static_assert(NR == 64 && NT % 64 == 0, "row of an item must equal the lane");
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
+            const int it = tid + m * NT;
             const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if ((NR * NG) % NT != 0 && cg >= NG) continue;
             U val, out;
             val.u = item(m);
 #pragma unroll
@@ -281,9 +281,9 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
     __device__ __forceinline__ void stash_T(S *dstT, int ldt, int tid) const {
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
+            const int it = tid + m * NT;
             const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if ((NR * NG) % NT != 0 && cg >= NG) continue;
             U val;
             val.u = item(m);
 #pragma unroll
@@ -294,12 +294,12 @@ template <bool BF, int DP, int NR = C> struct ChunkFrag {
     // Transposed copy scaled by `sc`; requires that every item of this
     // thread lies in row j == lane (NR == 64).
     __device__ __forceinline__ void stash_T_scaled(S *dstT, int ldt, int tid, float sc) const {
-        static_assert(NR == 64 && NTHR % 64 == 0, "row of an item must equal the lane");
+        static_assert(NR == 64 && NT % 64 == 0, "row of an item must equal the lane");
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NTHR;
+            const int it = tid + m * NT;
             const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NTHR != 0 && cg >= NG) continue;
+            if ((NR * NG) % NT != 0 && cg >= NG) continue;
             U val;
             val.u = item(m);
 #pragma unroll

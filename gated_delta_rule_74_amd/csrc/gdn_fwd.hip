@@ -90,6 +90,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         const float g = lane < n ? gr : 0.f, be = lane < n ? br : 0.f;
         const Decay dc = decay_lane(g, -exp((double)s.A_log[h]) * LOG2E, lane);
         gam2[lane] = dc.gam2;
+        if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
         bet[lane] = be;
         ck[lane] = be * dc.eg;
     }
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         if (cs) {
             for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
                 if (row < dk && col < nvc)
-                    cs[(((size_t)bh * s.NC + c) * dk + row) * dv + v0 + col] = from_f<BF>(accH[i][e]);
+                    cs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accH[i][e]);
             });
         }
         if (c + 1 < s.NC) fetch(c + 1);
@@ -317,6 +318,308 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     }
 }
 
+// ------------------------------------------------- wave-specialised chain
+//
+// bf16 path for head dims up to 64. One workgroup per (batch, head).
+// Waves 0..DT-1 ("chain waves", DT = D/16) each carry 16 value columns of
+// the state h [D][16] in MFMA accumulators and run only the recurrence
+//   W = U + NK h,   h <- e^{gam_n} h + K^T diag(e^{gam_n - gam}) W.
+// With 16x16x16 products an accumulator tile (rows 4*(lane/16)+e, column
+// lane%16) is already the B operand of a product over the same rows, so W
+// and h stay in the wave's registers on the serial path: no barrier and no
+// LDS round trip between the two products. The eight "helper" waves that
+// follow split the rest: they stage the next chunk's inputs into LDS, form
+// P = (Q K^T) o Gam and diag(e^gam) Q h for the current chunk, finish
+// O = ... + P W one chunk behind the chain (W arrives through LDS), and copy
+// the chunk-start states out. Helper w owns chunk rows 16*(w%4).. and half
+// of the value columns. One barrier per chunk hands the double-buffered LDS
+// over.
+//
+// Chunk-start states go out transposed, [dv][dk] per chunk.
+
+constexpr int WS_HELPERS = 8;
+
+template <int D> struct WsSmem {
+    static constexpr int VH = D / 32;  // value blocks per helper
+    static constexpr int LDD = D + 8;  // token rows [C][LDD]; h^T [D][LDD]
+    static constexpr int LDC = C + 8;  // W^T [D][LDC]
+    static constexpr int LDP = 16 + 8; // P^T of one 16-row block [C][LDP]
+    static constexpr int LDO = 16 * VH + 8;
+    static constexpr int szCD = C * LDD * 2;
+    static constexpr int szStage = 4 * szCD; // Q, K, -Kw, U
+    static constexpr int szHX = D * LDD * 2;
+    static constexpr int szWX = D * LDC * 2;
+    static constexpr int szP = C * LDP * 2;
+    static constexpr int szO = 16 * LDO * 2;
+    static constexpr int szDec = 3 * C * 4 + 16; // gam (log2), e^gam, e^{gam_n-gam}, e^{gam_n}
+    static constexpr int oStage = 0;
+    static constexpr int oHX = oStage + 2 * szStage;
+    static constexpr int oWX = oHX + 2 * szHX;
+    static constexpr int oP = oWX + 2 * szWX;
+    static constexpr int oO = oP + 2 * 4 * szP;
+    static constexpr int oDec = oO + WS_HELPERS * szO;
+    static constexpr int SIZE = oDec + 2 * szDec;
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ short4_t pack4(f32x4 x) {
+    uint2 u;
+    u.x = f2bf2(x[0], x[1]);
+    u.y = f2bf2(x[2], x[3]);
+    return __builtin_bit_cast(short4_t, u);
+}
+
+// One 16x16x16 operand from an LDS matrix stored with K as its row index,
+// X[k][m]: lane 16g + j receives X[k0 + 4g + e][m0 + j], e = 0..3.
+__device__ __forceinline__ short4_t operand_tr4(const u16 *X, int ld, int k0, int m0, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4 *)(X + (k0 + 4 * g + (sl >> 2)) * ld + m0 + 4 * (sl & 3)));
+}
+
+template <int D, bool VEC>
+__global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
+    constexpr int DT = D / 16, KS = D / 32;
+    constexpr int NHT = 64 * WS_HELPERS; // helper threads
+    using L = WsSmem<D>;
+    constexpr int LDD = L::LDD, LDC = L::LDC, LDP = L::LDP, LDO = L::LDO, VH = L::VH;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    auto stage = [&](int st, int m) { return (u16 *)(smem + L::oStage + st * L::szStage + m * L::szCD); };
+    auto hx = [&](int i) { return (u16 *)(smem + L::oHX + i * L::szHX); };
+    auto wx = [&](int i) { return (u16 *)(smem + L::oWX + i * L::szWX); };
+    auto pbuf = [&](int i, int ib) { return (u16 *)(smem + L::oP + (i * 4 + ib) * L::szP); };
+    auto obuf = [&](int hw) { return (u16 *)(smem + L::oO + hw * L::szO); };
+    auto gam_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec); };
+    auto eg_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 4); };
+    auto egn_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 8); };
+    auto egl_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 12); };
+
+    const SeqArgs &s = a.s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, r = lane & 15;
+    const int bh = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = bh / s.H, h = bh % s.H;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
+    const bool chain = wave < DT;
+    const bool add = s.additive != 0;
+
+    // ---- chain-wave state
+    const int v0 = 16 * wave;
+    f32x4 hacc[DT];
+    short4_t hb[DT];
+    // ---- helper-wave state: rows 16*ib.., value blocks vb0..vb0+VH-1
+    const int hw = wave - DT, htid = tid - 64 * DT;
+    const int ib = hw & 3, half = hw >> 2, vb0 = half * VH;
+    ChunkFrag<true, D, C, NHT> fq, fk, fn, fu;
+    float pg = 0.f;
+    f32x4 accO[VH];
+    const u16 *q = (const u16 *)s.q, *k = (const u16 *)s.k;
+    const u16 *U = (const u16 *)a.U, *NK = (const u16 *)a.NK;
+    u16 *o = (u16 *)a.o, *cs = (u16 *)a.cs;
+
+    auto fetch = [&](int c) {
+        const int n = min(C, T - c * C);
+        const size_t row0 = (size_t)b * T + c * C, cb = (size_t)bh * NC + c;
+        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
+        fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
+        if (!add) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, htid);
+        fu.template fetch<VEC>(U + cb * C * dv, (size_t)dv, n, dv, htid);
+        pg = a.gam[cb * C + lane];
+    };
+    auto stash = [&](int c) {
+        const int st = c & 1;
+        wait_vmem();
+        fq.stash(stage(st, 0), LDD, htid);
+        fk.stash(stage(st, 1), LDD, htid);
+        if (!add) fn.stash(stage(st, 2), LDD, htid);
+        fu.stash(stage(st, 3), LDD, htid);
+        if (hw == 0) {
+            const float last = __shfl(pg, 63, 64);
+            gam_of(st)[lane] = pg;
+            eg_of(st)[lane] = exp2_fast(pg);
+            egn_of(st)[lane] = exp2_fast(last - pg);
+            if (lane == 0) egl_of(st)[0] = exp2_fast(last);
+        }
+    };
+
+    // ---- prologue: initial state (chain) and chunk 0 in LDS (helpers)
+    if (chain) {
+#pragma unroll
+        for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = 16 * kb + 4 * g + e, v = v0 + r;
+                hacc[kb][e] = (s.h0 && d < dk && v < dv) ? s.h0[((size_t)bh * dk + d) * dv + v] : 0.f;
+            }
+            hb[kb] = pack4(hacc[kb]);
+            *(short4_t *)(hx(0) + (v0 + r) * LDD + 16 * kb + 4 * g) = hb[kb];
+        }
+    } else {
+        fetch(0);
+        stash(0);
+        if (NC > 1) fetch(1);
+    }
+    __syncthreads();
+
+    for (int c = 0; c <= NC; ++c) {
+        if (chain) {
+            if (c < NC) {
+                const int st = c & 1;
+                const u16 *Ks = stage(st, 1), *NKs = stage(st, 2), *Us = stage(st, 3);
+                const float *egn = egn_of(st);
+                const float el = egl_of(st)[0];
+                // W = U + (-Kw) h
+                f32x4 w[4];
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) {
+                    const short4_t u4 = operand_tr4(Us, LDD, 16 * tm, v0, lane);
+                    const uint2 uu = __builtin_bit_cast(uint2, u4);
+                    w[tm][0] = bf2f((u16)(uu.x & 0xFFFF));
+                    w[tm][1] = bf2f((u16)(uu.x >> 16));
+                    w[tm][2] = bf2f((u16)(uu.y & 0xFFFF));
+                    w[tm][3] = bf2f((u16)(uu.y >> 16));
+                }
+                if (!add) {
+#pragma unroll
+                    for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+                        for (int tm = 0; tm < 4; ++tm) {
+                            const short4_t an = *(const short4_t *)(NKs + (16 * tm + r) * LDD + 16 * kb + 4 * g);
+                            w[tm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(an, hb[kb], w[tm], 0, 0, 0);
+                        }
+                    }
+                }
+                // W out for the helpers; W diag(e^{gam_n - gam}) stays here
+                short4_t wb[4];
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) {
+                    *(short4_t *)(wx(st) + (v0 + r) * LDC + 16 * tm + 4 * g) = pack4(w[tm]);
+                    const float4 sc = *(const float4 *)(egn + 16 * tm + 4 * g);
+                    wb[tm] = pack4(f32x4{w[tm][0] * sc.x, w[tm][1] * sc.y, w[tm][2] * sc.z, w[tm][3] * sc.w});
+                }
+                // h <- e^{gam_n} h + K^T (W diag(e^{gam_n - gam}))
+#pragma unroll
+                for (int kb = 0; kb < DT; ++kb) {
+                    hacc[kb] *= el;
+#pragma unroll
+                    for (int tm = 0; tm < 4; ++tm) {
+                        const short4_t ak = operand_tr4(Ks, LDD, 16 * tm, 16 * kb, lane);
+                        hacc[kb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, wb[tm], hacc[kb], 0, 0, 0);
+                    }
+                    hb[kb] = pack4(hacc[kb]);
+                    *(short4_t *)(hx((c + 1) & 1) + (v0 + r) * LDD + 16 * kb + 4 * g) = hb[kb];
+                }
+            }
+        } else {
+            // chunk c+1 into LDS (requested one chunk ago), chunk c+2 requested;
+            // this chunk's stores are issued after these loads, so the next
+            // wait for loads does not wait on them
+            if (c + 1 < NC) stash(c + 1);
+            if (c + 2 < NC) fetch(c + 2);
+            // finish O of the previous chunk: + P W
+            if (o && c >= 1) {
+                const int pst = (c - 1) & 1, n = min(C, T - (c - 1) * C);
+                const u16 *Pt = pbuf(pst, ib), *WT = wx(pst);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 ap = operand_tr(Pt, LDP, 32 * ks, 0, lane);
+#pragma unroll
+                    for (int x = 0; x < VH; ++x) {
+                        const bf16x8 bw = *(const bf16x8 *)(WT + (16 * (vb0 + x) + r) * LDC + 32 * ks + 8 * g);
+                        accO[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bw, accO[x], 0, 0, 0);
+                    }
+                }
+                // the 16 x 16*VH block goes out through LDS as 16-byte row pieces
+                u16 *Os = obuf(hw);
+#pragma unroll
+                for (int x = 0; x < VH; ++x)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Os[(4 * g + e) * LDO + 16 * x + r] = f2bf(accO[x][e]);
+                const int nr = min(16, n - 16 * ib), vlo = 16 * vb0, nvc = min(16 * VH, dv - vlo);
+                u16 *orow = o + (((size_t)b * T + (c - 1) * C + 16 * ib) * H + h) * dv + vlo;
+                if (VEC) {
+                    for (int it = lane; it < 16 * 2 * VH; it += 64) {
+                        const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
+                        if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
+                    }
+                } else {
+                    for (int it = lane; it < 16 * 16 * VH; it += 64) {
+                        const int i = it / (16 * VH), v = it % (16 * VH);
+                        if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
+                    }
+                }
+            }
+            // chunk-start state h_c out, transposed [dv][dk]
+            if (cs && c < NC) {
+                const u16 *HT = hx(c & 1);
+                u16 *dst = cs + ((size_t)bh * NC + c) * dv * dk;
+                if (VEC) {
+                    for (int it = htid; it < dv * (dk / 8); it += NHT) {
+                        const int v = it / (dk / 8), d = (it % (dk / 8)) * 8;
+                        *(uint4 *)(dst + (size_t)v * dk + d) = *(const uint4 *)(HT + v * LDD + d);
+                    }
+                } else {
+                    for (int it = htid; it < dv * dk; it += NHT) {
+                        const int v = it / dk, d = it % dk;
+                        dst[(size_t)v * dk + d] = HT[v * LDD + d];
+                    }
+                }
+            }
+            // P (this helper's half of the columns) and diag(e^gam) Q h
+            if (o && c < NC) {
+                const int st = c & 1;
+                const u16 *Qs = stage(st, 0), *Ks = stage(st, 1), *HT = hx(st);
+                const float *gam = gam_of(st);
+                const float *eg = eg_of(st);
+                bf16x8 aq[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) aq[ks] = *(const bf16x8 *)(Qs + (16 * ib + r) * LDD + 32 * ks + 8 * g);
+                u16 *Pt = pbuf(st, ib);
+                const float4 gi = *(const float4 *)(gam + 16 * ib + 4 * g);
+                const float gil[4] = {gi.x, gi.y, gi.z, gi.w};
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int jb = 2 * half + y;
+                    f32x4 p = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 bk = *(const bf16x8 *)(Ks + (16 * jb + r) * LDD + 32 * ks + 8 * g);
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], bk, p, 0, 0, 0);
+                    }
+                    const int j = 16 * jb + r;
+                    const float gj = gam[j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        p[e] = (16 * ib + 4 * g + e >= j) ? p[e] * exp2_fast(gil[e] - gj) : 0.f;
+                    *(short4_t *)(Pt + j * LDP + 4 * g) = pack4(p);
+                }
+                const float4 sc = *(const float4 *)(eg + 16 * ib + 4 * g);
+#pragma unroll
+                for (int x = 0; x < VH; ++x) {
+                    f32x4 y4 = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 bh8 = *(const bf16x8 *)(HT + (16 * (vb0 + x) + r) * LDD + 32 * ks + 8 * g);
+                        y4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], bh8, y4, 0, 0, 0);
+                    }
+                    accO[x] = f32x4{y4[0] * sc.x, y4[1] * sc.y, y4[2] * sc.z, y4[3] * sc.w};
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (chain && a.hT) {
+#pragma unroll
+        for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = 16 * kb + 4 * g + e, v = v0 + r;
+                if (d < dk && v < dv) a.hT[((size_t)bh * dk + d) * dv + v] = hacc[kb][e];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch
 
 int pad_dim(int d, bool bf16) {
@@ -333,6 +636,16 @@ template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStre
         hipLaunchKernelGGL((fwd_prep_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
     else
         hipLaunchKernelGGL((fwd_prep_kernel<BF, D, false>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a, hipStream_t st) {
+    const int grid = a.s.B * a.s.H;
+    const int block = 64 * (D / 16 + WS_HELPERS);
+    if (vec_ok<true>(a.s))
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true>), dim3(grid), dim3(block), 0, st, a);
+    else
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false>), dim3(grid), dim3(block), 0, st, a);
     return hipGetLastError();
 }
 
@@ -367,8 +680,8 @@ hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t
     if (fwd_vblock(D) * a.NVB < a.s.dv) return hipErrorInvalidValue;
     if (bf16) {
         switch (D) {
-        case 32: return chain_inst<true, 32>(a, st);
-        case 64: return chain_inst<true, 64>(a, st);
+        case 32: return chain_ws_inst<32>(a, st);
+        case 64: return chain_ws_inst<64>(a, st);
         case 128: return chain_inst<true, 128>(a, st);
         }
     } else {

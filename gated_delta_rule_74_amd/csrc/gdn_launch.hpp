@@ -21,14 +21,16 @@ struct PrepArgs {
     SeqArgs s;
     void *U, *NK;
     void *Tsave; // may be null
+    float *gam;  // chunk-local cumulative log2-decay [B*H][NC][64], may be null
 };
 
 struct FwdChainArgs {
     SeqArgs s;
     const void *U, *NK;
+    const float *gam; // from fwd_prep
     void *o;   // may be null (state-only pass)
     float *hT; // may be null
-    void *cs;  // chunk-start states [B,H,NC,dk,dv] in operand dtype, may be null
+    void *cs;  // chunk-start states, transposed: [B,H,NC,dv,dk] in operand dtype; may be null
     int NVB;   // value-column blocks
 };
 
@@ -37,7 +39,7 @@ struct BwdChainArgs {
     const void *dout;
     const float *dhT; // may be null
     const void *NK;
-    void *dhs;        // [B,H,NC,dk,dv]: gradient wrt the state after each chunk
+    void *dhs;        // [B,H,NC,dv,dk]: gradient wrt the state after each chunk, transposed
     float *dh0;       // may be null
     int NVB;
 };
@@ -45,11 +47,11 @@ struct BwdChainArgs {
 struct BwdLocalArgs {
     SeqArgs s;
     const void *dout;
-    const void *cs;  // chunk-start states
+    const void *cs;  // chunk-start states (transposed)
     const void *NK;
     const void *U;   // U of every chunk (forward context)
     const void *Tm;  // (I + L)^{-1} of every chunk (forward context)
-    const void *dhs; // gradient wrt chunk-end states
+    const void *dhs; // gradient wrt chunk-end states (transposed)
     void *dq, *dk, *dv;
     float *dg, *dbeta;
     float *dA_part;  // [B*H*NC]
