@@ -12,6 +12,16 @@ around every library launch) and the fp64 CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Profiling aids (the counter runs behind the committed traffic summaries):
+    python bench.py --profile-run N      N untimed steps, then one plain
+                                         256 MiB device copy (the calibration
+                                         kernel for the HBM byte counters)
+    python bench.py --traffic-summary FETCH_DIR WRITE_DIR
+                                         turn two rocprofv3 --pmc runs
+                                         (FETCH_SIZE, then WRITE_SIZE) of the
+                                         above into per-kernel HBM traffic,
+                                         written to profiles/
 """
 import argparse
 import hashlib
@@ -83,6 +93,78 @@ def load_traffic(kernel):
     return t.get("traffic_bytes")
 
 
+COPY_BYTES = 256 << 20  # calibration copy of --profile-run
+
+
+def _counter_rows(d):
+    """(kernel name, counter, value) of every dispatch in a rocprofv3 csv dir."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r["Dispatch_Id"]))
+    return out
+
+
+def _per_kernel(rows, counter):
+    """Per-dispatch values of `counter` (summed over its instances) by kernel."""
+    import collections
+    per_disp = collections.defaultdict(float)
+    name_of = {}
+    for name, cn, val, disp in rows:
+        if cn.startswith(counter):
+            per_disp[disp] += val
+            name_of[disp] = name
+    by_kernel = collections.defaultdict(list)
+    for disp, v in per_disp.items():
+        by_kernel[name_of[disp]].append(v)
+    return by_kernel
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM bytes per launch of every gdn kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the reading of the same counter for the
+    plain 256 MiB copy (expected bytes / counted bytes)."""
+    fetch_all = _per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write_all = _per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+
+    def copy_of(tab):
+        # the largest dispatch of the runtime's copy kernel is the 256 MiB copy
+        cands = [max(v) for k, v in tab.items() if "copy" in k.lower() and "gdn" not in k]
+        if not cands:
+            raise SystemExit("calibration copy kernel not found in the counter output")
+        return max(cands)
+
+    def avg(tab):
+        return {k: sum(v) / len(v) for k, v in tab.items()}
+
+    fetch, write = avg(fetch_all), avg(write_all)
+
+    f_scale = COPY_BYTES / (copy_of(fetch_all) * 1024.0)
+    w_scale = COPY_BYTES / (copy_of(write_all) * 1024.0)
+    src = source_hash()
+    out = {}
+    for k in KERNELS:
+        fk = [v for n, v in fetch.items() if f"gdn::{k}_kernel" in n or f"gdn::{k}" in n]
+        wk = [v for n, v in write.items() if f"gdn::{k}_kernel" in n or f"gdn::{k}" in n]
+        if not fk or not wk:
+            continue
+        rd, wr = fk[0] * 1024.0 * f_scale, wk[0] * 1024.0 * w_scale
+        rec = {"kernel": k, "workload": WORKLOAD, "source_hash": src,
+               "fetch_kib_per_dispatch": round(fk[0], 1), "write_kib_per_dispatch": round(wk[0], 1),
+               "copy_fetch_scale": round(f_scale, 4), "copy_write_scale": round(w_scale, 4),
+               "read_bytes": round(rd), "write_bytes": round(wr), "traffic_bytes": round(rd + wr)}
+        with open(os.path.join(ROOT, "profiles", f"{k}_{WORKLOAD}_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        out[k] = rec
+    print(json.dumps(out, indent=1))
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -135,7 +217,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-run", type=int, default=0, metavar="N")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the gated delta rule path here is built and timed "
               "on a single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
@@ -175,6 +262,18 @@ def main():
     def step():
         gdn.fwd(q, k, v, g, beta, A_log, h0, o=o, hT=hT, context=ctx, workspace=fws)
         gdn.bwd(q, k, v, g, beta, A_log, do, h0, None, context=ctx, workspace=bws, out=grads)
+
+    if args.profile_run:
+        for i in range(args.profile_run):
+            step()
+            torch.cuda.synchronize()
+            print(f"profile step {i + 1}/{args.profile_run}", flush=True)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"calibration copy of {COPY_BYTES} bytes done", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -74,9 +74,11 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
 
     const SeqArgs &s = a.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // heads fastest: the rows of all heads of one token are adjacent in
+    // memory, so workgroups that share cache lines run together on one XCD
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int c = lid % s.NC, bh = lid / s.NC;
-    const int b = bh / s.H, h = bh % s.H;
+    const int h = lid % s.H, c = (lid / s.H) % s.NC, b = lid / (s.H * s.NC);
+    const int bh = b * s.H + h;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = (size_t)b * T + t0;
