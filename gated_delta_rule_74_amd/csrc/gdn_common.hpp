@@ -365,10 +365,12 @@ __device__ __forceinline__ float gamma_ij(const double *gam2, int i, int j) {
 
 constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 
-// T = (I + L)^{-1} for a strictly lower triangular 64 x 64 L (fp32, [C][LDF]),
-// written to Tm ([C][LDF], fp32). Diagonal 16 x 16 blocks by forward
-// substitution (one wave each), off-diagonal blocks by block forward
-// substitution
+// T = (I + L)^{-1} for a strictly lower triangular 64 x 64 L, given as its
+// transpose Lt[j][i] = L[i][j] (fp32, [C][LDF]); T is written to Tm
+// ([C][LDF], fp32). Diagonal 16 x 16 blocks by forward substitution, all four
+// in wave 0 (lane group g = block g, lane = column); the step-i multipliers
+// L[i+1..15][i] are one row of Lt, read two steps ahead so the LDS latency
+// overlaps the updates. Off-diagonal blocks by block forward substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
 // level by level (i - j = 1, 2, 3) with fp32 MFMA; waves 0..3 do the work.
 // xs: 4 x 16 x 17 floats.
@@ -377,37 +379,51 @@ constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 // column-scaled, and TT = T^T (WT).
 // Ends with a barrier.
 template <bool BF, bool WB, bool WK, bool WT>
-__device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs, int wave, int lane,
+__device__ __forceinline__ void tri_inverse(const float *Lt, float *Tm, float *xs, int wave, int lane,
                                             typename Op<BF>::S *Tb, typename Op<BF>::S *Tk,
                                             typename Op<BF>::S *TT, int ldt, const float *cb,
                                             const float *ck) {
     using S = typename Op<BF>::S;
-    if (wave < 4) {
-        // column c of the inverse of the diagonal block, right-looking
-        // substitution: once x_i is final, fold it into every later row
-        // (independent updates, dependency depth 16)
-        const int c = lane & 15, o = 16 * wave;
+    if (wave == 0) {
+        const int c = lane & 15, o = 16 * (lane >> 4);
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+        // right-looking: once x_i is final, fold it into every later row
+        auto ldrow = [&](int i, float4 *d) {
+            const float *p = Lt + (o + i) * LDF + o;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) d[q4] = *reinterpret_cast<const float4 *>(p + 4 * q4);
+        };
+        float4 r0[4], r1[4], r2[4];
+        ldrow(0, r0);
+        ldrow(1, r1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+            if (i + 2 < 16) ldrow(i + 2, r2);
+            const float l[16] = {r0[0].x, r0[0].y, r0[0].z, r0[0].w, r0[1].x, r0[1].y, r0[1].z, r0[1].w,
+                                 r0[2].x, r0[2].y, r0[2].z, r0[2].w, r0[3].x, r0[3].y, r0[3].z, r0[3].w};
 #pragma unroll
-            for (int rr = i + 1; rr < 16; ++rr) x[rr] -= L[(o + rr) * LDF + o + i] * x[i];
-        }
-        if (lane < 16) {
-            const float sb = WB ? cb[o + c] : 0.f, sk = WK ? ck[o + c] : 0.f;
+            for (int rr = i + 1; rr < 16; ++rr) x[rr] -= l[rr] * x[i];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                Tm[(o + i) * LDF + o + c] = x[i];
-                if constexpr (WB) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
-                if constexpr (WK) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
-                if constexpr (WT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                r0[q4] = r1[q4];
+                r1[q4] = r2[q4];
             }
         }
-        // zero the blocks right of the diagonal in this block row
+        const float sb = WB ? cb[o + c] : 0.f, sk = WK ? ck[o + c] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Tm[(o + i) * LDF + o + c] = x[i];
+            if constexpr (WB) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
+            if constexpr (WK) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
+            if constexpr (WT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
+        }
+    } else if (wave < 4) {
+        // zero the blocks right of the diagonal in block row wave - 1
+        const int o = 16 * (wave - 1);
         for (int e = lane; e < 16 * 48; e += 64) {
-            const int i = e / 48, cc = e % 48 + 16 * (wave + 1);
+            const int i = e / 48, cc = e % 48 + o + 16;
             if (cc < C) {
                 if constexpr (WB) Tb[(o + i) * ldt + cc] = S(0);
                 if constexpr (WK) Tk[(o + i) * ldt + cc] = S(0);
@@ -425,7 +441,7 @@ __device__ __forceinline__ void tri_inverse(const float *L, float *Tm, float *xs
             for (int bk = bj; bk < bi; ++bk) {
 #pragma unroll
                 for (int k0 = 0; k0 < 16; k0 += 4) {
-                    const float a = L[(16 * bi + r) * LDF + 16 * bk + k0 + kq];
+                    const float a = Lt[(16 * bk + k0 + kq) * LDF + 16 * bi + r];
                     const float b = Tm[(16 * bk + k0 + kq) * LDF + 16 * bj + r];
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
                 }

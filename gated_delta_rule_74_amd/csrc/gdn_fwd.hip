@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         for (int i = 0; i < 4; ++i) sk[i] = zero4();
         gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            Lm[row * LDF + col] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f;
+            Lm[col * LDF + row] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f; // L^T
         });
         __syncthreads(); // L complete, Ks no longer read
         tri_inverse<BF, true, true, false>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
