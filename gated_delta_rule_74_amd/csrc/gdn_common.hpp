@@ -194,21 +194,28 @@ __device__ __forceinline__ void store_N(const f32x4 *acc, typename Op<BF>::S *ds
 // Register fragment of an NR-row tile [NR][DP] (a chunk of a [B,T,H,*]
 // tensor, or a state matrix) in row-major global memory.
 // fetch() issues the global loads (16-byte vectors; one item = one vector of
-// one row), stash() writes the fragment to LDS straight and/or transposed.
-// Items are numbered so that consecutive lanes hold consecutive rows of the
-// same vector group: transposed LDS stores of a wave then hit consecutive
-// addresses, and straight 16-byte stores of 16 lanes cover all banks once.
+// one row), stash() writes the fragment to LDS (optionally row-scaled).
+// Items are numbered row-major: consecutive lanes hold consecutive 16-byte
+// pieces of a row, so the loads of one wave touch as few cache lines as the
+// tile's row layout allows.
 template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
     using S = typename Op<BF>::S;
     static constexpr int V = Op<BF>::VEC;
     static constexpr int NG = DP / V;
     static constexpr int NIT = (NR * NG + NT - 1) / NT;
+    static constexpr bool FULL = (NR * NG) % NT == 0; // every thread's items exist
     union U {
         uint4 u;
         S s[V];
     };
     U r[NIT];
     uint32_t ok; // bit m: item m lies inside the tensor (else it reads as zero)
+
+    // item it = row j, vector group cg (row-major)
+    __device__ __forceinline__ static void pos(int it, int &j, int &cg) {
+        j = it / NG;
+        cg = it % NG;
+    }
 
     // x: column 0 of row 0 of the tile, rs: elements between rows, n valid
     // rows (n >= 1), d valid columns. VEC: rows start on 16-byte boundaries
@@ -222,8 +229,9 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
 #pragma unroll
             for (int m = 0; m < NIT; ++m) {
                 const int it = tid + m * NT;
-                const int j = it % NR, cg = it / NR;
-                const bool in = ((NR * NG) % NT == 0 || cg < NG) && j < n && cg * V < d;
+                int j, cg;
+                pos(it, j, cg);
+                const bool in = (FULL || j < NR) && j < n && cg * V < d;
                 const int jj = min(j, n - 1), cc = min(cg * V, d - V);
                 r[m].u = *reinterpret_cast<const uint4 *>(x + (size_t)jj * rs + cc);
                 ok |= (in ? 1u : 0u) << m;
@@ -232,9 +240,10 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
 #pragma unroll
             for (int m = 0; m < NIT; ++m) {
                 const int it = tid + m * NT;
-                const int j = it % NR, cg = it / NR;
+                int j, cg;
+                pos(it, j, cg);
                 r[m].u = uint4{0u, 0u, 0u, 0u};
-                if ((NR * NG) % NT != 0 && cg >= NG) continue;
+                if (!FULL && j >= NR) continue;
                 if (j < n) {
 #pragma unroll
                     for (int e = 0; e < V; ++e)
@@ -253,57 +262,28 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
     __device__ __forceinline__ void stash(S *dst, int ldd, int tid) const {
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NT;
-            const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NT != 0 && cg >= NG) continue;
+            int j, cg;
+            pos(tid + m * NT, j, cg);
+            if (!FULL && j >= NR) continue;
             *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = item(m);
         }
     }
 
-    // Straight copy with every element scaled by `sc`; requires that every
-    // item of this thread lies in row j == lane (NR == 64).
+    // Straight copy with row j scaled by the value `sc` holds in lane j
+    // (NR == 64: every wave carries the 64 row scales, one per lane).
     __device__ __forceinline__ void stash_scaled(S *dst, int ldd, int tid, float sc) const {
-        static_assert(NR == 64 && NT % 64 == 0, "row of an item must equal the lane");
+        static_assert(NR == 64, "one row scale per lane");
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NT;
-            const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NT != 0 && cg >= NG) continue;
+            int j, cg;
+            pos(tid + m * NT, j, cg);
+            const float rsc = __shfl(sc, j, 64);
+            if (!FULL && j >= NR) continue;
             U val, out;
             val.u = item(m);
 #pragma unroll
-            for (int e = 0; e < V; ++e) out.s[e] = from_f<BF>(to_f(val.s[e]) * sc);
+            for (int e = 0; e < V; ++e) out.s[e] = from_f<BF>(to_f(val.s[e]) * rsc);
             *reinterpret_cast<uint4 *>(dst + j * ldd + cg * V) = out.u;
-        }
-    }
-
-    // Transposed copy to dstT [DP][ldt].
-    __device__ __forceinline__ void stash_T(S *dstT, int ldt, int tid) const {
-#pragma unroll
-        for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NT;
-            const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NT != 0 && cg >= NG) continue;
-            U val;
-            val.u = item(m);
-#pragma unroll
-            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = val.s[e];
-        }
-    }
-
-    // Transposed copy scaled by `sc`; requires that every item of this
-    // thread lies in row j == lane (NR == 64).
-    __device__ __forceinline__ void stash_T_scaled(S *dstT, int ldt, int tid, float sc) const {
-        static_assert(NR == 64 && NT % 64 == 0, "row of an item must equal the lane");
-#pragma unroll
-        for (int m = 0; m < NIT; ++m) {
-            const int it = tid + m * NT;
-            const int j = it % NR, cg = it / NR;
-            if ((NR * NG) % NT != 0 && cg >= NG) continue;
-            U val;
-            val.u = item(m);
-#pragma unroll
-            for (int e = 0; e < V; ++e) dstT[(cg * V + e) * ldt + j] = from_f<BF>(to_f(val.s[e]) * sc);
         }
     }
 };

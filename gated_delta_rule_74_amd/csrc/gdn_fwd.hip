@@ -29,10 +29,10 @@ template <bool BF, int D> struct PrepSmem {
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
     static constexpr int mx(int x, int y) { return x > y ? x : y; }
-    static constexpr int oK = 0;                                       // Ks [C][LDD] -> Tb [C][LDC]
-    static constexpr int oKT = oK + mx(C * LDD, C * LDC) * (int)sizeof(S); // KT [D][LDC]
-    static constexpr int oVT = oKT + D * LDC * (int)sizeof(S);        // VT [D][LDC]
-    static constexpr int oL = oVT + D * LDC * (int)sizeof(S);         // L fp32 [C][LDF]
+    static constexpr int oK = 0;                                       // Ks [C][LDD]
+    static constexpr int oV = oK + C * LDD * (int)sizeof(S);          // Vs [C][LDD]
+    static constexpr int oTb = oV + C * LDD * (int)sizeof(S);         // Tb [C][LDC]
+    static constexpr int oL = oTb + C * LDC * (int)sizeof(S);         // L^T fp32 [C][LDF]
     static constexpr int oT = oL + C * LDF * 4;                       // Tm fp32 [C][LDF]
     static constexpr int oTk = oT + C * LDF * 4;                      // Tk [C][LDC]
     static constexpr int oX = oTk + C * LDC * (int)sizeof(S);         // solve scratch
@@ -61,9 +61,8 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
-    S *Tb = (S *)(smem + L::oK);
-    S *KT = (S *)(smem + L::oKT);
-    S *VT = (S *)(smem + L::oVT);
+    S *Vs = (S *)(smem + L::oV);
+    S *Tb = (S *)(smem + L::oTb);
     float *Lm = (float *)(smem + L::oL);
     float *Tm = (float *)(smem + L::oT);
     S *Tk = (S *)(smem + L::oTk);
@@ -97,8 +96,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         ck[lane] = be * dc.eg;
     }
     fk.stash(Ks, LDD, tid);
-    fk.stash_T(KT, LDC, tid);
-    fv.stash_T(VT, LDC, tid);
+    fv.stash(Vs, LDD, tid);
     __syncthreads();
 
     if (!s.additive) {
@@ -109,7 +107,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             Lm[col * LDF + row] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f; // L^T
         });
-        __syncthreads(); // L complete, Ks no longer read
+        __syncthreads(); // L complete
         tri_inverse<BF, true, true, false>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
@@ -145,14 +143,14 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         f32x4 acc[Tiles<4, DT>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
-        gemm<BF, 4, DT, C>(Tb, LDC, VT, LDC, acc, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, acc, wave, lane);
         store_global<BF, 4, DT>(acc, (S *)a.U + cbase * C * dv, dv, C, dv, 1.f, wave, lane);
     }
     if (!s.additive) {
         f32x4 acc[Tiles<4, DT>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
-        gemm<BF, 4, DT, C>(Tk, LDC, KT, LDC, acc, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(Tk, LDC, Ks, LDD, acc, wave, lane);
         store_global<BF, 4, DT>(acc, (S *)a.NK + cbase * C * dk, dk, C, dk, -1.f, wave, lane);
     }
 }
