@@ -180,10 +180,10 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 // U and Tm come from the forward context, so no triangular solve runs here.
 // Eight LDS regions are reused phase by phase (Pn = phase n):
 //   R0 K                              R4 dh'^T (P4-5) -> -dV't (P6-7)
-//   R1 Q (P1) -> h^T (P3-5) -> V (P6) -> dSt (P7-8)
+//   R1 Q (P1) -> h^T (P3-5) -> V (P6) -> dSt (P7-8) -> dQ (P11)
 //   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7) -> dPGt (P9-10)
 //   R3 U (P3) -> dO (P4-9) -> partial sums (P11)
-//   R5 Wt (P3-9)                      R6 dWt (P4-6) -> dK't (P6-7)
+//   R5 Wt (P3-9) -> dK (P11)          R6 dWt (P4-6) -> dK't (P6-7)
 //   R7 -Kw (P3) -> dKw (P5-6) -> U (P7) -> Q (P9-10)
 // Inputs needed in two phases stay in registers between their stashes.
 
@@ -203,7 +203,7 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int o3 = o2 + mx(sCC, sCD);
     static constexpr int o4 = o3 + mx(sCD, sPart);
     static constexpr int o5 = o4 + mx(sDD, sDC);
-    static constexpr int o6 = o5 + sDC;
+    static constexpr int o6 = o5 + mx(sDC, sCD);
     static constexpr int o7 = o6 + sDC;
     static constexpr int oGam = o7 + mx(sCD, sCC);
     static constexpr int oEg = oGam + C * 8;
@@ -376,8 +376,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
             for (int e = 0; e < O::VEC; ++e) hd += to_f(x.s[e]) * to_f(y.s[e]);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
+        hd = wave_sum(hd);
         if (lane == 0) misc[16 + wave] = hd;
         // R7 (-Kw) and R2 (Pt) are free: dKw (token rows) and Tm go there
         if (!add) {
@@ -397,18 +396,16 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, DT, C, true, false>(R2, LDC, R6, LDC, accV, wave, lane);
         if (!add) gemm<BF, 4, DT, C, true, true>(R2, LDC, R7, LDD, accKp, wave, lane);
         __syncthreads(); // V visible; Tm, dWt, dKw reads done
-        S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < n && col < dv) dv_out[(size_t)row * H * dv + col] = from_f<BF>(bet[row] * accV[i][e]);
             const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
             rbD[i][e] += to_f(R1[row * LDD + col]) * accV[i][e] + eg[row] * kk;
             rgD[i][e] += bet[row] * eg[row] * kk;
             accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
         });
-        if (!add) {
 #pragma unroll
-            for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-            store_T<BF, 4, DT>(accV, R4, LDC, wave, lane);  // -dV't
+        for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
+        store_T<BF, 4, DT>(accV, R4, LDC, wave, lane); // -dV't (also the source of dv)
+        if (!add) {
             store_T<BF, 4, DT>(accKp, R6, LDC, wave, lane); // dK't
             fn.stash(R2, LDD, tid);                         // -Kw again
             fu.stash(R7, LDD, tid);                         // U again
@@ -457,14 +454,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         });
         gemm<BF, 4, DT, C, true, true>(R2, LDC, Ks, LDD, accQ, wave, lane);
         gemm<BF, 4, DT, C, false, true>(R2, LDC, R7, LDD, accKd, wave, lane);
-        S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
-        S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
-        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < n && col < dk) {
-                dq_out[(size_t)row * H * dk + col] = from_f<BF>(accQ[i][e]);
-                dk_out[(size_t)row * H * dk + col] = from_f<BF>(accKd[i][e]);
-            }
-        });
+        // dQ and dK leave through LDS (R1 and R5 are free) as 16-byte rows
+        store_N<BF, 4, DT>(accQ, R1, LDD, wave, lane);
+        store_N<BF, 4, DT>(accKd, R5, LDD, wave, lane);
     }
     // ---- P11: one fixed-order reduction of every dbeta / dgam contribution
     {
@@ -478,6 +470,46 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         row_partials<4, 4>(xgC, pRgC, wave, lane);
         col_partials<4, 4>(xgC, pCgC, wave, lane);
         __syncthreads();
+        // dq, dk, dv rows of the chunk: 16-byte stores (dv = -beta * (-dV'), from
+        // the transposed -dV't)
+        {
+            S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+            S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+            S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+            constexpr int V = O::VEC, NG = D / V;
+            if (VEC) {
+                for (int it = tid; it < C * NG; it += NTHR) {
+                    const int j = it / NG, c0 = (it % NG) * V;
+                    if (j >= n) continue;
+                    if (c0 < dk) {
+                        *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(R1 + j * LDD + c0);
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                    }
+                    if (c0 < dv) {
+                        union {
+                            uint4 u;
+                            S x[V];
+                        } pk;
+                        const float nb = -bet[j];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(R4[(c0 + e) * LDC + j]));
+                        *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
+                    }
+                }
+            } else {
+                for (int it = tid; it < C * D; it += NTHR) {
+                    const int j = it / D, col = it % D;
+                    if (j >= n) continue;
+                    if (col < dk) {
+                        dq_out[(size_t)j * H * dk + col] = R1[j * LDD + col];
+                        dk_out[(size_t)j * H * dk + col] = R5[j * LDD + col];
+                    }
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(R4[col * LDC + j]));
+                }
+            }
+        }
         if (wave == 0) {
             const int i = lane;
             float db = 0.f, dgm = 0.f, sj = 0.f;
@@ -494,20 +526,14 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             }
             // gam_n enters through e^{gam_n} h and e^{gam_n - gam_j}: its gradient
             // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row; -s_j to row j
-            float stot = sj;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) stot += __shfl_xor(stot, off, 64);
+            const float stot = wave_sum(sj);
             float hds = 0.f;
             for (int w = 0; w < NWAVE; ++w) hds += misc[16 + w];
             dgm -= sj;
             if (i == C - 1) dgm += misc[0] * hds + stot;
-            // dlam_r = sum_{i >= r} dgam_i
-            float x = dgm;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_down(x, off, 64);
-                if (lane + off < 64) x += o;
-            }
+            // dlam_r = sum_{i >= r} dgam_i = total - (prefix through r) + dgam_r
+            const float pre = wave_prefix(dgm);
+            const float x = lane_value(pre, 63) - pre + dgm;
             const float dg = (float)A * x;
             float p = (lane < n) ? gch[lane] * dg : 0.f;
             if (lane < n) {
@@ -515,8 +541,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                 a.dg[gi] = dg;
                 a.dbeta[gi] = db;
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+            p = wave_sum(p);
             if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
         }
     }

@@ -116,6 +116,24 @@ __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
     using O = Op<BF>;
     static_assert(KD % O::KSTEP == 0, "contraction length must be a multiple of the MFMA K");
     const int r = lane & 15, kq = lane >> 4;
+    if constexpr (BF && NWAVE % NT == 0 && Tiles<MT, NT>::N % NWAVE == 0 && Tiles<MT, NT>::PW > 1) {
+        // all tiles of this wave share the column block tn = wave % NT: read
+        // each B operand once per K step and reuse it for every tile
+        const int tn = wave % NT;
+#pragma unroll
+        for (int k0 = 0; k0 < KD; k0 += O::KSTEP) {
+            const bf16x8 bv = BTR ? operand_tr(B, ldb, k0, tn * 16, lane)
+                                  : *reinterpret_cast<const bf16x8 *>(B + (tn * 16 + r) * ldb + k0 + kq * 8);
+#pragma unroll
+            for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
+                const int tm = (wave + NWAVE * i) / NT;
+                const bf16x8 av = ATR ? operand_tr(A, lda, k0, tm * 16, lane)
+                                      : *reinterpret_cast<const bf16x8 *>(A + (tm * 16 + r) * lda + k0 + kq * 8);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
         const int t = wave + NWAVE * i;
@@ -461,12 +479,41 @@ template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
                                                                  0xF, true));
 }
 
+// x from the lane `CTRL` names, for the rows in ROWMASK only (other rows get 0).
+template <int CTRL, int ROWMASK> __device__ __forceinline__ float dpp_rows(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK,
+                                                                 0xF, false));
+}
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 // Sum over the 16 lanes of a row; every lane of the row gets the total.
 __device__ __forceinline__ float sum16(float x) {
     x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
     x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
     x += dpp_f<0x141>(x); // row_half_mirror
     x += dpp_f<0x140>(x); // row_mirror
+    return x;
+}
+
+// Sum over the 64 lanes (fixed order: row sums, then rows 0+1 and 2+3);
+// the same value in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = sum16(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets x_0 + ... +
+// x_l): shifts inside 16-lane rows, then the row totals carried across rows.
+__device__ __forceinline__ float wave_prefix(float x) {
+    x += dpp_f<0x111>(x); // row_shr:1 (lanes shifted in from outside the row read 0)
+    x += dpp_f<0x112>(x); // row_shr:2
+    x += dpp_f<0x114>(x); // row_shr:4
+    x += dpp_f<0x118>(x); // row_shr:8
+    x += dpp_rows<0x142, 0xA>(x); // row_bcast:15 into rows 1 and 3
+    x += dpp_rows<0x143, 0xC>(x); // row_bcast:31 into rows 2 and 3
     return x;
 }
 
