@@ -123,10 +123,31 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         if (!s.additive) fn.stash(NKs, LDD, tid);
         // stores go out between consuming one prefetch and issuing the next,
         // so waiting for the inputs never waits for a store
-        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < dk && col < nvc)
-                dhs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accDH[i][e]);
-        });
+        // 4 consecutive rows d of one column v per lane: one 8-byte store
+        // into the transposed [dv][dk] block when dk allows it
+        {
+            const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+            for (int i = 0; i < Tiles<DT, VT>::PW; ++i) {
+                const int t = wave + NWAVE * i;
+                if (Tiles<DT, VT>::N % NWAVE != 0 && t >= Tiles<DT, VT>::N) break;
+                const int d0 = (t / VT) * 16 + 4 * kq, col = (t % VT) * 16 + r16;
+                S *dst = dhs + (((size_t)bh * s.NC + c) * dv + v0 + col) * dk + d0;
+                if (col >= nvc) continue;
+                if (BF && dk % 4 == 0) {
+                    if (d0 < dk) {
+                        uint2 u;
+                        u.x = f2bf2(accDH[i][0], accDH[i][1]);
+                        u.y = f2bf2(accDH[i][2], accDH[i][3]);
+                        *reinterpret_cast<uint2 *>(dst) = u;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < dk) dst[e] = from_f<BF>(accDH[i][e]);
+                }
+            }
+        }
         if (c > 0) fetch(c - 1);
         __syncthreads();
 

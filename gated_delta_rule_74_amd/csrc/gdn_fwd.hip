@@ -139,19 +139,39 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
             *reinterpret_cast<uint4 *>(dst + e) = pk.u;
         }
     }
-    {
-        f32x4 acc[Tiles<4, DT>::PW];
+    f32x4 accU[Tiles<4, DT>::PW], accN[Tiles<4, DT>::PW];
 #pragma unroll
-        for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
-        gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, acc, wave, lane);
-        store_global<BF, 4, DT>(acc, (S *)a.U + cbase * C * dv, dv, C, dv, 1.f, wave, lane);
-    }
-    if (!s.additive) {
-        f32x4 acc[Tiles<4, DT>::PW];
+    for (int i = 0; i < Tiles<4, DT>::PW; ++i) accU[i] = accN[i] = zero4();
+    gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, accU, wave, lane);
+    if (!s.additive) gemm<BF, 4, DT, C, false, true>(Tk, LDC, Ks, LDD, accN, wave, lane);
+    S *Ug = (S *)a.U + cbase * C * dv, *Ng = (S *)a.NK + cbase * C * dk;
+    if constexpr (BF && 2 * C * D * (int)sizeof(S) <= C * LDF * 4) {
+        // U and NK leave through the spent L^T area as 16-byte pieces of
+        // their contiguous [64][d] blocks
+        S *Us = (S *)Lm, *Ns = Us + C * D;
 #pragma unroll
-        for (int i = 0; i < Tiles<4, DT>::PW; ++i) acc[i] = zero4();
-        gemm<BF, 4, DT, C, false, true>(Tk, LDC, Ks, LDD, acc, wave, lane);
-        store_global<BF, 4, DT>(acc, (S *)a.NK + cbase * C * dk, dk, C, dk, -1.f, wave, lane);
+        for (int i = 0; i < Tiles<4, DT>::PW; ++i) accN[i] = -accN[i];
+        store_N<BF, 4, DT>(accU, Us, D, wave, lane);
+        store_N<BF, 4, DT>(accN, Ns, D, wave, lane);
+        __syncthreads();
+        constexpr int V = O::VEC, NG = D / V;
+        if (VEC) {
+            for (int it = tid; it < C * NG; it += NTHR) {
+                const int j = it / NG, c0 = (it % NG) * V;
+                if (c0 < dv) *reinterpret_cast<uint4 *>(Ug + (size_t)j * dv + c0) = *reinterpret_cast<const uint4 *>(Us + j * D + c0);
+                if (!s.additive && c0 < dk)
+                    *reinterpret_cast<uint4 *>(Ng + (size_t)j * dk + c0) = *reinterpret_cast<const uint4 *>(Ns + j * D + c0);
+            }
+        } else {
+            for (int it = tid; it < C * D; it += NTHR) {
+                const int j = it / D, col = it % D;
+                if (col < dv) Ug[(size_t)j * dv + col] = Us[j * D + col];
+                if (!s.additive && col < dk) Ng[(size_t)j * dk + col] = Ns[j * D + col];
+            }
+        }
+    } else {
+        store_global<BF, 4, DT>(accU, Ug, dv, C, dv, 1.f, wave, lane);
+        if (!s.additive) store_global<BF, 4, DT>(accN, Ng, dk, C, dk, -1.f, wave, lane);
     }
 }
 
