@@ -25,7 +25,7 @@ __all__ = ["fwd", "bwd", "step", "GatedDeltaRule", "GdnError", "lib", "EXPORTS",
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
-           "gdn_fwd_context_size", "gdn_time_launches", "gdn_status_string",
+           "gdn_fwd_context_size", "gdn_time_launches", "gdn_launch_kind", "gdn_status_string",
            "gdn_last_error_detail"]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -66,6 +66,8 @@ def lib():
             f.restype = Z
         L.gdn_time_launches.argtypes = [P, I32]
         L.gdn_time_launches.restype = I32
+        L.gdn_launch_kind.argtypes = [I32]
+        L.gdn_launch_kind.restype = I32
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error_detail.argtypes = []
@@ -285,6 +287,13 @@ class LaunchTimer:
         torch.cuda.synchronize()
         n = min(self.count, len(self.events) // 2)
         return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
+
+    KINDS = ("fwd_prep", "fwd_chain", "bwd_chain", "bwd_local", "dA_reduce", "step")
+
+    def kinds(self):
+        """Kernel name of every bracketed launch, in launch order."""
+        n = min(self.count, len(self.events) // 2)
+        return [self.KINDS[lib().gdn_launch_kind(i)] for i in range(n)]
 
 
 class GatedDeltaRule(torch.autograd.Function):

@@ -126,9 +126,14 @@ int pad_of(const gdn_shape_t *s) {
 thread_local void *const *g_events = nullptr;
 thread_local int g_nevents = 0;
 thread_local int g_launch = 0;
+constexpr int KIND_LOG = 4096;
+thread_local int8_t g_kinds[KIND_LOG];
+thread_local int g_kind_n = 0; // launches logged by the last bracketing period
+enum Kind { K_FWD_PREP = 0, K_FWD_CHAIN, K_BWD_CHAIN, K_BWD_LOCAL, K_DA_REDUCE, K_STEP };
 
-template <class F> hipError_t timed(F &&launch, hipStream_t st) {
+template <class F> hipError_t timed(Kind kind, F &&launch, hipStream_t st) {
     const int i = g_launch;
+    if (g_events && i < KIND_LOG) g_kinds[i] = (int8_t)kind;
     const bool on = g_events && 2 * i + 1 < g_nevents;
     if (on) {
         const hipError_t e = hipEventRecord((hipEvent_t)g_events[2 * i], st);
@@ -166,8 +171,15 @@ const char *gdn_status_string(gdn_status_t st) {
 
 const char *gdn_last_error_detail(void) { return g_detail; }
 
+int32_t gdn_launch_kind(int32_t i) {
+    const int n = g_events ? g_launch : g_kind_n;
+    if (i < 0 || i >= n || i >= KIND_LOG) return -1;
+    return g_kinds[i];
+}
+
 int32_t gdn_time_launches(void *const *events, int32_t n) {
     const int32_t done = g_launch;
+    g_kind_n = done;
     g_events = events;
     g_nevents = events ? n : 0;
     g_launch = 0;
@@ -176,10 +188,13 @@ int32_t gdn_time_launches(void *const *events, int32_t n) {
 
 // per-token log2-decay of every chunk (fp32), written by fwd_prep
 size_t gam_bytes(const gdn_shape_t *s) { return (size_t)s->B * s->H * nchunks(s) * 64 * sizeof(float); }
+// one fp32 state per (batch, head): hand-off between chunk ranges
+size_t state32_bytes(const gdn_shape_t *s) { return (size_t)s->B * s->H * s->dk * s->dv * sizeof(float); }
 
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
-    return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)) + align_up(gam_bytes(s));
+    return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)) + align_up(gam_bytes(s)) +
+           align_up(state32_bytes(s));
 }
 
 size_t gdn_fwd_context_size(const gdn_shape_t *s) {
@@ -191,34 +206,107 @@ size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
     const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
     return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part +
-           align_up(gam_bytes(s)) /* forward decay */;
+           align_up(gam_bytes(s)) /* forward decay */ + align_up(state32_bytes(s)) /* forward hand-off */;
 }
 
 namespace {
 
-// Forward pass into caller-provided buffers: U and NK of every chunk, then
-// the serial state pass (o may be null: states only).
+// Second stream and events of this thread for one device: the forward
+// overlaps the prep of the next chunk range with the serial pass over the
+// current one. Created on first use, kept for the life of the process.
+constexpr int MAX_SEG = 8;
+struct Aux {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[MAX_SEG + 1] = {};
+};
+thread_local Aux g_aux[64];
+
+hipError_t aux_of_current(Aux *&out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    Aux &x = g_aux[dev];
+    if (!x.side) {
+        e = hipStreamCreateWithFlags(&x.side, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+        for (hipEvent_t &ev : x.ev) {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+    }
+    out = &x;
+    return hipSuccess;
+}
+
+// Number of chunk ranges the forward is split into (one when the serial
+// kernel cannot take a range, or the sequence is short).
+int fwd_segments(const gdn_shape_t *s, bool bf, int D) {
+    if (!gdn::fwd_segmentable(bf, D)) return 1;
+    const int n = nchunks(s) / 16;
+    return n < 1 ? 1 : (n > 4 ? 4 : n);
+}
+
+// Forward pass into caller-provided buffers: U, NK (and Tm, γ) of every
+// chunk, then the serial state pass (o may be null: states only). hs: fp32
+// [B,H,dk,dv] hand-off state between chunk ranges.
 hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
-                       void *Tsave, float *gam, void *o, float *hT, void *cs, hipStream_t strm) {
+                       void *Tsave, float *gam, float *hs, void *o, float *hT, void *cs, hipStream_t strm) {
+    const int NC = nchunks(s), nseg = fwd_segments(s, bf, D);
     gdn::PrepArgs pa;
     pa.s = sa;
     pa.U = U;
     pa.NK = NK;
     pa.Tsave = Tsave;
     pa.gam = gam;
-    hipError_t he = timed([&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
-    if (he != hipSuccess) return he;
     gdn::FwdChainArgs fa;
     fa.s = sa;
     fa.U = U;
     fa.NK = NK;
     fa.gam = gam;
     fa.o = o;
-    fa.hT = hT;
     fa.cs = cs;
     const int BV = gdn::fwd_vblock(D);
     fa.NVB = (s->dv + BV - 1) / BV;
-    return timed([&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
+    auto seg_lo = [&](int k) { return (int)((long long)k * NC / nseg); };
+    hipError_t he;
+    if (nseg == 1) {
+        pa.c0 = 0;
+        pa.ncs = NC;
+        he = timed(K_FWD_PREP, [&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
+        if (he != hipSuccess) return he;
+        fa.c0 = 0;
+        fa.c1 = NC;
+        fa.h_in = sa.h0;
+        fa.hT = hT;
+        return timed(K_FWD_CHAIN, [&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
+    }
+    Aux *x = nullptr;
+    if ((he = aux_of_current(x)) != hipSuccess) return he;
+    // fork: the second stream starts after the caller's earlier work
+    if ((he = hipEventRecord(x->ev[0], strm)) != hipSuccess) return he;
+    if ((he = hipStreamWaitEvent(x->side, x->ev[0], 0)) != hipSuccess) return he;
+    pa.c0 = 0;
+    pa.ncs = seg_lo(1);
+    he = timed(K_FWD_PREP, [&] { return gdn::launch_fwd_prep(pa, bf, D, strm); }, strm);
+    if (he != hipSuccess) return he;
+    for (int k = 0; k < nseg; ++k) {
+        if (k + 1 < nseg) {
+            pa.c0 = seg_lo(k + 1);
+            pa.ncs = seg_lo(k + 2) - pa.c0;
+            he = timed(K_FWD_PREP, [&] { return gdn::launch_fwd_prep(pa, bf, D, x->side); }, x->side);
+            if (he != hipSuccess) return he;
+            if ((he = hipEventRecord(x->ev[k + 1], x->side)) != hipSuccess) return he;
+        }
+        if (k > 0 && (he = hipStreamWaitEvent(strm, x->ev[k], 0)) != hipSuccess) return he;
+        fa.c0 = seg_lo(k);
+        fa.c1 = seg_lo(k + 1);
+        fa.h_in = k == 0 ? sa.h0 : hs;
+        fa.hT = k + 1 == nseg ? hT : hs;
+        he = timed(K_FWD_CHAIN, [&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
+        if (he != hipSuccess) return he;
+    }
+    return hipSuccess; // the last range waited for the second stream's last launch
 }
 
 } // namespace
@@ -260,8 +348,9 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     void *NK = ctx ? c + cl.nk : w + align_up(blocks_bytes(s, s->dv));
     void *Tsave = ctx ? c + cl.t : nullptr;
     float *gam = (float *)(w + align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)));
+    float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
-    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, gam, o, hT, ctx, (hipStream_t)stream),
+    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, o, hT, ctx, (hipStream_t)stream),
                       "gdn_fwd launch");
 }
 
@@ -317,11 +406,12 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     char *dhs = wctx + ctx_bytes(s);
     float *part = (float *)(dhs + align_up(states_bytes(s)));
     float *gam = (float *)((char *)part + align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float)));
+    float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     const CtxLayout cl = ctx_layout(s);
     hipError_t he;
     if (!ctx) {
-        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, nullptr, hT, wctx, strm);
+        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, hs, nullptr, hT, wctx, strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
         ctx = wctx;
     }
@@ -336,7 +426,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     ca.dh0 = dh0;
     const int BVc = gdn::bwd_chain_vblock(bf, D);
     ca.NVB = (s->dv + BVc - 1) / BVc;
-    he = timed([&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
+    he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd chain launch");
     gdn::BwdLocalArgs la;
     la.s = sa;
@@ -352,9 +442,9 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     la.dg = dg;
     la.dbeta = dbeta;
     la.dA_part = part;
-    he = timed([&] { return gdn::launch_bwd_local(la, bf, D, strm); }, strm);
+    he = timed(K_BWD_LOCAL, [&] { return gdn::launch_bwd_local(la, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd local launch");
-    he = timed([&] { return gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm); }, strm);
+    he = timed(K_DA_REDUCE, [&] { return gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm); }, strm);
     return hip_status(he, "gdn_bwd dA_log launch");
 }
 
@@ -395,7 +485,7 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
     a.dk = dk;
     a.dv = dv;
     a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
-    return hip_status(timed([&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
+    return hip_status(timed(K_STEP, [&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
                       "gdn_step launch");
 }
 

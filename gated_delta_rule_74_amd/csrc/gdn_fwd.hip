@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     // heads fastest: the rows of all heads of one token are adjacent in
     // memory, so workgroups that share cache lines run together on one XCD
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid % s.H, c = (lid / s.H) % s.NC, b = lid / (s.H * s.NC);
+    const int h = lid % s.H, c = a.c0 + (lid / s.H) % a.ncs, b = lid / (s.H * a.ncs);
     const int bh = b * s.H + h;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
     const int t0 = c * C, n = min(C, T - t0);
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     const int g = lane >> 4, r = lane & 15;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / s.H, h = bh % s.H;
-    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC, c0 = a.c0, c1 = a.c1;
     const bool chain = wave < DT;
     const bool add = s.additive != 0;
 
@@ -469,21 +469,21 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int d = 16 * kb + 4 * g + e, v = v0 + r;
-                hacc[kb][e] = (s.h0 && d < dk && v < dv) ? s.h0[((size_t)bh * dk + d) * dv + v] : 0.f;
+                hacc[kb][e] = (a.h_in && d < dk && v < dv) ? a.h_in[((size_t)bh * dk + d) * dv + v] : 0.f;
             }
             hb[kb] = pack4(hacc[kb]);
-            *(short4_t *)(hx(0) + (v0 + r) * LDD + 16 * kb + 4 * g) = hb[kb];
+            *(short4_t *)(hx(c0 & 1) + (v0 + r) * LDD + 16 * kb + 4 * g) = hb[kb];
         }
     } else {
-        fetch(0);
-        stash(0);
-        if (NC > 1) fetch(1);
+        fetch(c0);
+        stash(c0);
+        if (c1 - c0 > 1) fetch(c0 + 1);
     }
     __syncthreads();
 
-    for (int c = 0; c <= NC; ++c) {
+    for (int c = c0; c <= c1; ++c) {
         if (chain) {
-            if (c < NC) {
+            if (c < c1) {
                 const int st = c & 1;
                 const u16 *Ks = stage(st, 1), *NKs = stage(st, 2), *Us = stage(st, 3);
                 const float *egn = egn_of(st);
@@ -534,10 +534,10 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
             // chunk c+1 into LDS (requested one chunk ago), chunk c+2 requested;
             // this chunk's stores are issued after these loads, so the next
             // wait for loads does not wait on them
-            if (c + 1 < NC) stash(c + 1);
-            if (c + 2 < NC) fetch(c + 2);
+            if (c + 1 < c1) stash(c + 1);
+            if (c + 2 < c1) fetch(c + 2);
             // finish O of the previous chunk: + P W
-            if (o && c >= 1) {
+            if (o && c > c0) {
                 const int pst = (c - 1) & 1, n = min(C, T - (c - 1) * C);
                 const u16 *Pt = pbuf(pst, ib), *WT = wx(pst);
 #pragma unroll
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                 }
             }
             // chunk-start state h_c out, transposed [dv][dk]
-            if (cs && c < NC) {
+            if (cs && c < c1) {
                 const u16 *HT = hx(c & 1);
                 u16 *dst = cs + ((size_t)bh * NC + c) * dv * dk;
                 if (VEC) {
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                 }
             }
             // P (this helper's half of the columns) and diag(e^gam) Q h
-            if (o && c < NC) {
+            if (o && c < c1) {
                 const int st = c & 1;
                 const u16 *Qs = stage(st, 0), *Ks = stage(st, 1), *HT = hx(st);
                 const float *gam = gam_of(st);
@@ -650,8 +650,10 @@ int pad_dim(int d, bool bf16) {
 
 int fwd_vblock(int D) { return D >= 64 ? 32 : 16; }
 
+bool fwd_segmentable(bool bf16, int D) { return bf16 && (D == 32 || D == 64); }
+
 template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStream_t st) {
-    const int grid = a.s.B * a.s.H * a.s.NC;
+    const int grid = a.s.B * a.s.H * a.ncs;
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((fwd_prep_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
     else

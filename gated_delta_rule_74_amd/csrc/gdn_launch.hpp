@@ -22,6 +22,7 @@ struct PrepArgs {
     void *U, *NK;
     void *Tsave; // may be null
     float *gam;  // chunk-local cumulative log2-decay [B*H][NC][64], may be null
+    int c0, ncs; // chunks c0 .. c0 + ncs - 1 of every (batch, head)
 };
 
 struct FwdChainArgs {
@@ -32,6 +33,11 @@ struct FwdChainArgs {
     float *hT; // may be null
     void *cs;  // chunk-start states, transposed: [B,H,NC,dv,dk] in operand dtype; may be null
     int NVB;   // value-column blocks
+    // chunk range of this launch and the fp32 state at chunk c0 ([B,H,dk,dv],
+    // null: zero); hT receives the state after chunk c1 - 1. The general
+    // chain kernel supports only the whole range with h_in == s.h0.
+    int c0, c1;
+    const float *h_in;
 };
 
 struct BwdChainArgs {
@@ -75,6 +81,7 @@ template <bool BF> inline bool vec_ok(const SeqArgs &s) {
 // Padded head dimension the kernels are instantiated for.
 int pad_dim(int d, bool bf16);
 int fwd_vblock(int D);
+bool fwd_segmentable(bool bf16, int D); // chain launch accepts a chunk range
 int bwd_chain_vblock(bool bf16, int D);
 bool bwd_supported(bool bf16, int D);
 

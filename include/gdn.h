@@ -148,6 +148,14 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
  * of launches bracketed since the previous call. */
 int32_t gdn_time_launches(void *const *events, int32_t n);
 
+/* Which kernel the i-th bracketed launch of the current (or, once switched
+ * off, the last) bracketing period was: 0 forward prep, 1 forward serial
+ * pass, 2 backward serial pass, 3 backward local gradients, 4 dA_log
+ * reduction, 5 decode step; -1 when i is out of range. A forward call may launch its two kernels several times
+ * each, over consecutive chunk ranges (prep of the next range runs on a
+ * second stream while the serial pass works on the current one). */
+int32_t gdn_launch_kind(int32_t i);
+
 const char *gdn_status_string(gdn_status_t st);
 const char *gdn_last_error_detail(void);
 
