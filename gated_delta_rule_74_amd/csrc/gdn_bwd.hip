@@ -201,11 +201,12 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
 // U and Tm come from the forward context, so no triangular solve runs here.
 // Eight LDS regions are reused phase by phase (Pn = phase n):
 //   R0 K                              R4 dh'^T (P4-5) -> -dV't (P6-7)
-//   R1 Q (P1) -> h^T (P3-5) -> V (P6) -> dSt (P7-8) -> dQ (P11)
-//   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7) -> dPGt (P9-10)
-//   R3 U (P3) -> dO (P4-9) -> partial sums (P11)
-//   R5 Wt (P3-9) -> dK (P11)          R6 dWt (P4-6) -> dK't (P6-7)
-//   R7 -Kw (P3) -> dKw (P5-6) -> U (P7) -> Q (P9-10)
+//   R1 h^T (P3-5) -> V (P6) -> dSt (P7-8)
+//   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7)
+//   R3 U (P3) -> dO (P4-5) -> partial sums (P9)
+//   R5 Wt (P3-5) -> dK (P9)           R6 dWt (P4-6) -> dK't (P6-7)
+//   R7 -Kw (P3) -> dKw (P5-6) -> U (P7)
+//   RQ Q (whole chunk)                RP (dP o Gam)^T (P5-6) -> dQ (P9)
 // Inputs needed in two phases stay in registers between their stashes.
 
 template <bool BF, int D> struct LocalSmem {
@@ -226,7 +227,9 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int o5 = o4 + mx(sDD, sDC);
     static constexpr int o6 = o5 + mx(sDC, sCD);
     static constexpr int o7 = o6 + sDC;
-    static constexpr int oGam = o7 + mx(sCD, sCC);
+    static constexpr int oQ = o7 + mx(sCD, sCC);           // RQ: Q (whole chunk)
+    static constexpr int oP = oQ + sCD;                      // RP: dPGt (P5-6) -> dQ
+    static constexpr int oGam = oP + mx(sCC, sCD);
     static constexpr int oEg = oGam + C * 8;
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
@@ -252,6 +255,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     S *R5 = (S *)(smem + L::o5);
     S *R6 = (S *)(smem + L::o6);
     S *R7 = (S *)(smem + L::o7);
+    S *RQ = (S *)(smem + L::oQ);
+    S *RP = (S *)(smem + L::oP);
     S *Ks = R0;
     double *gam = (double *)(smem + L::oGam);
     float *eg = (float *)(smem + L::oEg);
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         if (lane == 0) misc[0] = dc.eglast;
     }
     fk.stash(Ks, LDD, tid);
-    fq.stash(R1, LDD, tid);
+    fq.stash(RQ, LDD, tid);
     __syncthreads();
     // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
     f32x4 gC[PWC], kkg[PWC], pC[PWC];
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
         for (int i = 0; i < PWC; ++i) sk[i] = sq[i] = zero4();
         if (!add) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
-        gemm<BF, 4, 4, D>(R1, LDD, Ks, LDD, sq, wave, lane);
+        gemm<BF, 4, 4, D>(RQ, LDD, Ks, LDD, sq, wave, lane);
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             const float G = gamma_ij(gam, row, col);
             gC[i][e] = G;
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         });
         store_T<BF, 4, 4>(pC, R2, LDC, wave, lane); // Pt
     }
-    __syncthreads(); // Q reads done
+    __syncthreads(); // Pt complete
     // ---- P3: W = U - Kw h
     fh.stash(R1, LDD, tid);
     fu.stash(R3, LDD, tid);
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         store_T<BF, 4, DT>(accdW, R6, LDC, wave, lane); // dWt
     }
     __syncthreads();
-    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>
+    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>, dP
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
@@ -399,6 +404,19 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         }
         hd = wave_sum(hd);
         if (lane == 0) misc[16 + wave] = hd;
+        // dP = dO W^T (lower incl. diagonal), dP o Gam -> RP
+        {
+            f32x4 accP[PWC];
+#pragma unroll
+            for (int i = 0; i < PWC; ++i) accP[i] = zero4();
+            gemm<BF, 4, 4, D, false, true>(R3, LDD, R5, LDC, accP, wave, lane);
+            for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
+                const float dp = row >= col ? accP[i][e] : 0.f;
+                xgC[i][e] += dp * pC[i][e]; // dP o P
+                accP[i][e] = dp * gC[i][e];
+            });
+            store_T<BF, 4, 4>(accP, RP, LDC, wave, lane); // dPGt
+        }
         // R7 (-Kw) and R2 (Pt) are free: dKw (token rows) and Tm go there
         if (!add) {
 #pragma unroll
@@ -408,7 +426,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         ft.stash(R2, LDC, tid);
     }
     __syncthreads(); // h, dh' no longer read
-    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw
+    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw, dQ, dK += (dP o Gam)^T Q
     fv.stash(R1, LDD, tid);
     {
         f32x4 accV[PWD], accKp[PWD];
@@ -416,6 +434,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
         gemm<BF, 4, DT, C, true, false>(R2, LDC, R6, LDC, accV, wave, lane);
         if (!add) gemm<BF, 4, DT, C, true, true>(R2, LDC, R7, LDD, accKp, wave, lane);
+        // dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
+        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
+            accQ[i][e] *= eg[row];
+            rgD[i][e] += accQ[i][e] * to_f(RQ[row * LDD + col]); // e^{gam_i} q_i . dOh_i
+        });
+        gemm<BF, 4, DT, C, true, true>(RP, LDC, Ks, LDD, accQ, wave, lane);
+        gemm<BF, 4, DT, C, false, true>(RP, LDC, RQ, LDD, accKd, wave, lane);
         __syncthreads(); // V visible; Tm, dWt, dKw reads done
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
             const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
@@ -452,36 +477,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, DT, C, true, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
         gemm<BF, 4, DT, C, false, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
     }
-    // ---- P9: dP = dO W^T (lower incl. diagonal), dP o Gam
+    // dQ and dK leave through LDS as 16-byte rows: RP was last read before the
+    // middle barrier of P6, R5 (Wt) in P5
+    store_N<BF, 4, DT>(accQ, RP, LDD, wave, lane);
+    store_N<BF, 4, DT>(accKd, R5, LDD, wave, lane);
+    // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
     {
-        f32x4 accP[PWC];
-#pragma unroll
-        for (int i = 0; i < PWC; ++i) accP[i] = zero4();
-        gemm<BF, 4, 4, D, false, true>(R3, LDD, R5, LDC, accP, wave, lane);
-        for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            const float dp = row >= col ? accP[i][e] : 0.f;
-            xgC[i][e] += dp * pC[i][e]; // dP o P
-            accP[i][e] = dp * gC[i][e];
-        });
-        store_T<BF, 4, 4>(accP, R2, LDC, wave, lane); // dPGt
-        fq.stash(R7, LDD, tid);                     // Q again
-    }
-    __syncthreads();
-    // ---- P10: dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
-    {
-        for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) {
-            accQ[i][e] *= eg[row];
-            rgD[i][e] += accQ[i][e] * to_f(R7[row * LDD + col]); // e^{gam_i} q_i . dOh_i
-        });
-        gemm<BF, 4, DT, C, true, true>(R2, LDC, Ks, LDD, accQ, wave, lane);
-        gemm<BF, 4, DT, C, false, true>(R2, LDC, R7, LDD, accKd, wave, lane);
-        // dQ and dK leave through LDS (R1 and R5 are free) as 16-byte rows
-        store_N<BF, 4, DT>(accQ, R1, LDD, wave, lane);
-        store_N<BF, 4, DT>(accKd, R5, LDD, wave, lane);
-    }
-    // ---- P11: one fixed-order reduction of every dbeta / dgam contribution
-    {
-        // R3 (dO) was last read before the P9 barrier
+        // R3 (dO) was last read in P5
         float *pRbD = (float *)R3, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
         float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
         row_partials<4, DT>(rbD, pRbD, wave, lane);
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
-                            *reinterpret_cast<const uint4 *>(R1 + j * LDD + c0);
+                            *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
                         *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
                             *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
                     }
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                     const int j = it / D, col = it % D;
                     if (j >= n) continue;
                     if (col < dk) {
-                        dq_out[(size_t)j * H * dk + col] = R1[j * LDD + col];
+                        dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
                         dk_out[(size_t)j * H * dk + col] = R5[j * LDD + col];
                     }
                     if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(R4[col * LDC + j]));
