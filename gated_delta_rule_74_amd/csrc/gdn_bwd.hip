@@ -23,6 +23,8 @@
 // chunk's intermediates from the saved chunk-start state h and dh' and forms
 // all local gradients, one workgroup per (batch, head, chunk); dA_reduce sums
 // the per-chunk dA_log parts in a fixed order.
+#include <atomic>
+
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -230,7 +232,7 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int oQ = o7 + mx(sCD, sCC);           // RQ: Q (whole chunk)
     static constexpr int oP = oQ + sCD;                      // RP: dPGt (P5-6) -> dQ
     static constexpr int oGam = oP + mx(sCC, sCD);
-    static constexpr int oEg = oGam + C * 8;
+    static constexpr int oEg = oGam + NWAVE * C * 8; // gam: one copy per wave
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
     static constexpr int oGch = oBet + C * 4;
@@ -266,45 +268,76 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     float *misc = (float *)(smem + L::oMisc);
 
     const SeqArgs &s = a.s;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // heads fastest: the rows of all heads of one token are adjacent in
-    // memory, so workgroups that share cache lines run together on one XCD
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid % s.H, c = (lid / s.H) % s.NC, b = lid / (s.H * s.NC);
-    const int bh = b * s.H + h;
+    const int tid0 = threadIdx.x;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
-    const int t0 = c * C, n = min(C, T - t0);
-    const double A = -exp((double)s.A_log[h]);
-    const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
-    const S *q = (const S *)s.q + (row0 * H + h) * dk;
-    const S *k = (const S *)s.k + (row0 * H + h) * dk;
-    const S *v = (const S *)s.v + (row0 * H + h) * dv;
-    const S *dO = (const S *)a.dout + (row0 * H + h) * dv;
-    const S *hc = (const S *)a.cs + cb * dk * dv;
-    const S *dhc = (const S *)a.dhs + cb * dk * dv;
-    const S *nk = (const S *)a.NK + cb * C * dk;
-    const S *uc = (const S *)a.U + cb * C * dv;
-    const S *tc = (const S *)a.Tm + cb * C * C;
     const bool add = s.additive != 0;
+    // Persistent blocks, each working through a list of chunks. Chunks are
+    // numbered heads fastest (the rows of all heads of one token are adjacent
+    // in memory). Block i runs on XCD i % 8; when the counts allow, each XCD
+    // walks one contiguous eighth of the numbering with its blocks side by
+    // side, so chunks that share cache lines run together on one XCD.
+    const int NCH = s.B * H * s.NC, G = gridDim.x;
+    const bool split = G % 8 == 0 && NCH % 8 == 0;
+    const int per = split ? NCH / 8 : NCH;
+    const int first = split ? ((int)blockIdx.x % 8) * per + (int)blockIdx.x / 8 : (int)blockIdx.x;
+    const int lim = split ? ((int)blockIdx.x % 8 + 1) * per : NCH; // end of this block's range
+    const int step = split ? G / 8 : G;
+    // chunk lid = (b * NC + c) * H + h, advanced by `step` with carries
+    struct Pos {
+        int lid, h, c, b;
+    };
+    const int sh = step % H, sc = (step / H) % s.NC, sb = step / (H * s.NC);
+    auto advance = [&](Pos p) {
+        p.lid += step;
+        p.h += sh;
+        int cy = p.h >= H;
+        p.h -= cy ? H : 0;
+        p.c += sc + cy;
+        cy = p.c >= s.NC;
+        p.c -= cy ? s.NC : 0;
+        p.b += sb + cy;
+        return p;
+    };
 
-    // all global inputs of the chunk are requested up front
+    // Global inputs are requested into registers well before their use: the
+    // ones the first phases need (K, Q, h, U, -Kw, gates) while the previous
+    // chunk finishes, the others at the top of the chunk itself.
     ChunkFrag<BF, D> fk, fq, fv, fo, fn, fu;
     ChunkFrag<BF, D, D> fh, fd;
     ChunkFrag<BF, C> ft;
-    fk.template fetch<VEC>(k, (size_t)H * dk, n, dk, tid);
-    fq.template fetch<VEC>(q, (size_t)H * dk, n, dk, tid);
-    fu.template fetch<VEC>(uc, (size_t)dv, n, dv, tid);
-    if (!add) fn.template fetch<VEC>(nk, (size_t)dk, n, dk, tid);
-    fh.template fetch<VEC>(hc, (size_t)dk, dv, dk, tid);
-    fo.template fetch<VEC>(dO, (size_t)H * dv, n, dv, tid);
-    fd.template fetch<VEC>(dhc, (size_t)dk, dv, dk, tid);
-    ft.template fetch<VEC>(tc, (size_t)C, C, C, tid);
-    fv.template fetch<VEC>(v, (size_t)H * dv, n, dv, tid);
-    float gr = 0.f, br = 0.f;
-    if (wave == 0) {
+    float gr = 0.f, br = 0.f, alr = 0.f;
+    auto fetch_early = [&](const Pos &p, int tid, int lane) {
+        const int h = p.h, c = p.c, b = p.b;
+        const int n = min(C, T - c * C);
+        const size_t row0 = (size_t)b * T + c * C, cb = ((size_t)b * H + h) * s.NC + c;
+        fk.template fetch<VEC>((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fq.template fetch<VEC>((const S *)s.q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fh.template fetch<VEC>((const S *)a.cs + cb * dk * dv, (size_t)dk, dv, dk, tid);
+        fu.template fetch<VEC>((const S *)a.U + cb * C * dv, (size_t)dv, n, dv, tid);
+        if (!add) fn.template fetch<VEC>((const S *)a.NK + cb * C * dk, (size_t)dk, n, dk, tid);
+        alr = s.A_log[h];
         gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
         br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
-    }
+    };
+    if (first >= lim) return;
+    Pos cur{first, first % H, (first / H) % s.NC, first / (H * s.NC)};
+    fetch_early(cur, tid0, tid0 & 63);
+    for (;;) {
+    // the thread index is hidden from the optimiser at the top of every
+    // chunk, so per-lane addresses are formed where they are used instead of
+    // being hoisted out of the loop and held in registers throughout
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int h = cur.h, c = cur.c, b = cur.b;
+    const int bh = b * H + h;
+    const int t0 = c * C, n = min(C, T - t0);
+    const double A = -exp((double)alr);
+    const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
+    fo.template fetch<VEC>((const S *)a.dout + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
+    fd.template fetch<VEC>((const S *)a.dhs + cb * dk * dv, (size_t)dk, dv, dk, tid);
+    ft.template fetch<VEC>((const S *)a.Tm + cb * C * C, (size_t)C, C, C, tid);
+    fv.template fetch<VEC>((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
 
     // Contributions to dbeta and dgam, accumulated per lane at the (row, col)
     // positions this lane owns and reduced once at the end:
@@ -317,15 +350,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
 
     // ---- P1: gates, decay, K K^T and Q K^T
-    if (wave == 0) {
-        gch[lane] = lane < n ? gr : 0.f;
-        bet[lane] = lane < n ? br : 0.f;
-        const Decay dc = decay_lane(gch[lane], A * LOG2E, lane);
-        gam[lane] = dc.gam2;
-        eg[lane] = dc.eg;
-        egn[lane] = dc.egn;
-        if (lane == 0) misc[0] = dc.eglast;
-    }
     fk.stash(Ks, LDD, tid);
     fq.stash(RQ, LDD, tid);
     __syncthreads();
@@ -337,8 +361,21 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWC; ++i) sk[i] = sq[i] = zero4();
         if (!add) gemm<BF, 4, 4, D>(Ks, LDD, Ks, LDD, sk, wave, lane);
         gemm<BF, 4, 4, D>(RQ, LDD, Ks, LDD, sq, wave, lane);
+        // while the products run, every wave forms the chunk's decay (lane =
+        // row) and keeps a copy of gam of its own; wave 0 publishes the rest
+        const float gl = lane < n ? gr : 0.f;
+        const Decay dc = decay_lane(gl, A * LOG2E, lane);
+        double *gw = gam + wave * C;
+        gw[lane] = dc.gam2;
+        if (wave == 0) {
+            gch[lane] = gl;
+            bet[lane] = lane < n ? br : 0.f;
+            eg[lane] = dc.eg;
+            egn[lane] = dc.egn;
+            if (lane == 0) misc[0] = dc.eglast;
+        }
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
-            const float G = gamma_ij(gam, row, col);
+            const float G = gamma_ij(gw, row, col);
             gC[i][e] = G;
             kkg[i][e] = (row > col) ? sk[i][e] * G : 0.f;
             pC[i][e] = sq[i][e] * G;
@@ -477,6 +514,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, DT, C, true, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
         gemm<BF, 4, DT, C, false, true>(R1, LDC, Ks, LDD, accKd, wave, lane);
     }
+    // every fragment is stashed and the products are done: request the first
+    // inputs of the next chunk (the current one again after the last, so the
+    // loads never depend on a branch)
+    const Pos nxt = advance(cur);
+    const bool more = nxt.lid < lim;
+    fetch_early(more ? nxt : cur, tid, lane);
     // dQ and dK leave through LDS as 16-byte rows: RP was last read before the
     // middle barrier of P6, R5 (Wt) in P5
     store_N<BF, 4, DT>(accQ, RP, LDD, wave, lane);
@@ -486,11 +529,21 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         // R3 (dO) was last read in P5
         float *pRbD = (float *)R3, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
         float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
+        if constexpr (DT == 4) {
+            // [C][D] and [C][C] tiles sit at the same places: add the row
+            // contributions before the cross-lane sums
+#pragma unroll
+            for (int i = 0; i < PWD; ++i) {
+                rbD[i] += rbC[i];
+                rgD[i] += xgC[i];
+            }
+        } else {
+            row_partials<4, 4>(rbC, pRbC, wave, lane);
+            row_partials<4, 4>(xgC, pRgC, wave, lane);
+        }
         row_partials<4, DT>(rbD, pRbD, wave, lane);
         row_partials<4, DT>(rgD, pRgD, wave, lane);
         row_partials<4, DT>(rsD, pRsD, wave, lane);
-        row_partials<4, 4>(rbC, pRbC, wave, lane);
-        row_partials<4, 4>(xgC, pRgC, wave, lane);
         col_partials<4, 4>(xgC, pCgC, wave, lane);
         __syncthreads();
         // dq, dk, dv rows of the chunk: 16-byte stores (dv = -beta * (-dV'), from
@@ -544,8 +597,11 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                db += pRbC[i * 4 + t];
-                dgm += pRgC[i * 4 + t] - pCgC[i * 4 + t];
+                if constexpr (DT != 4) {
+                    db += pRbC[i * 4 + t];
+                    dgm += pRgC[i * 4 + t];
+                }
+                dgm -= pCgC[i * 4 + t];
             }
             // gam_n enters through e^{gam_n} h and e^{gam_n - gam_j}: its gradient
             // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row; -s_j to row j
@@ -568,6 +624,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
         }
     }
+    if (!more) break;
+    cur = nxt;
+    __syncthreads(); // outputs read from LDS before the next chunk's stashes
+    } // chunk loop
 }
 
 // dA_log[h] = sum over (b, c) of part[b, h, c]: one workgroup per head,
@@ -620,13 +680,38 @@ hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t
     return hipErrorInvalidValue;
 }
 
-template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hipStream_t st) {
-    const int grid = a.s.B * a.s.H * a.s.NC;
-    if (vec_ok<BF>(a.s))
-        hipLaunchKernelGGL((bwd_local_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_local_kernel<BF, D, false>), dim3(grid), dim3(NTHR), 0, st, a);
+// Blocks of a persistent kernel that are resident at once on the current
+// device (compute units x blocks per unit), looked up once per device.
+template <typename K> static hipError_t resident_blocks(K kernel, int &out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int slot = dev & 63;
+    int v = cache[slot].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        int cus = 0, per = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, NTHR, 0)) != hipSuccess) return e;
+        v = cus * (per > 0 ? per : 1);
+        cache[slot].store(v, std::memory_order_relaxed);
+    }
+    out = v;
+    return hipSuccess;
+}
+
+template <bool BF, int D, bool VEC> static hipError_t local_launch(const BwdLocalArgs &a, hipStream_t st) {
+    const int nch = a.s.B * a.s.H * a.s.NC;
+    int grid = 0;
+    const hipError_t e = resident_blocks(bwd_local_kernel<BF, D, VEC>, grid);
+    if (e != hipSuccess) return e;
+    grid = grid < nch ? grid : nch;
+    hipLaunchKernelGGL((bwd_local_kernel<BF, D, VEC>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
+}
+
+template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hipStream_t st) {
+    return vec_ok<BF>(a.s) ? local_launch<BF, D, true>(a, st) : local_launch<BF, D, false>(a, st);
 }
 
 hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st) {

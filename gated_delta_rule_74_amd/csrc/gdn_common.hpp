@@ -338,24 +338,6 @@ __device__ __forceinline__ void zero_pad(typename Op<BF>::S *m, int ld, int d0, 
 // difference of two prefix sums keeps its precision. Rows past the end of
 // the sequence pass g = 0, so gam2 stays at its last valid value there.
 // Every wave can run this on its own copy of the gates.
-struct Decay {
-    double gam2;  // log2 of the cumulative decay up to this row
-    float eg;     // exp(gam_i)
-    float egn;    // exp(gam_last - gam_i)
-    float eglast; // exp(gam_last)
-};
-
-__device__ __forceinline__ Decay decay_lane(float g, double A2, int lane) {
-    double s = (double)g * A2;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(s, off, 64);
-        if (lane >= off) s += o;
-    }
-    const double last = __shfl(s, 63, 64);
-    return Decay{s, exp2_fast((float)s), exp2_fast((float)(last - s)), exp2_fast((float)last)};
-}
-
 // Gam_ij = exp(gam_i - gam_j) for i >= j, else 0 (gam2 in LDS, log2 domain).
 __device__ __forceinline__ float gamma_ij(const double *gam2, int i, int j) {
     return (i >= j) ? exp2_fast((float)(gam2[i] - gam2[j])) : 0.f;
@@ -515,6 +497,40 @@ __device__ __forceinline__ float wave_prefix(float x) {
     x += dpp_rows<0x142, 0xA>(x); // row_bcast:15 into rows 1 and 3
     x += dpp_rows<0x143, 0xC>(x); // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+struct Decay {
+    double gam2;  // log2 of the cumulative decay up to this row
+    float eg;     // exp(gam_i)
+    float egn;    // exp(gam_last - gam_i)
+    float eglast; // exp(gam_last)
+};
+
+// fp64 value moved like dpp_f / dpp_rows (both 32-bit halves with the same
+// control; lanes that read nothing get +0.0).
+template <int CTRL, int ROWMASK, bool BC> __device__ __forceinline__ double dpp_d(double x) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROWMASK, 0xF, BC);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROWMASK, 0xF, BC);
+    return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Chunk decay for lane = row: gam2 = A2 * (g_0 + ... + g_lane) (log2 domain,
+// fp64 inclusive scan with the same data-parallel moves as wave_prefix).
+__device__ __forceinline__ Decay decay_lane(float g, double A2, int lane) {
+    double s = (double)g * A2;
+    s += dpp_d<0x111, 0xF, true>(s); // row_shr:1
+    s += dpp_d<0x112, 0xF, true>(s); // row_shr:2
+    s += dpp_d<0x114, 0xF, true>(s); // row_shr:4
+    s += dpp_d<0x118, 0xF, true>(s); // row_shr:8
+    s += dpp_d<0x142, 0xA, false>(s); // row_bcast:15 into rows 1 and 3
+    s += dpp_d<0x143, 0xC, false>(s); // row_bcast:31 into rows 2 and 3
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, s);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
+    const double last = __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+    (void)lane;
+    return Decay{s, exp2_fast((float)s), exp2_fast((float)(last - s)), exp2_fast((float)last)};
 }
 
 // Per-tile row sums of x (x[i][e] is this lane's value at (row, col) of tile
