@@ -24,6 +24,7 @@
 // all local gradients, one workgroup per (batch, head, chunk); dA_reduce sums
 // the per-chunk dA_log parts in a fixed order.
 #include <atomic>
+#include <type_traits>
 
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
@@ -190,6 +191,319 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc) a.dh0[((size_t)bh * dk + row) * dv + v0 + col] = accDH[i][e];
         });
+    }
+}
+
+// ------------------------------------------------- wave-specialised chain
+//
+// bf16 path for head dims up to 64. One workgroup per (batch, head, block of
+// BV value columns). Waves 0..VT-1 ("chain waves", VT = BV/16) each carry 16
+// value columns of dh [D][16] in MFMA accumulators and run only
+//   dW = diag(e^{gam_n - gam}) K dh' + X,   dh = e^{gam_n} dh' + Y + (-Kw)^T dW
+// with X = P^T dO and Y = Q^T diag(e^gam) dO. With 16x16x16 products an
+// accumulator tile is already the B operand of the next product over the
+// same rows, so dW and dh never leave the wave's registers on the serial
+// path. The eight helper waves that follow work ahead of the chain in two
+// groups of four that swap roles every chunk: while the chain handles chunk
+// c, the group that owns chunks of c's parity stages chunk c-2 into LDS and
+// requests chunk c-4 (so its loads have two chunks' time to land), and the
+// other group forms X and Y of chunk c-1.
+// K, -Kw and the decay live three chunks in LDS, Q and dO two, X and Y two;
+// one barrier per chunk hands them over. The chain waves store dh' of every
+// chunk (bf16, transposed [dv][dk]) and the final dh themselves.
+
+constexpr int BWS_HELPERS = 8;
+
+template <int D, int BV> struct BwsSmem {
+    static constexpr int LDD = D + 8;  // token rows [C][LDD]
+    static constexpr int LDV = BV + 8; // dO rows [C][LDV]
+    static constexpr int LDX = C + 4;  // X^T, Y^T [BV][LDX] fp32
+    static constexpr int szCD = C * LDD * 2;
+    static constexpr int szCV = C * LDV * 2;
+    static constexpr int szX = BV * LDX * 4;
+    static constexpr int szDec = C * 4 + C * 4 + 16; // gam (log2), e^{gam_n - gam}, e^{gam_n}
+    static constexpr int oK = 0;                  // 3 x K
+    static constexpr int oN = oK + 3 * szCD;      // 3 x -Kw
+    static constexpr int oQ = oN + 3 * szCD;      // 2 x Q
+    static constexpr int oO = oQ + 2 * szCD;      // 2 x dO
+    static constexpr int oOe = oO + 2 * szCV;     // 2 x diag(e^gam) dO
+    static constexpr int oX = oOe + 2 * szCV;     // 2 x X^T
+    static constexpr int oY = oX + 2 * szX;       // 2 x Y^T
+    static constexpr int oDec = oY + 2 * szX;     // 3 x decay
+    static constexpr int SIZE = oDec + 3 * szDec;
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int BV, bool VEC>
+__global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_kernel(BwdChainArgs a) {
+    constexpr int DT = D / 16, VT = BV / 16, KS = D / 32;
+    constexpr int NHT = 64 * BWS_HELPERS; // helper threads
+    using L = BwsSmem<D, BV>;
+    constexpr int LDD = L::LDD, LDV = L::LDV, LDX = L::LDX;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    auto kbuf = [&](int i) { return (u16 *)(smem + L::oK + i * L::szCD); };
+    auto nbuf = [&](int i) { return (u16 *)(smem + L::oN + i * L::szCD); };
+    auto qbuf = [&](int i) { return (u16 *)(smem + L::oQ + i * L::szCD); };
+    auto obuf = [&](int i) { return (u16 *)(smem + L::oO + i * L::szCV); };
+    auto oebuf = [&](int i) { return (u16 *)(smem + L::oOe + i * L::szCV); };
+    auto xbuf = [&](int i) { return (float *)(smem + L::oX + i * L::szX); };
+    auto ybuf = [&](int i) { return (float *)(smem + L::oY + i * L::szX); };
+    auto gam_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec); };
+    auto egn_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 4); };
+    auto el_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 8); };
+
+    const SeqArgs &s = a.s;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    // per-lane indices are re-derived from an opaque copy of the thread index
+    // at every chunk, so addresses built from them are formed where they are
+    // used rather than hoisted out of the loop and held in registers
+    int lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int vb = lid % a.NVB, bh = lid / a.NVB;
+    const int b = bh / s.H, h = bh % s.H;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC, CN = NC - 1;
+    const int V0 = vb * BV, nvc = min(BV, dv - V0);
+    const bool chain = wave < VT;
+    const bool add = s.additive != 0;
+    const double A2 = -exp((double)s.A_log[h]) * LOG2E;
+
+    // ---- chain-wave state: value columns V0 + v0 + (0..15)
+    const int v0 = 16 * wave;
+    f32x4 hacc[DT];
+    u16 *dhs = (u16 *)a.dhs;
+
+    // ---- helper-wave state; group gp (helpers 4gp..4gp+3) stages the chunks
+    // of parity gp
+    constexpr int NGT = NHT / 2; // threads of a group
+    const int hw = wave - VT, gp = hw >> 2;
+    int gtid = (tid - 64 * VT) & (NGT - 1);
+    ChunkFrag<true, D, C, NGT> fk, fq, fn;
+    ChunkFrag<true, BV, C, NGT> fo;
+    float pg = 0.f;
+    const u16 *q = (const u16 *)s.q, *k = (const u16 *)s.k, *dO = (const u16 *)a.dout;
+    // additive: -Kw is never read; its loads repeat K so that every step
+    // issues the same loads
+    const u16 *NK = add ? nullptr : (const u16 *)a.NK;
+    auto fetch = [&](int c) {
+        c = max(c, 0); // past the first chunk: a harmless repeat of chunk 0
+        const int n = min(C, T - c * C);
+        const size_t row0 = (size_t)b * T + c * C, cb = (size_t)bh * NC + c;
+        fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, gtid);
+        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, gtid);
+        const bool kw = NK != nullptr;
+        fn.template fetch<VEC>(kw ? NK + cb * C * dk : k + (row0 * H + h) * dk, kw ? (size_t)dk : (size_t)H * dk, n,
+                               dk, gtid);
+        fo.template fetch<VEC>(dO + (row0 * H + h) * dv + V0, (size_t)H * dv, n, nvc, gtid);
+        pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+    };
+    auto stash = [&](int c) {
+        const int n = min(C, T - c * C), i3 = c % 3, i2 = c & 1;
+        wait_vmem();
+        const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
+        if ((hw & 3) == 0) {
+            gam_of(i3)[lane] = (float)dc.gam2;
+            egn_of(i3)[lane] = dc.egn;
+            if (lane == 0) el_of(i3)[0] = dc.eglast;
+        }
+        fk.stash(kbuf(i3), LDD, gtid);
+        if (!add) fn.stash(nbuf(i3), LDD, gtid);
+        fq.stash(qbuf(i2), LDD, gtid);
+        fo.stash(obuf(i2), LDV, gtid);
+        fo.stash_scaled(oebuf(i2), LDV, gtid, dc.eg);
+    };
+    // X^T = dO^T P and Y^T = (diag(e^gam) dO)^T Q of chunk c, by the four
+    // helpers of group hg: helpers 0 and 1 form P's column blocks {0, 3} and
+    // {1, 2} (lower-triangular, so five 16 x 16 blocks each) and the X tiles
+    // that need them, helpers 2 and 3 split the Y tiles
+    auto xy = [&](int c, int hl) {
+        const int i3 = c % 3, i2 = c & 1;
+        const u16 *Ks = kbuf(i3), *Qs = qbuf(i2), *dOs = obuf(i2), *dOe = oebuf(i2);
+        if (hl < 2) {
+            if (add) return;
+            const float *gm = gam_of(i3);
+            float *XT = xbuf(i2);
+            auto pcol = [&](auto JB) {
+                constexpr int jb = decltype(JB)::value;
+                const float gj = gm[16 * jb + r];
+                f32x4 p[4];
+#pragma unroll
+                for (int ib = jb; ib < 4; ++ib) {
+                    p[ib] = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 aq = *(const bf16x8 *)(Qs + (16 * ib + r) * LDD + 32 * ks + 8 * g);
+                        const bf16x8 bk = *(const bf16x8 *)(Ks + (16 * jb + r) * LDD + 32 * ks + 8 * g);
+                        p[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, p[ib], 0, 0, 0);
+                    }
+                }
+                short4_t pb[4];
+#pragma unroll
+                for (int ib = jb; ib < 4; ++ib) {
+                    // p[ib][e] = P[i = 16 ib + 4g + e][j = 16 jb + r]: decay and
+                    // mask without branches
+                    const float4 gv = *(const float4 *)(gm + 16 * ib + 4 * g);
+                    const float gi[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = exp2_fast(gi[e] - gj);
+                        p[ib][e] = (ib > jb || 4 * g + e >= r) ? p[ib][e] * f : 0.f;
+                    }
+                    pb[ib] = pack4(p[ib]);
+                }
+#pragma unroll
+                for (int vx = 0; vx < VT; ++vx) {
+                    f32x4 ax = zero4();
+#pragma unroll
+                    for (int ib = jb; ib < 4; ++ib) {
+                        const short4_t ad = operand_tr4(dOs, LDV, 16 * ib, 16 * vx, lane);
+                        ax = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ad, pb[ib], ax, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) XT[(16 * vx + 4 * g + e) * LDX + 16 * jb + r] = ax[e];
+                }
+            };
+            if (hl == 0) {
+                pcol(std::integral_constant<int, 0>{});
+                pcol(std::integral_constant<int, 3>{});
+            } else {
+                pcol(std::integral_constant<int, 1>{});
+                pcol(std::integral_constant<int, 2>{});
+            }
+        } else {
+            float *YT = ybuf(i2);
+            constexpr int NY = DT * VT, HY = (NY + 1) / 2;
+#pragma unroll
+            for (int t0 = 0; t0 < HY; ++t0) {
+                const int t = (hl - 2) * HY + t0;
+                if (NY % 2 != 0 && t >= NY) break;
+                const int vy = t / DT, db = t % DT;
+                f32x4 ay = zero4();
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    const short4_t ad = operand_tr4(dOe, LDV, 16 * ib, 16 * vy, lane);
+                    const short4_t bq = operand_tr4(Qs, LDD, 16 * ib, 16 * db, lane);
+                    ay = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ad, bq, ay, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) YT[(16 * vy + 4 * g + e) * LDX + 16 * db + r] = ay[e];
+            }
+        }
+    };
+    // one step of the chain on chunk c; dh' of chunk c goes out first
+    auto chain_step = [&](int c) {
+        const int i3 = c % 3, i2 = c & 1;
+        const u16 *Ks = kbuf(i3), *NKs = nbuf(i3);
+        const float *egn = egn_of(i3), *XT = xbuf(i2), *YT = ybuf(i2);
+        const float el = el_of(i3)[0];
+        short4_t hb[DT];
+        const int v = v0 + r;
+        u16 *dst = dhs + (((size_t)bh * NC + c) * dv + V0 + v) * dk;
+#pragma unroll
+        for (int kb = 0; kb < DT; ++kb) {
+            hb[kb] = pack4(hacc[kb]);
+            const int d0 = 16 * kb + 4 * g;
+            if (v < nvc) {
+                if (dk % 4 == 0) {
+                    if (d0 < dk) *(short4_t *)(dst + d0) = hb[kb];
+                } else {
+                    const uint2 u = __builtin_bit_cast(uint2, hb[kb]);
+                    const u16 x4[4] = {(u16)(u.x & 0xFFFF), (u16)(u.x >> 16), (u16)(u.y & 0xFFFF), (u16)(u.y >> 16)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < dk) dst[d0 + e] = x4[e];
+                }
+            }
+        }
+        if (!add) {
+            // dW = diag(e^{gam_n - gam}) K dh' + X
+            f32x4 w[4];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) w[tm] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) {
+                    const short4_t ak = *(const short4_t *)(Ks + (16 * tm + r) * LDD + 16 * kb + 4 * g);
+                    w[tm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, hb[kb], w[tm], 0, 0, 0);
+                }
+            }
+            short4_t wb[4];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const float4 sc = *(const float4 *)(egn + 16 * tm + 4 * g);
+                const float4 x = *(const float4 *)(XT + v * LDX + 16 * tm + 4 * g);
+                wb[tm] = pack4(f32x4{w[tm][0] * sc.x + x.x, w[tm][1] * sc.y + x.y, w[tm][2] * sc.z + x.z,
+                                     w[tm][3] * sc.w + x.w});
+            }
+            // dh = e^{gam_n} dh' + Y + (-Kw)^T dW
+#pragma unroll
+            for (int kb = 0; kb < DT; ++kb) {
+                const float4 y = *(const float4 *)(YT + v * LDX + 16 * kb + 4 * g);
+                hacc[kb] = f32x4{hacc[kb][0] * el + y.x, hacc[kb][1] * el + y.y, hacc[kb][2] * el + y.z,
+                                 hacc[kb][3] * el + y.w};
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) {
+                    const short4_t an = operand_tr4(NKs, LDD, 16 * tm, 16 * kb, lane);
+                    hacc[kb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(an, wb[tm], hacc[kb], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < DT; ++kb) {
+                const float4 y = *(const float4 *)(YT + v * LDX + 16 * kb + 4 * g);
+                hacc[kb] = f32x4{hacc[kb][0] * el + y.x, hacc[kb][1] * el + y.y, hacc[kb][2] * el + y.z,
+                                 hacc[kb][3] * el + y.w};
+            }
+        }
+    };
+
+    // ---- prologue: dh at the end of the sequence (chain), first two chunks
+    // requested (helpers)
+    if (chain) {
+#pragma unroll
+        for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = 16 * kb + 4 * g + e, vv = v0 + r;
+                hacc[kb][e] = (a.dhT && d < dk && vv < nvc) ? a.dhT[((size_t)bh * dk + d) * dv + V0 + vv] : 0.f;
+            }
+        }
+    } else {
+        fetch(((CN & 1) == gp) ? CN : CN - 1);
+    }
+
+    // step c: chain on chunk c; helpers form X, Y of chunk c-1; the group of
+    // c's parity stages chunk c-2 and requests chunk c-4
+    for (int c = CN + 2; c >= 0; --c) {
+        {
+            int t = tid;
+            asm volatile("" : "+v"(t));
+            lane = t & 63;
+            g = lane >> 4;
+            r = lane & 15;
+            gtid = (t - 64 * VT) & (NGT - 1);
+        }
+        if (chain) {
+            if (c <= CN) chain_step(c);
+        } else {
+            if ((c & 1) == gp) {
+                if (c - 2 >= 0 && c - 2 <= CN) stash(c - 2);
+                fetch(c - 4);
+            } else if (c - 1 >= 0 && c - 1 <= CN) {
+                xy(c - 1, hw & 3);
+            }
+        }
+        __syncthreads();
+    }
+    if (chain && a.dh0) {
+#pragma unroll
+        for (int kb = 0; kb < DT; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = 16 * kb + 4 * g + e, vv = v0 + r;
+                if (d < dk && vv < nvc) a.dh0[((size_t)bh * dk + d) * dv + V0 + vv] = hacc[kb][e];
+            }
+        }
     }
 }
 
@@ -658,6 +972,14 @@ static int chain_vblock(bool, int D) { return D >= 64 ? 32 : 16; }
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
     constexpr int BV = D >= 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
+    if constexpr (BF) {
+        const dim3 block(64 * (BV / 16 + BWS_HELPERS));
+        if (vec_ok<BF>(a.s))
+            hipLaunchKernelGGL((bwd_chain_ws_kernel<D, BV, true>), dim3(grid), block, 0, st, a);
+        else
+            hipLaunchKernelGGL((bwd_chain_ws_kernel<D, BV, false>), dim3(grid), block, 0, st, a);
+        return hipGetLastError();
+    }
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
     else

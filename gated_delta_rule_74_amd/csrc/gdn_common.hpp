@@ -106,6 +106,21 @@ __device__ __forceinline__ bf16x8 operand_tr(const u16 *X, int ld, int k0, int m
     return __builtin_bit_cast(bf16x8, u);
 }
 
+__device__ __forceinline__ short4_t pack4(f32x4 x) {
+    uint2 u;
+    u.x = f2bf2(x[0], x[1]);
+    u.y = f2bf2(x[2], x[3]);
+    return __builtin_bit_cast(short4_t, u);
+}
+
+// One 16x16x16 operand from an LDS matrix stored with K as its row index,
+// X[k][m]: lane 16g + j receives X[k0 + 4g + e][m0 + j], e = 0..3.
+__device__ __forceinline__ short4_t operand_tr4(const u16 *X, int ld, int k0, int m0, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4 *)(X + (k0 + 4 * g + (sl >> 2)) * ld + m0 + 4 * (sl & 3)));
+}
+
 // acc[i] += A * B over K = KD for the tiles of this wave.
 // A is stored [M][K] (ATR = false) or [K][M] (ATR = true); B is stored [N][K]
 // (BTR = false, i.e. B transposed) or [K][N] (BTR = true). Row strides lda, ldb.
@@ -339,8 +354,11 @@ __device__ __forceinline__ void zero_pad(typename Op<BF>::S *m, int ld, int d0, 
 // the sequence pass g = 0, so gam2 stays at its last valid value there.
 // Every wave can run this on its own copy of the gates.
 // Gam_ij = exp(gam_i - gam_j) for i >= j, else 0 (gam2 in LDS, log2 domain).
+// Both reads and the exponential happen on every lane and the mask is a
+// select, so no lane branches around LDS reads.
 __device__ __forceinline__ float gamma_ij(const double *gam2, int i, int j) {
-    return (i >= j) ? exp2_fast((float)(gam2[i] - gam2[j])) : 0.f;
+    const float f = exp2_fast((float)(gam2[i] - gam2[j]));
+    return (i >= j) ? f : 0.f;
 }
 
 constexpr int LDF = C + 4; // row stride of fp32 C x C matrices

@@ -382,21 +382,6 @@ template <int D> struct WsSmem {
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ short4_t pack4(f32x4 x) {
-    uint2 u;
-    u.x = f2bf2(x[0], x[1]);
-    u.y = f2bf2(x[2], x[3]);
-    return __builtin_bit_cast(short4_t, u);
-}
-
-// One 16x16x16 operand from an LDS matrix stored with K as its row index,
-// X[k][m]: lane 16g + j receives X[k0 + 4g + e][m0 + j], e = 0..3.
-__device__ __forceinline__ short4_t operand_tr4(const u16 *X, int ld, int k0, int m0, int lane) {
-    const int g = lane >> 4, sl = lane & 15;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_short4 *)(X + (k0 + 4 * g + (sl >> 2)) * ld + m0 + 4 * (sl & 3)));
-}
-
 template <int D, bool VEC>
 __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
     constexpr int DT = D / 16, KS = D / 32;
