@@ -472,6 +472,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
         fetch(((CN & 1) == gp) ? CN : CN - 1);
     }
 
+    // the serial path issues first wherever it shares a SIMD with helpers
+    if (chain) __builtin_amdgcn_s_setprio(3);
     // step c: chain on chunk c; helpers form X, Y of chunk c-1; the group of
     // c's parity stages chunk c-2 and requests chunk c-4
     for (int c = CN + 2; c >= 0; --c) {
