@@ -205,8 +205,11 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s) {
 size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
     const size_t part = align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float));
+    const int nch = s->B * s->H * nchunks(s);
+    const size_t wide = align_up(gdn::bwd_wide_scratch_bytes(s->dtype == GDN_BF16, pad_of(s), nch));
     return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part +
-           align_up(gam_bytes(s)) /* forward decay */ + align_up(state32_bytes(s)) /* forward hand-off */;
+           align_up(gam_bytes(s)) /* forward decay */ + align_up(state32_bytes(s)) /* forward hand-off */ +
+           wide /* local-gradient scratch for wide heads */;
 }
 
 namespace {
@@ -407,6 +410,8 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     float *part = (float *)(dhs + align_up(states_bytes(s)));
     float *gam = (float *)((char *)part + align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float)));
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
+    float *wide = (float *)((char *)hs + align_up(state32_bytes(s)));
+    const bool has_wide = gdn::bwd_wide_scratch_bytes(bf, D, s->B * s->H * nchunks(s)) > 0;
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     const CtxLayout cl = ctx_layout(s);
     hipError_t he;
@@ -442,6 +447,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     la.dg = dg;
     la.dbeta = dbeta;
     la.dA_part = part;
+    la.wide = has_wide ? wide : nullptr;
     he = timed(K_BWD_LOCAL, [&] { return gdn::launch_bwd_local(la, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd local launch");
     he = timed(K_DA_REDUCE, [&] { return gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm); }, strm);

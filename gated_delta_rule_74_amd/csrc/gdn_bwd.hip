@@ -946,6 +946,251 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     } // chunk loop
 }
 
+// --------------------------------------------------------------- wide local
+//
+// Local gradients of one chunk for head dims the LDS-resident kernel above
+// does not hold (bf16 d > 64, fp32 d > 16): the same quantities and the same
+// formulas, formed product by product. Every 64 x d and 64 x 64 intermediate
+// goes to fp32 scratch of the workgroup's own (it stays in L2 between the
+// phases); each product runs on the vector units through LDS tiles, one 4 x 4
+// block of the result per thread. Persistent workgroups over a fixed grid, so
+// the scratch does not grow with the sequence.
+
+constexpr int WIDE_GRID = 1024;
+constexpr int WIDE_LD = 128;                                 // row stride of 64 x d scratch
+constexpr int WIDE_SCRATCH = 5 * C * C + 7 * C * WIDE_LD;    // floats per workgroup
+
+// out = A (M x K) * B (K x N) for M, N <= 128 and M * N <= 8192; fa(m, k) and
+// fb(k, n) fetch operands (only in range). Thread tid owns rows m0..m0+3 and
+// columns n0..n0+3 of the result when `on`. Ends with a barrier.
+template <class FA, class FB>
+__device__ __forceinline__ void wide_mm(int M, int N, int K, FA fa, FB fb, float *As, float *Bs, int tid,
+                                        float (&acc)[4][4], int &m0, int &n0, bool &on) {
+    const int Mp = (M + 3) & ~3, Np = (N + 3) & ~3, tpr = Np / 4;
+    on = tid < (Mp / 4) * tpr;
+    m0 = (tid / tpr) * 4;
+    n0 = (tid % tpr) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        for (int e = tid; e < Mp * 16; e += NTHR) {
+            const int m = e >> 4, kk = e & 15;
+            As[m * 17 + kk] = (m < M && k0 + kk < K) ? fa(m, k0 + kk) : 0.f;
+        }
+        for (int e = tid; e < 16 * Np; e += NTHR) {
+            const int kk = e / Np, n = e % Np;
+            Bs[kk * (WIDE_LD + 4) + n] = (n < N && k0 + kk < K) ? fb(k0 + kk, n) : 0.f;
+        }
+        __syncthreads();
+        if (on) {
+#pragma unroll 4
+            for (int kk = 0; kk < 16; ++kk) {
+                float av[4], bv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) av[i] = As[(m0 + i) * 17 + kk];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = Bs[kk * (WIDE_LD + 4) + n0 + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel(BwdLocalArgs a) {
+    using S = typename Op<BF>::S;
+    __shared__ float As[128 * 17];
+    __shared__ float Bs[16 * (WIDE_LD + 4)];
+    __shared__ double gam[C];
+    __shared__ float eg[C], egn[C], bet[C], gch[C], red[NTHR];
+    const SeqArgs &s = a.s;
+    const int tid0 = threadIdx.x;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
+    const bool add = s.additive != 0;
+    float *sc = a.wide + (size_t)blockIdx.x * WIDE_SCRATCH;
+    float *sP = sc, *sKG = sP + C * C, *sdP = sKG + C * C, *sdL = sdP + C * C, *sT = sdL + C * C;
+    float *sW = sT + C * C, *sdW = sW + C * WIDE_LD, *sdOh = sdW + C * WIDE_LD, *sdKw = sdOh + C * WIDE_LD;
+    float *sdKt = sdKw + C * WIDE_LD, *sdVp = sdKt + C * WIDE_LD, *sdKp = sdVp + C * WIDE_LD;
+    const int NCH = s.B * H * NC;
+    for (int lid = blockIdx.x; lid < NCH; lid += gridDim.x) {
+        // the thread index is hidden from the optimiser per chunk, so per-lane
+        // addresses are formed where they are used, not held across the loop
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid >> 6, lane = tid & 63;
+        // chunks numbered heads fastest (rows of all heads of a token are adjacent)
+        const int h = lid % H, c = (lid / H) % NC, b = lid / (H * NC);
+        const int bh = b * H + h, t0 = c * C, n = min(C, T - t0);
+        const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * NC + c;
+        const S *qb = (const S *)s.q + (row0 * H + h) * dk;
+        const S *kb = (const S *)s.k + (row0 * H + h) * dk;
+        const S *vb = (const S *)s.v + (row0 * H + h) * dv;
+        const S *ob = (const S *)a.dout + (row0 * H + h) * dv;
+        const S *hc = (const S *)a.cs + cb * dk * dv;  // h^T [dv][dk]
+        const S *dhc = (const S *)a.dhs + cb * dk * dv; // dh'^T [dv][dk]
+        const S *uc = (const S *)a.U + cb * C * dv;
+        const S *nk = (const S *)a.NK + cb * C * dk;
+        const S *tc = (const S *)a.Tm + cb * C * C;
+        const size_t sq = (size_t)H * dk, sv = (size_t)H * dv;
+        auto Q = [&](int i, int d) { return i < n ? to_f(qb[i * sq + d]) : 0.f; };
+        auto K = [&](int i, int d) { return i < n ? to_f(kb[i * sq + d]) : 0.f; };
+        auto V = [&](int i, int e) { return i < n ? to_f(vb[i * sv + e]) : 0.f; };
+        auto dO = [&](int i, int e) { return i < n ? to_f(ob[i * sv + e]) : 0.f; };
+        auto Hm = [&](int d, int e) { return to_f(hc[(size_t)e * dk + d]); };
+        auto dH = [&](int d, int e) { return to_f(dhc[(size_t)e * dk + d]); };
+        auto Um = [&](int i, int e) { return to_f(uc[(size_t)i * dv + e]); };
+        auto NKm = [&](int i, int d) { return add ? 0.f : to_f(nk[(size_t)i * dk + d]); };
+        auto Tmm = [&](int i, int j) { return to_f(tc[(size_t)i * C + j]); };
+        auto Gm = [&](int i, int j) { return i >= j ? exp2_fast((float)(gam[i] - gam[j])) : 0.f; };
+        const double A = -exp((double)s.A_log[h]);
+
+        // ---- decay of the chunk (wave 0), gates
+        if (wave == 0) {
+            const float gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+            const float br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
+            const float gl = lane < n ? gr : 0.f;
+            const Decay dcy = decay_lane(gl, A * LOG2E, lane);
+            gam[lane] = dcy.gam2;
+            eg[lane] = dcy.eg;
+            egn[lane] = dcy.egn;
+            bet[lane] = lane < n ? br : 0.f;
+            gch[lane] = gl;
+            if (lane == 0) red[0] = dcy.eglast;
+        }
+        __syncthreads();
+        const float eglast = red[0];
+        float acc[4][4], acc2[4][4];
+        int m0, n0;
+        bool on;
+        auto each = [&](int M, int N, auto f) {
+            if (!on) return;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (m0 + i < M && n0 + j < N) f(m0 + i, n0 + j, i, j);
+        };
+        // ---- P = (Q K^T) o Gam (lower incl. diagonal); K K^T o Gam (strict)
+        wide_mm(C, C, dk, Q, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc, m0, n0, on);
+        each(C, C, [&](int i, int j, int x, int y) { sP[i * C + j] = acc[x][y] * Gm(i, j); });
+        wide_mm(C, C, dk, K, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc, m0, n0, on);
+        each(C, C, [&](int i, int j, int x, int y) { sKG[i * C + j] = (!add && i > j) ? acc[x][y] * Gm(i, j) : 0.f; });
+        // ---- W = U + (-Kw) h
+        wide_mm(C, dv, dk, NKm, Hm, As, Bs, tid, acc, m0, n0, on);
+        each(C, dv, [&](int i, int e, int x, int y) { sW[i * WIDE_LD + e] = Um(i, e) + acc[x][y]; });
+        __syncthreads();
+        // ---- dW = P^T dO + diag(e^{gam_n - gam}) K dh'
+        wide_mm(C, dv, C, [&](int i, int j) { return sP[j * C + i]; }, dO, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, dv, dk, K, dH, As, Bs, tid, acc2, m0, n0, on);
+        each(C, dv, [&](int i, int e, int x, int y) { sdW[i * WIDE_LD + e] = acc[x][y] + egn[i] * acc2[x][y]; });
+        __syncthreads();
+        // ---- dOh = dO h^T; dKw = -dW h^T; dKt = W dh'^T; dP = dO W^T (lower)
+        wide_mm(C, dk, dv, dO, [&](int e, int d) { return Hm(d, e); }, As, Bs, tid, acc, m0, n0, on);
+        each(C, dk, [&](int i, int d, int x, int y) { sdOh[i * WIDE_LD + d] = acc[x][y]; });
+        wide_mm(C, dk, dv, [&](int i, int e) { return sdW[i * WIDE_LD + e]; }, [&](int e, int d) { return Hm(d, e); },
+                As, Bs, tid, acc, m0, n0, on);
+        each(C, dk, [&](int i, int d, int x, int y) { sdKw[i * WIDE_LD + d] = add ? 0.f : -acc[x][y]; });
+        wide_mm(C, dk, dv, [&](int i, int e) { return sW[i * WIDE_LD + e]; }, [&](int e, int d) { return dH(d, e); },
+                As, Bs, tid, acc, m0, n0, on);
+        each(C, dk, [&](int i, int d, int x, int y) { sdKt[i * WIDE_LD + d] = acc[x][y]; });
+        wide_mm(C, C, dv, dO, [&](int e, int j) { return sW[j * WIDE_LD + e]; }, As, Bs, tid, acc, m0, n0, on);
+        each(C, C, [&](int i, int j, int x, int y) { sdP[i * C + j] = i >= j ? acc[x][y] : 0.f; });
+        __syncthreads();
+        // ---- dV' = Tm^T dW, dK' = Tm^T dKw
+        wide_mm(C, dv, C, [&](int i, int j) { return Tmm(j, i); }, [&](int j, int e) { return sdW[j * WIDE_LD + e]; },
+                As, Bs, tid, acc, m0, n0, on);
+        each(C, dv, [&](int i, int e, int x, int y) { sdVp[i * WIDE_LD + e] = acc[x][y]; });
+        wide_mm(C, dk, C, [&](int i, int j) { return Tmm(j, i); }, [&](int j, int d) { return sdKw[j * WIDE_LD + d]; },
+                As, Bs, tid, acc, m0, n0, on);
+        each(C, dk, [&](int i, int d, int x, int y) { sdKp[i * WIDE_LD + d] = add ? 0.f : acc[x][y]; });
+        __syncthreads();
+        // ---- dL = -(dV' U^T + dK' Kw^T) = -dV' U^T + dK' (-Kw)^T, strictly lower
+        wide_mm(C, C, dv, [&](int i, int e) { return sdVp[i * WIDE_LD + e]; }, [&](int e, int j) { return Um(j, e); },
+                As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, C, dk, [&](int i, int d) { return sdKp[i * WIDE_LD + d]; }, [&](int d, int j) { return NKm(j, d); },
+                As, Bs, tid, acc2, m0, n0, on);
+        each(C, C, [&](int i, int j, int x, int y) { sdL[i * C + j] = (!add && i > j) ? acc2[x][y] - acc[x][y] : 0.f; });
+        __syncthreads();
+        // dS + dS^T with dS = diag(beta)(dL o Gam), kept for the dK product
+        for (int e = tid; e < C * C; e += NTHR) {
+            const int i = e / C, j = e % C;
+            sT[e] = bet[i] * sdL[i * C + j] * Gm(i, j) + bet[j] * sdL[j * C + i] * Gm(j, i);
+        }
+        __syncthreads();
+        // ---- dQ = diag(e^gam) dO h^T + (dP o Gam) K
+        wide_mm(C, dk, C, [&](int i, int j) { return sdP[i * C + j] * Gm(i, j); }, K, As, Bs, tid, acc, m0, n0, on);
+        S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+        each(C, dk, [&](int i, int d, int x, int y) {
+            if (i < n) dq_out[i * sq + d] = from_f<BF>(eg[i] * sdOh[i * WIDE_LD + d] + acc[x][y]);
+        });
+        // ---- dK = (dP o Gam)^T Q + diag(e^{gam_n - gam}) dKt + diag(beta e^gam) dK' + (dS + dS^T) K
+        wide_mm(C, dk, C, [&](int i, int j) { return sdP[j * C + i] * Gm(j, i); }, Q, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, dk, C, [&](int i, int j) { return sT[i * C + j]; }, K, As, Bs, tid, acc2, m0, n0, on);
+        S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+        each(C, dk, [&](int i, int d, int x, int y) {
+            if (i < n)
+                dk_out[i * sq + d] = from_f<BF>(acc[x][y] + acc2[x][y] + egn[i] * sdKt[i * WIDE_LD + d] +
+                                                bet[i] * eg[i] * sdKp[i * WIDE_LD + d]);
+        });
+        // ---- dV = diag(beta) dV'
+        S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+        for (int e = tid; e < n * dv; e += NTHR) {
+            const int i = e / dv, f = e % dv;
+            dv_out[i * sv + f] = from_f<BF>(bet[i] * sdVp[i * WIDE_LD + f]);
+        }
+        // ---- <h, dh'> in a fixed order
+        float hd = 0.f;
+        for (int e = tid; e < dk * dv; e += NTHR) hd += to_f(hc[e]) * to_f(dhc[e]);
+        red[tid] = hd;
+        __syncthreads();
+        for (int w = NTHR / 2; w > 0; w >>= 1) {
+            if (tid < w) red[tid] += red[tid + w];
+            __syncthreads();
+        }
+        const float hds = red[0];
+        // ---- dbeta and dgam per row (wave 0, lane = row), then dg and dA_log
+        if (wave == 0) {
+            const int i = lane;
+            float db = 0.f, dgm = 0.f, sj = 0.f, kdk = 0.f;
+            for (int e = 0; e < dv; ++e) db += V(i, e) * sdVp[i * WIDE_LD + e];
+            for (int d = 0; d < dk; ++d) {
+                kdk += K(i, d) * sdKp[i * WIDE_LD + d];
+                dgm += Q(i, d) * sdOh[i * WIDE_LD + d];
+                sj += K(i, d) * sdKt[i * WIDE_LD + d];
+            }
+            db += eg[i] * kdk;
+            dgm = eg[i] * dgm + bet[i] * eg[i] * kdk;
+            sj *= egn[i];
+            for (int j = 0; j < C; ++j) {
+                db += sdL[i * C + j] * sKG[i * C + j];
+                dgm += sdP[i * C + j] * sP[i * C + j] - sdP[j * C + i] * sP[j * C + i];
+                dgm += bet[i] * sdL[i * C + j] * sKG[i * C + j] - bet[j] * sdL[j * C + i] * sKG[j * C + i];
+            }
+            const float stot = wave_sum(sj);
+            dgm -= sj;
+            if (i == C - 1) dgm += eglast * hds + stot;
+            const float pre = wave_prefix(dgm);
+            const float x = lane_value(pre, 63) - pre + dgm;
+            const float dg = (float)A * x;
+            float p = (lane < n) ? gch[lane] * dg : 0.f;
+            if (lane < n) {
+                const size_t gi = (row0 + lane) * H + h;
+                a.dg[gi] = dg;
+                a.dbeta[gi] = db;
+            }
+            p = wave_sum(p);
+            if (lane == 0) a.dA_part[cb] = p;
+        }
+        __syncthreads(); // LDS and scratch are reused by the next chunk
+    }
+}
+
 // dA_log[h] = sum over (b, c) of part[b, h, c]: one workgroup per head,
 // per-thread strided sums, then a fixed tree, so the order never changes.
 __global__ __launch_bounds__(NTHR) void dA_reduce_kernel(const float *__restrict__ part,
@@ -974,7 +1219,7 @@ static int chain_vblock(bool, int D) { return D >= 64 ? 32 : 16; }
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
     constexpr int BV = D >= 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
-    if constexpr (BF) {
+    if constexpr (BF && D <= 64) {
         const dim3 block(64 * (BV / 16 + BWS_HELPERS));
         if (vec_ok<BF>(a.s))
             hipLaunchKernelGGL((bwd_chain_ws_kernel<D, BV, true>), dim3(grid), block, 0, st, a);
@@ -995,10 +1240,13 @@ hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t
         switch (D) {
         case 32: return chain_inst<true, 32>(a, st);
         case 64: return chain_inst<true, 64>(a, st);
+        case 128: return chain_inst<true, 128>(a, st);
         }
     } else {
         switch (D) {
         case 16: return chain_inst<false, 16>(a, st);
+        case 32: return chain_inst<false, 32>(a, st);
+        case 64: return chain_inst<false, 64>(a, st);
         }
     }
     return hipErrorInvalidValue;
@@ -1038,18 +1286,34 @@ template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hi
     return vec_ok<BF>(a.s) ? local_launch<BF, D, true>(a, st) : local_launch<BF, D, false>(a, st);
 }
 
+template <bool BF> static hipError_t wide_inst(const BwdLocalArgs &a, hipStream_t st) {
+    const int nch = a.s.B * a.s.H * a.s.NC;
+    const int grid = nch < WIDE_GRID ? nch : WIDE_GRID;
+    hipLaunchKernelGGL((bwd_local_wide_kernel<BF>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st) {
     if (bf16) {
         switch (D) {
         case 32: return local_inst<true, 32>(a, st);
         case 64: return local_inst<true, 64>(a, st);
+        case 128: return a.wide ? wide_inst<true>(a, st) : hipErrorInvalidValue;
         }
     } else {
         switch (D) {
         case 16: return local_inst<false, 16>(a, st);
+        case 32:
+        case 64: return a.wide ? wide_inst<false>(a, st) : hipErrorInvalidValue;
         }
     }
     return hipErrorInvalidValue;
+}
+
+size_t bwd_wide_scratch_bytes(bool bf16, int D, int nchunks_total) {
+    if (bf16 ? D <= 64 : D <= 16) return 0;
+    const int grid = nchunks_total < WIDE_GRID ? nchunks_total : WIDE_GRID;
+    return (size_t)grid * WIDE_SCRATCH * sizeof(float);
 }
 
 hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st) {
@@ -1057,7 +1321,7 @@ hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int 
     return hipGetLastError();
 }
 
-bool bwd_supported(bool bf16, int D) { return bf16 ? (D == 32 || D == 64) : (D == 16); }
+bool bwd_supported(bool bf16, int D) { return bf16 ? (D == 32 || D == 64 || D == 128) : (D == 16 || D == 32 || D == 64); }
 
 int bwd_chain_vblock(bool bf16, int D) { return chain_vblock(bf16, D); }
 

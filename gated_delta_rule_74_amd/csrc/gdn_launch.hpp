@@ -61,6 +61,7 @@ struct BwdLocalArgs {
     void *dq, *dk, *dv;
     float *dg, *dbeta;
     float *dA_part;  // [B*H*NC]
+    float *wide;     // scratch of the wide-head kernel (null for the others)
 };
 
 struct StepArgs {
@@ -84,6 +85,9 @@ int fwd_vblock(int D);
 bool fwd_segmentable(bool bf16, int D); // chain launch accepts a chunk range
 int bwd_chain_vblock(bool bf16, int D);
 bool bwd_supported(bool bf16, int D);
+// Scratch bytes the local-gradient pass needs for this padded head dim (0
+// when the LDS-resident kernel covers it).
+size_t bwd_wide_scratch_bytes(bool bf16, int D, int nchunks_total);
 
 hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t st);

@@ -121,8 +121,10 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
  *                 when ctx is NULL
  *   ws, ws_bytes  workspace of gdn_bwd_workspace_size() bytes, 256-byte
  *                 aligned
- * Supported head dimensions: bf16 up to 64, fp32 up to 16 (others return
- * GDN_EUNSUPPORTED). */
+ * Supported head dimensions: those of gdn_fwd (bf16 up to 128, fp32 up to
+ * 64). The local gradients of heads wider than 64 (bf16) or 16 (fp32) run in
+ * a kernel that keeps its intermediates in the workspace; the workspace size
+ * query includes that scratch. */
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
                      const float *g, const float *beta, const float *A_log, const float *h0,
                      const void *ctx, const void *dout, const float *dhT, void *dq, void *dk,

@@ -99,7 +99,7 @@ def test_bwd_validation(L):
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need - 1) == EWORKSPACE
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dq=None) == EINVAL
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, cs=fake(15), hT=fake(16)) == EINVAL
-    assert bwd_call(L, gdn.Shape(1, 8, 2, 100, 100, 1, 64, 0), ws=fake(20), ws_bytes=need) == EUNSUPPORTED
+    assert bwd_call(L, gdn.Shape(1, 8, 2, 100, 100, 0, 64, 0), ws=fake(20), ws_bytes=need) == EUNSUPPORTED
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dq=fake(1)) == EINVAL  # dq aliases q
     assert bwd_call(L, s, ws=fake(20), ws_bytes=need, dk=fake(20)) == EINVAL  # dk in workspace
 

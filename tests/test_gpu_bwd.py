@@ -109,6 +109,32 @@ def test_head_dims_bf16(dk, dv):
     check_bwd(with_dhT(x, 7), "bf16")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (100, 70), (72, 128)])
+def test_wide_head_dims_bf16(dk, dv):
+    """Head dims past 64 (bf16): the local gradients run in the wide-head
+    kernel, the reverse state pass in the LDS-staged chain kernel."""
+    say(f"bwd bf16 wide dk={dk} dv={dv}")
+    x = gi.gen_seq(1, 150, 2, dk, dv, "bf16", seed=1250 + dk, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 11), "bf16")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 64), (40, 24)])
+def test_wide_head_dims_fp32(dk, dv):
+    say(f"bwd fp32 wide dk={dk} dv={dv}")
+    x = gi.gen_seq(1, 140, 2, dk, dv, "f32", seed=1260 + dk, h0="randn", with_do=True, decay="weak")
+    check_bwd(with_dhT(x, 12), "f32")
+
+
+def test_wide_head_additive_and_recompute():
+    x = with_dhT(gi.gen_seq(1, 100, 2, 128, 128, "bf16", seed=1270, h0="randn", with_do=True,
+                            decay="weak"), 13)
+    check_bwd(x, "bf16", additive=True)
+    a = run_bwd(x, use_saved=True)
+    b = run_bwd(x, use_saved=False)
+    for name in GRADS + ["dA_log"]:
+        assert torch.equal(a[name], b[name]), name
+
+
 def test_recompute_path_equals_saved_states_path():
     x = with_dhT(gi.gen_seq(2, 200, 2, 56, 56, "bf16", seed=1300, h0="randn", with_do=True,
                             decay="weak"), 8)
@@ -142,6 +168,15 @@ def test_autograd_function():
     for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
                       ("A_log", "dA_log"), ("h0", "dh0")]:
         assert_close(f"autograd {key}", host(ts[name].grad), ref[key], TOL["bf16"])
+
+
+def test_full_size_long_context_fwdbwd_sampled():
+    """B1 H16 T32768 d128 bf16, nonzero initial state (the long-context
+    configuration, weak decay so the 512-step chain matters): oracle on two
+    sampled heads."""
+    say("bwd full long_ctx")
+    x = gi.gen_config("long_ctx", decay="weak")
+    check_bwd(x, "bf16", units=[3, 12])
 
 
 @pytest.mark.parametrize("decay", ["normal", "weak"])
