@@ -519,11 +519,11 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
 // U and Tm come from the forward context, so no triangular solve runs here.
 // Eight LDS regions are reused phase by phase (Pn = phase n):
 //   R0 K                              R4 dh'^T (P4-5) -> -dV't (P6-7)
-//   R1 h^T (P3-5) -> V (P6) -> dSt (P7-8)
+//   R1 h^T (P1-5) -> V (P6) -> dSt (P7-8)
 //   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7)
-//   R3 U (P3) -> dO (P4-5) -> partial sums (P9)
-//   R5 Wt (P3-5) -> dK (P9)           R6 dWt (P4-6) -> dK't (P6-7)
-//   R7 -Kw (P3) -> dKw (P5-6) -> U (P7)
+//   R3 U (P1) -> dO (P4-5) -> partial sums (P9)
+//   R5 Wt (P1-5) -> dK (P9)           R6 dWt (P4-6) -> dK't (P6-7)
+//   R7 -Kw (P1) -> dKw (P5-6) -> U (P7)
 //   RQ Q (whole chunk)                RP (dP o Gam)^T (P5-6) -> dQ (P9)
 // Inputs needed in two phases stay in registers between their stashes.
 
@@ -665,9 +665,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
     for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
 
-    // ---- P1: gates, decay, K K^T and Q K^T
+    // ---- P1: gates, decay, K K^T and Q K^T; W = U - Kw h
     fk.stash(Ks, LDD, tid);
     fq.stash(RQ, LDD, tid);
+    fh.stash(R1, LDD, tid);
+    fu.stash(R3, LDD, tid);
+    if (!add) fn.stash(R7, LDD, tid);
     __syncthreads();
     // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
     f32x4 gC[PWC], kkg[PWC], pC[PWC];
@@ -698,19 +701,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         });
         store_T<BF, 4, 4>(pC, R2, LDC, wave, lane); // Pt
     }
-    __syncthreads(); // Pt complete
-    // ---- P3: W = U - Kw h
-    fh.stash(R1, LDD, tid);
-    fu.stash(R3, LDD, tid);
-    if (!add) fn.stash(R7, LDD, tid);
-    __syncthreads();
     {
         f32x4 accW[PWD];
         for_tiles<4, DT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(R3[row * LDD + col]); });
         if (!add) gemm<BF, 4, DT, D, false, false>(R7, LDD, R1, LDD, accW, wave, lane); // + (-Kw) h
         store_T<BF, 4, DT>(accW, R5, LDC, wave, lane);                               // Wt
     }
-    __syncthreads(); // U reads done
+    __syncthreads(); // Pt and Wt complete; U reads done
     // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
     fo.stash(R3, LDD, tid);
     fd.stash(R4, LDD, tid);
