@@ -225,7 +225,8 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the gated delta rule path here is built and timed "
-              "on a single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              "on a single MI355X ((batch, head) units would be split across GPUs with no "
+              "communication but one all-reduce of dA_log); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
     GDN_OK = 0,
     GDN_EINVAL = 1,       /* bad argument (size, null pointer, alignment, aliasing) */
-    GDN_EUNSUPPORTED = 2, /* valid request this build does not implement */
+    GDN_EUNSUPPORTED = 2, /* valid request the library does not implement */
     GDN_EWORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
     GDN_EHIP = 4          /* a HIP runtime call or kernel launch failed */
 } gdn_status_t;
