@@ -364,23 +364,24 @@ __device__ __forceinline__ float gamma_ij(const double *gam2, int i, int j) {
 constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 
 // T = (I + L)^{-1} for a strictly lower triangular 64 x 64 L, given as its
-// transpose Lt[j][i] = L[i][j] (fp32, [C][LDF]); T is written to Tm
-// ([C][LDF], fp32). Diagonal 16 x 16 blocks by forward substitution, all four
-// in wave 0 (lane group g = block g, lane = column); the step-i multipliers
+// transpose Lt[j][i] = L[i][j] (fp32, [C][LDF]). T is written over the lower
+// triangle (diagonal blocks included) of the same array: the blocks of Lt the
+// solve reads after the diagonal step lie strictly above the block diagonal,
+// and each diagonal block is read whole into registers before it is
+// overwritten. Diagonal 16 x 16 blocks by forward substitution, all four in
+// wave 0 (lane group g = block g, lane = column); the step-i multipliers
 // L[i+1..15][i] are one row of Lt, read two steps ahead so the LDS latency
 // overlaps the updates. Off-diagonal blocks by block forward substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
 // level by level (i - j = 1, 2, 3) with fp32 MFMA; waves 0..3 do the work.
-// xs: 4 x 16 x 17 floats.
-// Operand copies written as the blocks are produced ([C][ldt]), each only
-// when its flag is set: Tb = T diag(cb) (WB), Tk = T diag(ck) (WK), both
-// column-scaled, and TT = T^T (WT).
+// xs: 4 x 16 x 17 floats. Tb ([C][ldt]) receives T in the operand type as
+// its blocks are produced, zeros above the block diagonal.
 // Ends with a barrier.
-template <bool BF, bool WB, bool WK, bool WT>
-__device__ __forceinline__ void tri_inverse(const float *Lt, float *Tm, float *xs, int wave, int lane,
-                                            typename Op<BF>::S *Tb, typename Op<BF>::S *Tk,
-                                            typename Op<BF>::S *TT, int ldt, const float *cb,
-                                            const float *ck) {
+template <bool BF>
+__device__ __forceinline__ void tri_inverse(float *LT, float *xs, int wave, int lane, typename Op<BF>::S *Tb,
+                                            int ldt) {
+    const float *Lt = LT;
+    float *Tm = LT;
     using S = typename Op<BF>::S;
     if (wave == 0) {
         const int c = lane & 15, o = 16 * (lane >> 4);
@@ -409,24 +410,17 @@ __device__ __forceinline__ void tri_inverse(const float *Lt, float *Tm, float *x
                 r1[q4] = r2[q4];
             }
         }
-        const float sb = WB ? cb[o + c] : 0.f, sk = WK ? ck[o + c] : 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             Tm[(o + i) * LDF + o + c] = x[i];
-            if constexpr (WB) Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sb);
-            if constexpr (WK) Tk[(o + i) * ldt + o + c] = from_f<BF>(x[i] * sk);
-            if constexpr (WT) TT[(o + c) * ldt + o + i] = from_f<BF>(x[i]);
+            Tb[(o + i) * ldt + o + c] = from_f<BF>(x[i]);
         }
     } else if (wave < 4) {
         // zero the blocks right of the diagonal in block row wave - 1
         const int o = 16 * (wave - 1);
         for (int e = lane; e < 16 * 48; e += 64) {
             const int i = e / 48, cc = e % 48 + o + 16;
-            if (cc < C) {
-                if constexpr (WB) Tb[(o + i) * ldt + cc] = S(0);
-                if constexpr (WK) Tk[(o + i) * ldt + cc] = S(0);
-                if constexpr (WT) TT[cc * ldt + o + i] = S(0);
-            }
+            if (cc < C) Tb[(o + i) * ldt + cc] = S(0);
         }
     }
     __syncthreads();
@@ -457,15 +451,12 @@ __device__ __forceinline__ void tri_inverse(const float *Lt, float *Tm, float *x
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
             }
             const int col = 16 * bj + r;
-            const float sb = WB ? cb[col] : 0.f, sk = WK ? ck[col] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * bi + 4 * kq + e;
                 const float t = -acc[e];
                 Tm[row * LDF + col] = t;
-                if constexpr (WB) Tb[row * ldt + col] = from_f<BF>(t * sb);
-                if constexpr (WK) Tk[row * ldt + col] = from_f<BF>(t * sk);
-                if constexpr (WT) TT[col * ldt + row] = from_f<BF>(t);
+                Tb[row * ldt + col] = from_f<BF>(t);
             }
         }
         __syncthreads();

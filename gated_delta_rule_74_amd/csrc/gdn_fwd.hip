@@ -28,20 +28,38 @@ template <bool BF, int D> struct PrepSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
-    static constexpr int mx(int x, int y) { return x > y ? x : y; }
     static constexpr int oK = 0;                                       // Ks [C][LDD]
     static constexpr int oV = oK + C * LDD * (int)sizeof(S);          // Vs [C][LDD]
     static constexpr int oTb = oV + C * LDD * (int)sizeof(S);         // Tb [C][LDC]
-    static constexpr int oL = oTb + C * LDC * (int)sizeof(S);         // L^T fp32 [C][LDF]
-    static constexpr int oT = oL + C * LDF * 4;                       // Tm fp32 [C][LDF]
-    static constexpr int oTk = oT + C * LDF * 4;                      // Tk [C][LDC]
-    static constexpr int oX = oTk + C * LDC * (int)sizeof(S);         // solve scratch
+    static constexpr int oL = oTb + C * LDC * (int)sizeof(S);         // L^T, then Tm, fp32 [C][LDF]
+    static constexpr int oX = oL + C * LDF * 4;                       // solve scratch
     static constexpr int oGam = oX + 4 * 16 * 17 * 4;                 // double[C]
     static constexpr int oBet = oGam + C * 8;                         // float[C]
     static constexpr int oCk = oBet + C * 4;                          // beta e^gam
     static constexpr int SIZE = oCk + C * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
+    // three workgroups per compute unit for bf16 heads up to 64 wide
+    static_assert(!BF || D > 64 || 3 * SIZE <= 160 * 1024, "prep occupancy");
 };
+
+// X[row][0..D) *= sc[row] in place for the 16-byte pieces p0, p0 + np, ...
+template <bool BF, int D>
+__device__ __forceinline__ void scale_rows(typename Op<BF>::S *X, int ld, const float *sc, int p0, int np) {
+    using S = typename Op<BF>::S;
+    constexpr int V = Op<BF>::VEC, NG = D / V;
+    for (int it = p0; it < C * NG; it += np) {
+        const int row = it / NG, c0 = (it % NG) * V;
+        const float f = sc[row];
+        union {
+            uint4 u;
+            S x[V];
+        } pk;
+        pk.u = *reinterpret_cast<const uint4 *>(X + row * ld + c0);
+#pragma unroll
+        for (int j = 0; j < V; ++j) pk.x[j] = from_f<BF>(to_f(pk.x[j]) * f);
+        *reinterpret_cast<uint4 *>(X + row * ld + c0) = pk.u;
+    }
+}
 
 // Store this wave's tiles of an [MT*16][NT*16] accumulator grid to a
 // row-major global matrix (rows < nr, cols < nc), times `sign`.
@@ -64,8 +82,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     S *Vs = (S *)(smem + L::oV);
     S *Tb = (S *)(smem + L::oTb);
     float *Lm = (float *)(smem + L::oL);
-    float *Tm = (float *)(smem + L::oT);
-    S *Tk = (S *)(smem + L::oTk);
+    float *Tm = Lm;
     float *xs = (float *)(smem + L::oX);
     double *gam2 = (double *)(smem + L::oGam);
     float *bet = (float *)(smem + L::oBet);
@@ -99,6 +116,9 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     fv.stash(Vs, LDD, tid);
     __syncthreads();
 
+    // U = Tm (diag(beta) V) and -Kw = -Tm (diag(beta e^gam) K): the row
+    // scales go onto V and K in LDS (after K K^T has read K), so a single
+    // operand copy Tb of Tm serves both products
     if (!s.additive) {
         f32x4 sk[4];
 #pragma unroll
@@ -107,13 +127,19 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         for_tiles<4, 4>(wave, lane, [&](int i, int e, int row, int col) {
             Lm[col * LDF + row] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f; // L^T
         });
-        __syncthreads(); // L complete
-        tri_inverse<BF, true, true, false>(Lm, Tm, xs, wave, lane, Tb, Tk, nullptr, LDC, bet, ck);
+        __syncthreads(); // L complete, K K^T done
+        // waves 4..7 are idle during the diagonal solve
+        if (wave >= 4) {
+            scale_rows<BF, D>(Vs, LDD, bet, tid - 4 * 64, NTHR - 4 * 64);
+            scale_rows<BF, D>(Ks, LDD, ck, tid - 4 * 64, NTHR - 4 * 64);
+        }
+        tri_inverse<BF>(Lm, xs, wave, lane, Tb, LDC);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
             const int row = e / C, col = e % C;
-            Tb[row * LDC + col] = from_f<BF>(row == col ? bet[col] : 0.f);
+            Tb[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
         }
+        scale_rows<BF, D>(Vs, LDD, bet, tid, NTHR);
         __syncthreads();
     }
 
@@ -143,11 +169,12 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int i = 0; i < Tiles<4, DT>::PW; ++i) accU[i] = accN[i] = zero4();
     gemm<BF, 4, DT, C, false, true>(Tb, LDC, Vs, LDD, accU, wave, lane);
-    if (!s.additive) gemm<BF, 4, DT, C, false, true>(Tk, LDC, Ks, LDD, accN, wave, lane);
+    if (!s.additive) gemm<BF, 4, DT, C, false, true>(Tb, LDC, Ks, LDD, accN, wave, lane);
     S *Ug = (S *)a.U + cbase * C * dv, *Ng = (S *)a.NK + cbase * C * dk;
     if constexpr (BF && 2 * C * D * (int)sizeof(S) <= C * LDF * 4) {
-        // U and NK leave through the spent L^T area as 16-byte pieces of
-        // their contiguous [64][d] blocks
+        // U and NK leave through the Tm area as 16-byte pieces of their
+        // contiguous [64][d] blocks, once every wave has stored Tm out
+        __syncthreads();
         S *Us = (S *)Lm, *Ns = Us + C * D;
 #pragma unroll
         for (int i = 0; i < Tiles<4, DT>::PW; ++i) accN[i] = -accN[i];
