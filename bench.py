@@ -11,7 +11,12 @@ the dominant kernel (per-kernel durations measured here with HIP events
 around every library launch) and the fp64 CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
+
+The line also carries "decode_step": the single-token state update on its own
+workload (256 sequences x 16 heads x d 56, 1024 consecutive steps, fp32 state
+carried in place, fresh bf16 tokens per step), timed as one captured HIP graph
+of the 1024 launches, with the step kernel's HBM roofline.
 
 Profiling aids (the counter runs behind the committed traffic summaries):
     python bench.py --profile-run N      N untimed steps, then one plain
@@ -165,6 +170,93 @@ def traffic_summary(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def decode_bytes_per_step(N, H, dk, dv):
+    """Algorithmic HBM bytes of one decode step: the fp32 state read and
+    written once, bf16 q, k, v read and o written, fp32 g and beta read."""
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + dv * 2 + 8)
+
+
+def decode_bench(dev, n_sets_cold=6):
+    """The decode workload: 1024 consecutive single-token steps of 256
+    sequences x 16 heads from a carried state. Hot: one state set updated in
+    place (51 MB, which the 256 MB Infinity Cache can hold between steps).
+    Cold: n_sets_cold independent state sets served round-robin (> 256 MB),
+    so each step's state comes from HBM."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_74_amd as gdn
+    import gdn_inputs as gi
+
+    cfg = gi.CONFIGS["decode_step"]
+    N, H, dk, dv, S = cfg.B, cfg.H, cfg.dk, cfg.dv, cfg.steps
+    x = gi.gen_decode(N, H, dk, dv, S, cfg.dtype, seed=cfg.seed)
+
+    def to_dev(a):
+        if isinstance(a, gi.Tensor):
+            return torch.from_numpy(a.data.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v, g, beta, A_log, h0 = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "A_log", "h0"))
+    del x
+    o = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
+
+    def chain(hs):
+        for t in range(S):
+            h = hs[t % len(hs)]
+            gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, h, o=o)
+
+    def run(n_sets):
+        hs = [h0.clone() for _ in range(n_sets)]
+        # eager reference of one pass, then the same pass as one graph replay
+        chain(hs)
+        torch.cuda.synchronize()
+        ref = [h.clone() for h in hs]
+        graph = None
+        try:
+            for h in hs:
+                h.copy_(h0)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                chain(hs)
+            for h in hs:
+                h.copy_(h0)
+            graph.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(hs, ref)):
+                graph = None
+        except RuntimeError:
+            graph = None
+        for _ in range(2):  # warm
+            graph.replay() if graph else chain(hs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay() if graph else chain(hs)
+        e1.record()
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+        timer = gdn.LaunchTimer(S)
+        with timer:
+            chain(hs)
+        d = timer.durations_ms()
+        kern_ms = float(np.mean(d))
+        nbytes = decode_bytes_per_step(N, H, dk, dv)
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        return {"state_sets": n_sets, "graph": graph is not None,
+                "us_per_step": round(total_ms * 1e3 / S, 3),
+                "tokens_per_s": N * S / (total_ms * 1e-3),
+                "roofline": {"bound": "hbm", "kernel": "gdn_step", "achieved": round(achieved, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": nbytes, "avg_launch_ms": round(kern_ms, 5)}}
+
+    hot = run(1)
+    cold = run(n_sets_cold)
+    return {"workload": "decode_step", "sequences": N, "heads": H, "d_k": dk, "d_v": dv, "steps": S,
+            "dtype": "bf16 tokens, fp32 state", "hot": hot, "cold": cold}
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -216,6 +308,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", type=int, default=0, metavar="N")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -348,6 +441,8 @@ def main():
         "wall_s_timed": round(wall_s, 3),
         "cpu_baseline": None,
     }
+    if not args.no_decode:
+        out["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, B, T, H, args.cpu_seconds)
     print(json.dumps(out), flush=True)
