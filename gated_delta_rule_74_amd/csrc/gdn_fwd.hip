@@ -376,11 +376,14 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
 // and h stay in the wave's registers on the serial path: no barrier and no
 // LDS round trip between the two products. The eight "helper" waves that
 // follow split the rest: they stage the next chunk's inputs into LDS, form
-// P = (Q K^T) o Gam and diag(e^gam) Q h for the current chunk, finish
-// O = ... + P W one chunk behind the chain (W arrives through LDS), and copy
-// the chunk-start states out. Helper w owns chunk rows 16*(w%4).. and half
-// of the value columns. One barrier per chunk hands the double-buffered LDS
-// over.
+// P = (Q K^T) o Gam and diag(e^gam) Q h for the current chunk, and finish
+// O = ... + P W one chunk behind the chain (W arrives through LDS). Helper w
+// owns chunk rows 16*(w%4).. and half of the value columns. One barrier per
+// chunk hands the double-buffered LDS over. Helpers 0..3 issue every global
+// load and helpers 4..7 store O (their own rows, and the rows helpers 0..3
+// leave in LDS one chunk earlier), so the wait of a loading wave for its
+// prefetch never includes stores; the chain waves store each chunk-start
+// state from their registers.
 //
 // Chunk-start states go out transposed, [dv][dk] per chunk.
 
@@ -404,7 +407,8 @@ template <int D> struct WsSmem {
     static constexpr int oWX = oHX + 2 * szHX;
     static constexpr int oP = oWX + 2 * szWX;
     static constexpr int oO = oP + 2 * 4 * szP;
-    static constexpr int oDec = oO + WS_HELPERS * szO;
+    static constexpr int oOA = oO + WS_HELPERS * szO; // O rows of helpers 0..3, two chunks
+    static constexpr int oDec = oOA + 2 * 4 * szO;
     static constexpr int SIZE = oDec + 2 * szDec;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
@@ -412,7 +416,7 @@ template <int D> struct WsSmem {
 template <int D, bool VEC>
 __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
     constexpr int DT = D / 16, KS = D / 32;
-    constexpr int NHT = 64 * WS_HELPERS; // helper threads
+    constexpr int NLT = 64 * 4; // loading helper threads (helpers 0..3)
     using L = WsSmem<D>;
     constexpr int LDD = L::LDD, LDC = L::LDC, LDP = L::LDP, LDO = L::LDO, VH = L::VH;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
@@ -421,6 +425,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     auto wx = [&](int i) { return (u16 *)(smem + L::oWX + i * L::szWX); };
     auto pbuf = [&](int i, int ib) { return (u16 *)(smem + L::oP + (i * 4 + ib) * L::szP); };
     auto obuf = [&](int hw) { return (u16 *)(smem + L::oO + hw * L::szO); };
+    auto obufA = [&](int c, int i) { return (u16 *)(smem + L::oOA + ((c & 1) * 4 + i) * L::szO); };
     auto gam_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec); };
     auto eg_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 4); };
     auto egn_of = [&](int i) { return (float *)(smem + L::oDec + i * L::szDec + C * 8); };
@@ -442,7 +447,8 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     // ---- helper-wave state: rows 16*ib.., value blocks vb0..vb0+VH-1
     const int hw = wave - DT, htid = tid - 64 * DT;
     const int ib = hw & 3, half = hw >> 2, vb0 = half * VH;
-    ChunkFrag<true, D, C, NHT> fq, fk, fn, fu;
+    const bool loader = !chain && hw < 4;
+    ChunkFrag<true, D, C, NLT> fq, fk, fn, fu;
     float pg = 0.f;
     f32x4 accO[VH];
     const u16 *q = (const u16 *)s.q, *k = (const u16 *)s.k;
@@ -474,6 +480,25 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         }
     };
 
+    // rows 16*bi.. and value blocks vb..vb+VH-1 of O of chunk cc, from LDS
+    // (16 rows of LDO elements) to global
+    auto store_o = [&](int cc, int bi, int vb, const u16 *Os) {
+        const int n = min(C, T - cc * C);
+        const int nr = min(16, n - 16 * bi), vlo = 16 * vb, nvc = min(16 * VH, dv - vlo);
+        u16 *orow = o + (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
+        if (VEC) {
+            for (int it = lane; it < 16 * 2 * VH; it += 64) {
+                const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
+                if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
+            }
+        } else {
+            for (int it = lane; it < 16 * 16 * VH; it += 64) {
+                const int i = it / (16 * VH), v = it % (16 * VH);
+                if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
+            }
+        }
+    };
+
     // ---- prologue: initial state (chain) and chunk 0 in LDS (helpers)
     if (chain) {
 #pragma unroll
@@ -486,7 +511,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
             hb[kb] = pack4(hacc[kb]);
             *(short4_t *)(hx(c0 & 1) + (v0 + r) * LDD + 16 * kb + 4 * g) = hb[kb];
         }
-    } else {
+    } else if (loader) {
         fetch(c0);
         stash(c0);
         if (c1 - c0 > 1) fetch(c0 + 1);
@@ -498,6 +523,26 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
             if (c < c1) {
                 const int st = c & 1;
                 const u16 *Ks = stage(st, 1), *NKs = stage(st, 2), *Us = stage(st, 3);
+                // chunk-start state h_c out from the registers, transposed
+                // [dv][dk]: 4 consecutive key rows of one value column per
+                // lane (one 8-byte store when dk % 8 == 0, else per element)
+                if (cs) {
+                    u16 *dst = cs + ((size_t)bh * NC + c) * dv * dk;
+                    const int v = v0 + r;
+#pragma unroll
+                    for (int kb = 0; kb < DT; ++kb) {
+                        const int d = 16 * kb + 4 * g;
+                        if (v < dv && d < dk) {
+                            if (VEC) {
+                                *(short4_t *)(dst + (size_t)v * dk + d) = hb[kb];
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (d + e < dk) dst[(size_t)v * dk + d + e] = (u16)hb[kb][e];
+                            }
+                        }
+                    }
+                }
                 const float *egn = egn_of(st);
                 const float el = egl_of(st)[0];
                 // W = U + (-Kw) h
@@ -543,14 +588,17 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                 }
             }
         } else {
-            // chunk c+1 into LDS (requested one chunk ago), chunk c+2 requested;
-            // this chunk's stores are issued after these loads, so the next
-            // wait for loads does not wait on them
-            if (c + 1 < c1) stash(c + 1);
-            if (c + 2 < c1) fetch(c + 2);
+            // chunk c+1 into LDS (requested one chunk ago), chunk c+2 requested
+            if (loader) {
+                if (c + 1 < c1) stash(c + 1);
+                if (c + 2 < c1) fetch(c + 2);
+            } else if (o && c > c0 + 1) {
+                // O rows helper hw - 4 finished one chunk ago
+                store_o(c - 2, ib, 0, obufA(c - 2, hw - 4));
+            }
             // finish O of the previous chunk: + P W
             if (o && c > c0) {
-                const int pst = (c - 1) & 1, n = min(C, T - (c - 1) * C);
+                const int pst = (c - 1) & 1;
                 const u16 *Pt = pbuf(pst, ib), *WT = wx(pst);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -561,41 +609,14 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                         accO[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bw, accO[x], 0, 0, 0);
                     }
                 }
-                // the 16 x 16*VH block goes out through LDS as 16-byte row pieces
-                u16 *Os = obuf(hw);
+                // the 16 x 16*VH block goes out through LDS as 16-byte row
+                // pieces; helpers 0..3 leave it for helpers 4..7
+                u16 *Os = loader ? obufA(c - 1, hw) : obuf(hw);
 #pragma unroll
                 for (int x = 0; x < VH; ++x)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Os[(4 * g + e) * LDO + 16 * x + r] = f2bf(accO[x][e]);
-                const int nr = min(16, n - 16 * ib), vlo = 16 * vb0, nvc = min(16 * VH, dv - vlo);
-                u16 *orow = o + (((size_t)b * T + (c - 1) * C + 16 * ib) * H + h) * dv + vlo;
-                if (VEC) {
-                    for (int it = lane; it < 16 * 2 * VH; it += 64) {
-                        const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
-                        if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
-                    }
-                } else {
-                    for (int it = lane; it < 16 * 16 * VH; it += 64) {
-                        const int i = it / (16 * VH), v = it % (16 * VH);
-                        if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
-                    }
-                }
-            }
-            // chunk-start state h_c out, transposed [dv][dk]
-            if (cs && c < c1) {
-                const u16 *HT = hx(c & 1);
-                u16 *dst = cs + ((size_t)bh * NC + c) * dv * dk;
-                if (VEC) {
-                    for (int it = htid; it < dv * (dk / 8); it += NHT) {
-                        const int v = it / (dk / 8), d = (it % (dk / 8)) * 8;
-                        *(uint4 *)(dst + (size_t)v * dk + d) = *(const uint4 *)(HT + v * LDD + d);
-                    }
-                } else {
-                    for (int it = htid; it < dv * dk; it += NHT) {
-                        const int v = it / dk, d = it % dk;
-                        dst[(size_t)v * dk + d] = HT[v * LDD + d];
-                    }
-                }
+                if (!loader) store_o(c - 1, ib, vb0, Os);
             }
             // P (this helper's half of the columns) and diag(e^gam) Q h
             if (o && c < c1) {
@@ -640,6 +661,8 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         }
         __syncthreads();
     }
+    // the last O rows of helpers 0..3 (finished in the final iteration)
+    if (o && !chain && !loader && c1 > c0) store_o(c1 - 1, ib, 0, obufA(c1 - 1, hw - 4));
     if (chain && a.hT) {
 #pragma unroll
         for (int kb = 0; kb < DT; ++kb) {
