@@ -949,61 +949,65 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
 // does not hold (bf16 d > 64, fp32 d > 16): the same quantities and the same
 // formulas, formed product by product. Every 64 x d and 64 x 64 intermediate
 // goes to fp32 scratch of the workgroup's own (it stays in L2 between the
-// phases); each product runs on the vector units through LDS tiles, one 4 x 4
-// block of the result per thread. Persistent workgroups over a fixed grid, so
+// phases); each product runs on fp32 MFMA tiles through LDS, 64-wide slices of
+// the inner dimension at a time. Persistent workgroups over a fixed grid, so
 // the scratch does not grow with the sequence.
 
 constexpr int WIDE_GRID = 1024;
 constexpr int WIDE_LD = 128;                                 // row stride of 64 x d scratch
 constexpr int WIDE_SCRATCH = 5 * C * C + 7 * C * WIDE_LD;    // floats per workgroup
+constexpr int WIDE_KS = 64;                                  // inner-dimension slice per staging
+constexpr int WIDE_LDA = WIDE_KS + 4;                        // A slice [64][LDA]: rows 4 banks apart
+constexpr int WIDE_LDB = WIDE_LD + 16;                       // B slice [KS][LDB]: rows 16 banks apart
 
-// out = A (M x K) * B (K x N) for M, N <= 128 and M * N <= 8192; fa(m, k) and
-// fb(k, n) fetch operands (only in range). Thread tid owns rows m0..m0+3 and
-// columns n0..n0+3 of the result when `on`. Ends with a barrier.
+// out = A (M x K) * B (K x N) for M <= 64, N <= 128; fa(m, k) and fb(k, n)
+// fetch operands (only in range). The result is a grid of 16 x 16 tiles,
+// row-major; wave w owns tiles w, w + 8, w + 16, w + 24, and in tile x lane
+// l holds acc[x][y] = out[16 tm + 4 (l / 16) + y][16 tn + l % 16]
+// (v_mfma_f32_16x16x4f32 layout). Ends with a barrier.
 template <class FA, class FB>
 __device__ __forceinline__ void wide_mm(int M, int N, int K, FA fa, FB fb, float *As, float *Bs, int tid,
-                                        float (&acc)[4][4], int &m0, int &n0, bool &on) {
-    const int Mp = (M + 3) & ~3, Np = (N + 3) & ~3, tpr = Np / 4;
-    on = tid < (Mp / 4) * tpr;
-    m0 = (tid / tpr) * 4;
-    n0 = (tid % tpr) * 4;
+                                        float (&acc)[4][4]) {
+    const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+    const int TM = (M + 15) >> 4, TN = (N + 15) >> 4, NT = TM * TN, Np = 16 * TN;
+    f32x4 c[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int x = 0; x < 4; ++x) c[x] = zero4();
 #pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        for (int e = tid; e < Mp * 16; e += NTHR) {
-            const int m = e >> 4, kk = e & 15;
-            As[m * 17 + kk] = (m < M && k0 + kk < K) ? fa(m, k0 + kk) : 0.f;
+    for (int k0 = 0; k0 < K; k0 += WIDE_KS) {
+        for (int e = tid; e < C * WIDE_KS; e += NTHR) {
+            const int m = e / WIDE_KS, kk = e % WIDE_KS;
+            As[m * WIDE_LDA + kk] = (m < M && k0 + kk < K) ? fa(m, k0 + kk) : 0.f;
         }
-        for (int e = tid; e < 16 * Np; e += NTHR) {
+        for (int e = tid; e < WIDE_KS * Np; e += NTHR) {
             const int kk = e / Np, n = e % Np;
-            Bs[kk * (WIDE_LD + 4) + n] = (n < N && k0 + kk < K) ? fb(k0 + kk, n) : 0.f;
+            Bs[kk * WIDE_LDB + n] = (n < N && k0 + kk < K) ? fb(k0 + kk, n) : 0.f;
         }
         __syncthreads();
-        if (on) {
-#pragma unroll 4
-            for (int kk = 0; kk < 16; ++kk) {
-                float av[4], bv[4];
+        const int kn = min(WIDE_KS, K - k0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) av[i] = As[(m0 + i) * 17 + kk];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bv[j] = Bs[kk * (WIDE_LD + 4) + n0 + j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+        for (int x = 0; x < 4; ++x) {
+            const int t = wave + NWAVE * x;
+            if (t < NT) {
+                const int tm = t / TN, tn = t % TN;
+                const float *ap = As + (16 * tm + r) * WIDE_LDA + kq;
+                const float *bp = Bs + kq * WIDE_LDB + 16 * tn + r;
+                for (int kk = 0; kk < kn; kk += 4)
+                    c[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[kk], bp[kk * WIDE_LDB], c[x], 0, 0, 0);
             }
         }
         __syncthreads();
     }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = c[x][y];
 }
 
 template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel(BwdLocalArgs a) {
     using S = typename Op<BF>::S;
-    __shared__ float As[128 * 17];
-    __shared__ float Bs[16 * (WIDE_LD + 4)];
+    __shared__ float As[C * WIDE_LDA];
+    __shared__ float Bs[WIDE_KS * WIDE_LDB];
     __shared__ double gam[C];
     __shared__ float eg[C], egn[C], bet[C], gch[C], red[NTHR];
     const SeqArgs &s = a.s;
@@ -1063,55 +1067,59 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
         __syncthreads();
         const float eglast = red[0];
         float acc[4][4], acc2[4][4];
-        int m0, n0;
-        bool on;
+        // visit this lane's elements of an M x N product (wide_mm's layout)
         auto each = [&](int M, int N, auto f) {
-            if (!on) return;
+            const int TN = (N + 15) >> 4, NT = ((M + 15) >> 4) * TN;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int x = 0; x < 4; ++x) {
+                const int t = wave + NWAVE * x;
+                if (t < NT) {
+                    const int i0 = 16 * (t / TN) + 4 * (lane >> 4), j = 16 * (t % TN) + (lane & 15);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (m0 + i < M && n0 + j < N) f(m0 + i, n0 + j, i, j);
+                    for (int y = 0; y < 4; ++y)
+                        if (i0 + y < M && j < N) f(i0 + y, j, x, y);
+                }
+            }
         };
         // ---- P = (Q K^T) o Gam (lower incl. diagonal); K K^T o Gam (strict)
-        wide_mm(C, C, dk, Q, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, C, dk, Q, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc);
         each(C, C, [&](int i, int j, int x, int y) { sP[i * C + j] = acc[x][y] * Gm(i, j); });
-        wide_mm(C, C, dk, K, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, C, dk, K, [&](int d, int j) { return K(j, d); }, As, Bs, tid, acc);
         each(C, C, [&](int i, int j, int x, int y) { sKG[i * C + j] = (!add && i > j) ? acc[x][y] * Gm(i, j) : 0.f; });
         // ---- W = U + (-Kw) h
-        wide_mm(C, dv, dk, NKm, Hm, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, dv, dk, NKm, Hm, As, Bs, tid, acc);
         each(C, dv, [&](int i, int e, int x, int y) { sW[i * WIDE_LD + e] = Um(i, e) + acc[x][y]; });
         __syncthreads();
         // ---- dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-        wide_mm(C, dv, C, [&](int i, int j) { return sP[j * C + i]; }, dO, As, Bs, tid, acc, m0, n0, on);
-        wide_mm(C, dv, dk, K, dH, As, Bs, tid, acc2, m0, n0, on);
+        wide_mm(C, dv, C, [&](int i, int j) { return sP[j * C + i]; }, dO, As, Bs, tid, acc);
+        wide_mm(C, dv, dk, K, dH, As, Bs, tid, acc2);
         each(C, dv, [&](int i, int e, int x, int y) { sdW[i * WIDE_LD + e] = acc[x][y] + egn[i] * acc2[x][y]; });
         __syncthreads();
         // ---- dOh = dO h^T; dKw = -dW h^T; dKt = W dh'^T; dP = dO W^T (lower)
-        wide_mm(C, dk, dv, dO, [&](int e, int d) { return Hm(d, e); }, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, dk, dv, dO, [&](int e, int d) { return Hm(d, e); }, As, Bs, tid, acc);
         each(C, dk, [&](int i, int d, int x, int y) { sdOh[i * WIDE_LD + d] = acc[x][y]; });
         wide_mm(C, dk, dv, [&](int i, int e) { return sdW[i * WIDE_LD + e]; }, [&](int e, int d) { return Hm(d, e); },
-                As, Bs, tid, acc, m0, n0, on);
+                As, Bs, tid, acc);
         each(C, dk, [&](int i, int d, int x, int y) { sdKw[i * WIDE_LD + d] = add ? 0.f : -acc[x][y]; });
         wide_mm(C, dk, dv, [&](int i, int e) { return sW[i * WIDE_LD + e]; }, [&](int e, int d) { return dH(d, e); },
-                As, Bs, tid, acc, m0, n0, on);
+                As, Bs, tid, acc);
         each(C, dk, [&](int i, int d, int x, int y) { sdKt[i * WIDE_LD + d] = acc[x][y]; });
-        wide_mm(C, C, dv, dO, [&](int e, int j) { return sW[j * WIDE_LD + e]; }, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, C, dv, dO, [&](int e, int j) { return sW[j * WIDE_LD + e]; }, As, Bs, tid, acc);
         each(C, C, [&](int i, int j, int x, int y) { sdP[i * C + j] = i >= j ? acc[x][y] : 0.f; });
         __syncthreads();
         // ---- dV' = Tm^T dW, dK' = Tm^T dKw
         wide_mm(C, dv, C, [&](int i, int j) { return Tmm(j, i); }, [&](int j, int e) { return sdW[j * WIDE_LD + e]; },
-                As, Bs, tid, acc, m0, n0, on);
+                As, Bs, tid, acc);
         each(C, dv, [&](int i, int e, int x, int y) { sdVp[i * WIDE_LD + e] = acc[x][y]; });
         wide_mm(C, dk, C, [&](int i, int j) { return Tmm(j, i); }, [&](int j, int d) { return sdKw[j * WIDE_LD + d]; },
-                As, Bs, tid, acc, m0, n0, on);
+                As, Bs, tid, acc);
         each(C, dk, [&](int i, int d, int x, int y) { sdKp[i * WIDE_LD + d] = add ? 0.f : acc[x][y]; });
         __syncthreads();
         // ---- dL = -(dV' U^T + dK' Kw^T) = -dV' U^T + dK' (-Kw)^T, strictly lower
         wide_mm(C, C, dv, [&](int i, int e) { return sdVp[i * WIDE_LD + e]; }, [&](int e, int j) { return Um(j, e); },
-                As, Bs, tid, acc, m0, n0, on);
+                As, Bs, tid, acc);
         wide_mm(C, C, dk, [&](int i, int d) { return sdKp[i * WIDE_LD + d]; }, [&](int d, int j) { return NKm(j, d); },
-                As, Bs, tid, acc2, m0, n0, on);
+                As, Bs, tid, acc2);
         each(C, C, [&](int i, int j, int x, int y) { sdL[i * C + j] = (!add && i > j) ? acc2[x][y] - acc[x][y] : 0.f; });
         __syncthreads();
         // dS + dS^T with dS = diag(beta)(dL o Gam), kept for the dK product
@@ -1121,14 +1129,14 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
         }
         __syncthreads();
         // ---- dQ = diag(e^gam) dO h^T + (dP o Gam) K
-        wide_mm(C, dk, C, [&](int i, int j) { return sdP[i * C + j] * Gm(i, j); }, K, As, Bs, tid, acc, m0, n0, on);
+        wide_mm(C, dk, C, [&](int i, int j) { return sdP[i * C + j] * Gm(i, j); }, K, As, Bs, tid, acc);
         S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
         each(C, dk, [&](int i, int d, int x, int y) {
             if (i < n) dq_out[i * sq + d] = from_f<BF>(eg[i] * sdOh[i * WIDE_LD + d] + acc[x][y]);
         });
         // ---- dK = (dP o Gam)^T Q + diag(e^{gam_n - gam}) dKt + diag(beta e^gam) dK' + (dS + dS^T) K
-        wide_mm(C, dk, C, [&](int i, int j) { return sdP[j * C + i] * Gm(j, i); }, Q, As, Bs, tid, acc, m0, n0, on);
-        wide_mm(C, dk, C, [&](int i, int j) { return sT[i * C + j]; }, K, As, Bs, tid, acc2, m0, n0, on);
+        wide_mm(C, dk, C, [&](int i, int j) { return sdP[j * C + i] * Gm(j, i); }, Q, As, Bs, tid, acc);
+        wide_mm(C, dk, C, [&](int i, int j) { return sT[i * C + j]; }, K, As, Bs, tid, acc2);
         S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
         each(C, dk, [&](int i, int d, int x, int y) {
             if (i < n)
