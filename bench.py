@@ -13,7 +13,8 @@ sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
 
-The line also carries "decode_step": the single-token state update on its own
+The line also carries "forward": the inference forward alone at the same
+shape (no context saved), and "decode_step": the single-token state update on its own
 workload (256 sequences x 16 heads x d 56, 1024 consecutive steps, fp32 state
 carried in place, fresh bf16 tokens per step), timed as one captured HIP graph
 of the 1024 launches, with the step kernel's HBM roofline.
@@ -199,6 +200,45 @@ def traffic_summary(fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
+
+
+def forward_bench(gi, to_dev, dev, steps, warmup):
+    """The inference forward at the layer shape (workload fwd_model: B=8,
+    H=16, T=4096, d 56, bf16, zero initial state, final state returned, no
+    context saved for a backward)."""
+    import torch
+
+    import gated_delta_rule_74_amd as gdn
+
+    c = gi.CONFIGS["fwd_model"]
+    x = gi.gen_config("fwd_model")
+    q, k, v, g, beta, A_log = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "A_log"))
+    o = torch.empty_like(v)
+    hT = torch.empty(c.B, c.H, c.dk, c.dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.fwd_workspace_size(q, v), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        gdn.fwd(q, k, v, g, beta, A_log, None, o=o, hT=hT, workspace=ws, save_context=False)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nch = c.B * c.H * ((c.T + C - 1) // C)
+    d = c.dk
+    flops = nch * (10 * C * C * d + 6 * C * d * d + C ** 3 / 3)
+    nbytes = c.B * c.T * c.H * (4 * 2 * d + 8) + c.B * c.H * d * d * 4  # q,k,v in, o out, g,beta; hT
+    return {"workload": "fwd_model", "B": c.B, "H": c.H, "T": c.T, "d_k": c.dk, "d_v": c.dv,
+            "ms": round(ms, 4), "tokens_per_s": c.B * c.T / (ms * 1e-3),
+            "hbm_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "flops": flops, "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
 
 
 def decode_bytes_per_step(N, H, dk, dv):
@@ -472,6 +512,7 @@ def main():
         "wall_s_timed": round(wall_s, 3),
         "cpu_baseline": None,
     }
+    out["forward"] = forward_bench(gi, to_dev, dev, args.steps, args.warmup)
     if not args.no_decode:
         out["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:

@@ -88,3 +88,42 @@ def test_decode_chain_matches_forward():
                            tr(f64(x["beta"])), f64(x["A_log"]), f64(x["h0"]))
     assert_close("o chain vs forward", tr(np.stack(got_o)), ro, TOL["bf16"])
     assert_close("state chain vs forward", got_h, rh, TOL["bf16"])
+
+
+def test_decode_graph_replay():
+    """The decode chain captured in a HIP graph (the way bench.py times it)
+    gives the eager result bit for bit on every replay, with eager work and
+    synchronisations between the replays."""
+    say("step graph replay N16 H4 d56, 12 steps")
+    S = 12
+    x = gi.gen_decode(16, 4, 56, 56, S, "bf16", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0 = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    o = torch.empty(16, 4, 56, dtype=torch.bfloat16, device=q.device)
+
+    def chain(h, out):
+        for t in range(S):
+            gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, h, o=out)
+
+    h = h0.clone()
+    chain(h, o)
+    torch.cuda.synchronize()
+    ref_h, ref_o = h.clone(), o.clone()
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain(h, o)
+    for rep in range(3):
+        h.copy_(h0)
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref_h), f"state differs on replay {rep}"
+        assert torch.equal(o, ref_o), f"output differs on replay {rep}"
+        # eager work of the program between replays
+        h2, o2 = h0.clone(), torch.empty_like(o)
+        chain(h2, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(h2, ref_h)
