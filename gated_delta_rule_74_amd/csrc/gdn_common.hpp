@@ -373,8 +373,8 @@ constexpr int LDF = C + 4; // row stride of fp32 C x C matrices
 // L[i+1..15][i] are one row of Lt, read two steps ahead so the LDS latency
 // overlaps the updates. Off-diagonal blocks by block forward substitution
 //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj
-// level by level (i - j = 1, 2, 3) with fp32 MFMA; waves 0..3 do the work.
-// xs: 4 x 16 x 17 floats. Tb ([C][ldt]) receives T in the operand type as
+// level by level (i - j = 1, 2, 3) with fp32 MFMA; waves 0..3 do the work,
+// one barrier per level. xs: 4 x 16 x 17 floats, one 16 x 17 tile per wave. Tb ([C][ldt]) receives T in the operand type as
 // its blocks are produced, zeros above the block diagonal.
 // Ends with a barrier.
 template <bool BF>
@@ -441,7 +441,11 @@ __device__ __forceinline__ void tri_inverse(float *LT, float *xs, int wave, int 
 #pragma unroll
             for (int e = 0; e < 4; ++e) X[(4 * kq + e) * 17 + r] = acc[e];
         }
-        __syncthreads();
+        // X is this wave's own: its LDS writes are ordered before the reads
+        // below without a workgroup barrier
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (bi < 4) {
             f32x4 acc = zero4();
 #pragma unroll

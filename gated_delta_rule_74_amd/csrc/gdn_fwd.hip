@@ -99,14 +99,22 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = (size_t)b * T + t0;
 
+    // wave 0 requests the gates first, so the decay scan waits for them only
+    // while the key and value rows are still in flight
+    float gr = 0.f, br = 0.f, alg = 0.f;
+    if (wave == 0) {
+        gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
+        alg = s.A_log[h];
+    }
     ChunkFrag<BF, D> fk, fv;
     fk.template fetch<VEC>((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
     fv.template fetch<VEC>((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
     if (wave == 0) {
-        const float gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
-        const float br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
+        // first use of the gates here, after the row loads are issued
+        asm volatile("" : "+v"(gr), "+v"(br), "+v"(alg));
         const float g = lane < n ? gr : 0.f, be = lane < n ? br : 0.f;
-        const Decay dc = decay_lane(g, -exp((double)s.A_log[h]) * LOG2E, lane);
+        const Decay dc = decay_lane(g, -exp((double)alg) * LOG2E, lane);
         gam2[lane] = dc.gam2;
         if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
         bet[lane] = be;
