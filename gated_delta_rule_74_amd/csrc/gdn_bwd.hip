@@ -1219,10 +1219,12 @@ __global__ __launch_bounds__(NTHR) void dA_reduce_kernel(const float *__restrict
 
 // --------------------------------------------------------------- launch
 
-static int chain_vblock(bool, int D) { return D >= 64 ? 32 : 16; }
+// value columns per workgroup of the reverse serial pass (16 for 128-wide
+// heads: more workgroups share the chain, each carrying half the gradient)
+static int chain_vblock(bool, int D) { return D == 64 ? 32 : 16; }
 
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
-    constexpr int BV = D >= 64 ? 32 : 16;
+    constexpr int BV = D == 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
     if constexpr (BF && D <= 64) {
         const dim3 block(64 * (BV / 16 + BWS_HELPERS));

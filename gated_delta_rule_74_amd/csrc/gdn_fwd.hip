@@ -691,7 +691,10 @@ int pad_dim(int d, bool bf16) {
     return D;
 }
 
-int fwd_vblock(int D) { return D >= 64 ? 32 : 16; }
+// value columns per workgroup of the generic serial pass; 128-wide heads take
+// 16 so that twice as many workgroups share the chain (each carries half the
+// state), which measured faster on the long-context shape (16 heads)
+int fwd_vblock(int D) { return D == 64 ? 32 : 16; }
 
 bool fwd_segmentable(bool bf16, int D) { return bf16 && (D == 32 || D == 64); }
 
@@ -715,7 +718,7 @@ template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a, hipStrea
 }
 
 template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
-    constexpr int BV = D >= 64 ? 32 : 16;
+    constexpr int BV = D == 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
