@@ -1159,24 +1159,45 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
             __syncthreads();
         }
         const float hds = red[0];
-        // ---- dbeta and dgam per row (wave 0, lane = row), then dg and dA_log
+        // ---- dbeta and dgam per row. Every thread sums one eighth of a row
+        // (row-contiguous reads of the scratch; the column sums of the C x C
+        // term read along rows too), the eighths meet in LDS (As is free after
+        // the last product) and wave 0 adds them in group order.
+        {
+            const int i = tid >> 3, gq = tid & 7;
+            float qa = 0.f, qb = 0.f, qc = 0.f, qd = 0.f, qe = 0.f, qf = 0.f, qg = 0.f;
+            for (int e = gq * 16; e < min(dv, gq * 16 + 16); ++e) qa += V(i, e) * sdVp[i * WIDE_LD + e];
+            for (int d = gq * 16; d < min(dk, gq * 16 + 16); ++d) {
+                qb += K(i, d) * sdKp[i * WIDE_LD + d];
+                qc += Q(i, d) * sdOh[i * WIDE_LD + d];
+                qd += K(i, d) * sdKt[i * WIDE_LD + d];
+            }
+            // Z = dP o P + diag(beta) (dL o (K K^T o Gam)): row sums minus column sums
+            for (int j = gq * 8; j < gq * 8 + 8; ++j) {
+                const float lk = sdL[i * C + j] * sKG[i * C + j];
+                qe += lk;
+                qf += sdP[i * C + j] * sP[i * C + j] + bet[i] * lk;
+                qg += sdP[j * C + i] * sP[j * C + i] + bet[j] * sdL[j * C + i] * sKG[j * C + i];
+            }
+            float *pq = As; // [7][C][8]
+            const float qv[7] = {qa, qb, qc, qd, qe, qf, qg};
+#pragma unroll
+            for (int u = 0; u < 7; ++u) pq[(u * C + i) * 8 + gq] = qv[u];
+        }
+        __syncthreads();
         if (wave == 0) {
             const int i = lane;
-            float db = 0.f, dgm = 0.f, sj = 0.f, kdk = 0.f;
-            for (int e = 0; e < dv; ++e) db += V(i, e) * sdVp[i * WIDE_LD + e];
-            for (int d = 0; d < dk; ++d) {
-                kdk += K(i, d) * sdKp[i * WIDE_LD + d];
-                dgm += Q(i, d) * sdOh[i * WIDE_LD + d];
-                sj += K(i, d) * sdKt[i * WIDE_LD + d];
+            const float *pq = As;
+            float t[7];
+#pragma unroll
+            for (int u = 0; u < 7; ++u) {
+                t[u] = 0.f;
+                for (int gq = 0; gq < 8; ++gq) t[u] += pq[(u * C + i) * 8 + gq];
             }
-            db += eg[i] * kdk;
-            dgm = eg[i] * dgm + bet[i] * eg[i] * kdk;
-            sj *= egn[i];
-            for (int j = 0; j < C; ++j) {
-                db += sdL[i * C + j] * sKG[i * C + j];
-                dgm += sdP[i * C + j] * sP[i * C + j] - sdP[j * C + i] * sP[j * C + i];
-                dgm += bet[i] * sdL[i * C + j] * sKG[i * C + j] - bet[j] * sdL[j * C + i] * sKG[j * C + i];
-            }
+            const float kdk = t[1];
+            const float db = t[0] + eg[i] * kdk + t[4];
+            float dgm = eg[i] * t[2] + bet[i] * eg[i] * kdk + t[5] - t[6];
+            const float sj = egn[i] * t[3];
             const float stot = wave_sum(sj);
             dgm -= sj;
             if (i == C - 1) dgm += eglast * hds + stot;
