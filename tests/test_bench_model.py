@@ -1,0 +1,51 @@
+"""The roofline accounting bench.py reports: algorithmic FLOPs and HBM bytes
+of the measured workloads, checked against figures derived by hand from the
+operation's inputs and outputs (no GPU needed)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_fwdbwd_model_flops_and_bytes():
+    # B8 H16 T4096 d56, chunk 64: 8192 chunk-heads; per chunk-head
+    # fwd 10 C^2 d + 6 C d^2 + C^3 / 3, bwd 20 C^2 d + 12 C d^2 + 4 C^3
+    flops, nbytes = bench.step_model(8, 4096, 16, 56)
+    assert flops == pytest.approx(95.27e9, rel=1e-3)
+    # read q, k, v, do (bf16), g, beta; write o, dq, dk, dv (bf16), dg, dbeta;
+    # h0 and dh0 / hT states fp32, dA_log
+    assert nbytes == pytest.approx(664.93e6, rel=1e-4)
+
+
+def test_per_kernel_bytes_sum_to_the_step():
+    per = bench.kernel_bytes_per_token_head(56)
+    th = 8 * 4096 * 16
+    states = 8 * 16 * 56 * 56 * 4
+    total = sum(per.values()) * th
+    # every tensor of the step is counted by exactly one kernel except k and g
+    # (read by both forward kernels) and q, k, do and g (read by both backward
+    # kernels); the states and dA_log belong to no per-token figure
+    e = 2 * 56
+    double_counted = th * ((e + 4) + (3 * e + 4))
+    _, step_bytes = bench.step_model(8, 4096, 16, 56)
+    assert total - double_counted == step_bytes - 4 * states - 16 * 4
+
+
+def test_decode_step_bytes():
+    # 256 x 16 states of 56 x 56 fp32 read and written, bf16 q, k, v in, o out,
+    # fp32 g and beta in
+    assert bench.decode_bytes_per_step(256, 16, 56, 56) == 104_628_224
+    assert bench.decode_bytes_per_step(256, 16, 56, 56) == pytest.approx(104.63e6, rel=1e-4)
+
+
+def test_multi_gpu_request_is_refused(capsys, monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
