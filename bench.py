@@ -28,6 +28,8 @@ Profiling aids (the counter runs behind the committed traffic summaries):
                                          (FETCH_SIZE, then WRITE_SIZE) of the
                                          above into per-kernel HBM traffic,
                                          written to profiles/
+    python bench.py --mfma-summary DIR   per-kernel MFMA busy % and flops from
+                                         one --pmc run of MFMA_COUNTERS
 """
 import argparse
 import hashlib
@@ -328,6 +330,68 @@ def decode_bench(dev, n_sets_cold=6):
             "dtype": "bf16 tokens, fp32 state", "hot": hot, "cold": cold}
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE"
+SIMD_NUM = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+XCD_NUM = 8         # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
+
+
+def mfma_summary(counter_dir):
+    """MFMA use per kernel from one rocprofv3 --pmc run of the counters in
+    MFMA_COUNTERS over `bench.py --profile-run N`: busy % = MFMA busy cycles
+    summed over SIMDs / (active cycles of one XCD x SIMDs); MFMA flops =
+    MFMA ops x 512 (the counters count ops in units of 512); TFLOP/s over the
+    dispatch's own start and end timestamps; all averaged over launches."""
+    import collections
+    import csv
+    import glob
+
+    per = collections.defaultdict(dict)
+    name = {}
+    for f in glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                d = r["Dispatch_Id"]
+                per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                per[d]["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                name[d] = r["Kernel_Name"]
+    nch = 8 * 16 * 64
+    d = 56
+    alg = {"fwd_prep": nch * (4 * C * C * d + C ** 3 / 3) / 4,  # K K^T, U, Kw, inverse; 4 launches
+           "fwd_chain": nch * (6 * C * C * d + 6 * C * d * d) / 4,
+           "bwd_chain": nch * (2 * C * C * d + 6 * C * d * d),
+           "bwd_local": nch * (18 * C * C * d + 6 * C * d * d + 4 * C ** 3)}
+    lines = [
+        f"# MFMA use per launch, workload {WORKLOAD} (B=8, H=16, T=4096, d=56, bf16), one MI355X",
+        "#",
+        "# command (from /tmp on the GPU host, TMPDIR=/tmp):",
+        f"#   rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d <dir> -o p -- python3 <repo>/bench.py --profile-run 2",
+        "#   python3 <repo>/bench.py --mfma-summary <dir>   (writes this file)",
+        "#",
+        f"# busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCD_NUM} XCDs x {SIMD_NUM} SIMDs);",
+        "# MFMA flops = (MOPS_BF16 + MOPS_F32) x 512, which counts the padding of d = 56 to 64 and the",
+        "# masked halves of the 64 x 64 products; TFLOP/s over each dispatch's own duration (profiled);",
+        "# algorithmic flops = the chunk-form count of the kernel's products per launch.",
+        f"# source_hash {source_hash()}",
+        "",
+        f"{'kernel':12s} {'launches':>8s} {'busy %':>7s} {'bf16 GFLOP':>11s} {'fp32 GFLOP':>11s} {'alg. GFLOP':>11s}"
+        f" {'us':>8s} {'MFMA TFLOP/s':>13s}",
+    ]
+    for k in KERNELS:
+        ds = [x for x in per if f"gdn::{k}" in name[x]]
+        if not ds:
+            continue
+        mean = lambda key: sum(per[x].get(key, 0.0) for x in ds) / len(ds)
+        act = mean("GRBM_GUI_ACTIVE") / XCD_NUM
+        util = 100.0 * mean("SQ_VALU_MFMA_BUSY_CYCLES") / (act * SIMD_NUM) if act > 0 else float("nan")
+        fb, ff = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512, mean("SQ_INSTS_VALU_MFMA_MOPS_F32") * 512
+        ns = mean("ns")
+        lines.append(f"{k:12s} {len(ds):8d} {util:7.2f} {fb / 1e9:11.3f} {ff / 1e9:11.3f} {alg.get(k, 0) / 1e9:11.3f}"
+                     f" {ns / 1e3:8.1f} {(fb + ff) / (ns * 1e-9) / 1e12:13.1f}")
+    with open(os.path.join(ROOT, "profiles", f"mfma_{WORKLOAD}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -383,9 +447,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", type=int, default=0, metavar="N")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma-summary", metavar="COUNTER_DIR")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the gated delta rule path here is built and timed "
