@@ -17,7 +17,8 @@ The line also carries "forward": the inference forward alone at the same
 shape (no context saved), and "decode_step": the single-token state update on its own
 workload (256 sequences x 16 heads x d 56, 1024 consecutive steps, fp32 state
 carried in place, fresh bf16 tokens per step), timed as one captured HIP graph
-of the 1024 launches, with the step kernel's HBM roofline.
+of the 1024 launches, with the step kernel's HBM roofline; "mtp3_*" runs the
+same tokens three per call (the state read and written once per 3 tokens).
 
 Profiling aids (the counter runs behind the committed traffic summaries):
     python bench.py --profile-run N      N untimed steps, then one plain
@@ -243,18 +244,20 @@ def forward_bench(gi, to_dev, dev, steps, warmup):
             "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
 
 
-def decode_bytes_per_step(N, H, dk, dv):
-    """Algorithmic HBM bytes of one decode step: the fp32 state read and
-    written once, bf16 q, k, v read and o written, fp32 g and beta read."""
-    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + dv * 2 + 8)
+def decode_bytes_per_step(N, H, dk, dv, S=1):
+    """Algorithmic HBM bytes of one decode call of S tokens: the fp32 state
+    read and written once, bf16 q, k, v read and o written and fp32 g and
+    beta read for every token."""
+    return N * H * (2 * dk * dv * 4 + S * ((2 * dk + dv) * 2 + dv * 2 + 8))
 
 
 def decode_bench(dev, n_sets_cold=6):
     """The decode workload: 1024 consecutive single-token steps of 256
-    sequences x 16 heads from a carried state. Hot: one state set updated in
-    place (51 MB, which the 256 MB Infinity Cache can hold between steps).
-    Cold: n_sets_cold independent state sets served round-robin (> 256 MB),
-    so each step's state comes from HBM."""
+    sequences x 16 heads from a carried state, and the same tokens as 341
+    steps of 3 tokens (a multi-token prediction's draft verified per step).
+    Hot: one state set updated in place (51 MB, which the 256 MB Infinity
+    Cache can hold between steps). Cold: n_sets_cold independent state sets
+    served round-robin (> 256 MB), so each step's state comes from HBM."""
     import numpy as np
     import torch
 
@@ -262,8 +265,8 @@ def decode_bench(dev, n_sets_cold=6):
     import gdn_inputs as gi
 
     cfg = gi.CONFIGS["decode_step"]
-    N, H, dk, dv, S = cfg.B, cfg.H, cfg.dk, cfg.dv, cfg.steps
-    x = gi.gen_decode(N, H, dk, dv, S, cfg.dtype, seed=cfg.seed)
+    N, H, dk, dv, T = cfg.B, cfg.H, cfg.dk, cfg.dv, cfg.steps
+    x = gi.gen_decode(N, H, dk, dv, T, cfg.dtype, seed=cfg.seed)
 
     def to_dev(a):
         if isinstance(a, gi.Tensor):
@@ -272,14 +275,25 @@ def decode_bench(dev, n_sets_cold=6):
 
     q, k, v, g, beta, A_log, h0 = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "A_log", "h0"))
     del x
-    o = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
 
-    def chain(hs):
-        for t in range(S):
-            h = hs[t % len(hs)]
-            gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, h, o=o)
+    def tokens_of(S):
+        """[steps, N, S, H, *] copies of the first steps * S tokens."""
+        n = T // S
+        grp = lambda t: t[: n * S].reshape(n, S, *t.shape[1:]).transpose(1, 2).contiguous()
+        return n, [grp(t) for t in (q, k, v, g, beta)]
 
-    def run(n_sets):
+    def run(n_sets, S):
+        n_steps, (qs, ks, vs, gs, bs) = tokens_of(S) if S > 1 else (T, (q, k, v, g, beta))
+        o = torch.empty((N, S, H, dv) if S > 1 else (N, H, dv), dtype=q.dtype, device=dev)
+
+        def chain(hs):
+            for t in range(n_steps):
+                h = hs[t % len(hs)]
+                if S > 1:
+                    gdn.step_tokens(qs[t], ks[t], vs[t], gs[t], bs[t], A_log, h, h, o=o)
+                else:
+                    gdn.step(qs[t], ks[t], vs[t], gs[t], bs[t], A_log, h, h, o=o)
+
         hs = [h0.clone() for _ in range(n_sets)]
         # eager reference of one pass, then the same pass as one graph replay
         chain(hs)
@@ -310,24 +324,25 @@ def decode_bench(dev, n_sets_cold=6):
         e1.record()
         torch.cuda.synchronize()
         total_ms = e0.elapsed_time(e1)
-        # the kernel's duration is taken as the whole chain's time per step
+        # the kernel's duration is taken as the whole chain's time per call
         # (gaps between the graph's launches included, so an upper bound):
         # events around each ~20 us launch would add their own overhead
-        kern_ms = total_ms / S
-        nbytes = decode_bytes_per_step(N, H, dk, dv)
+        kern_ms = total_ms / n_steps
+        nbytes = decode_bytes_per_step(N, H, dk, dv, S)
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
-        return {"state_sets": n_sets, "graph": graph is not None,
-                "us_per_step": round(total_ms * 1e3 / S, 3),
-                "tokens_per_s": N * S / (total_ms * 1e-3),
+        return {"state_sets": n_sets, "tokens_per_call": S, "graph": graph is not None,
+                "us_per_step": round(total_ms * 1e3 / n_steps, 3),
+                "tokens_per_s": N * n_steps * S / (total_ms * 1e-3),
                 "roofline": {"bound": "hbm", "kernel": "gdn_step", "achieved": round(achieved, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                              "bytes_per_launch": nbytes, "avg_launch_ms": round(kern_ms, 5),
-                             "timing": "graph of 1024 launches, per step"}}
+                             "timing": f"graph of {n_steps} launches, per launch"}}
 
-    hot = run(1)
-    cold = run(n_sets_cold)
-    return {"workload": "decode_step", "sequences": N, "heads": H, "d_k": dk, "d_v": dv, "steps": S,
-            "dtype": "bf16 tokens, fp32 state", "hot": hot, "cold": cold}
+    out = {"workload": "decode_step", "sequences": N, "heads": H, "d_k": dk, "d_v": dv, "steps": T,
+           "dtype": "bf16 tokens, fp32 state", "hot": run(1, 1), "cold": run(n_sets_cold, 1)}
+    out["mtp3_hot"] = run(1, 3)
+    out["mtp3_cold"] = run(n_sets_cold, 3)
+    return out
 
 
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE"

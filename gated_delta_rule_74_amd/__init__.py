@@ -9,6 +9,7 @@ calls raise.
     o, hT, ctx = fwd(q, k, v, g, beta, A_log, h0=None, save_context=True)
     grads      = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, context=ctx)
     o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
+    o, h      = step_tokens(q, k, v, g, beta, A_log, h_in)     # [N, S, H, *] tokens
     o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0)
 """
 from __future__ import annotations
@@ -18,13 +19,13 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "step", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
+__all__ = ["fwd", "bwd", "step", "step_tokens", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
            "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size",
            "LaunchTimer"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
+EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_step_tokens", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
            "gdn_fwd_context_size", "gdn_time_launches", "gdn_launch_kind", "gdn_status_string",
            "gdn_last_error_detail"]
 
@@ -59,7 +60,8 @@ def lib():
         L.gdn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         L.gdn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
-        for f in (L.gdn_fwd, L.gdn_bwd, L.gdn_step):
+        L.gdn_step_tokens.argtypes = [I32, I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
+        for f in (L.gdn_fwd, L.gdn_bwd, L.gdn_step, L.gdn_step_tokens):
             f.restype = ctypes.c_int
         for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_fwd_context_size):
             f.argtypes = [S]
@@ -258,6 +260,36 @@ def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=No
                         _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out), _p(o),
                         _stream(dev))
     _check("gdn_step", st)
+    return o, h_out
+
+
+def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=None):
+    """S consecutive decode tokens per sequence from a carried state (e.g. the
+    draft tokens of a multi-token prediction). q, k [N,S,H,dk]; v [N,S,H,dv];
+    g, beta [N,S,H]; h_in [N,H,dk,dv] fp32 or None; h_out may be h_in.
+    Returns (o [N,S,H,dv], h_out)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [N, S, H, dk]")
+    N, S, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype, (N, S, H, dk))
+    _need(k, "k", q.dtype, (N, S, H, dk), dev)
+    _need(v, "v", q.dtype, (N, S, H, dv), dev)
+    _need(g, "g", torch.float32, (N, S, H), dev)
+    _need(beta, "beta", torch.float32, (N, S, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    _need(h_in, "h_in", torch.float32, (N, H, dk, dv), dev)
+    if h_out is None:
+        h_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(h_out, "h_out", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, S, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, S, H, dv), dev)
+    st = lib().gdn_step_tokens(N, S, H, dk, dv, _dtype_code(q), GDN_FLAG_ADDITIVE if additive else 0,
+                               _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out),
+                               _p(o), _stream(dev))
+    _check("gdn_step_tokens", st)
     return o, h_out
 
 

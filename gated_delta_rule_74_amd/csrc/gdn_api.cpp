@@ -454,24 +454,26 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     return hip_status(he, "gdn_bwd dA_log launch");
 }
 
-gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
-                      const void *q, const void *k, const void *v, const float *g, const float *beta,
-                      const float *A_log, const float *h_in, float *h_out, void *o, void *stream) {
-    if (N < 1 || H < 1) return fail(GDN_EINVAL, "N and H must be >= 1");
+gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
+                             uint32_t flags, const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *A_log, const float *h_in, float *h_out, void *o,
+                             void *stream) {
+    if (N < 1 || H < 1 || S < 1) return fail(GDN_EINVAL, "N, S and H must be >= 1");
     if (dk < 1 || dv < 1 || dk > 128 || dv > 128) return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", dtype);
     if (flags & ~GDN_FLAG_ADDITIVE) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
-    if ((double)N * H * dk * dv >= 2147483648.0) return fail(GDN_EINVAL, "state too large");
+    if ((double)N * H * dk * dv >= 2147483648.0 || (double)N * S * H * (dk > dv ? dk : dv) >= 2147483648.0)
+        return fail(GDN_EINVAL, "state or tokens too large");
     if (!q || !k || !v || !g || !beta || !A_log || !h_out || !o)
         return fail(GDN_EINVAL, "a required pointer is NULL");
     const void *all[] = {q, k, v, o, g, beta, A_log, h_in, h_out};
     for (const void *p : all)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "pointers must be 4-byte aligned");
-    const size_t e = esize(dtype), NH = (size_t)N * H, sb = NH * dk * dv * 4;
-    const Range in[] = {{q, NH * dk * e, "q"},        {k, NH * dk * e, "k"},     {v, NH * dv * e, "v"},
-                        {g, NH * 4, "g"},             {beta, NH * 4, "beta"},    {A_log, (size_t)H * 4, "A_log"},
+    const size_t e = esize(dtype), NSH = (size_t)N * S * H, sb = (size_t)N * H * dk * dv * 4;
+    const Range in[] = {{q, NSH * dk * e, "q"},        {k, NSH * dk * e, "k"},     {v, NSH * dv * e, "v"},
+                        {g, NSH * 4, "g"},             {beta, NSH * 4, "beta"},    {A_log, (size_t)H * 4, "A_log"},
                         {h_in == h_out ? nullptr : h_in, sb, "h_in"}};
-    const Range out[] = {{h_out, sb, "h_out"}, {o, NH * dv * e, "o"}};
+    const Range out[] = {{h_out, sb, "h_out"}, {o, NSH * dv * e, "o"}};
     gdn_status_t st = check_aliasing(in, 7, out, 2);
     if (st != GDN_OK) return st;
     if (h_in && h_in != h_out && overlap(Range{h_in, sb, "h_in"}, Range{h_out, sb, "h_out"}))
@@ -491,8 +493,15 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
     a.dk = dk;
     a.dv = dv;
     a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
+    a.S = S;
     return hip_status(timed(K_STEP, [&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
                       "gdn_step launch");
+}
+
+gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
+                      const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *A_log, const float *h_in, float *h_out, void *o, void *stream) {
+    return gdn_step_tokens(N, 1, H, dk, dv, dtype, flags, q, k, v, g, beta, A_log, h_in, h_out, o, stream);
 }
 
 } // extern "C"

@@ -70,6 +70,7 @@ struct StepArgs {
     float *h_out;
     void *o;
     int N, H, dk, dv, additive;
+    int S; // tokens per sequence; q, k, v, o, g, beta are [N, S, H, *]
 };
 
 // 16-byte vector loads are possible when every row of q/k/v (and of the

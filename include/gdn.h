@@ -28,7 +28,7 @@
  *   A_log, dA_log       [H]             fp32
  *   h0, hT, dhT, dh0    [B, H, dk, dv]  fp32 (row i = key index)
  *   decode (gdn_step):  q,k [N,H,dk], v,o [N,H,dv], g,beta [N,H],
- *                       states [N,H,dk,dv]
+ *                       states [N,H,dk,dv]; gdn_step_tokens: [N,S,H,*]
  * bf16 outputs are rounded to nearest even. The library applies no scaling
  * to q and no normalisation to k.
  *
@@ -140,6 +140,22 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
                       const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const float *A_log, const float *h_in, float *h_out,
                       void *o, void *stream);
+
+/* S consecutive decode tokens for each of N independent sequences from a
+ * carried state: the recurrence applied token after token (the serial
+ * definition of "GDN & MLA Mechanism Deep-Dive", Step 4), as when the draft
+ * tokens of a multi-token prediction are verified ("HyMo-434M documentation
+ * portal", 04 MTP SPECULATION: a depth-2 draft, three tokens accepted per
+ * step). q, k are
+ * [N,S,H,dk], v, o [N,S,H,dv], g, beta [N,S,H] (the forward's layouts with
+ * B = N, T = S); the states are [N,H,dk,dv]. The state is read once and
+ * written once per call (heads up to 64 wide keep it on chip between the
+ * tokens). h_in may be NULL (zero state) or equal h_out; S >= 1. gdn_step is
+ * this call with S = 1 and the [N,H,*] layouts. */
+gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
+                             uint32_t flags, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *A_log,
+                             const float *h_in, float *h_out, void *o, void *stream);
 
 /* Timing aid for benchmarks (no effect on results). While `events` is
  * non-NULL, every kernel the library launches from this thread is bracketed

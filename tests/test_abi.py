@@ -134,6 +134,22 @@ def test_step_validation(L):
     assert L.gdn_step(4, 16, 56, 56, 1, 0, *bad, None) == EINVAL
 
 
+def test_step_tokens_validation(L):
+    P = fake
+    ok = (P(1), P(2), P(3), P(4), P(5), P(6), None, P(7), P(8))
+    assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *ok, None) == EINVAL  # S < 1
+    assert L.gdn_step_tokens(0, 3, 16, 56, 56, 1, 0, *ok, None) == EINVAL
+    assert L.gdn_step_tokens(4, 3, 16, 56, 129, 1, 0, *ok, None) == EINVAL
+    assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 2, *ok, None) == EINVAL
+    bad = list(ok)
+    bad[8] = P(3)  # o aliases v
+    assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 0, *bad, None) == EINVAL
+    # o of S tokens runs into h_out when placed S - 1 token rows below it
+    bad = list(ok)
+    bad[8] = ctypes.c_void_p(P(7).value - 2 * 4 * 16 * 56)
+    assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 0, *bad, None) == EINVAL
+
+
 def test_product_path_has_no_cpu_fallback():
     """The binding must not reach the oracle or any host implementation."""
     src = open(os.path.join(ROOT, "gated_delta_rule_74_amd", "__init__.py")).read()

@@ -127,3 +127,54 @@ def test_decode_graph_replay():
         chain(h2, o2)
         torch.cuda.synchronize()
         assert torch.equal(h2, ref_h)
+
+
+def check_tokens(N, S, H, dk, dv, dtype, decay="weak", additive=False, inplace=True, zero_start=False,
+                 seed=7413):
+    """step_tokens over S tokens per sequence against the oracle's serial
+    forward over the same S tokens from the same state."""
+    x = gi.gen_seq(N, S, H, dk, dv, dtype, seed=seed, h0="randn", decay=decay)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log = dev(x["g"]), dev(x["beta"]), dev(x["A_log"])
+    h = None if zero_start else dev(x["h0"]).clone()
+    o, hN = gdn.step_tokens(q, k, v, g, beta, A_log, h, h if (inplace and h is not None) else None,
+                            additive=additive)
+    torch.cuda.synchronize()
+    ro, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                           f64(x["A_log"]), None if zero_start else f64(x["h0"]), delta=not additive)
+    tol = TOL[dtype]
+    assert_close(f"o of {S} tokens", host(o), ro, tol)
+    assert_close(f"state after {S} tokens", host(hN), rh, tol)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5])
+@pytest.mark.parametrize("decay", ["normal", "weak"])
+def test_step_tokens_bf16(S, decay):
+    say(f"step_tokens bf16 N32 H16 d56 S={S} decay={decay}")
+    check_tokens(32, S, 16, 56, 56, "bf16", decay=decay)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (100, 70), (5, 3)])
+def test_step_tokens_head_dims(dk, dv):
+    """Wide heads (state read and written per token) and narrow ones."""
+    say(f"step_tokens bf16 dk={dk} dv={dv} S=3")
+    check_tokens(4, 3, 2, dk, dv, "bf16")
+
+
+def test_step_tokens_fp32_additive_zero_start_out_of_place():
+    check_tokens(4, 4, 3, 16, 16, "f32", inplace=False)
+    check_tokens(4, 3, 3, 56, 56, "bf16", additive=True)
+    check_tokens(4, 3, 3, 56, 56, "bf16", zero_start=True)
+    check_tokens(4, 3, 2, 128, 128, "bf16", zero_start=True)
+
+
+def test_step_tokens_one_token_equals_step():
+    """S = 1 is gdn_step: the same outputs bit for bit."""
+    x = gi.gen_decode(8, 4, 56, 56, 1, "bf16", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0 = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    o1, h1 = gdn.step(q[0], k[0], v[0], g[0], beta[0], A_log, h0, None)
+    o2, h2 = gdn.step_tokens(q[0][:, None], k[0][:, None], v[0][:, None], g[0][:, None],
+                             beta[0][:, None], A_log, h0, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(h1, h2)
