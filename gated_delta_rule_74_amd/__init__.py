@@ -31,6 +31,7 @@ EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_step_tokens", "gdn_fwd_workspa
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_ADDITIVE = 1
+GDN_FLAG_GATE_LOGITS = 2
 _lib = None
 
 
@@ -116,9 +117,13 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _shape(q, v, additive):
+def _flags(additive, gate_logits):
+    return (GDN_FLAG_ADDITIVE if additive else 0) | (GDN_FLAG_GATE_LOGITS if gate_logits else 0)
+
+
+def _shape(q, v, additive, gate_logits=False):
     B, T, H, dk = q.shape
-    return Shape(B, T, H, dk, v.shape[-1], _dtype_code(q), 64, GDN_FLAG_ADDITIVE if additive else 0)
+    return Shape(B, T, H, dk, v.shape[-1], _dtype_code(q), 64, _flags(additive, gate_logits))
 
 
 def _check_seq(q, k, v, g, beta, A_log, h0=None):
@@ -167,12 +172,13 @@ def bwd_workspace_size(q, v, additive=False):
     return int(lib().gdn_bwd_workspace_size(ctypes.byref(s)))
 
 
-def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_context=False,
+def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, save_context=False,
         want_hT=True, o=None, hT=None, context=None, workspace=None):
     """Chunked forward. Returns (o, hT or None, context or None); the context
-    (a byte tensor) lets bwd() skip recomputing the forward."""
+    (a byte tensor) lets bwd() skip recomputing the forward. gate_logits: g
+    and beta are logits (the kernels apply the sigmoid)."""
     B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
-    s = _shape(q, v, additive)
+    s = _shape(q, v, additive, gate_logits)
     dev = q.device
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
@@ -196,15 +202,16 @@ def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, save_context=False,
 
 
 def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additive=False,
-        want_dh0=True, want_hT=False, workspace=None, out=None):
+        gate_logits=False, want_dh0=True, want_hT=False, workspace=None, out=None):
     """Backward of sum(do * o) + sum(dhT * hT). Returns a dict with dq, dk,
-    dv, dg, dbeta, dA_log, dh0 (or None) and hT (when want_hT)."""
+    dv, dg, dbeta, dA_log, dh0 (or None) and hT (when want_hT); with
+    gate_logits, dg and dbeta are with respect to the logits."""
     B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
     dev = q.device
     _need(do, "do", q.dtype, (B, T, H, dv), dev)
     _need(dhT, "dhT", torch.float32, (B, H, dk, dv), dev)
     _need(context, "context", torch.uint8, None, dev)
-    s = _shape(q, v, additive)
+    s = _shape(q, v, additive, gate_logits)
     L = lib()
     if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
         raise ValueError("context is smaller than gdn_fwd_context_size()")
@@ -234,7 +241,7 @@ def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additiv
     return r
 
 
-def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=None):
+def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate_logits=False, o=None):
     """One decode token per sequence. q, k [N,H,dk]; v [N,H,dv]; g, beta
     [N,H]; h_in [N,H,dk,dv] fp32 or None. h_out may be h_in (in place).
     Returns (o, h_out)."""
@@ -256,14 +263,15 @@ def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=No
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (N, H, dv), dev)
-    st = lib().gdn_step(N, H, dk, dv, _dtype_code(q), GDN_FLAG_ADDITIVE if additive else 0, _p(q),
+    st = lib().gdn_step(N, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits), _p(q),
                         _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out), _p(o),
                         _stream(dev))
     _check("gdn_step", st)
     return o, h_out
 
 
-def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, o=None):
+def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate_logits=False,
+                o=None):
     """S consecutive decode tokens per sequence from a carried state (e.g. the
     draft tokens of a multi-token prediction). q, k [N,S,H,dk]; v [N,S,H,dv];
     g, beta [N,S,H]; h_in [N,H,dk,dv] fp32 or None; h_out may be h_in.
@@ -286,7 +294,7 @@ def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=Fals
     if o is None:
         o = torch.empty((N, S, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (N, S, H, dv), dev)
-    st = lib().gdn_step_tokens(N, S, H, dk, dv, _dtype_code(q), GDN_FLAG_ADDITIVE if additive else 0,
+    st = lib().gdn_step_tokens(N, S, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits),
                                _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out),
                                _p(o), _stream(dev))
     _check("gdn_step_tokens", st)

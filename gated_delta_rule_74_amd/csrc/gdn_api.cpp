@@ -64,7 +64,8 @@ gdn_status_t check_shape(const gdn_shape_t *s) {
         return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", s->dtype);
     if (s->chunk != 0 && s->chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 0 or 64");
-    if (s->flags & ~GDN_FLAG_ADDITIVE) return fail(GDN_EINVAL, "unknown flag bits 0x%x", s->flags);
+    if (s->flags & ~(GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS))
+        return fail(GDN_EINVAL, "unknown flag bits 0x%x", s->flags);
     if (s->dtype == GDN_F32 && (s->dk > 64 || s->dv > 64))
         return fail(GDN_EUNSUPPORTED, "fp32 supports dk, dv <= 64");
     const double elems = (double)s->B * s->T * s->H * (s->dk > s->dv ? s->dk : s->dv);
@@ -115,6 +116,7 @@ gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void 
     a.dv = s->dv;
     a.NC = nchunks(s);
     a.additive = (s->flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
+    a.logits = (s->flags & GDN_FLAG_GATE_LOGITS) ? 1 : 0;
     return a;
 }
 
@@ -461,7 +463,7 @@ gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_
     if (N < 1 || H < 1 || S < 1) return fail(GDN_EINVAL, "N, S and H must be >= 1");
     if (dk < 1 || dv < 1 || dk > 128 || dv > 128) return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", dtype);
-    if (flags & ~GDN_FLAG_ADDITIVE) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
+    if (flags & ~(GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS)) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
     if ((double)N * H * dk * dv >= 2147483648.0 || (double)N * S * H * (dk > dv ? dk : dv) >= 2147483648.0)
         return fail(GDN_EINVAL, "state or tokens too large");
     if (!q || !k || !v || !g || !beta || !A_log || !h_out || !o)
@@ -493,6 +495,7 @@ gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_
     a.dk = dk;
     a.dv = dv;
     a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
+    a.logits = (flags & GDN_FLAG_GATE_LOGITS) ? 1 : 0;
     a.S = S;
     return hip_status(timed(K_STEP, [&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
                       "gdn_step launch");

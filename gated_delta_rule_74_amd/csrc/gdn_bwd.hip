@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         wait_vmem();
         // every wave computes the decay of its lane's row: the copy of Q
         // whose row j = lane is scaled by e^{gam_j} while it is stored
-        const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
+        const Decay dc = decay_lane(lane < n ? gate_of(pg, s.logits) : 0.f, A2, lane);
         if (wave == 0) {
             gam2[lane] = dc.gam2;
             egn[lane] = dc.egn;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
     auto stash = [&](int c) {
         const int n = min(C, T - c * C), i3 = c % 3, i2 = c & 1;
         wait_vmem();
-        const Decay dc = decay_lane(lane < n ? pg : 0.f, A2, lane);
+        const Decay dc = decay_lane(lane < n ? gate_of(pg, s.logits) : 0.f, A2, lane);
         if ((hw & 3) == 0) {
             gam_of(i3)[lane] = (float)dc.gam2;
             egn_of(i3)[lane] = dc.egn;
@@ -682,13 +682,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, 4, D>(RQ, LDD, Ks, LDD, sq, wave, lane);
         // while the products run, every wave forms the chunk's decay (lane =
         // row) and keeps a copy of gam of its own; wave 0 publishes the rest
-        const float gl = lane < n ? gr : 0.f;
+        const float gl = lane < n ? gate_of(gr, s.logits) : 0.f;
         const Decay dc = decay_lane(gl, A * LOG2E, lane);
         double *gw = gam + wave * C;
         gw[lane] = dc.gam2;
         if (wave == 0) {
             gch[lane] = gl;
-            bet[lane] = lane < n ? br : 0.f;
+            bet[lane] = lane < n ? gate_of(br, s.logits) : 0.f;
             eg[lane] = dc.eg;
             egn[lane] = dc.egn;
             if (lane == 0) misc[0] = dc.eglast;
@@ -930,8 +930,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             float p = (lane < n) ? gch[lane] * dg : 0.f;
             if (lane < n) {
                 const size_t gi = (row0 + lane) * H + h;
-                a.dg[gi] = dg;
-                a.dbeta[gi] = db;
+                // with logit inputs, through the sigmoid: d/dx = s (1 - s) d/ds
+                const float gs = gch[lane], bs = bet[lane];
+                a.dg[gi] = s.logits ? dg * gs * (1.f - gs) : dg;
+                a.dbeta[gi] = s.logits ? db * bs * (1.f - bs) : db;
             }
             p = wave_sum(p);
             if (lane == 0) a.dA_part[(size_t)bh * s.NC + c] = p;
@@ -1055,12 +1057,12 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
         if (wave == 0) {
             const float gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
             const float br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
-            const float gl = lane < n ? gr : 0.f;
+            const float gl = lane < n ? gate_of(gr, s.logits) : 0.f;
             const Decay dcy = decay_lane(gl, A * LOG2E, lane);
             gam[lane] = dcy.gam2;
             eg[lane] = dcy.eg;
             egn[lane] = dcy.egn;
-            bet[lane] = lane < n ? br : 0.f;
+            bet[lane] = lane < n ? gate_of(br, s.logits) : 0.f;
             gch[lane] = gl;
             if (lane == 0) red[0] = dcy.eglast;
         }
@@ -1207,8 +1209,10 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
             float p = (lane < n) ? gch[lane] * dg : 0.f;
             if (lane < n) {
                 const size_t gi = (row0 + lane) * H + h;
-                a.dg[gi] = dg;
-                a.dbeta[gi] = db;
+                // with logit inputs, through the sigmoid: d/dx = s (1 - s) d/ds
+                const float gs = gch[lane], bs = bet[lane];
+                a.dg[gi] = s.logits ? dg * gs * (1.f - gs) : dg;
+                a.dbeta[gi] = s.logits ? db * bs * (1.f - bs) : db;
             }
             p = wave_sum(p);
             if (lane == 0) a.dA_part[cb] = p;

@@ -329,6 +329,10 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
 // all prefetched registers are needed anyway, it also tells the compiler's
 // wait tracking that no load into them is still outstanding, so later loads
 // into the same registers are not held back behind stores.
+// A gate from its input: the logistic sigmoid of a logit when the inputs are
+// logits, else the input itself.
+__device__ __forceinline__ float gate_of(float x, bool logit) { return logit ? 1.f / (1.f + expf(-x)) : x; }
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float load_row_scalar(const float *__restrict__ p, size_t stride, int lane,

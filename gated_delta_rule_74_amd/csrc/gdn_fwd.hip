@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
     if (wave == 0) {
         // first use of the gates here, after the row loads are issued
         asm volatile("" : "+v"(gr), "+v"(br), "+v"(alg));
-        const float g = lane < n ? gr : 0.f, be = lane < n ? br : 0.f;
+        const float g = lane < n ? gate_of(gr, s.logits) : 0.f, be = lane < n ? gate_of(br, s.logits) : 0.f;
         const Decay dc = decay_lane(g, -exp((double)alg) * LOG2E, lane);
         gam2[lane] = dc.gam2;
         if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
         if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
         fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
-        pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        pg = gate_of(load_row_scalar(s.g + row0 * H + h, H, lane, n), s.logits);
     };
     // O of a chunk is held in registers and written out during the next
     // chunk, after that chunk's inputs have arrived: stores are issued only

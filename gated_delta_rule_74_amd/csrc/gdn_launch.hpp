@@ -12,6 +12,7 @@ struct SeqArgs {
     const float *g, *beta, *A_log, *h0;
     int B, T, H, dk, dv, NC;
     int additive;
+    int logits; // g and beta are logits (sigmoid applied where they are used)
 };
 
 // Per-chunk products that do not depend on the state:
@@ -71,6 +72,7 @@ struct StepArgs {
     void *o;
     int N, H, dk, dv, additive;
     int S; // tokens per sequence; q, k, v, o, g, beta are [N, S, H, *]
+    int logits;
 };
 
 // 16-byte vector loads are possible when every row of q/k/v (and of the

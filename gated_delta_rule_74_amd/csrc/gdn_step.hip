@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         S *o = (S *)a.o + tok * dv;
         const float *src = t == 0 ? hin : hout; // state before this token (not KEEP)
 
-        const float alpha = expf(a.g[tok] * A), beta = a.beta[tok];
+        const float alpha = expf(gate_of(a.g[tok], a.logits) * A), beta = gate_of(a.beta[tok], a.logits);
         const float qa = lane < dk ? to_f(q[lane]) : 0.f, ka = lane < dk ? to_f(k[lane]) : 0.f;
         const float qb = lane + 64 < dk ? to_f(q[lane + 64]) : 0.f;
         const float kb = lane + 64 < dk ? to_f(k[lane + 64]) : 0.f;

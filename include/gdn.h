@@ -73,12 +73,19 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
  * Mechanism Deep-Dive", Step 4 write line, write key b_t = beta_t k_t). */
 #define GDN_FLAG_ADDITIVE 1u
 
+/* g and beta are given as logits: the library applies the logistic sigmoid
+ * on load (g = sigmoid(dt_proj(x)) in "GDN & MLA Mechanism Deep-Dive", Step 4;
+ * the write gate beta likewise), and gdn_bwd returns dg and dbeta with
+ * respect to the logits. dA_log is unchanged (it is taken through the gate
+ * values). Without the flag g and beta are the gate values themselves. */
+#define GDN_FLAG_GATE_LOGITS 2u
+
 typedef struct {
     int32_t B, T, H; /* batch, tokens, heads */
     int32_t dk, dv;  /* key and value head dimensions */
     int32_t dtype;   /* gdn_dtype_t of q, k, v, o, do, dq, dk, dv */
     int32_t chunk;   /* 0 or 64 */
-    uint32_t flags;  /* 0 or GDN_FLAG_ADDITIVE */
+    uint32_t flags;  /* GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS, or 0 */
 } gdn_shape_t;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this shape. Return 0
@@ -135,7 +142,8 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
  * recurrence from a carried state (the O(1)-state read/write of "GDN & MLA
  * Mechanism Deep-Dive", Intuition). h_in may be NULL (zero state) and may
  * equal h_out (in-place update); no other aliasing is allowed. `dtype` is the
- * gdn_dtype_t of q, k, v and o; `flags` is 0 or GDN_FLAG_ADDITIVE. */
+ * gdn_dtype_t of q, k, v and o; `flags` is GDN_FLAG_ADDITIVE and/or
+ * GDN_FLAG_GATE_LOGITS, or 0. */
 gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
                       const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const float *A_log, const float *h_in, float *h_out,

@@ -14,6 +14,9 @@ Parity status of each function:
          hand-worked fixture; see tests/test_oracle_pins.py)
   bwd  - pinned by central finite differences of fwd and the dA_log identity
   step - pinned against fwd (a chain of steps equals one forward pass)
+  gates_from_logits, logit_grads - the sigmoid of the gate logits and the
+         chain rule through it; pinned by central finite differences of fwd
+         composed with gates_from_logits (tests/test_oracle_grad.py)
 """
 from __future__ import annotations
 
@@ -139,3 +142,18 @@ def step(q, k, v, g, beta, A_log, h_in=None, delta=True, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"gdn_oracle_step failed ({rc})")
     return o, h_out
+
+
+def gates_from_logits(x):
+    """Gate values from logits: the logistic sigmoid 1 / (1 + e^-x) in
+    float64 (the gate of "GDN & MLA Mechanism Deep-Dive", Step 4, is
+    g = sigmoid(dt_proj(x)); the write gate beta is formed the same way)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def logit_grads(d_gate, gate):
+    """Gradient with respect to a logit from the gradient with respect to its
+    gate value s = sigmoid(x): ds/dx = s (1 - s)."""
+    gate = np.asarray(gate, dtype=np.float64)
+    return np.asarray(d_gate, dtype=np.float64) * gate * (1.0 - gate)

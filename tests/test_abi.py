@@ -57,7 +57,7 @@ def test_fwd_rejects_bad_shapes(L):
     good = dict(B=1, T=8, H=2, dk=16, dv=16, dtype=1, chunk=64, flags=0)
     for key, val, code in [("B", 0, EINVAL), ("T", 0, EINVAL), ("H", -1, EINVAL), ("dk", 0, EINVAL),
                            ("dv", 129, EINVAL), ("dtype", 7, EINVAL), ("chunk", 32, EUNSUPPORTED),
-                           ("flags", 2, EINVAL)]:
+                           ("flags", 4, EINVAL)]:
         d = dict(good, **{key: val})
         s = gdn.Shape(*[d[f] for f, _ in gdn.Shape._fields_])
         assert fwd_call(L, s) == code, key
@@ -140,7 +140,7 @@ def test_step_tokens_validation(L):
     assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *ok, None) == EINVAL  # S < 1
     assert L.gdn_step_tokens(0, 3, 16, 56, 56, 1, 0, *ok, None) == EINVAL
     assert L.gdn_step_tokens(4, 3, 16, 56, 129, 1, 0, *ok, None) == EINVAL
-    assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 2, *ok, None) == EINVAL
+    assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 4, *ok, None) == EINVAL
     bad = list(ok)
     bad[8] = P(3)  # o aliases v
     assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 0, *bad, None) == EINVAL

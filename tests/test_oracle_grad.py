@@ -90,3 +90,41 @@ def test_reverse_pass_thread_count_invariant(oracle_mod):
                        nthreads=5)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_logit_gradients_match_central_differences(oracle_mod):
+    """Gates given as logits: the forward composed with the sigmoid, and the
+    reverse pass composed with the chain rule through it, against central
+    differences of the composed loss with respect to the logits."""
+    x, do, dhT = _inputs(40, T=7)
+    rng = np.random.default_rng(41)
+    gl = rng.standard_normal(x["g"].shape) * 2.0
+    bl = rng.standard_normal(x["beta"].shape) * 2.0
+
+    def loss(gl_, bl_):
+        xx = dict(x, g=oracle_mod.gates_from_logits(gl_), beta=oracle_mod.gates_from_logits(bl_))
+        return _loss(oracle_mod, xx, do, dhT, True)
+
+    gs, bs = oracle_mod.gates_from_logits(gl), oracle_mod.gates_from_logits(bl)
+    gr = oracle_mod.bwd(x["q"], x["k"], x["v"], gs, bs, x["A_log"], x["h0"], do, dhT, nthreads=1)
+    dgl = oracle_mod.logit_grads(gr["dg"], gs)
+    dbl = oracle_mod.logit_grads(gr["dbeta"], bs)
+    eps = 1e-6
+    for arr, ana, which in ((gl, dgl, "g"), (bl, dbl, "beta")):
+        fd = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            lp = loss(a1, bl) if which == "g" else loss(gl, a1)
+            lm = loss(a2, bl) if which == "g" else loss(gl, a2)
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - ana))
+        assert err < 1e-7 * max(1.0, np.max(np.abs(fd))), (which, err)
+    # the sigmoid itself: sigmoid(0) = 1/2, symmetric, and matches tanh's identity
+    z = np.linspace(-8, 8, 33)
+    assert oracle_mod.gates_from_logits(0.0) == 0.5
+    assert np.allclose(oracle_mod.gates_from_logits(z) + oracle_mod.gates_from_logits(-z), 1.0, atol=0, rtol=1e-15)
+    assert np.allclose(oracle_mod.gates_from_logits(z), 0.5 * (1.0 + np.tanh(z / 2)), atol=1e-15, rtol=0)
