@@ -29,27 +29,26 @@ template <bool BF, int D> struct PrepSmem {
     static constexpr int LDD = D + Op<BF>::PAD;
     static constexpr int LDC = C + Op<BF>::PAD;
     static constexpr int oK = 0;                                       // Ks [C][LDD]
-    static constexpr int oV = oK + C * LDD * (int)sizeof(S);          // Vs [C][LDD]
-    static constexpr int oTb = oV + C * LDD * (int)sizeof(S);         // Tb [C][LDC]
-    static constexpr int oL = oTb + C * LDC * (int)sizeof(S);         // L^T, then Tm, fp32 [C][LDF]
+    static constexpr int oTb = oK + C * LDD * (int)sizeof(S);         // Tb [C][LDC]
+    static constexpr int oL = oTb + C * LDC * (int)sizeof(S);         // L^T, Tm, then V, fp32 [C][LDF]
     static constexpr int oX = oL + C * LDF * 4;                       // solve scratch
     static constexpr int oGam = oX + 4 * 16 * 17 * 4;                 // double[C]
     static constexpr int oBet = oGam + C * 8;                         // float[C]
-    static constexpr int oCk = oBet + C * 4;                          // beta e^gam
-    static constexpr int SIZE = oCk + C * 4;
+    static constexpr int SIZE = oBet + C * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
-    // three workgroups per compute unit for bf16 heads up to 64 wide
-    static_assert(!BF || D > 64 || 3 * SIZE <= 160 * 1024, "prep occupancy");
+    static_assert(C * LDD * (int)sizeof(S) <= C * LDF * 4, "V fits the L^T / Tm area");
+    // four workgroups per compute unit for bf16 heads up to 64 wide
+    static_assert(!BF || D > 64 || 4 * SIZE <= 160 * 1024, "prep occupancy");
 };
 
-// X[row][0..D) *= sc[row] in place for the 16-byte pieces p0, p0 + np, ...
-template <bool BF, int D>
-__device__ __forceinline__ void scale_rows(typename Op<BF>::S *X, int ld, const float *sc, int p0, int np) {
+// X[row][0..D) *= sc(row) in place for the 16-byte pieces p0, p0 + np, ...
+template <bool BF, int D, class F>
+__device__ __forceinline__ void scale_rows(typename Op<BF>::S *X, int ld, F sc, int p0, int np) {
     using S = typename Op<BF>::S;
     constexpr int V = Op<BF>::VEC, NG = D / V;
     for (int it = p0; it < C * NG; it += np) {
         const int row = it / NG, c0 = (it % NG) * V;
-        const float f = sc[row];
+        const float f = sc(row);
         union {
             uint4 u;
             S x[V];
@@ -72,21 +71,20 @@ __device__ __forceinline__ void store_global(const f32x4 *acc, typename Op<BF>::
 }
 
 template <bool BF, int D, bool VEC>
-__global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(NTHR, 8) void fwd_prep_kernel(PrepArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
     using L = PrepSmem<BF, D>;
     constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *Ks = (S *)(smem + L::oK);
-    S *Vs = (S *)(smem + L::oV);
     S *Tb = (S *)(smem + L::oTb);
     float *Lm = (float *)(smem + L::oL);
     float *Tm = Lm;
+    S *Vs = (S *)Lm; // V is staged once Tm has been stored out
     float *xs = (float *)(smem + L::oX);
     double *gam2 = (double *)(smem + L::oGam);
     float *bet = (float *)(smem + L::oBet);
-    float *ck = (float *)(smem + L::oCk);
 
     const SeqArgs &s = a.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -118,15 +116,14 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
         gam2[lane] = dc.gam2;
         if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
         bet[lane] = be;
-        ck[lane] = be * dc.eg;
     }
     fk.stash(Ks, LDD, tid);
-    fv.stash(Vs, LDD, tid);
     __syncthreads();
 
     // U = Tm (diag(beta) V) and -Kw = -Tm (diag(beta e^gam) K): the row
-    // scales go onto V and K in LDS (after K K^T has read K), so a single
-    // operand copy Tb of Tm serves both products
+    // scales go onto V and K in LDS (K after K K^T has read it; V, kept in
+    // registers until then, into the Tm area once Tm is stored out), so a
+    // single operand copy Tb of Tm serves both products
     if (!s.additive) {
         f32x4 sk[4];
 #pragma unroll
@@ -136,18 +133,17 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
             Lm[col * LDF + row] = (row > col) ? bet[row] * sk[i][e] * gamma_ij(gam2, row, col) : 0.f; // L^T
         });
         __syncthreads(); // L complete, K K^T done
-        // waves 4..7 are idle during the diagonal solve
-        if (wave >= 4) {
-            scale_rows<BF, D>(Vs, LDD, bet, tid - 4 * 64, NTHR - 4 * 64);
-            scale_rows<BF, D>(Ks, LDD, ck, tid - 4 * 64, NTHR - 4 * 64);
-        }
+        // waves 4..7 are idle during the diagonal solve: rows of K times
+        // beta e^gam (the same e^gam the decay scan forms)
+        if (wave >= 4)
+            scale_rows<BF, D>(Ks, LDD, [&](int row) { return bet[row] * exp2_fast((float)gam2[row]); },
+                              tid - 4 * 64, NTHR - 4 * 64);
         tri_inverse<BF>(Lm, xs, wave, lane, Tb, LDC);
     } else {
         for (int e = tid; e < C * C; e += NTHR) {
             const int row = e / C, col = e % C;
             Tb[row * LDC + col] = from_f<BF>(row == col ? 1.f : 0.f);
         }
-        scale_rows<BF, D>(Vs, LDD, bet, tid, NTHR);
         __syncthreads();
     }
 
@@ -173,6 +169,9 @@ __global__ __launch_bounds__(NTHR) void fwd_prep_kernel(PrepArgs a) {
             *reinterpret_cast<uint4 *>(dst + e) = pk.u;
         }
     }
+    __syncthreads(); // Tm read out: V (times beta) takes its place
+    fv.stash_scaled(Vs, LDD, tid, bet[lane]);
+    __syncthreads();
     f32x4 accU[Tiles<4, DT>::PW], accN[Tiles<4, DT>::PW];
 #pragma unroll
     for (int i = 0; i < Tiles<4, DT>::PW; ++i) accU[i] = accN[i] = zero4();
