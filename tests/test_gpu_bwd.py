@@ -186,3 +186,45 @@ def test_full_size_fwdbwd_sampled(decay):
     say(f"bwd full fwdbwd_model decay={decay}")
     x = gi.gen_config("fwdbwd_model", decay=decay)
     check_bwd(x, "bf16", units=[0, 45, 90, 127])
+
+
+def test_fwd_bwd_graph_replay():
+    """One forward (context saved, the prep of later chunk ranges on a second
+    stream) plus backward captured in a HIP graph gives the eager results bit
+    for bit on every replay, with eager work and synchronisations between
+    replays."""
+    say("fwd+bwd graph replay B1 T2048 H4 d56 (two chunk ranges, so both streams)")
+    x = gi.gen_seq(1, 2048, 4, 56, 56, "bf16", seed=7430, h0="randn", with_do=True, decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0, do = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"]), dev(x["do"])
+    o = torch.empty_like(v)
+    hT = torch.empty_like(h0)
+    ctx = torch.empty(gdn.context_size(q, v), dtype=torch.uint8, device=q.device)
+    fws = torch.empty(gdn.fwd_workspace_size(q, v), dtype=torch.uint8, device=q.device)
+    bws = torch.empty(gdn.bwd_workspace_size(q, v), dtype=torch.uint8, device=q.device)
+    grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+             "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta), "dA_log": torch.empty_like(A_log),
+             "dh0": torch.empty_like(h0)}
+
+    def step():
+        gdn.fwd(q, k, v, g, beta, A_log, h0, o=o, hT=hT, context=ctx, workspace=fws)
+        gdn.bwd(q, k, v, g, beta, A_log, do, h0, None, context=ctx, workspace=bws, out=grads)
+
+    step()
+    torch.cuda.synchronize()
+    outs = {"o": o, "hT": hT, **{kk: vv for kk, vv in grads.items() if vv is not None}}
+    ref = {kk: vv.clone() for kk, vv in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in outs.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(t, ref[name]), f"{name} differs on replay {rep}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref["o"])
