@@ -16,6 +16,8 @@
 // One wave per (sequence, head); lane j owns value column j (and j + 64 when
 // dv > 64), so every state row is one coalesced access across the wave and
 // the reductions over the key index are plain per-lane sums in a fixed order.
+// Calls of 2 to 4 tokens on heads up to 64 wide load all their tokens' inputs
+// first (step_pre_kernel).
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -157,6 +159,82 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
     }
 }
 
+// Calls of 2 to 4 tokens with dk, dv <= 64: the same update as step_kernel
+// with the state in registers, but every token's inputs are loaded before the
+// first update, so the loads of later tokens do not wait behind the work of
+// earlier ones (a separate kernel: folding this into step_kernel changed the
+// single-token schedule for the worse).
+constexpr int PRE_TOKENS = 4;
+
+template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepArgs a) {
+    using S = typename Op<BF>::S;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nh = blockIdx.x * NWAVE + wave;
+    if (nh >= a.N * a.H) return;
+    const int seq = nh / a.H, h = nh % a.H, dk = a.dk, dv = a.dv, NT = a.S;
+    const float *hin = a.h_in ? a.h_in + (size_t)nh * dk * dv : nullptr;
+    float *hout = a.h_out + (size_t)nh * dk * dv;
+    const float A = -expf(a.A_log[h]);
+    const bool ok = lane < dv;
+
+    float hr[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+        if (i < dk) hr[i] = (hin && ok) ? hin[(size_t)i * dv + lane] : 0.f;
+    // inputs of every token (lane: key index for q, k; value column for v)
+    float gg[PRE_TOKENS], bb[PRE_TOKENS], qq[PRE_TOKENS], kk[PRE_TOKENS], vv[PRE_TOKENS];
+#pragma unroll
+    for (int t = 0; t < PRE_TOKENS; ++t) {
+        if (t < NT) {
+            const size_t tok = ((size_t)seq * NT + t) * a.H + h;
+            gg[t] = a.g[tok];
+            bb[t] = a.beta[tok];
+            qq[t] = lane < dk ? to_f(((const S *)a.q)[tok * dk + lane]) : 0.f;
+            kk[t] = lane < dk ? to_f(((const S *)a.k)[tok * dk + lane]) : 0.f;
+            vv[t] = ok ? to_f(((const S *)a.v)[tok * dv + lane]) : 0.f;
+        }
+    }
+    bool have = hin != nullptr;
+#pragma unroll
+    for (int t = 0; t < PRE_TOKENS; ++t) {
+        if (t < NT) {
+            const size_t tok = ((size_t)seq * NT + t) * a.H + h;
+            const float alpha = expf(gate_of(gg[t], a.logits) * A), beta = gate_of(bb[t], a.logits);
+            const float qa = qq[t], ka = kk[t];
+            float sk = qa * ka;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sk += __shfl_xor(sk, off, 64);
+            float r = 0.f, u = 0.f;
+            if (have) {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) {
+                    if (i < dk) {
+                        r += hr[i] * lane_bcast(qa, i);
+                        u += hr[i] * lane_bcast(ka, i);
+                    }
+                }
+            }
+            const float vj = vv[t];
+            float oj, w;
+            if (a.additive) {
+                oj = alpha * r + beta * sk * vj;
+                w = beta * vj;
+            } else {
+                oj = alpha * (r - beta * sk * u) + beta * sk * vj;
+                w = beta * (vj - alpha * u);
+            }
+            if (ok) ((S *)a.o)[tok * dv + lane] = from_f<BF>(oj);
+#pragma unroll
+            for (int i = 0; i < 64; ++i)
+                if (i < dk) hr[i] = (have ? alpha * hr[i] : 0.f) + lane_bcast(ka, i) * w;
+            have = true;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+        if (i < dk && ok) hout[(size_t)i * dv + lane] = hr[i];
+}
+
 template <bool BF, bool ONE> static hipError_t step_inst(const StepArgs &a, hipStream_t st) {
     const int grid = (a.N * a.H + NWAVE - 1) / NWAVE;
     const bool keep = a.dk <= 64;
@@ -172,6 +250,12 @@ template <bool BF, bool ONE> static hipError_t step_inst(const StepArgs &a, hipS
 
 hipError_t launch_step(const StepArgs &a, bool bf16, hipStream_t st) {
     if (a.S == 1) return bf16 ? step_inst<true, true>(a, st) : step_inst<false, true>(a, st);
+    if (a.S <= PRE_TOKENS && a.dk <= 64 && a.dv <= 64) {
+        const int grid = (a.N * a.H + NWAVE - 1) / NWAVE;
+        if (bf16) hipLaunchKernelGGL(step_pre_kernel<true>, dim3(grid), dim3(NTHR), 0, st, a);
+        else hipLaunchKernelGGL(step_pre_kernel<false>, dim3(grid), dim3(NTHR), 0, st, a);
+        return hipGetLastError();
+    }
     return bf16 ? step_inst<true, false>(a, st) : step_inst<false, false>(a, st);
 }
 

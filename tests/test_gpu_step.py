@@ -147,14 +147,14 @@ def check_tokens(N, S, H, dk, dv, dtype, decay="weak", additive=False, inplace=T
     assert_close(f"state after {S} tokens", host(hN), rh, tol)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 5])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])  # 2..4: all inputs loaded first; 5: token loop
 @pytest.mark.parametrize("decay", ["normal", "weak"])
 def test_step_tokens_bf16(S, decay):
     say(f"step_tokens bf16 N32 H16 d56 S={S} decay={decay}")
     check_tokens(32, S, 16, 56, 56, "bf16", decay=decay)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (100, 70), (5, 3)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (100, 70), (64, 64), (65, 64), (64, 65), (5, 3)])
 def test_step_tokens_head_dims(dk, dv):
     """Wide heads (state read and written per token) and narrow ones."""
     say(f"step_tokens bf16 dk={dk} dv={dv} S=3")
