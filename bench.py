@@ -80,10 +80,20 @@ def step_model(B, T, H, d):
     return flops, fwd_bytes + bwd_bytes
 
 
-def source_hash():
+# translation unit of each timed kernel; every kernel also depends on the
+# shared headers and on the launch code of the C ABI
+KERNEL_SOURCE = {"fwd_prep": "gdn_fwd.hip", "fwd_chain": "gdn_fwd.hip", "bwd_chain": "gdn_bwd.hip",
+                 "bwd_local": "gdn_bwd.hip", "dA_reduce": "gdn_bwd.hip"}
+SHARED_SOURCES = ("gdn_common.hpp", "gdn_launch.hpp", "gdn_api.cpp")
+
+
+def source_hash(kernel=None):
+    """Hash of the sources a kernel is built from (all library sources when
+    kernel is None): a stored counter reading is used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_74_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = sorted(os.listdir(csrc)) if kernel is None else sorted((KERNEL_SOURCE[kernel],) + SHARED_SOURCES)
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -97,7 +107,7 @@ def load_traffic(kernel):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(kernel):
         return None
     return t.get("traffic_bytes")
 
@@ -156,9 +166,9 @@ def traffic_summary(fetch_dir, write_dir):
 
     f_scale = COPY_BYTES / (copy_of(fetch_all) * 1024.0)
     w_scale = COPY_BYTES / (copy_of(write_all) * 1024.0)
-    src = source_hash()
     out = {}
     for k in KERNELS:
+        src = source_hash(k)
         fk = [v for n, v in fetch.items() if f"gdn::{k}_kernel" in n or f"gdn::{k}" in n]
         wk = [v for n, v in write.items() if f"gdn::{k}_kernel" in n or f"gdn::{k}" in n]
         if not fk or not wk:
@@ -196,7 +206,7 @@ def traffic_summary(fetch_dir, write_dir):
         ratio = f"{tot / alg:6.2f}" if alg > 0 else "   nan"
         lines.append(f"{k:12s} {nl:8d} {rec['fetch_kib_per_dispatch']:10.1f} {rec['write_kib_per_dispatch']:10.1f}"
                      f" {rec['read_bytes'] / 1e6:8.1f} {rec['write_bytes'] / 1e6:9.1f} {tot:9.1f} {alg:15.1f}"
-                     f" {ratio}  {src}")
+                     f" {ratio}  {rec['source_hash']}")
     lines += ["", "# algorithmic = the operation's own inputs and outputs only (kernel_bytes_per_token_head);",
               "# the rest is the library's own context and workspace traffic (U, -Kw, Tm, chunk states,",
               "# dh per chunk, the decay) plus partially used cache lines."]
