@@ -130,7 +130,7 @@ static void bwd_unit(job_t *J, int unit) {
     const size_t S = (size_t)dk * dv;
     const double A = -exp(J->A_log[h]);
     const int nseg = (T + SEG - 1) / SEG;
-    double *ck = (double *)calloc((size_t)nseg * S, sizeof(double));  /* state before each segment */
+    double *ck = (double *)calloc((size_t)(nseg > 0 ? nseg : 1) * S, sizeof(double)); /* state before each segment */
     double *st = (double *)calloc((size_t)(SEG + 1) * S, sizeof(double)); /* states inside a segment */
     double *dh = (double *)calloc(S, sizeof(double));
     double *Hh = (double *)calloc(S, sizeof(double));
@@ -297,8 +297,10 @@ static int run(job_t *J, void *(*fn)(void *), int nthreads) {
     return J->failed ? -2 : 0;
 }
 
+/* T = 0 is an empty sequence: no step of the recurrence runs, so the final
+ * state is h0 and the gradient reaching h0 is dhT */
 static int check_dims(int B, int T, int H, int dk, int dv) {
-    return (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) ? -1 : 0;
+    return (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) ? -1 : 0;
 }
 
 /* units: optional list of b*H+h indices to compute (NULL = all B*H). Outputs

@@ -276,3 +276,25 @@ def test_step_chain_equals_forward(oracle_mod, delta):
                                  delta=delta)
         assert rel(ot, o[:, t]) < 1e-13
     assert rel(st, hT) < 1e-13
+
+
+def test_empty_sequence_is_zero_steps():
+    """T = 0 runs no step of the recurrence (the Step 4 loop of "GDN & MLA
+    Mechanism Deep-Dive" over no tokens): the final state is h0, the gradient
+    of h0 is dhT, and every other gradient is empty or zero."""
+    import oracle as O
+
+    B, T, H, dk, dv = 2, 0, 3, 5, 4
+    rng = np.random.default_rng(7600)
+    z = lambda *s: np.zeros(s)
+    h0 = rng.standard_normal((B, H, dk, dv))
+    dhT = rng.standard_normal((B, H, dk, dv))
+    args = (z(B, T, H, dk), z(B, T, H, dk), z(B, T, H, dv), z(B, T, H), z(B, T, H), rng.standard_normal(H))
+    o, hT = O.fwd(*args, h0)
+    assert o.shape == (B, 0, H, dv) and np.array_equal(hT, h0)
+    _, hz = O.fwd(*args, None)
+    assert np.array_equal(hz, np.zeros_like(h0))
+    r = O.bwd(*args, h0, z(B, T, H, dv), dhT)
+    assert np.array_equal(r["dh0"], dhT)
+    assert np.array_equal(r["dA_log"], np.zeros(H))
+    assert r["dq"].shape == (B, 0, H, dk) and r["dg"].shape == (B, 0, H)
