@@ -59,7 +59,7 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 gdn_status_t check_shape(const gdn_shape_t *s) {
     if (!s) return fail(GDN_EINVAL, "shape is NULL");
-    if (s->B < 1 || s->T < 1 || s->H < 1) return fail(GDN_EINVAL, "B, T, H must be >= 1");
+    if (s->B < 1 || s->T < 0 || s->H < 1) return fail(GDN_EINVAL, "B and H must be >= 1, T >= 0");
     if (s->dk < 1 || s->dv < 1 || s->dk > 128 || s->dv > 128)
         return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", s->dtype);
@@ -316,11 +316,45 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
 
 } // namespace
 
+// An empty sequence (T = 0) runs no step of the recurrence: the final state
+// is h0 (zero when h0 is NULL); backward, the gradient of h0 is dhT (zero when
+// NULL) and dA_log is zero. Arrays whose extent has a factor T hold nothing and
+// may be NULL; no workspace is used.
+static gdn_status_t fwd_empty(const gdn_shape_t *s, const float *h0, float *hT, hipStream_t st) {
+    const size_t sb = state32_bytes(s);
+    if ((h0 && !aligned(h0, 4)) || (hT && !aligned(hT, 4)))
+        return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    const Range in[] = {{h0, h0 ? sb : 0, "h0"}};
+    const Range out[] = {{hT, hT ? sb : 0, "hT"}};
+    gdn_status_t e = check_aliasing(in, 1, out, 1);
+    if (e != GDN_OK || !hT) return e;
+    return hip_status(gdn::launch_copy_or_zero(hT, h0, sb / 4, st), "gdn_fwd (empty sequence)");
+}
+
+static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *h0, const void *ctx, const float *dhT,
+                              float *dA_log, float *dh0, float *hT, hipStream_t st) {
+    if (!dA_log) return fail(GDN_EINVAL, "a required pointer is NULL");
+    if (ctx && hT) return fail(GDN_EINVAL, "hT can only be recomputed when ctx is NULL");
+    const float *f32[] = {h0, dhT, dA_log, dh0, hT};
+    for (const float *p : f32)
+        if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
+    const size_t sb = state32_bytes(s);
+    const Range in[] = {{h0, h0 ? sb : 0, "h0"}, {dhT, dhT ? sb : 0, "dhT"}};
+    const Range out[] = {{dA_log, (size_t)s->H * 4, "dA_log"}, {dh0, dh0 ? sb : 0, "dh0"}, {hT, hT ? sb : 0, "hT"}};
+    gdn_status_t e = check_aliasing(in, 2, out, 3);
+    if (e != GDN_OK) return e;
+    hipError_t he = gdn::launch_copy_or_zero(dA_log, nullptr, (size_t)s->H, st);
+    if (he == hipSuccess && dh0) he = gdn::launch_copy_or_zero(dh0, dhT, sb / 4, st);
+    if (he == hipSuccess && hT) he = gdn::launch_copy_or_zero(hT, h0, sb / 4, st);
+    return hip_status(he, "gdn_bwd (empty sequence)");
+}
+
 gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
                      const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
                      void *ws, size_t ws_bytes, void *stream) {
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
+    if (s->T == 0) return fwd_empty(s, h0, hT, (hipStream_t)stream);
     if (!q || !k || !v || !g || !beta || !A_log || !o)
         return fail(GDN_EINVAL, "q, k, v, g, beta, A_log and o must not be NULL");
     const void *vec[] = {q, k, v, o};
@@ -366,6 +400,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
                      void *stream) {
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
+    if (s->T == 0) return bwd_empty(s, h0, ctx, dhT, dA_log, dh0, hT, (hipStream_t)stream);
     if (!q || !k || !v || !g || !beta || !A_log || !dout || !dq || !dk || !dv || !dg || !dbeta || !dA_log)
         return fail(GDN_EINVAL, "a required pointer is NULL");
     if (ctx && hT) return fail(GDN_EINVAL, "hT can only be recomputed when ctx is NULL");

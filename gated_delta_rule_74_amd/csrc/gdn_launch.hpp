@@ -98,5 +98,7 @@ hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t
 hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st);
 hipError_t launch_step(const StepArgs &a, bool bf16, hipStream_t st);
+// dst[0..n) = src[0..n), or zeros when src is null
+hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream_t st);
 
 } // namespace gdn

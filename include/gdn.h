@@ -45,9 +45,14 @@
  * last non-OK status of the calling thread. NaN/Inf inputs propagate.
  * Results are bitwise reproducible for a given build, shape and device.
  *
- * Supported sizes: T >= 1 (a last chunk shorter than 64 is handled on chip),
+ * Supported sizes: T >= 0 (a last chunk shorter than 64 is handled on chip),
  * 1 <= dk, dv <= 128 for bf16 and <= 64 for fp32, chunk 0 or 64, base
  * pointers 16-byte aligned, B*H < 2^31, tensors below 2^31 elements.
+ *
+ * Empty sequences (T = 0) run no step: gdn_fwd sets hT = h0 (zeros when h0
+ * is NULL); gdn_bwd sets dh0 = dhT (zeros when dhT is NULL), dA_log = 0 and,
+ * when asked, hT = h0. Pointers to arrays with a factor T in their extent may
+ * then be NULL, and no workspace or context is used.
  */
 #ifndef GDN_H
 #define GDN_H

@@ -55,7 +55,7 @@ def fwd_call(L, shape, **over):
 
 def test_fwd_rejects_bad_shapes(L):
     good = dict(B=1, T=8, H=2, dk=16, dv=16, dtype=1, chunk=64, flags=0)
-    for key, val, code in [("B", 0, EINVAL), ("T", 0, EINVAL), ("H", -1, EINVAL), ("dk", 0, EINVAL),
+    for key, val, code in [("B", 0, EINVAL), ("T", -1, EINVAL), ("H", -1, EINVAL), ("dk", 0, EINVAL),
                            ("dv", 129, EINVAL), ("dtype", 7, EINVAL), ("chunk", 32, EUNSUPPORTED),
                            ("flags", 4, EINVAL)]:
         d = dict(good, **{key: val})
@@ -114,6 +114,8 @@ def test_workspace_and_context_sizes(L):
     assert ctx >= states + 2 * blocks + tms and ctx < states + 2 * blocks + tms + 1024
     assert L.gdn_fwd_workspace_size(ctypes.byref(s)) >= 2 * blocks
     assert L.gdn_bwd_workspace_size(ctypes.byref(s)) >= ctx + states + 8 * 16 * 64 * 4
+    empty = gdn.Shape(2, 0, 3, 16, 16, 1, 64, 0)  # T = 0: no chunk, no context
+    assert L.gdn_fwd_context_size(ctypes.byref(empty)) == 0
     bad = gdn.Shape(0, 1, 1, 1, 1, 1, 64, 0)
     assert L.gdn_fwd_context_size(ctypes.byref(bad)) == 0
     assert L.gdn_fwd_workspace_size(ctypes.byref(bad)) == 0
@@ -155,3 +157,17 @@ def test_product_path_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "gated_delta_rule_74_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "import numpy" not in src
+
+
+def test_empty_sequence_host_logic(L):
+    """T = 0 needs neither the T-sized arrays nor a workspace; with no state
+    output requested nothing is launched (so this runs without a GPU), and
+    the backward still requires dA_log and rejects aliasing of its outputs."""
+    s = gdn.Shape(2, 0, 3, 16, 16, 1, 64, 0)
+    assert L.gdn_fwd(ctypes.byref(s), *[None] * 7, None, None, None, None, 0, None) == 0
+    assert L.gdn_fwd(ctypes.byref(s), *[None] * 6, fake(1), None, fake(1), None, None, 0, None) == EINVAL
+    args = [None] * 19 + [0, None]
+    assert L.gdn_bwd(ctypes.byref(s), *args) == EINVAL  # dA_log NULL
+    a = list(args)
+    a[15], a[16] = fake(2), fake(2)  # dA_log and dh0 overlap
+    assert L.gdn_bwd(ctypes.byref(s), *a) == EINVAL

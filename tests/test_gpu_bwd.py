@@ -228,3 +228,45 @@ def test_fwd_bwd_graph_replay():
         step()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(o, ref["o"])
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 56), (torch.bfloat16, 128), (torch.float32, 16)])
+def test_empty_sequence(dtype, d):
+    """T = 0: no step runs. Forward: hT = h0 (zeros without h0); backward:
+    dh0 = dhT (zeros without dhT), dA_log = 0, the recomputed hT = h0, all
+    against the oracle's zero-step results. Outputs start as NaN so that every
+    element is seen to be written."""
+    say(f"empty sequence B2 T0 H3 d{d} {dtype}")
+    O = _oracle()
+    B, H = 2, 3
+    rng = np.random.default_rng(7610)
+    h0n = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dhTn = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    A_logn = rng.standard_normal(H).astype(np.float32)
+    cuda = torch.device("cuda")
+    q = torch.empty((B, 0, H, d), dtype=dtype, device=cuda)
+    k, v, do = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    g = torch.empty((B, 0, H), dtype=torch.float32, device=cuda)
+    beta = torch.empty_like(g)
+    A_log, h0, dhT = (torch.from_numpy(x).to(cuda) for x in (A_logn, h0n, dhTn))
+    nan = lambda: torch.full((B, H, d, d), float("nan"), device=cuda)
+    o, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, hT=nan(), save_context=True)
+    _, hz, _ = gdn.fwd(q, k, v, g, beta, A_log, None, hT=nan())
+    out = {"dA_log": torch.full((H,), float("nan"), device=cuda), "dh0": nan(), "hT": nan()}
+    r = gdn.bwd(q, k, v, g, beta, A_log, do, h0, dhT, want_hT=True, out=out)
+    r0 = gdn.bwd(q, k, v, g, beta, A_log, do, h0, None, context=cs,
+                 out={"dA_log": torch.full((H,), float("nan"), device=cuda), "dh0": nan()})
+    torch.cuda.synchronize()
+    z = lambda *s: np.zeros(s)
+    args = (z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H), z(B, 0, H), A_logn.astype(np.float64))
+    _, ref_hT = O.fwd(*args, h0n.astype(np.float64))
+    rg = O.bwd(*args, h0n.astype(np.float64), z(B, 0, H, d), dhTn.astype(np.float64))
+    assert o.shape == (B, 0, H, d)
+    assert np.array_equal(host(hT), ref_hT)
+    assert np.array_equal(host(hz), np.zeros((B, H, d, d)))
+    assert np.array_equal(host(r["dh0"]), rg["dh0"])
+    assert np.array_equal(host(r["dA_log"]), rg["dA_log"])
+    assert np.array_equal(host(r["hT"]), ref_hT)
+    assert np.array_equal(host(r0["dh0"]), np.zeros((B, H, d, d)))
+    assert np.array_equal(host(r0["dA_log"]), np.zeros(H))
+    assert r["dq"].shape == (B, 0, H, d) and r["dg"].shape == (B, 0, H)
