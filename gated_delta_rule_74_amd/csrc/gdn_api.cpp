@@ -491,16 +491,31 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     return hip_status(he, "gdn_bwd dA_log launch");
 }
 
+// S = 0: no token, so the state is carried over unchanged (h_out = h_in,
+// zeros when h_in is NULL); the token arrays may be NULL
+static gdn_status_t step_empty(int32_t N, int32_t H, int32_t dk, int32_t dv, const float *h_in, float *h_out,
+                               hipStream_t st) {
+    if (!h_out) return fail(GDN_EINVAL, "a required pointer is NULL");
+    if ((h_in && !aligned(h_in, 4)) || !aligned(h_out, 4)) return fail(GDN_EINVAL, "pointers must be 4-byte aligned");
+    const size_t sb = (size_t)N * H * dk * dv * 4;
+    if (h_in == h_out) return GDN_OK;
+    if (h_in && overlap(Range{h_in, sb, "h_in"}, Range{h_out, sb, "h_out"}))
+        return fail(GDN_EINVAL, "h_in and h_out overlap without being equal");
+    return hip_status(gdn::launch_copy_or_zero(h_out, h_in, sb / 4, st), "gdn_step_tokens (no token)");
+}
+
 gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
                              uint32_t flags, const void *q, const void *k, const void *v, const float *g,
                              const float *beta, const float *A_log, const float *h_in, float *h_out, void *o,
                              void *stream) {
-    if (N < 1 || H < 1 || S < 1) return fail(GDN_EINVAL, "N, S and H must be >= 1");
+    if (N < 0 || H < 1 || S < 0) return fail(GDN_EINVAL, "N, S must be >= 0 and H >= 1");
     if (dk < 1 || dv < 1 || dk > 128 || dv > 128) return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", dtype);
     if (flags & ~(GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS)) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
     if ((double)N * H * dk * dv >= 2147483648.0 || (double)N * S * H * (dk > dv ? dk : dv) >= 2147483648.0)
         return fail(GDN_EINVAL, "state or tokens too large");
+    if (N == 0) return GDN_OK; // no sequence: nothing to read or write
+    if (S == 0) return step_empty(N, H, dk, dv, h_in, h_out, (hipStream_t)stream);
     if (!q || !k || !v || !g || !beta || !A_log || !h_out || !o)
         return fail(GDN_EINVAL, "a required pointer is NULL");
     const void *all[] = {q, k, v, o, g, beta, A_log, h_in, h_out};

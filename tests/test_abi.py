@@ -124,7 +124,7 @@ def test_workspace_and_context_sizes(L):
 def test_step_validation(L):
     P = fake
     ok = (P(1), P(2), P(3), P(4), P(5), P(6), None, P(7), P(8))
-    assert L.gdn_step(0, 16, 56, 56, 1, 0, *ok, None) == EINVAL
+    assert L.gdn_step(-1, 16, 56, 56, 1, 0, *ok, None) == EINVAL
     assert L.gdn_step(4, 16, 0, 56, 1, 0, *ok, None) == EINVAL
     assert L.gdn_step(4, 16, 56, 56, 3, 0, *ok, None) == EINVAL
     assert L.gdn_step(4, 16, 56, 56, 1, 4, *ok, None) == EINVAL
@@ -139,8 +139,8 @@ def test_step_validation(L):
 def test_step_tokens_validation(L):
     P = fake
     ok = (P(1), P(2), P(3), P(4), P(5), P(6), None, P(7), P(8))
-    assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *ok, None) == EINVAL  # S < 1
-    assert L.gdn_step_tokens(0, 3, 16, 56, 56, 1, 0, *ok, None) == EINVAL
+    assert L.gdn_step_tokens(4, -1, 16, 56, 56, 1, 0, *ok, None) == EINVAL  # S < 0
+    assert L.gdn_step_tokens(-1, 3, 16, 56, 56, 1, 0, *ok, None) == EINVAL
     assert L.gdn_step_tokens(4, 3, 16, 56, 129, 1, 0, *ok, None) == EINVAL
     assert L.gdn_step_tokens(4, 3, 16, 56, 56, 1, 4, *ok, None) == EINVAL
     bad = list(ok)
@@ -171,3 +171,16 @@ def test_empty_sequence_host_logic(L):
     a = list(args)
     a[15], a[16] = fake(2), fake(2)  # dA_log and dh0 overlap
     assert L.gdn_bwd(ctypes.byref(s), *a) == EINVAL
+
+
+def test_empty_decode_host_logic(L):
+    """N = 0 does nothing; S = 0 carries the state over (in place: nothing to
+    launch, so this runs without a GPU) and still needs h_out and rejects a
+    partial overlap of the states."""
+    assert L.gdn_step_tokens(0, 3, 16, 56, 56, 1, 0, *[None] * 10) == 0
+    assert L.gdn_step(0, 16, 56, 56, 1, 0, *[None] * 10) == 0
+    h = fake(3)
+    assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, h, None, None) == 0
+    assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, None, None, None) == EINVAL
+    shifted = ctypes.c_void_p(h.value + 4)
+    assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, shifted, None, None) == EINVAL

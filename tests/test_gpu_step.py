@@ -178,3 +178,40 @@ def test_step_tokens_one_token_equals_step():
                              beta[0][:, None], A_log, h0, None)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[:, 0]) and torch.equal(h1, h2)
+
+
+def test_step_tokens_empty():
+    """S = 0 carries the state over (h_out = the oracle's zero-token forward
+    from h_in, i.e. h_in; zeros without h_in; in place nothing changes);
+    N = 0 gives empty results. Outputs start as NaN so every element is seen
+    to be written."""
+    import oracle as O
+
+    say("step_tokens empty: N4 S0 H3 d56, N0 S3")
+    N, H, d = 4, 3, 56
+    rng = np.random.default_rng(7620)
+    h_n = rng.standard_normal((N, H, d, d)).astype(np.float32)
+    A_n = rng.standard_normal(H).astype(np.float32)
+    cuda = torch.device("cuda")
+    q = torch.empty((N, 0, H, d), dtype=torch.bfloat16, device=cuda)
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    g = torch.empty((N, 0, H), dtype=torch.float32, device=cuda)
+    beta = torch.empty_like(g)
+    A_log, h_in = torch.from_numpy(A_n).to(cuda), torch.from_numpy(h_n).to(cuda)
+    nan = lambda: torch.full((N, H, d, d), float("nan"), device=cuda)
+    o, h_out = gdn.step_tokens(q, k, v, g, beta, A_log, h_in, nan())
+    _, hz = gdn.step_tokens(q, k, v, g, beta, A_log, None, nan())
+    h2 = h_in.clone()
+    gdn.step_tokens(q, k, v, g, beta, A_log, h2, h2)
+    qe = torch.empty((0, 3, H, d), dtype=torch.bfloat16, device=cuda)
+    ge = torch.empty((0, 3, H), dtype=torch.float32, device=cuda)
+    oe, he = gdn.step_tokens(qe, qe, qe, ge, ge, A_log, None)
+    torch.cuda.synchronize()
+    z = lambda *s: np.zeros(s)
+    _, ref = O.fwd(z(N, 0, H, d), z(N, 0, H, d), z(N, 0, H, d), z(N, 0, H), z(N, 0, H),
+                   A_n.astype(np.float64), h_n.astype(np.float64))
+    assert o.shape == (N, 0, H, d)
+    assert np.array_equal(host(h_out), ref)
+    assert np.array_equal(host(hz), np.zeros((N, H, d, d)))
+    assert np.array_equal(host(h2), ref)
+    assert oe.shape == (0, 3, H, d) and he.shape == (0, H, d, d)
