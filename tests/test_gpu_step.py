@@ -129,6 +129,57 @@ def test_decode_graph_replay():
         assert torch.equal(h2, ref_h)
 
 
+def test_step_tokens_graph_replay():
+    """Three-token calls (the kernel that loads all tokens first) and an
+    empty call captured in a HIP graph replay the eager result bit for bit."""
+    say("step_tokens graph replay N16 S3 H4 d56, 4 calls")
+    calls, S = 4, 3
+    x = gi.gen_decode(16, 4, 56, 56, calls * S, "bf16", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0 = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    # [steps, N, H, *] -> per call [N, S, H, *]
+    tok = lambda t, c: t[c * S:(c + 1) * S].transpose(0, 1).contiguous()
+    qs = [tok(q, c) for c in range(calls)]
+    ks = [tok(k, c) for c in range(calls)]
+    vs = [tok(v, c) for c in range(calls)]
+    gs = [tok(g, c) for c in range(calls)]
+    bs = [tok(beta, c) for c in range(calls)]
+    o = torch.empty(calls, 16, S, 4, 56, dtype=torch.bfloat16, device=q.device)
+    q0 = torch.empty((16, 0, 4, 56), dtype=torch.bfloat16, device=q.device)
+    g0 = torch.empty((16, 0, 4), dtype=torch.float32, device=q.device)
+    h_copy = torch.empty_like(h0)
+
+    def chain(h, out):
+        for c in range(calls):
+            gdn.step_tokens(qs[c], ks[c], vs[c], gs[c], bs[c], A_log, h, h, o=out[c])
+        gdn.step_tokens(q0, q0, q0, g0, g0, A_log, h, h_copy)  # S = 0: copy of the state
+
+    h = h0.clone()
+    chain(h, o)
+    torch.cuda.synchronize()
+    ref_h, ref_o = h.clone(), o.clone()
+    assert torch.equal(h_copy, ref_h)
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain(h, o)
+    for rep in range(3):
+        h.copy_(h0)
+        o.zero_()
+        h_copy.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref_h), f"state differs on replay {rep}"
+        assert torch.equal(o, ref_o), f"output differs on replay {rep}"
+        assert torch.equal(h_copy, ref_h), f"empty-call copy differs on replay {rep}"
+        h2, o2 = h0.clone(), torch.empty_like(o)
+        chain(h2, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(h2, ref_h)
+
+
 def check_tokens(N, S, H, dk, dv, dtype, decay="weak", additive=False, inplace=True, zero_start=False,
                  seed=7413):
     """step_tokens over S tokens per sequence against the oracle's serial
