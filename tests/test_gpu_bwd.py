@@ -270,3 +270,63 @@ def test_empty_sequence(dtype, d):
     assert np.array_equal(host(r0["dh0"]), np.zeros((B, H, d, d)))
     assert np.array_equal(host(r0["dA_log"]), np.zeros(H))
     assert r["dq"].shape == (B, 0, H, d) and r["dg"].shape == (B, 0, H)
+
+
+def test_max_size_fwdbwd():
+    """Tensors just below the 2^31-element limit: B1 H8 T2097088 d128 bf16
+    (q holds 2,147,418,112 elements; ~91 GB of device memory in all). The
+    inputs repeat a seeded block of P = 4099 tokens (not a power of two, so
+    an address that wrapped by any power of two would read other values).
+    The gate of token r = T - 129 is 200 (A <= -1 here), so its decay
+    exp(g A) underflows to 0: the state is reset there and the tokens from r
+    on are a sequence of their own, which the oracle computes from a zero
+    state; do is zero before r. Checked against the oracle: o on the first 128 tokens (from
+    h0), o, hT and every gradient from r on; before r every gradient, and
+    dh0, must vanish."""
+    O = _oracle()
+    B, H, d, P = 1, 8, 128, 4099
+    T = (1 << 21) - 64
+    r = T - 129
+    say(f"max size B{B} T{T} H{H} d{d} bf16, reset at token {r}")
+    x = gi.gen_seq(1, P, H, d, d, "bf16", seed=7630, h0="randn", with_do=True, decay="normal")
+    reps = -(-T // P)
+
+    def big(t):
+        t = dev(t)
+        return t.repeat(1, reps, *([1] * (t.dim() - 2)))[:, :T]
+
+    q, k, v, beta = big(x["q"]), big(x["k"]), big(x["v"]), big(x["beta"])
+    g = big(x["g"]).clone()
+    g[0, r, :] = 200.0
+    A_log, h0 = dev(x["A_log"]), dev(x["h0"])
+    tail = np.arange(r, T) % P
+    do = torch.zeros_like(q)
+    do[0, r:] = dev(x["do"])[0, torch.from_numpy(tail).to(q.device)]
+    torch.cuda.synchronize()
+    o, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, save_context=True)
+    res = gdn.bwd(q, k, v, g, beta, A_log, do, h0, context=cs)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    # head: the first 128 tokens from h0
+    head = lambda a: f64(a)[:, :128]
+    ro, _ = O.fwd(head(x["q"]), head(x["k"]), head(x["v"]), head(x["g"]), head(x["beta"]),
+                  f64(x["A_log"]), f64(x["h0"]))
+    assert_close("o head", host(o[:, :128]), ro, tol)
+    # tail: tokens r.. from a zero state
+    tl = lambda a: f64(a)[:, tail]
+    gt = tl(x["g"])
+    gt[0, 0, :] = 200.0
+    args = (tl(x["q"]), tl(x["k"]), tl(x["v"]), gt, tl(x["beta"]), f64(x["A_log"]))
+    ro, rh = O.fwd(*args, None)
+    assert_close("o tail", host(o[:, r:]), ro, tol)
+    assert_close("hT", host(hT), rh, tol)
+    rg = O.bwd(*args, None, tl(x["do"]), None)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert_close(f"{name} tail", host(res[name][:, r:]), rg[name], tol)
+    assert_close("dA_log", host(res["dA_log"]), rg["dA_log"], tol)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        m = res[name][:, :r].abs().max().item()
+        assert m <= 1e-30, f"{name} before the reset: max |.| = {m}"
+    assert res["dh0"].abs().max().item() <= 1e-30
+    del q, k, v, g, beta, do, o, hT, cs, res
+    torch.cuda.empty_cache()
