@@ -173,14 +173,15 @@ def bwd_workspace_size(q, v, additive=False):
 
 
 def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, save_context=False,
-        want_hT=True, o=None, hT=None, context=None, workspace=None):
-    """Chunked forward. Returns (o, hT or None, context or None); the context
-    (a byte tensor) lets bwd() skip recomputing the forward. gate_logits: g
-    and beta are logits (the kernels apply the sigmoid)."""
+        want_hT=True, want_o=True, o=None, hT=None, context=None, workspace=None):
+    """Chunked forward. Returns (o or None, hT or None, context or None); the
+    context (a byte tensor) lets bwd() skip recomputing the forward.
+    gate_logits: g and beta are logits (the kernels apply the sigmoid).
+    want_o=False: a state-only pass (e.g. a prefill for decoding)."""
     B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
     s = _shape(q, v, additive, gate_logits)
     dev = q.device
-    if o is None:
+    if o is None and want_o:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (B, T, H, dv), dev)
     if hT is None and want_hT:

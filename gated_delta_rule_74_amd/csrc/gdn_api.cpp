@@ -355,8 +355,8 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
     if (s->T == 0) return fwd_empty(s, h0, hT, (hipStream_t)stream);
-    if (!q || !k || !v || !g || !beta || !A_log || !o)
-        return fail(GDN_EINVAL, "q, k, v, g, beta, A_log and o must not be NULL");
+    if (!q || !k || !v || !g || !beta || !A_log)
+        return fail(GDN_EINVAL, "q, k, v, g, beta and A_log must not be NULL");
     const void *vec[] = {q, k, v, o};
     for (const void *p : vec)
         if (!aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, o must be 16-byte aligned");

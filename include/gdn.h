@@ -109,7 +109,9 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s);
  * Step 4 and Step 5).
  *   q, k, v, g, beta, A_log  inputs (layouts above)
  *   h0            initial state or NULL (zero state)
- *   o             output [B,T,H,dv]
+ *   o             output [B,T,H,dv], or NULL: a state-only pass (e.g. the
+ *                 prefill of a decode state), which writes hT and/or ctx
+ *                 and skips the outputs
  *   hT            final state or NULL (not written)
  *   ctx           NULL, or gdn_fwd_context_size() bytes (256-byte aligned)
  *                 that receive the forward context for gdn_bwd

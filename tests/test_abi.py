@@ -74,7 +74,8 @@ def test_fwd_rejects_bad_shapes(L):
 def test_fwd_rejects_null_misaligned_and_aliased(L):
     s = gdn.Shape(1, 8, 2, 16, 16, 1, 64, 0)
     assert fwd_call(L, s, q=None) == EINVAL
-    assert fwd_call(L, s, o=None) == EINVAL
+    assert fwd_call(L, s, A_log=None) == EINVAL
+    assert fwd_call(L, s, o=None, hT=fake(4)) == EINVAL  # state-only pass still checks aliasing
     assert fwd_call(L, s, k=ctypes.c_void_p(fake(2).value + 2)) == EINVAL
     assert fwd_call(L, s, o=fake(1)) == EINVAL  # o aliases q
     assert b"overlaps" in L.gdn_last_error_detail()

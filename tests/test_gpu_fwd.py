@@ -141,3 +141,24 @@ def test_full_size_long_context_forward_sampled():
     say("fwd full long_ctx")
     x = gi.gen_config("long_ctx", decay="weak")
     check_fwd(x, "bf16", units=[3, 12])
+
+
+@pytest.mark.parametrize("dtype,T,d", [("bf16", 2048, 56), ("bf16", 200, 128), ("f32", 130, 32)])
+def test_state_only_forward(dtype, T, d):
+    """o = NULL (a state-only pass, e.g. a prefill): the final state and the
+    saved context equal those of the full forward bit for bit (2048 tokens
+    at d 56 run two chunk ranges on two streams), and the state matches the
+    oracle."""
+    say(f"state-only forward B2 T{T} H4 d{d} {dtype}")
+    x = gi.gen_seq(2, T, 4, d, d, dtype, seed=7640, h0="randn", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0 = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    _, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, save_context=True)
+    o2, hT2, cs2 = gdn.fwd(q, k, v, g, beta, A_log, h0, save_context=True, want_o=False)
+    torch.cuda.synchronize()
+    assert o2 is None
+    assert torch.equal(hT, hT2)
+    assert torch.equal(cs, cs2)
+    _, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                          f64(x["A_log"]), f64(x["h0"]))
+    assert_close("hT", host(hT2), rh, TOL[dtype])

@@ -266,3 +266,23 @@ def test_step_tokens_empty():
     assert np.array_equal(host(hz), np.zeros((N, H, d, d)))
     assert np.array_equal(host(h2), ref)
     assert oe.shape == (0, 3, H, d) and he.shape == (0, H, d, d)
+
+
+def test_prefill_then_decode():
+    """A state-only forward over a 200-token prompt, then three decode tokens
+    in one call from its final state (in place), equal the oracle's forward
+    over all 203 tokens: the decode outputs and the final state."""
+    say("prefill T200 then step_tokens S3, N4 H4 d56 bf16")
+    N, H, d, T0, S = 4, 4, 56, 200, 3
+    x = gi.gen_seq(N, T0 + S, H, d, d, "bf16", seed=7650, h0="randn", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0 = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    pre = lambda t: t[:, :T0].contiguous()
+    new = lambda t: t[:, T0:].contiguous()
+    _, h, _ = gdn.fwd(pre(q), pre(k), pre(v), pre(g), pre(beta), A_log, h0, want_o=False)
+    o, h = gdn.step_tokens(new(q), new(k), new(v), new(g), new(beta), A_log, h, h)
+    torch.cuda.synchronize()
+    ro, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
+                           f64(x["A_log"]), f64(x["h0"]))
+    assert_close("decode o", host(o), ro[:, T0:], TOL["bf16"])
+    assert_close("final state", host(h), rh, TOL["bf16"])
