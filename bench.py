@@ -14,7 +14,8 @@ sample of the same workload on this host's cores.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
 
 The line also carries "forward": the inference forward alone at the same
-shape (no context saved), and "decode_step": the single-token state update on its own
+shape (no context saved; "state_only_*" times the same pass without the
+outputs, as a prefill that only needs the final state), and "decode_step": the single-token state update on its own
 workload (256 sequences x 16 heads x d 56, 1024 consecutive steps, fp32 state
 carried in place, fresh bf16 tokens per step), timed as one captured HIP graph
 of the 1024 launches, with the step kernel's HBM roofline; "mtp3_*" runs the
@@ -233,16 +234,23 @@ def forward_bench(gi, to_dev, dev, steps, warmup):
     def fwd():
         gdn.fwd(q, k, v, g, beta, A_log, None, o=o, hT=hT, workspace=ws, save_context=False)
 
-    for _ in range(warmup):
-        fwd()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fwd()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def prefill():  # state-only pass: the final state without the outputs
+        gdn.fwd(q, k, v, g, beta, A_log, None, hT=hT, workspace=ws, save_context=False, want_o=False)
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(fwd)
+    ms_state = timed(prefill)
     nch = c.B * c.H * ((c.T + C - 1) // C)
     d = c.dk
     flops = nch * (10 * C * C * d + 6 * C * d * d + C ** 3 / 3)
@@ -251,7 +259,9 @@ def forward_bench(gi, to_dev, dev, steps, warmup):
             "ms": round(ms, 4), "tokens_per_s": c.B * c.T / (ms * 1e-3),
             "hbm_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
             "flops": flops, "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+            "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "state_only_ms": round(ms_state, 4),
+            "state_only_tokens_per_s": c.B * c.T / (ms_state * 1e-3)}
 
 
 def decode_bytes_per_step(N, H, dk, dv, S=1):
