@@ -278,7 +278,7 @@ static void *step_worker(void *arg) {
     return NULL;
 }
 
-/* ------------------------------------------------------------ driver */
+/* ------------------------------------------------------- thread pool */
 
 static int run(job_t *J, void *(*fn)(void *), int nthreads) {
     if (nthreads < 1) nthreads = 1;
