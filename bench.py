@@ -32,6 +32,13 @@ Profiling aids (the counter runs behind the committed traffic summaries):
                                          written to profiles/
     python bench.py --mfma-summary DIR   per-kernel MFMA busy % and flops from
                                          one --pmc run of MFMA_COUNTERS
+    python bench.py --trace-summary KT_DIR KT_LOG BENCH_LOG
+                                         kernel-trace tables of the fwd+bwd and
+                                         decode workloads from one
+                                         rocprofv3 --kernel-trace --stats run
+                                         (KT_DIR, its printed line in KT_LOG)
+                                         and a bench.py run without the
+                                         profiler (BENCH_LOG)
 """
 import argparse
 import hashlib
@@ -370,6 +377,86 @@ SIMD_NUM = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
 XCD_NUM = 8         # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 
 
+def _last_json(path):
+    with open(path) as f:
+        return json.loads([ln for ln in f if ln.startswith("{")][-1])
+
+
+def trace_summary(kt_dir, kt_log, bench_log):
+    """Write profiles/kernel_trace_{fwdbwd_model,decode_step}.txt from the
+    kernel statistics of a rocprofv3 --kernel-trace --stats run of bench.py
+    (KT_DIR, with the run's own JSON line in KT_LOG) and the JSON line of a
+    bench.py run without the profiler (BENCH_LOG)."""
+    import csv
+    import glob
+
+    b, k = _last_json(bench_log), _last_json(kt_log)
+    stats = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {kt_dir}")
+    with open(stats[0]) as f:
+        rows = list(csv.DictReader(f))
+    cmd = ["#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv \\",
+           "#     -d <out> -o bench -- python3 <repo>/bench.py --steps 10 --warmup 2 --no-cpu-baseline > <kt.log>",
+           "#   python3 <repo>/bench.py > <bench.log>   (no profiler)",
+           "#   python3 <repo>/bench.py --trace-summary <out> <kt.log> <bench.log>   (writes this file)"]
+
+    def table(keep):
+        out = [f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+        for r in rows:
+            if keep(r["Name"]):
+                out.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f}"
+                           f" {float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f}")
+        return out
+
+    f, rl = b["forward"], b["roofline"]
+    lines = ["# Kernel trace: gated delta rule fwd+bwd step, workload fwdbwd_model",
+             "# (B=8, H=16, T=4096, d_k=d_v=56, bf16, chunk 64), one MI355X", "#",
+             "# commands (from the repository root, on the GPU host):"] + cmd + [
+        "#",
+        "# 22 steps = 2 warmup + 10 timed + 10 per-kernel-timed, then the forward-only and decode",
+        "# workloads. The forward runs in 4 chunk ranges (prep and serial pass launched 4 times per",
+        "# step, prep of the next range overlapping the serial pass of the current one); each backward",
+        "# kernel runs once per step. The rows below count every launch of the run (fwd+bwd steps",
+        "# and the forward-only timing).",
+        f"# the profiled run's own line: {k['ms_per_step']} ms per step; per-kernel HIP-event sums per step:"
+        f" {k['kernels_ms']}",
+        f"# bench.py without the profiler (separate run, 20 steps): {b['ms_per_step']} ms per step,"
+        f" {b['value']:.4g} tokens/s;",
+        f"#   per-kernel sums per step {b['kernels_ms']}",
+        f"#   dominant kernel bwd_local: {rl['avg_launch_ms']} ms per launch, {rl['achieved']} GB/s algorithmic"
+        f" = {rl['frac'] * 100:.1f} % of 8 TB/s",
+        f"#   forward alone (fwd_model, no context): {f['ms']} ms = {f['tokens_per_s']:.4g} tokens/s,"
+        f" {f['hbm_frac'] * 100:.1f} % of HBM, {f['tflops']} TFLOP/s",
+        ""] + table(lambda n: "gdn::" in n and "step_" not in n)
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_fwdbwd_model.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    d = b["decode_step"]
+    lines = ["# Kernel trace: decode step, workload decode_step",
+             "# (256 sequences x 16 heads, d_k=d_v=56, bf16 tokens, fp32 state in place, 1024 consecutive"
+             " tokens), one MI355X", "#",
+             "# commands (the same runs as kernel_trace_fwdbwd_model.txt; bench.py times the decode workload"
+             " after the fwd+bwd step):"] + cmd + [
+        "#",
+        "# bench.py runs the 1024 single-token steps for one state set (hot: 51 MB, held by the 256 MB"
+        " Infinity Cache)",
+        "# and for 6 state sets served round-robin (cold: 308 MB), then the same tokens as 341 calls of 3"
+        " tokens",
+        "# (gdn_step_tokens); per variant an eager pass, a captured graph checked bitwise against it, 2 warm",
+        "# replays and 1 timed replay. step_kernel<..., true> is the one-token instance, step_pre_kernel the"
+        " 3-token calls.",
+        f"# bench.py without the profiler: hot {d['hot']['us_per_step']} us per step ="
+        f" {d['hot']['roofline']['achieved']} GB/s ({d['hot']['roofline']['frac'] * 100:.1f} % of 8 TB/s),",
+        f"#   cold {d['cold']['us_per_step']} us per step = {d['cold']['roofline']['achieved']} GB/s"
+        f" ({d['cold']['roofline']['frac'] * 100:.1f} %), {d['hot']['roofline']['bytes_per_launch']}"
+        " algorithmic bytes per step;",
+        f"#   3 tokens per call: hot {d['mtp3_hot']['us_per_step']} us = {d['mtp3_hot']['tokens_per_s']:.4g}"
+        f" tokens/s, cold {d['mtp3_cold']['us_per_step']} us = {d['mtp3_cold']['tokens_per_s']:.4g} tokens/s",
+        ""] + table(lambda n: "gdn::step_" in n)
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_decode_step.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def mfma_summary(counter_dir):
     """MFMA use per kernel from one rocprofv3 --pmc run of the counters in
     MFMA_COUNTERS over `bench.py --profile-run N`: busy % = MFMA busy cycles
@@ -483,7 +570,11 @@ def main():
     ap.add_argument("--profile-run", type=int, default=0, metavar="N")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-summary", metavar="COUNTER_DIR")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("KT_DIR", "KT_LOG", "BENCH_LOG"))
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
