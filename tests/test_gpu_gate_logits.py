@@ -87,3 +87,39 @@ def test_decode_with_gate_logits(S):
     ro, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), gs, bs, f64(x["A_log"]), f64(x["h0"]))
     assert_close("o", host(o), ro, TOL["bf16"])
     assert_close("state", host(hN), rh, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 56), ("bf16", 128), ("f32", 32)])
+def test_additive_with_gate_logits(dtype, d):
+    """Both flags at once (erase term off, gates as logits): forward, backward
+    (saved context) and a three-token decode call against the oracle's
+    additive form composed with the sigmoid and its chain rule."""
+    say(f"additive + gate logits fwd+bwd B2 T130 H2 d{d} {dtype}, decode S3")
+    x = with_logits(gi.gen_seq(2, 130, 2, d, d, dtype, seed=7426, h0="randn", with_do=True,
+                               decay="weak"), 7427)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    gl, bl, A_log, h0, do = dev(x["gl"]), dev(x["bl"]), dev(x["A_log"]), dev(x["h0"]), dev(x["do"])
+    o, hT, cs = gdn.fwd(q, k, v, gl, bl, A_log, h0, additive=True, gate_logits=True, save_context=True)
+    r = gdn.bwd(q, k, v, gl, bl, A_log, do, h0, context=cs, additive=True, gate_logits=True)
+    tail = lambda t: t[:, -3:].contiguous()
+    h = h0.clone()
+    od, hd = gdn.step_tokens(tail(q), tail(k), tail(v), tail(gl), tail(bl), A_log, h, h, additive=True,
+                             gate_logits=True)
+    torch.cuda.synchronize()
+    gs, bs = _ref_gates(x)
+    O = _oracle()
+    tol = TOL[dtype]
+    args = (f64(x["q"]), f64(x["k"]), f64(x["v"]), gs, bs, f64(x["A_log"]), f64(x["h0"]))
+    ro, rh = O.fwd(*args, delta=False)
+    assert_close("o", host(o), ro, tol)
+    assert_close("hT", host(hT), rh, tol)
+    rg = O.bwd(*args, f64(x["do"]), delta=False)
+    ref = dict(rg, dg=O.logit_grads(rg["dg"], gs), dbeta=O.logit_grads(rg["dbeta"], bs))
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "dh0"):
+        assert_close(name, host(r[name]), ref[name], tol)
+    # decode: the last three tokens from h0 as a sequence of their own
+    t3 = lambda a: f64(a)[:, -3:]
+    rdo, rdh = O.fwd(t3(x["q"]), t3(x["k"]), t3(x["v"]), gs[:, -3:], bs[:, -3:], f64(x["A_log"]),
+                     f64(x["h0"]), delta=False)
+    assert_close("decode o", host(od), rdo, tol)
+    assert_close("decode state", host(hd), rdh, tol)
