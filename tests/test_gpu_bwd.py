@@ -330,3 +330,34 @@ def test_max_size_fwdbwd():
     assert res["dh0"].abs().max().item() <= 1e-30
     del q, k, v, g, beta, do, o, hT, cs, res
     torch.cuda.empty_cache()
+
+
+def test_caller_stream():
+    """Work goes on the caller's current stream: forward (two chunk ranges,
+    so the second internal stream forks from and joins the caller's), backward
+    and a decode call issued on a side stream, on inputs written by that
+    stream just before, equal the default-stream results bit for bit."""
+    say("caller stream: fwd+bwd B1 T2048 H4 d56, step_tokens S3")
+    x = gi.gen_seq(1, 2048, 4, 56, 56, "bf16", seed=7660, h0="randn", with_do=True, decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h0, do = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"]), dev(x["do"])
+    t3 = lambda t: t[:, -3:].contiguous()
+
+    def run(q, k, v, g, beta, h0, do):
+        o, hT, cs = gdn.fwd(q, k, v, g, beta, A_log, h0, save_context=True)
+        r = gdn.bwd(q, k, v, g, beta, A_log, do, h0, context=cs)
+        h = hT.clone()
+        od, _ = gdn.step_tokens(t3(q), t3(k), t3(v), t3(g), t3(beta), A_log, h, h)
+        return dict(r, o=o, hT=hT, od=od, hd=h)
+
+    ref = run(q, k, v, g, beta, h0, do)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ins = [t.clone() for t in (q, k, v, g, beta, h0, do)]
+        got = run(*ins)
+    torch.cuda.synchronize()
+    for name, t in ref.items():
+        if t is not None:
+            assert torch.equal(got[name], t), name
