@@ -168,6 +168,8 @@ constexpr int PRE_TOKENS = 4;
 
 template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepArgs a) {
     using S = typename Op<BF>::S;
+    // q and k of every token of the wave's item, as 4-row broadcast reads
+    __shared__ __attribute__((aligned(16))) float qk[NWAVE][2][PRE_TOKENS][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nh = blockIdx.x * NWAVE + wave;
     if (nh >= a.N * a.H) return;
@@ -177,43 +179,56 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepA
     const float A = -expf(a.A_log[h]);
     const bool ok = lane < dv;
 
+    // rows past dk hold zeros, so whole groups of 4 rows can be processed
     float hr[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
-        if (i < dk) hr[i] = (hin && ok) ? hin[(size_t)i * dv + lane] : 0.f;
+    for (int i = 0; i < 64; ++i) hr[i] = (i < dk && hin && ok) ? hin[(size_t)i * dv + lane] : 0.f;
     // inputs of every token (lane: key index for q, k; value column for v)
-    float gg[PRE_TOKENS], bb[PRE_TOKENS], qq[PRE_TOKENS], kk[PRE_TOKENS], vv[PRE_TOKENS];
+    float gg[PRE_TOKENS], bb[PRE_TOKENS], vv[PRE_TOKENS];
+    float(*qs)[64] = qk[wave][0], (*ks)[64] = qk[wave][1];
 #pragma unroll
     for (int t = 0; t < PRE_TOKENS; ++t) {
         if (t < NT) {
             const size_t tok = ((size_t)seq * NT + t) * a.H + h;
             gg[t] = a.g[tok];
             bb[t] = a.beta[tok];
-            qq[t] = lane < dk ? to_f(((const S *)a.q)[tok * dk + lane]) : 0.f;
-            kk[t] = lane < dk ? to_f(((const S *)a.k)[tok * dk + lane]) : 0.f;
+            qs[t][lane] = lane < dk ? to_f(((const S *)a.q)[tok * dk + lane]) : 0.f;
+            ks[t][lane] = lane < dk ? to_f(((const S *)a.k)[tok * dk + lane]) : 0.f;
             vv[t] = ok ? to_f(((const S *)a.v)[tok * dv + lane]) : 0.f;
         }
     }
+    // the wave reads back only what it wrote: no barrier beyond the wave's
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     bool have = hin != nullptr;
 #pragma unroll
     for (int t = 0; t < PRE_TOKENS; ++t) {
         if (t < NT) {
             const size_t tok = ((size_t)seq * NT + t) * a.H + h;
             const float alpha = expf(gate_of(gg[t], a.logits) * A), beta = gate_of(bb[t], a.logits);
-            const float qa = qq[t], ka = kk[t];
-            float sk = qa * ka;
+            // s = k . q, and r = h^T q, u = h^T k over four interleaved row sets
+            float sk = qs[t][lane] * ks[t][lane];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) sk += __shfl_xor(sk, off, 64);
-            float r = 0.f, u = 0.f;
+            float r4[4] = {0.f, 0.f, 0.f, 0.f}, u4[4] = {0.f, 0.f, 0.f, 0.f};
             if (have) {
 #pragma unroll
-                for (int i = 0; i < 64; ++i) {
+                for (int i = 0; i < 64; i += 4) {
                     if (i < dk) {
-                        r += hr[i] * lane_bcast(qa, i);
-                        u += hr[i] * lane_bcast(ka, i);
+                        const float4 q4 = *(const float4 *)&qs[t][i], k4 = *(const float4 *)&ks[t][i];
+                        r4[0] += hr[i] * q4.x;
+                        r4[1] += hr[i + 1] * q4.y;
+                        r4[2] += hr[i + 2] * q4.z;
+                        r4[3] += hr[i + 3] * q4.w;
+                        u4[0] += hr[i] * k4.x;
+                        u4[1] += hr[i + 1] * k4.y;
+                        u4[2] += hr[i + 2] * k4.z;
+                        u4[3] += hr[i + 3] * k4.w;
                     }
                 }
             }
+            const float r = (r4[0] + r4[1]) + (r4[2] + r4[3]), u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
             const float vj = vv[t];
             float oj, w;
             if (a.additive) {
@@ -225,8 +240,15 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepA
             }
             if (ok) ((S *)a.o)[tok * dv + lane] = from_f<BF>(oj);
 #pragma unroll
-            for (int i = 0; i < 64; ++i)
-                if (i < dk) hr[i] = (have ? alpha * hr[i] : 0.f) + lane_bcast(ka, i) * w;
+            for (int i = 0; i < 64; i += 4) {
+                if (i < dk) {
+                    const float4 k4 = *(const float4 *)&ks[t][i];
+                    hr[i] = (have ? alpha * hr[i] : 0.f) + k4.x * w;
+                    hr[i + 1] = (have ? alpha * hr[i + 1] : 0.f) + k4.y * w;
+                    hr[i + 2] = (have ? alpha * hr[i + 2] : 0.f) + k4.z * w;
+                    hr[i + 3] = (have ? alpha * hr[i + 3] : 0.f) + k4.w * w;
+                }
+            }
             have = true;
         }
     }
