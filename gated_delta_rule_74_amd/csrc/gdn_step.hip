@@ -47,9 +47,19 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         col[c] = lane + 64 * c;
         ok[c] = col[c] < dv;
     }
-    // KEEP: the state rows stay in registers across the tokens of the call
+    // KEEP: the state rows stay in registers across the tokens of the call;
+    // rows past dk hold zeros, so whole groups of 4 rows can be processed,
+    // and each token's q and k go through the wave's LDS (4-row broadcasts)
     constexpr int KR = KEEP ? 64 : 1;
+    __shared__ __attribute__((aligned(16))) float qk_s[NWAVE][2][64];
+    float *qs = qk_s[wave][0], *ks = qk_s[wave][1];
     float hr[KR][NCOL];
+    if (KEEP) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i)
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) hr[i][c] = 0.f;
+    }
     if (KEEP && hin) {
 #pragma unroll
         for (int i = 0; i < KR; ++i) {
@@ -78,22 +88,47 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         float sk = qa * ka + qb * kb;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) sk += __shfl_xor(sk, off, 64);
+        if (KEEP) {
+            // the wave reads back only what it wrote (in order after the
+            // previous token's reads): no barrier beyond the wave's
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            qs[lane] = qa;
+            ks[lane] = ka;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
 
         float r[NCOL], u[NCOL];
 #pragma unroll
         for (int c = 0; c < NCOL; ++c) r[c] = u[c] = 0.f;
         if (have) {
             if (KEEP) {
+                // four interleaved row sets, summed at the end
+                float r4[4][NCOL], u4[4][NCOL];
 #pragma unroll
-                for (int i = 0; i < KR; ++i) {
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < NCOL; ++c) r4[e][c] = u4[e][c] = 0.f;
+#pragma unroll
+                for (int i = 0; i < KR; i += 4) {
                     if (i < dk) {
-                        const float qi = lane_bcast(qa, i), ki = lane_bcast(ka, i);
+                        const float4 q4 = *(const float4 *)(qs + i), k4 = *(const float4 *)(ks + i);
+                        const float qv[4] = {q4.x, q4.y, q4.z, q4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                        for (int c = 0; c < NCOL; ++c) {
-                            r[c] += hr[i][c] * qi;
-                            u[c] += hr[i][c] * ki;
-                        }
+                        for (int e = 0; e < 4; ++e)
+#pragma unroll
+                            for (int c = 0; c < NCOL; ++c) {
+                                r4[e][c] += hr[i + e][c] * qv[e];
+                                u4[e][c] += hr[i + e][c] * kv[e];
+                            }
                     }
+                }
+#pragma unroll
+                for (int c = 0; c < NCOL; ++c) {
+                    r[c] = (r4[0][c] + r4[1][c]) + (r4[2][c] + r4[3][c]);
+                    u[c] = (u4[0][c] + u4[1][c]) + (u4[2][c] + u4[3][c]);
                 }
             } else {
                 for (int i = 0; i < dk; ++i) {
@@ -124,11 +159,15 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         }
         if (KEEP) {
 #pragma unroll
-            for (int i = 0; i < KR; ++i) {
+            for (int i = 0; i < KR; i += 4) {
                 if (i < dk) {
-                    const float ki = lane_bcast(ka, i);
+                    const float4 k4 = *(const float4 *)(ks + i);
+                    const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                    for (int c = 0; c < NCOL; ++c) hr[i][c] = (have ? alpha * hr[i][c] : 0.f) + ki * w[c];
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int c = 0; c < NCOL; ++c)
+                            hr[i + e][c] = (have ? alpha * hr[i + e][c] : 0.f) + kv[e] * w[c];
                 }
             }
         } else {
