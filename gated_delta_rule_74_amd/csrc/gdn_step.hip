@@ -15,9 +15,12 @@
 //
 // One wave per (sequence, head); lane j owns value column j (and j + 64 when
 // dv > 64), so every state row is one coalesced access across the wave and
-// the reductions over the key index are plain per-lane sums in a fixed order.
-// Calls of 2 to 4 tokens on heads up to 64 wide load all their tokens' inputs
-// first (step_pre_kernel).
+// the reductions over the key index are per-lane sums in a fixed order. With
+// dk <= 64 the state stays in registers, and each token's q and k pass
+// through the wave's own LDS so that every lane reads 4 key rows' values with
+// one broadcast read; the sums run over four interleaved row sets. Calls of
+// 2 to 4 tokens on heads up to 64 wide load all their tokens' inputs first
+// (step_pre_kernel).
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
