@@ -18,7 +18,7 @@
 // the reductions over the key index are per-lane sums in a fixed order. With
 // dk <= 64 the state stays in registers, and each token's q and k pass
 // through the wave's own LDS so that every lane reads 4 key rows' values with
-// one broadcast read; the sums run over four interleaved row sets. Calls of
+// one broadcast read; the sums run over eight interleaved row sets. Calls of
 // 2 to 4 tokens on heads up to 64 wide load all their tokens' inputs first
 // (step_pre_kernel).
 #include "gdn_common.hpp"
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
     // rows past dk hold zeros, so whole groups of 4 rows can be processed,
     // and each token's q and k go through the wave's LDS (4-row broadcasts)
     constexpr int KR = KEEP ? 64 : 1;
+    constexpr int RS = 8; // interleaved row sets of the reductions (divides 64)
     __shared__ __attribute__((aligned(16))) float qk_s[NWAVE][2][64];
     float *qs = qk_s[wave][0], *ks = qk_s[wave][1];
     float hr[KR][NCOL];
@@ -108,30 +109,42 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         for (int c = 0; c < NCOL; ++c) r[c] = u[c] = 0.f;
         if (have) {
             if (KEEP) {
-                // four interleaved row sets, summed at the end
-                float r4[4][NCOL], u4[4][NCOL];
+                // RS interleaved row sets, summed pairwise at the end
+                float rs[RS][NCOL], us[RS][NCOL];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < RS; ++e)
 #pragma unroll
-                    for (int c = 0; c < NCOL; ++c) r4[e][c] = u4[e][c] = 0.f;
+                    for (int c = 0; c < NCOL; ++c) rs[e][c] = us[e][c] = 0.f;
 #pragma unroll
-                for (int i = 0; i < KR; i += 4) {
+                for (int i = 0; i < KR; i += RS) {
                     if (i < dk) {
-                        const float4 q4 = *(const float4 *)(qs + i), k4 = *(const float4 *)(ks + i);
-                        const float qv[4] = {q4.x, q4.y, q4.z, q4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
+                        for (int e4 = 0; e4 < RS; e4 += 4) {
+                            const float4 q4 = *(const float4 *)(qs + i + e4), k4 = *(const float4 *)(ks + i + e4);
+                            const float qv[4] = {q4.x, q4.y, q4.z, q4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                            for (int c = 0; c < NCOL; ++c) {
-                                r4[e][c] += hr[i + e][c] * qv[e];
-                                u4[e][c] += hr[i + e][c] * kv[e];
-                            }
+                            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                                for (int c = 0; c < NCOL; ++c) {
+                                    rs[e4 + e][c] += hr[i + e4 + e][c] * qv[e];
+                                    us[e4 + e][c] += hr[i + e4 + e][c] * kv[e];
+                                }
+                        }
                     }
                 }
 #pragma unroll
+                for (int w2 = RS / 2; w2 > 0; w2 >>= 1)
+#pragma unroll
+                    for (int e = 0; e < w2; ++e)
+#pragma unroll
+                        for (int c = 0; c < NCOL; ++c) {
+                            rs[e][c] += rs[e + w2][c];
+                            us[e][c] += us[e + w2][c];
+                        }
+#pragma unroll
                 for (int c = 0; c < NCOL; ++c) {
-                    r[c] = (r4[0][c] + r4[1][c]) + (r4[2][c] + r4[3][c]);
-                    u[c] = (u4[0][c] + u4[1][c]) + (u4[2][c] + u4[3][c]);
+                    r[c] = rs[0][c];
+                    u[c] = us[0][c];
                 }
             } else {
                 for (int i = 0; i < dk; ++i) {
