@@ -220,6 +220,7 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
 // earlier ones (a separate kernel: folding this into step_kernel changed the
 // single-token schedule for the worse).
 constexpr int PRE_TOKENS = 4;
+constexpr int PRE_RS = 8; // interleaved row sets of the reductions (divides 64)
 
 template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepArgs a) {
     using S = typename Op<BF>::S;
@@ -266,24 +267,34 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepA
             float sk = qs[t][lane] * ks[t][lane];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) sk += __shfl_xor(sk, off, 64);
-            float r4[4] = {0.f, 0.f, 0.f, 0.f}, u4[4] = {0.f, 0.f, 0.f, 0.f};
+            float rs[PRE_RS], us[PRE_RS];
+#pragma unroll
+            for (int e = 0; e < PRE_RS; ++e) rs[e] = us[e] = 0.f;
             if (have) {
 #pragma unroll
-                for (int i = 0; i < 64; i += 4) {
+                for (int i = 0; i < 64; i += PRE_RS) {
                     if (i < dk) {
-                        const float4 q4 = *(const float4 *)&qs[t][i], k4 = *(const float4 *)&ks[t][i];
-                        r4[0] += hr[i] * q4.x;
-                        r4[1] += hr[i + 1] * q4.y;
-                        r4[2] += hr[i + 2] * q4.z;
-                        r4[3] += hr[i + 3] * q4.w;
-                        u4[0] += hr[i] * k4.x;
-                        u4[1] += hr[i + 1] * k4.y;
-                        u4[2] += hr[i + 2] * k4.z;
-                        u4[3] += hr[i + 3] * k4.w;
+#pragma unroll
+                        for (int e4 = 0; e4 < PRE_RS; e4 += 4) {
+                            const float4 q4 = *(const float4 *)&qs[t][i + e4], k4 = *(const float4 *)&ks[t][i + e4];
+                            const float qv[4] = {q4.x, q4.y, q4.z, q4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                rs[e4 + e] += hr[i + e4 + e] * qv[e];
+                                us[e4 + e] += hr[i + e4 + e] * kv[e];
+                            }
+                        }
                     }
                 }
             }
-            const float r = (r4[0] + r4[1]) + (r4[2] + r4[3]), u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
+#pragma unroll
+            for (int w2 = PRE_RS / 2; w2 > 0; w2 >>= 1)
+#pragma unroll
+                for (int e = 0; e < w2; ++e) {
+                    rs[e] += rs[e + w2];
+                    us[e] += us[e + w2];
+                }
+            const float r = rs[0], u = us[0];
             const float vj = vv[t];
             float oj, w;
             if (a.additive) {
