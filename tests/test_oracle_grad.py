@@ -92,10 +92,12 @@ def test_reverse_pass_thread_count_invariant(oracle_mod):
         assert np.array_equal(a[key], b[key]), key
 
 
-def test_logit_gradients_match_central_differences(oracle_mod):
+@pytest.mark.parametrize("delta", [True, False])
+def test_logit_gradients_match_central_differences(oracle_mod, delta):
     """Gates given as logits: the forward composed with the sigmoid, and the
     reverse pass composed with the chain rule through it, against central
-    differences of the composed loss with respect to the logits."""
+    differences of the composed loss with respect to the logits (delta rule
+    and additive form)."""
     x, do, dhT = _inputs(40, T=7)
     rng = np.random.default_rng(41)
     gl = rng.standard_normal(x["g"].shape) * 2.0
@@ -103,10 +105,10 @@ def test_logit_gradients_match_central_differences(oracle_mod):
 
     def loss(gl_, bl_):
         xx = dict(x, g=oracle_mod.gates_from_logits(gl_), beta=oracle_mod.gates_from_logits(bl_))
-        return _loss(oracle_mod, xx, do, dhT, True)
+        return _loss(oracle_mod, xx, do, dhT, delta)
 
     gs, bs = oracle_mod.gates_from_logits(gl), oracle_mod.gates_from_logits(bl)
-    gr = oracle_mod.bwd(x["q"], x["k"], x["v"], gs, bs, x["A_log"], x["h0"], do, dhT, nthreads=1)
+    gr = oracle_mod.bwd(x["q"], x["k"], x["v"], gs, bs, x["A_log"], x["h0"], do, dhT, delta=delta, nthreads=1)
     dgl = oracle_mod.logit_grads(gr["dg"], gs)
     dbl = oracle_mod.logit_grads(gr["dbeta"], bs)
     eps = 1e-6
