@@ -49,3 +49,41 @@ def test_multi_gpu_request_is_refused(capsys, monkeypatch):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def _write_counters(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "p_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for disp, (name, val) in enumerate(rows):
+            f.write(f'{disp},"{name}",{counter},{val}\n')
+
+
+def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    """HBM traffic = counter KiB x 1024 x (copy bytes / copy counter bytes),
+    per counter, averaged over dispatches; written with the kernel's source
+    hash. Synthetic counter files: the 256 MiB copy reads as 2x its size on
+    FETCH_SIZE and 1x on WRITE_SIZE."""
+    root = tmp_path / "repo"
+    (root / "profiles").mkdir(parents=True)
+    os.symlink(os.path.join(ROOT, "gated_delta_rule_74_amd"), root / "gated_delta_rule_74_amd")
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    copy_kib = bench.COPY_BYTES / 1024
+    _write_counters(str(tmp_path / "fetch"), "FETCH_SIZE",
+                    [("__amd_rocclr_copyBuffer", 2 * copy_kib), ("void gdn::bwd_local_kernel<true, 64, true>(x)", 1000.0),
+                     ("void gdn::bwd_local_kernel<true, 64, true>(x)", 3000.0)])
+    _write_counters(str(tmp_path / "write"), "WRITE_SIZE",
+                    [("__amd_rocclr_copyBuffer", copy_kib), ("void gdn::bwd_local_kernel<true, 64, true>(x)", 500.0),
+                     ("void gdn::bwd_local_kernel<true, 64, true>(x)", 500.0)])
+    bench.traffic_summary(str(tmp_path / "fetch"), str(tmp_path / "write"))
+    import json
+
+    with open(root / "profiles" / f"bwd_local_{bench.WORKLOAD}_traffic.json") as f:
+        rec = json.load(f)
+    assert rec["copy_fetch_scale"] == 0.5 and rec["copy_write_scale"] == 1.0
+    assert rec["read_bytes"] == round(2000.0 * 1024 * 0.5)
+    assert rec["write_bytes"] == round(500.0 * 1024)
+    assert rec["traffic_bytes"] == rec["read_bytes"] + rec["write_bytes"]
+    assert rec["source_hash"] == bench.source_hash("bwd_local")
+    assert bench.load_traffic("bwd_local") == rec["traffic_bytes"]
+    assert (root / "profiles" / "traffic_fwdbwd_model.txt").exists()
