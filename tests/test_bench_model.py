@@ -87,3 +87,28 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert rec["source_hash"] == bench.source_hash("bwd_local")
     assert bench.load_traffic("bwd_local") == rec["traffic_bytes"]
     assert (root / "profiles" / "traffic_fwdbwd_model.txt").exists()
+
+
+def test_mfma_summary_arithmetic(tmp_path, monkeypatch):
+    """busy % = MFMA busy cycles / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);
+    flops = MOPS x 512; TFLOP/s over the dispatch's own duration. Synthetic
+    counters: 25 % busy, 1e6 bf16 MOPS in 1 ms."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_hash", lambda kernel=None: "test")
+    d = tmp_path / "mfma"
+    d.mkdir()
+    name = "void gdn::bwd_local_kernel<true, 64, true>(x)"
+    vals = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1000 * bench.SIMD_NUM,
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e6, "SQ_INSTS_VALU_MFMA_MOPS_F32": 0.0}
+    with open(d / "p_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        for cn, v in vals.items():
+            f.write(f'7,"{name}",{cn},{v},1000,1001000\n')
+    bench.mfma_summary(str(d))
+    row = [ln for ln in open(tmp_path / "profiles" / f"mfma_{bench.WORKLOAD}.txt") if ln.startswith("bwd_local")]
+    assert len(row) == 1
+    f = row[0].split()
+    assert f[1] == "1" and float(f[2]) == 25.0
+    assert float(f[3]) == 0.512 and float(f[4]) == 0.0
+    assert float(f[6]) == 1000.0 and float(f[7]) == 0.5
