@@ -165,7 +165,10 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
  * [N,S,H,dk], v, o [N,S,H,dv], g, beta [N,S,H] (the forward's layouts with
  * B = N, T = S); the states are [N,H,dk,dv]. The state is read once and
  * written once per call (heads up to 64 wide keep it on chip between the
- * tokens). h_in may be NULL (zero state) or equal h_out. S = 0 carries the
+ * tokens). For draft verification, call out of place: h_in then stays the
+ * state to roll back to, and if only the first j tokens are accepted, a call
+ * over those j tokens from h_in gives the state to keep.
+ * h_in may be NULL (zero state) or equal h_out. S = 0 carries the
  * state over unchanged (h_out = h_in, zeros when h_in is NULL; the token
  * arrays may be NULL); N = 0 does nothing. gdn_step is this call with S = 1
  * and the [N,H,*] layouts. */

@@ -286,3 +286,27 @@ def test_prefill_then_decode():
                            f64(x["A_log"]), f64(x["h0"]))
     assert_close("decode o", host(o), ro[:, T0:], TOL["bf16"])
     assert_close("final state", host(h), rh, TOL["bf16"])
+
+
+def test_draft_rollback():
+    """Verification of a three-token draft out of place: h_in is left bit for
+    bit; with only the first two tokens accepted, a second call over them
+    from h_in gives the state the oracle reaches after those two tokens."""
+    say("draft rollback N8 H4 d56 S3 -> accept 2")
+    x = gi.gen_seq(8, 3, 4, 56, 56, "bf16", seed=7670, h0="randn", decay="weak")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log, h_in = dev(x["g"]), dev(x["beta"]), dev(x["A_log"]), dev(x["h0"])
+    keep = h_in.clone()
+    _, h3 = gdn.step_tokens(q, k, v, g, beta, A_log, h_in)
+    two = lambda t: t[:, :2].contiguous()
+    o2, h2 = gdn.step_tokens(two(q), two(k), two(v), two(g), two(beta), A_log, h_in)
+    torch.cuda.synchronize()
+    assert torch.equal(h_in, keep)
+    t2 = lambda a: f64(a)[:, :2]
+    ro, rh = _oracle().fwd(t2(x["q"]), t2(x["k"]), t2(x["v"]), t2(x["g"]), t2(x["beta"]), f64(x["A_log"]),
+                           f64(x["h0"]))
+    assert_close("o of the accepted tokens", host(o2), ro, TOL["bf16"])
+    assert_close("state after the accepted tokens", host(h2), rh, TOL["bf16"])
+    _, r3 = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]), f64(x["A_log"]),
+                          f64(x["h0"]))
+    assert_close("state after the whole draft", host(h3), r3, TOL["bf16"])
