@@ -10,7 +10,7 @@ calls raise.
     grads      = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, context=ctx)
     o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
     o, h      = step_tokens(q, k, v, g, beta, A_log, h_in)     # [N, S, H, *] tokens
-    o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0)
+    o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0, additive, gate_logits)
 """
 from __future__ import annotations
 
@@ -19,8 +19,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "step", "step_tokens", "GatedDeltaRule", "GdnError", "lib", "EXPORTS", "LIB_PATH",
-           "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size",
+__all__ = ["fwd", "bwd", "step", "step_tokens", "GatedDeltaRule", "GdnError", "lib", "EXPORTS",
+           "LIB_PATH", "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size",
            "LaunchTimer"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -342,10 +342,12 @@ class GatedDeltaRule(torch.autograd.Function):
     per-chunk key blocks), backward reads it instead of recomputing."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False):
-        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, save_context=True)
+    def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False, gate_logits=False):
+        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, gate_logits=gate_logits,
+                        save_context=True)
         ctx.save_for_backward(q, k, v, g, beta, A_log, h0, cs)
         ctx.additive = additive
+        ctx.gate_logits = gate_logits
         return o, hT
 
     @staticmethod
@@ -355,5 +357,5 @@ class GatedDeltaRule(torch.autograd.Function):
             do = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
         r = bwd(q, k, v, g, beta, A_log, do.contiguous(), h0,
                 None if dhT is None else dhT.contiguous(), context=cs,
-                additive=ctx.additive, want_dh0=h0 is not None)
-        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None
+                additive=ctx.additive, gate_logits=ctx.gate_logits, want_dh0=h0 is not None)
+        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None, None

@@ -44,7 +44,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libgdn.so; always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp]

@@ -226,13 +226,24 @@ struct Aux {
 };
 thread_local Aux g_aux[64];
 
-hipError_t aux_of_current(Aux *&out) {
+// out = the current device's second stream, created here on first use. When
+// it does not exist yet and `strm` is being captured into a graph, nothing is
+// created (a stream or event made in the middle of a capture would be a side
+// effect of the capture) and out = nullptr: the caller then runs on `strm` alone.
+hipError_t aux_of_current(Aux *&out, hipStream_t strm) {
+    out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     Aux &x = g_aux[dev];
     if (!x.side) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(strm, &cap) != hipSuccess) {
+            (void)hipGetLastError(); // a failed query must not fail a later launch check
+            return hipSuccess;
+        }
+        if (cap != hipStreamCaptureStatusNone) return hipSuccess;
         e = hipStreamCreateWithFlags(&x.side, hipStreamNonBlocking);
         if (e != hipSuccess) return e;
         for (hipEvent_t &ev : x.ev) {
@@ -254,10 +265,20 @@ int fwd_segments(const gdn_shape_t *s, bool bf, int D) {
 
 // Forward pass into caller-provided buffers: U, NK (and Tm, γ) of every
 // chunk, then the serial state pass (o may be null: states only). hs: fp32
-// [B,H,dk,dv] hand-off state between chunk ranges.
+// [B,H,dk,dv] hand-off state between chunk ranges. With one_stream (or when
+// no second stream can be had) everything runs on `strm` as a single chunk
+// range; the results are the same bit for bit, only the overlap is lost.
 hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
-                       void *Tsave, float *gam, float *hs, void *o, float *hT, void *cs, hipStream_t strm) {
-    const int NC = nchunks(s), nseg = fwd_segments(s, bf, D);
+                       void *Tsave, float *gam, float *hs, void *o, float *hT, void *cs, hipStream_t strm,
+                       bool one_stream = false) {
+    const int NC = nchunks(s);
+    int nseg = one_stream ? 1 : fwd_segments(s, bf, D);
+    Aux *x = nullptr;
+    if (nseg > 1) {
+        const hipError_t e = aux_of_current(x, strm);
+        if (e != hipSuccess) return e;
+        if (!x) nseg = 1;
+    }
     gdn::PrepArgs pa;
     pa.s = sa;
     pa.U = U;
@@ -286,8 +307,6 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
         fa.hT = hT;
         return timed(K_FWD_CHAIN, [&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
     }
-    Aux *x = nullptr;
-    if ((he = aux_of_current(x)) != hipSuccess) return he;
     // fork: the second stream starts after the caller's earlier work
     if ((he = hipEventRecord(x->ev[0], strm)) != hipSuccess) return he;
     if ((he = hipStreamWaitEvent(x->side, x->ev[0], 0)) != hipSuccess) return he;
@@ -349,9 +368,14 @@ static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *h0, const void 
     return hip_status(he, "gdn_bwd (empty sequence)");
 }
 
-gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
-                     void *ws, size_t ws_bytes, void *stream) {
+} // extern "C"
+
+namespace gdn {
+
+gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                       void *ws, size_t ws_bytes, void *stream, bool one_stream,
+                       gdn_status_t (*ws_lookup)(void *&ws)) {
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
     if (s->T == 0) return fwd_empty(s, h0, hT, (hipStream_t)stream);
@@ -365,9 +389,13 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
     if (ctx && !aligned(ctx, 256)) return fail(GDN_EINVAL, "ctx must be 256-byte aligned");
     const size_t need = gdn_fwd_workspace_size(s);
-    if (!ws || ws_bytes < need)
-        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-    if (!aligned(ws, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    if (!ws_lookup) {
+        if (!ws || ws_bytes < need)
+            return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+        if (!aligned(ws, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    } else if (ws_bytes < need) {
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed, %zu available", need, ws_bytes);
+    }
     const size_t e = esize(s->dtype), BTH = (size_t)s->B * s->T * s->H;
     const size_t sb = (size_t)s->B * s->H * s->dk * s->dv * 4;
     const Range in[] = {{q, BTH * s->dk * e, "q"},     {k, BTH * s->dk * e, "k"}, {v, BTH * s->dv * e, "v"},
@@ -376,9 +404,12 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     const Range out[] = {{o, BTH * s->dv * e, "o"},
                          {hT, hT ? sb : 0, "hT"},
                          {ctx, ctx ? ctx_bytes(s) : 0, "ctx"},
-                         {ws, need, "workspace"}};
+                         {ws, ws_lookup ? 0 : need, "workspace"}};
     st = check_aliasing(in, 7, out, 4);
     if (st != GDN_OK) return st;
+    // a workspace the library owns is looked up only once the call is known
+    // to be valid (its lookup is the first device call)
+    if (ws_lookup && (st = ws_lookup(ws)) != GDN_OK) return st;
     const bool bf = s->dtype == GDN_BF16;
     const int D = pad_of(s);
     char *w = (char *)ws, *c = (char *)ctx;
@@ -389,8 +420,21 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
     float *gam = (float *)(w + align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)));
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
-    return hip_status(run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, o, hT, ctx, (hipStream_t)stream),
-                      "gdn_fwd launch");
+    return hip_status(
+        run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, o, hT, ctx, (hipStream_t)stream, one_stream),
+        "gdn_fwd launch");
+}
+
+gdn_status_t fail_detail(gdn_status_t st, const char *text) { return fail(st, "%s", text); }
+
+} // namespace gdn
+
+extern "C" {
+
+gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                     void *ws, size_t ws_bytes, void *stream) {
+    return gdn::fwd_entry(s, q, k, v, g, beta, A_log, h0, o, hT, ctx, ws, ws_bytes, stream, false, nullptr);
 }
 
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,

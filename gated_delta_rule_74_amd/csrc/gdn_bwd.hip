@@ -1285,8 +1285,10 @@ hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t
 }
 
 // Blocks of a persistent kernel that are resident at once on the current
-// device (compute units x blocks per unit), looked up once per device.
-template <typename K> static hipError_t resident_blocks(K kernel, int &out) {
+// device (compute units x blocks per unit), looked up once per device and
+// kernel: KERNEL is the kernel itself, so every instance keeps its own cache.
+template <auto KERNEL> static hipError_t resident_blocks(int &out) {
+    const auto kernel = KERNEL;
     static std::atomic<int> cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1307,7 +1309,7 @@ template <typename K> static hipError_t resident_blocks(K kernel, int &out) {
 template <bool BF, int D, bool VEC> static hipError_t local_launch(const BwdLocalArgs &a, hipStream_t st) {
     const int nch = a.s.B * a.s.H * a.s.NC;
     int grid = 0;
-    const hipError_t e = resident_blocks(bwd_local_kernel<BF, D, VEC>, grid);
+    const hipError_t e = resident_blocks<bwd_local_kernel<BF, D, VEC>>(grid);
     if (e != hipSuccess) return e;
     grid = grid < nch ? grid : nch;
     hipLaunchKernelGGL((bwd_local_kernel<BF, D, VEC>), dim3(grid), dim3(NTHR), 0, st, a);

@@ -5,7 +5,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
+
+// gdn_fwd with a choice of streams: one_stream runs every launch on the
+// caller's stream (no second stream is created or used). With ws_lookup set,
+// ws is ignored: once every argument has passed validation, ws_lookup
+// supplies the workspace (ws_bytes long, library-owned, so it aliases no
+// argument).
+gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                       void *ws, size_t ws_bytes, void *stream, bool one_stream,
+                       gdn_status_t (*ws_lookup)(void *&ws));
+// Sets the text gdn_last_error_detail() returns and passes st through.
+gdn_status_t fail_detail(gdn_status_t st, const char *text);
 
 struct SeqArgs {
     const void *q, *k, *v;

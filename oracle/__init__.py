@@ -62,10 +62,16 @@ def _load():
 
 
 def default_threads() -> int:
+    """Cores this process may use: its affinity mask, capped by
+    OMP_NUM_THREADS when that is set (a host's CPU share per job)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
 
 
 def _f64(x):

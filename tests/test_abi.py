@@ -185,3 +185,4 @@ def test_empty_decode_host_logic(L):
     assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, None, None, None) == EINVAL
     shifted = ctypes.c_void_p(h.value + 4)
     assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, shifted, None, None) == EINVAL
+

@@ -75,17 +75,18 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     _write_counters(str(tmp_path / "write"), "WRITE_SIZE",
                     [("__amd_rocclr_copyBuffer", copy_kib), ("void gdn::bwd_local_kernel<true, 64, true>(x)", 500.0),
                      ("void gdn::bwd_local_kernel<true, 64, true>(x)", 500.0)])
-    bench.traffic_summary(str(tmp_path / "fetch"), str(tmp_path / "write"))
+    bench.traffic_summary(str(tmp_path / "fetch"), str(tmp_path / "write"), bench.HEADLINE)
     import json
 
-    with open(root / "profiles" / f"bwd_local_{bench.WORKLOAD}_traffic.json") as f:
+    with open(root / "profiles" / f"bwd_local_{bench.HEADLINE}_traffic.json") as f:
         rec = json.load(f)
     assert rec["copy_fetch_scale"] == 0.5 and rec["copy_write_scale"] == 1.0
     assert rec["read_bytes"] == round(2000.0 * 1024 * 0.5)
     assert rec["write_bytes"] == round(500.0 * 1024)
     assert rec["traffic_bytes"] == rec["read_bytes"] + rec["write_bytes"]
     assert rec["source_hash"] == bench.source_hash("bwd_local")
-    assert bench.load_traffic("bwd_local") == rec["traffic_bytes"]
+    assert bench.load_traffic("bwd_local", bench.HEADLINE) == rec["traffic_bytes"]
+    assert bench.load_traffic("bwd_local", "long_ctx") is None
     assert (root / "profiles" / "traffic_fwdbwd_model.txt").exists()
 
 
@@ -105,10 +106,33 @@ def test_mfma_summary_arithmetic(tmp_path, monkeypatch):
         f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
         for cn, v in vals.items():
             f.write(f'7,"{name}",{cn},{v},1000,1001000\n')
-    bench.mfma_summary(str(d))
-    row = [ln for ln in open(tmp_path / "profiles" / f"mfma_{bench.WORKLOAD}.txt") if ln.startswith("bwd_local")]
+    bench.mfma_summary(str(d), bench.HEADLINE)
+    row = [ln for ln in open(tmp_path / "profiles" / f"mfma_{bench.HEADLINE}.txt") if ln.startswith("bwd_local")]
     assert len(row) == 1
     f = row[0].split()
     assert f[1] == "1" and float(f[2]) == 25.0
     assert float(f[3]) == 0.512 and float(f[4]) == 0.0
     assert float(f[6]) == 1000.0 and float(f[7]) == 0.5
+
+
+def test_kernel_names_map_to_timed_kernels():
+    """Device kernel symbols (every instance, the wave-specialised and wide
+    variants included) are grouped under the timed kernel they belong to."""
+    assert bench.kernel_of("void gdn::fwd_chain_ws_kernel<64, true>(gdn::FwdChainArgs)") == "fwd_chain"
+    assert bench.kernel_of("void gdn::bwd_local_wide_kernel<true>(gdn::BwdLocalArgs)") == "bwd_local"
+    assert bench.kernel_of("gdn::dA_reduce_kernel(float const*, float*, int, int, int)") == "dA_reduce"
+    assert bench.kernel_of("void gdn::step_kernel<true, 64, true>(gdn::StepArgs)") is None
+    assert bench.kernel_of("__amd_rocclr_copyBuffer") is None
+
+
+def test_long_context_model():
+    # B1 H16 T32768 d128: 8192 chunk-heads
+    flops, nbytes = bench.step_model(1, 32768, 16, 128)
+    assert flops == pytest.approx(292.77e9, rel=1e-3)
+    assert nbytes == pytest.approx(1493.17e6, rel=1e-4)
+
+
+def test_sample_units():
+    assert bench._sample_units(1.0, 128, 16, 4.0) == 64     # 4 s x 16 threads of 1 s units
+    assert bench._sample_units(0.001, 128, 16, 4.0) == 128  # capped at the whole workload
+    assert bench._sample_units(100.0, 128, 16, 4.0) == 1    # at least one unit

@@ -170,22 +170,34 @@ def test_autograd_function():
         assert_close(f"autograd {key}", host(ts[name].grad), ref[key], TOL["bf16"])
 
 
-def test_full_size_long_context_fwdbwd_sampled():
+@pytest.mark.parametrize("decay", ["normal", "weak"])
+def test_full_size_long_context_fwdbwd(decay):
     """B1 H16 T32768 d128 bf16, nonzero initial state (the long-context
-    configuration, weak decay so the 512-step chain matters): oracle on two
-    sampled heads."""
-    say("bwd full long_ctx")
-    x = gi.gen_config("long_ctx", decay="weak")
-    check_bwd(x, "bf16", units=[3, 12])
+    configuration; with weak decay the 512-step chain matters): every
+    gradient of every head, and dA_log, against the oracle."""
+    say(f"bwd full long_ctx decay={decay}")
+    x = gi.gen_config("long_ctx", decay=decay)
+    check_bwd(x, "bf16")
 
 
 @pytest.mark.parametrize("decay", ["normal", "weak"])
-def test_full_size_fwdbwd_sampled(decay):
+def test_full_size_fwdbwd(decay):
     """B8 H16 T4096 d56 bf16 at full size with the launch configuration the
-    benchmark times (saved chunk states); oracle on sampled (b, h) units."""
+    benchmark times (saved context): every gradient of every (b, h) unit, and
+    dA_log, against the oracle."""
     say(f"bwd full fwdbwd_model decay={decay}")
     x = gi.gen_config("fwdbwd_model", decay=decay)
-    check_bwd(x, "bf16", units=[0, 45, 90, 127])
+    check_bwd(x, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 56), ("f32", 16)])
+def test_beta_zero(dtype, d):
+    """beta = 0: nothing is written, yet dbeta is not zero (every write's
+    effect is still differentiated); all gradients against the oracle."""
+    say(f"bwd beta = 0 {dtype} d{d}")
+    x = gi.gen_seq(2, 200, 3, d, d, dtype, seed=7720 + d, h0="randn", with_do=True, decay="weak")
+    x["beta"] = np.zeros_like(x["beta"])
+    check_bwd(with_dhT(x, 14), dtype)
 
 
 def test_fwd_bwd_graph_replay():

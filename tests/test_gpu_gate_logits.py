@@ -123,3 +123,22 @@ def test_additive_with_gate_logits(dtype, d):
                      f64(x["h0"]), delta=False)
     assert_close("decode o", host(od), rdo, tol)
     assert_close("decode state", host(hd), rdh, tol)
+
+
+def test_autograd_with_gate_logits():
+    """GatedDeltaRule.apply with gate_logits=True: gradients reach the logits
+    (through the kernels' sigmoid) and match the oracle's chain rule."""
+    say("gate logits through autograd B1 T100 H2 d56 bf16")
+    x = with_logits(gi.gen_seq(1, 100, 2, 56, 56, "bf16", seed=7425, h0="randn", with_do=True,
+                               decay="weak"), 7426)
+    ts = {n: dev(x[n]).requires_grad_(True) for n in ("q", "k", "v", "gl", "bl", "A_log", "h0")}
+    o, hT = gdn.GatedDeltaRule.apply(ts["q"], ts["k"], ts["v"], ts["gl"], ts["bl"], ts["A_log"],
+                                     ts["h0"], False, True)
+    o.backward(dev(x["do"]))
+    gs, bs = _ref_gates(x)
+    O = _oracle()
+    rg = O.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), gs, bs, f64(x["A_log"]), f64(x["h0"]), f64(x["do"]))
+    ref = dict(rg, dg=O.logit_grads(rg["dg"], gs), dbeta=O.logit_grads(rg["dbeta"], bs))
+    for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("gl", "dg"), ("bl", "dbeta"),
+                      ("A_log", "dA_log"), ("h0", "dh0")]:
+        assert_close(f"autograd {key}", host(ts[name].grad), ref[key], TOL["bf16"])

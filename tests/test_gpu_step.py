@@ -78,8 +78,8 @@ def test_decode_head_dims(dk, dv):
 
 
 def test_decode_chain_matches_forward():
-    """1024 consecutive steps equal one forward pass over the same 1024 tokens
-    (checked against the oracle forward on one sequence)."""
+    """256 consecutive in-place steps of 2 sequences x 2 heads equal one
+    oracle forward pass over the same 256 tokens."""
     x = gi.gen_decode(2, 2, 56, 56, 256, "bf16", decay="weak")
     got_o, got_h = run_chain(x, 256)
     # rearrange [steps, N, H, .] -> [N, steps, H, .]
@@ -310,3 +310,31 @@ def test_draft_rollback():
     _, r3 = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]), f64(x["A_log"]),
                           f64(x["h0"]))
     assert_close("state after the whole draft", host(h3), r3, TOL["bf16"])
+
+
+@pytest.mark.parametrize("decay", ["normal", "weak"])
+def test_decode_step_as_configured(decay):
+    """The decode workload as configured: 256 sequences x 16 heads x d56,
+    bf16 tokens, fp32 state from 0.1 N(0,1), 1024 consecutive in-place
+    steps. Every output of every step and the final state are compared with
+    the oracle's serial forward over the same 1024 tokens per sequence (a
+    chain of oracle steps equals that forward; pinned on the CPU)."""
+    c = gi.CONFIGS["decode_step"]
+    N, H, dk, dv, S = c.B, c.H, c.dk, c.dv, c.steps
+    say(f"step as configured N{N} H{H} d{dk} {S} steps decay={decay}")
+    x = gi.gen_decode(N, H, dk, dv, S, c.dtype, seed=c.seed, decay=decay)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    g, beta, A_log = dev(x["g"]), dev(x["beta"]), dev(x["A_log"])
+    h = dev(x["h0"]).clone()
+    o = torch.empty((S, N, H, dv), dtype=torch.bfloat16, device=q.device)
+    for t in range(S):
+        gdn.step(q[t], k[t], v[t], g[t], beta[t], A_log, h, h, o=o[t])
+    torch.cuda.synchronize()
+    del q, k, v
+    # [steps, N, H, .] -> [N, steps, H, .], one array at a time
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(f64(a), 0, 1))
+    ro, rh = _oracle().fwd(tr(x["q"]), tr(x["k"]), tr(x["v"]), tr(x["g"]), tr(x["beta"]),
+                           f64(x["A_log"]), f64(x["h0"]))
+    got = np.swapaxes(host(o), 0, 1)
+    assert_close(f"o, all {S} steps", got, ro, TOL["bf16"])
+    assert_close("final state", host(h), rh, TOL["bf16"])
