@@ -11,6 +11,7 @@ calls raise.
     o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
     o, h      = step_tokens(q, k, v, g, beta, A_log, h_in)     # [N, S, H, *] tokens
     o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0, additive, gate_logits)
+    o, hT, ctx = fwd_noalloc(q, k, v, g, beta, A_log, h0, o=o)   # no device allocation
 """
 from __future__ import annotations
 
@@ -19,17 +20,18 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "step", "step_tokens", "GatedDeltaRule", "GdnError", "lib", "EXPORTS",
+__all__ = ["fwd", "fwd_noalloc", "bwd", "step", "step_tokens", "GatedDeltaRule", "GdnError", "lib", "EXPORTS",
            "LIB_PATH", "context_size", "context_states", "fwd_workspace_size", "bwd_workspace_size",
-           "LaunchTimer"]
+           "LaunchTimer", "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ["gdn_fwd", "gdn_bwd", "gdn_step", "gdn_step_tokens", "gdn_fwd_workspace_size", "gdn_bwd_workspace_size",
            "gdn_fwd_context_size", "gdn_time_launches", "gdn_launch_kind", "gdn_status_string",
-           "gdn_last_error_detail"]
+           "gdn_last_error_detail", "gdn_fwd_noalloc"]
 
 GDN_F32, GDN_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 GDN_FLAG_ADDITIVE = 1
 GDN_FLAG_GATE_LOGITS = 2
 _lib = None
@@ -59,10 +61,11 @@ def lib():
         P, S, Z = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_size_t
         I32, U32 = ctypes.c_int32, ctypes.c_uint32
         L.gdn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.gdn_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P]
         L.gdn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
         L.gdn_step_tokens.argtypes = [I32, I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
-        for f in (L.gdn_fwd, L.gdn_bwd, L.gdn_step, L.gdn_step_tokens):
+        for f in (L.gdn_fwd, L.gdn_fwd_noalloc, L.gdn_bwd, L.gdn_step, L.gdn_step_tokens):
             f.restype = ctypes.c_int
         for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_fwd_context_size):
             f.argtypes = [S]
@@ -199,6 +202,27 @@ def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, 
     st = L.gdn_fwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0), _p(o),
                    _p(hT), _p(context), _p(workspace), workspace.numel(), _stream(dev))
     _check("gdn_fwd", st)
+    return o, hT, context
+
+
+def fwd_noalloc(q, k, v, g, beta, A_log, h0=None, *, o, hT=None, context=None, additive=False,
+                gate_logits=False):
+    """The forward through gdn_fwd_noalloc: the library takes its workspace
+    from a static device array, so the call allocates nothing. Every output
+    is the caller's (o may be None only for a state-only pass, given
+    explicitly as o=None). Returns (o, hT, context)."""
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
+    s = _shape(q, v, additive, gate_logits)
+    dev = q.device
+    _need(o, "o", q.dtype, (B, T, H, dv), dev)
+    _need(hT, "hT", torch.float32, (B, H, dk, dv), dev)
+    _need(context, "context", torch.uint8, None, dev)
+    L = lib()
+    if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
+        raise ValueError("context is smaller than gdn_fwd_context_size()")
+    st = L.gdn_fwd_noalloc(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0),
+                           _p(o), _p(hT), _p(context), _stream(dev))
+    _check("gdn_fwd_noalloc", st)
     return o, hT, context
 
 

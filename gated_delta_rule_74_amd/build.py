@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_step.hip", "gdn_util.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_step.hip", "gdn_util.hip", "gdn_noalloc.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -121,6 +121,25 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
                      const float *g, const float *beta, const float *A_log, const float *h0,
                      void *o, float *hT, void *ctx, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the static device scratch gdn_fwd_noalloc uses as its workspace
+ * (64 MiB per GPU, held until the process ends). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdn_fwd without a workspace argument and without any device allocation,
+ * for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same computation,
+ * arguments and results as gdn_fwd (bit for bit), with every launch on
+ * `stream`. The workspace is a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES in the library, one per GPU, shared by every
+ * call on that GPU: calls that overlap in time on one GPU race and must be
+ * ordered by the caller (e.g. issued on one stream). Shapes whose
+ * gdn_fwd_workspace_size() exceeds GDN_NOALLOC_SCRATCH_BYTES are rejected
+ * with GDN_EWORKSPACE before anything is enqueued (at d = 56 in bf16 the
+ * scratch holds about 290,000 token-heads, e.g. B*T = 18,000 at H = 16). */
+gdn_status_t gdn_fwd_noalloc(const gdn_shape_t *s, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *A_log, const float *h0,
+                             void *o, float *hT, void *ctx, void *stream);
+
 /* Backward pass: gradients of sum(do * o) + sum(dhT * hT) with respect to q,
  * k, v, g, beta, A_log and h0, by the reverse-chunk derivative of the chunked
  * forward. Inputs are those of the gdn_fwd call; do is the upstream gradient of

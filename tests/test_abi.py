@@ -186,3 +186,22 @@ def test_empty_decode_host_logic(L):
     shifted = ctypes.c_void_p(h.value + 4)
     assert L.gdn_step_tokens(4, 0, 16, 56, 56, 1, 0, *[None] * 6, h, shifted, None, None) == EINVAL
 
+
+def test_fwd_noalloc_validation(L):
+    """The allocation-free forward rejects a shape whose workspace exceeds its
+    static scratch, and bad arguments, before any device call."""
+    s = gdn.Shape(8, 4096, 16, 56, 56, 1, 64, 0)  # the layer shape: far beyond 64 MiB
+    need = L.gdn_fwd_workspace_size(ctypes.byref(s))
+    assert need > gdn.NOALLOC_SCRATCH_BYTES
+    args = [fake(i) for i in range(1, 7)] + [None, fake(7), None, None, None]
+    assert L.gdn_fwd_noalloc(ctypes.byref(s), *args) == EWORKSPACE
+    assert b"static scratch" in L.gdn_last_error_detail()
+    small = gdn.Shape(1, 256, 4, 56, 56, 1, 64, 0)
+    assert L.gdn_fwd_workspace_size(ctypes.byref(small)) <= gdn.NOALLOC_SCRATCH_BYTES
+    bad = list(args)
+    bad[0] = None  # q
+    assert L.gdn_fwd_noalloc(ctypes.byref(small), *bad) == EINVAL
+    bad = list(args)
+    bad[7] = args[0]  # o aliases q
+    assert L.gdn_fwd_noalloc(ctypes.byref(small), *bad) == EINVAL
+    assert L.gdn_fwd_noalloc(ctypes.byref(gdn.Shape(1, 8, 2, 16, 16, 1, 32, 0)), *args) == EUNSUPPORTED
