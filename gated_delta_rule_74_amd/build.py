@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_step.hip", "gdn_util.hip", "gdn_noalloc.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_bwd128.hip", "gdn_step.hip", "gdn_util.hip", "gdn_noalloc.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -44,7 +44,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libgdn.so; always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp]

@@ -1332,7 +1332,7 @@ hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t
         switch (D) {
         case 32: return local_inst<true, 32>(a, st);
         case 64: return local_inst<true, 64>(a, st);
-        case 128: return a.wide ? wide_inst<true>(a, st) : hipErrorInvalidValue;
+        case 128: return launch_bwd_local128(a, st);
         }
     } else {
         switch (D) {
@@ -1345,7 +1345,7 @@ hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t
 }
 
 size_t bwd_wide_scratch_bytes(bool bf16, int D, int nchunks_total) {
-    if (bf16 ? D <= 64 : D <= 16) return 0;
+    if (bf16 || D <= 16) return 0;
     const int grid = nchunks_total < WIDE_GRID ? nchunks_total : WIDE_GRID;
     return (size_t)grid * WIDE_SCRATCH * sizeof(float);
 }

@@ -1,0 +1,551 @@
+// Local gradients of the chunked gated delta rule for bf16 heads wider than
+// 64 (padded to 128, e.g. the long-context shape with d_k = d_v = 128).
+//
+// The formulas are those of bwd_local_kernel in gdn_bwd.hip (reverse of the
+// per-chunk closed form of "GDN & MLA Mechanism Deep-Dive", Step 5, with the
+// WY/UT representation): given the chunk-start state h, the gradient dh'
+// with respect to the chunk-end state, the saved U, -Kw and Tm,
+//   W   = U - Kw h,  P = (Q K^T) o Gam,  dW = P^T dO + diag(e^{gam_n-gam}) K dh'
+//   dQ  = diag(e^gam) dO h^T + (dP o Gam) K,       dP = dO W^T (lower)
+//   dKw = -dW h^T,  dV' = Tm^T dW,  dK' = Tm^T dKw,  dL = -(dV' U^T + dK' Kw^T)
+//   dK  = (dP o Gam)^T Q + diag(e^{gam_n-gam}) W dh'^T + diag(beta e^gam) dK'
+//         + dS K + dS^T K,  dS = diag(beta)(dL o Gam),  dV = diag(beta) dV'
+// plus the dbeta / dgam row sums. Every intermediate stays on chip: one
+// workgroup per compute unit works through a list of chunks with
+// eight LDS regions (162 KB in all) reused phase by phase, all products as
+// bf16 16x16x32 MFMA tiles with fp32 accumulation. The two 128 x 128 states
+// are staged whole; the products that need both states run in the same
+// phase (K dh', W dh'^T next to dW) so the gradient state leaves LDS before
+// the chunk's value-side products start.
+//
+// Regions (bf16 unless noted; rows padded by 16 bytes):
+//   X0 K [64][136]                    whole chunk
+//   X1 h^T [128][136] (P1-P5) -> V | Q, then U (P6-P7) -> dq rows (P9)
+//   X2 -Kw | U (P1) -> dh'^T [128][136] (P4) -> dKw rows (P5-P6) -> -Kw (P7)
+//   X3 Q (P1) -> dO (P4-P5) -> -dV'^T [128][72] (P6-P9)
+//   X4 W^T [128][72] (P1-P5) -> dK'^T (P6-P7)
+//   X5 dW^T [128][72] (P4-P6) -> dk rows (P9)
+//   X6 P^T [64][72] (P1-P4) -> Tm (P6) -> row/column partial sums (P9, fp32)
+//   X7 (dP o Gam)^T [64][72] (P5-P6) -> dS^T (P7-P8)
+#include "gdn_common.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+// waves per workgroup: 8 (1.01 ms at the long-context shape) measured a
+// little faster than 16 (1.04 ms; 128 registers per lane, some spilled)
+#ifndef GDN_W128
+#define GDN_W128 8
+#endif
+constexpr int NWD = GDN_W128;
+constexpr int NTD = 64 * NWD; // threads per workgroup
+constexpr int DW = 128;       // padded head dim
+constexpr int KUNR = 2;       // K steps unrolled per product (register budget)
+
+struct Wide128 {
+    static constexpr int LDD = DW + 8; // [rows][LDD] token rows and states
+    static constexpr int LDC = C + 8;  // [rows][LDC] chunk-column matrices
+    static constexpr int sCD = C * LDD * 2;
+    static constexpr int sDD = DW * LDD * 2;
+    static constexpr int sDC = DW * LDC * 2;
+    static constexpr int sCC = C * LDC * 2;
+    static constexpr int sPart = (2 * C * (DW / 16) + 3 * C * 4) * 4;
+    static constexpr int x0 = 0;
+    static constexpr int x1 = x0 + sCD;
+    static constexpr int x2 = x1 + sDD;
+    static constexpr int x3 = x2 + sDD;
+    static constexpr int x4 = x3 + sDC;
+    static constexpr int x5 = x4 + sDC;
+    static constexpr int x6 = x5 + sDC;
+    static constexpr int x7 = x6 + sCC;
+    static constexpr int oEg = x7 + sCC;
+    static constexpr int oEgn = oEg + C * 4;
+    static constexpr int oBet = oEgn + C * 4;
+    static constexpr int oGch = oBet + C * 4;
+    static constexpr int oMisc = oGch + C * 4;
+    static constexpr int SIZE = oMisc + (16 + 2 * NWD) * 4;
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+
+    static_assert(sCD <= sDC && 2 * sCD == sDD, "region sharing");
+    static_assert(sPart <= sCC, "partial sums fit X6");
+};
+
+// Row sums of a contribution x at this wave's tiles of an MT x NT grid,
+// reduced over each tile's 16 columns at once, so a whole phase's
+// contribution costs one register: lane (g, r) keeps the sum of tile
+// i = (r % 4PW) / 4, row 4g + r % 4 (the other lanes hold copies).
+template <int MT, int NT> __device__ __forceinline__ float row_compact(const f32x4 *x, int lane) {
+    constexpr int PW = Tiles<MT, NT, NWD>::PW;
+    const int r = lane & 15;
+    float out = 0.f;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float sm = sum16(x[i][e]);
+            out = (r % (4 * PW) == 4 * i + e) ? sm : out;
+        }
+    return out;
+}
+
+// Column sums over the rows of this wave's tiles of a [C][C] grid (all in
+// one column block tn = wave % 4): lane (g, r) gets column 16 tn + r.
+__device__ __forceinline__ float col_compact(const f32x4 *x) {
+    constexpr int PW = Tiles<4, 4, NWD>::PW;
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) sm += (x[i][0] + x[i][1]) + (x[i][2] + x[i][3]);
+    sm += __shfl_xor(sm, 16, 64);
+    sm += __shfl_xor(sm, 32, 64);
+    return sm;
+}
+
+// Keeps a reduced value where it is formed: without this the compiler may
+// sink the reduction to the value's only use at the end of the chunk and
+// keep every partial sum alive until then.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
+// part[row * NT + tn] = the row sum row_compact left in this lane (one writer
+// per slot, so a later fixed-order sum over tn is deterministic).
+template <int MT, int NT> __device__ __forceinline__ void write_rows(float v, float *part, int wave, int lane) {
+    constexpr int PW = Tiles<MT, NT, NWD>::PW;
+    const int r = lane & 15, g = lane >> 4;
+    if (r < 4 * PW) {
+        const int t = wave + NWD * (r >> 2);
+        if (t < MT * NT) part[(16 * (t / NT) + 4 * g + (r & 3)) * NT + t % NT] = v;
+    }
+}
+
+} // namespace
+
+template <bool VEC>
+__global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
+    using L = Wide128;
+    using S = u16;
+    constexpr int D = DW, DT = D / 16, LDD = L::LDD, LDC = L::LDC;
+    constexpr int PWC = Tiles<4, 4, NWD>::PW;  // [C][C] tiles per wave
+    constexpr int PWD = Tiles<4, DT, NWD>::PW; // [C][D] tiles per wave
+    constexpr int PWM = Tiles<DT, 4, NWD>::PW; // [D][C] tiles per wave
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
+    S *X0 = (S *)(smem + L::x0), *X1 = (S *)(smem + L::x1), *X2 = (S *)(smem + L::x2);
+    S *X3 = (S *)(smem + L::x3), *X4 = (S *)(smem + L::x4), *X5 = (S *)(smem + L::x5);
+    S *X6 = (S *)(smem + L::x6), *X7 = (S *)(smem + L::x7);
+    S *X1b = X1 + C * LDD, *X2b = X2 + C * LDD; // second [64][LDD] halves
+    float *eg = (float *)(smem + L::oEg);
+    float *egn = (float *)(smem + L::oEgn);
+    float *bet = (float *)(smem + L::oBet);
+    float *gch = (float *)(smem + L::oGch);
+    float *misc = (float *)(smem + L::oMisc);
+
+    const SeqArgs &s = a.s;
+    const int tid0 = threadIdx.x;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
+    const bool add = s.additive != 0;
+    // Persistent blocks over chunks numbered heads fastest; block i runs on
+    // XCD i % 8 and, when the counts allow, each XCD walks one contiguous
+    // eighth of the numbering (chunks that share cache lines meet in one L2).
+    const int NCH = s.B * H * s.NC, G = gridDim.x;
+    const bool split = G % 8 == 0 && NCH % 8 == 0;
+    const int per = split ? NCH / 8 : NCH;
+    const int first = split ? ((int)blockIdx.x % 8) * per + (int)blockIdx.x / 8 : (int)blockIdx.x;
+    const int lim = split ? ((int)blockIdx.x % 8 + 1) * per : NCH;
+    const int step = split ? G / 8 : G;
+    struct Pos {
+        int lid, h, c, b;
+    };
+    const int sh = step % H, sc = (step / H) % s.NC, sb = step / (H * s.NC);
+    auto advance = [&](Pos p) {
+        p.lid += step;
+        p.h += sh;
+        int cy = p.h >= H;
+        p.h -= cy ? H : 0;
+        p.c += sc + cy;
+        cy = p.c >= s.NC;
+        p.c -= cy ? s.NC : 0;
+        p.b += sb + cy;
+        return p;
+    };
+
+    ChunkFrag<true, D, C, NTD> fk, fq, fv, fo, fn, fu;
+    ChunkFrag<true, D, D, NTD> fh, fd;
+    ChunkFrag<true, C, C, NTD> ft;
+    float gr = 0.f, br = 0.f, alr = 0.f;
+    auto fetch_early = [&](const Pos &p, int tid, int lane) {
+        const int h = p.h, c = p.c, b = p.b;
+        const int n = min(C, T - c * C);
+        const size_t row0 = (size_t)b * T + c * C, cb = ((size_t)b * H + h) * s.NC + c;
+        fk.template fetch<VEC>((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fq.template fetch<VEC>((const S *)s.q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        fh.template fetch<VEC>((const S *)a.cs + cb * dk * dv, (size_t)dk, dv, dk, tid);
+        fu.template fetch<VEC>((const S *)a.U + cb * C * dv, (size_t)dv, n, dv, tid);
+        if (!add) fn.template fetch<VEC>((const S *)a.NK + cb * C * dk, (size_t)dk, n, dk, tid);
+        alr = s.A_log[h];
+        gr = load_row_scalar(s.g + row0 * H + h, H, lane, n);
+        br = load_row_scalar(s.beta + row0 * H + h, H, lane, n);
+    };
+    if (first >= lim) return;
+    Pos cur{first, first % H, (first / H) % s.NC, first / (H * s.NC)};
+    fetch_early(cur, tid0, tid0 & 63);
+    for (;;) {
+    // the thread index is hidden from the optimiser at the top of every chunk,
+    // so per-lane addresses are formed where they are used
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int kq = lane >> 4, r16 = lane & 15;
+    const int h = cur.h, c = cur.c, b = cur.b;
+    const int bh = b * H + h;
+    const int t0 = c * C, n = min(C, T - t0);
+    // A = -exp(A_log) in fp32 (1 ulp): an fp64 exp would keep its polynomial
+    // constants in vector registers across the whole chunk loop
+    const double A = -(double)expf(alr);
+    const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
+    fo.template fetch<VEC>((const S *)a.dout + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
+    fd.template fetch<VEC>((const S *)a.dhs + cb * dk * dv, (size_t)dk, dv, dk, tid);
+
+    // dbeta / dgam contributions, row-summed per tile as they are formed
+    // (row_compact / col_compact): rb, rg over [C][D] grids (dbeta, dgam; the
+    // s_j terms of dgam enter rg with their sign, their total a per-wave
+    // slot); rbc row sums, xgr row sums and xgc column sums over [C][C]
+    float rb = 0.f, rg = 0.f, rbc = 0.f, xgr = 0.f, xgc = 0.f;
+
+    // ---- P1: K K^T, Q K^T, decay; W = U - Kw h
+    fk.stash(X0, LDD, tid);
+    fq.stash(X3, LDD, tid);
+    fh.stash(X1, LDD, tid);
+    if (!add) fn.stash(X2, LDD, tid);
+    fu.stash(X2b, LDD, tid);
+    __syncthreads();
+    // Gam at this lane's [C][C] positions stays in registers; P goes to LDS
+    // (read back for the dP o P sums) and K K^T o Gam is formed again when
+    // dL needs it
+    f32x4 gC[PWC];
+    {
+        f32x4 sq[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) sq[i] = zero4();
+        gemm<true, 4, 4, D, false, false, NWD, KUNR>(X3, LDD, X0, LDD, sq, wave, lane);
+        // decay of the chunk (lane = row) in every wave; Gam at this wave's
+        // [C][C] tile from the rows' and the column's log-decay
+        const float gl = lane < n ? gate_of(gr, s.logits) : 0.f;
+        const Decay dc = decay_lane(gl, A * LOG2E, lane);
+        if (wave == 0) {
+            gch[lane] = gl;
+            bet[lane] = lane < n ? gate_of(br, s.logits) : 0.f;
+            eg[lane] = dc.eg;
+            egn[lane] = dc.egn;
+            if (lane == 0) misc[0] = dc.eglast;
+        }
+        for_tiles<4, 4, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+            const double grow = __shfl(dc.gam2, row, 64), gcol = __shfl(dc.gam2, col, 64);
+            const float f = exp2_fast((float)(grow - gcol));
+            const float G = row >= col ? f : 0.f;
+            gC[i][e] = G;
+            sq[i][e] *= G;
+        });
+        store_T<true, 4, 4, NWD>(sq, X6, LDC, wave, lane); // P^T
+    }
+    {
+        f32x4 accW[PWD];
+        for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(X2b[row * LDD + col]); });
+        if (!add) gemm<true, 4, DT, D, false, false, NWD, KUNR>(X2, LDD, X1, LDD, accW, wave, lane); // + (-Kw) h
+        store_T<true, 4, DT, NWD>(accW, X4, LDC, wave, lane);                              // W^T
+    }
+    __syncthreads(); // P^T, W^T complete; Q, -Kw, U reads done
+    // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh';  dKt = W dh'^T;  <h, dh'>
+    fo.stash(X3, LDD, tid);
+    fd.stash(X2, LDD, tid);
+    ft.template fetch<VEC>((const S *)a.Tm + cb * C * C, (size_t)C, C, C, tid);
+    fv.template fetch<VEC>((const S *)s.v + (row0 * H + h) * dv, (size_t)H * dv, n, dv, tid);
+    __syncthreads();
+    f32x4 accKd[PWD];
+    {
+        f32x4 accdW[PWD], accX[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
+        gemm<true, 4, DT, C, false, true, NWD, KUNR>(X6, LDC, X3, LDD, accdW, wave, lane); // P^T dO
+        gemm<true, 4, DT, D, false, false, NWD, KUNR>(X0, LDD, X2, LDD, accX, wave, lane); // K dh'
+        for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
+        store_T<true, 4, DT, NWD>(accdW, X5, LDC, wave, lane); // dW^T
+        f32x4 accKt[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
+        gemm<true, 4, DT, D, true, true, NWD, KUNR>(X4, LDC, X2, LDD, accKt, wave, lane); // W dh'^T
+        // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
+        // enters dgam_j with a minus sign and the last row with its total
+        float st = 0.f;
+        for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+            const float x = egn[row] * accKt[i][e];
+            accKd[i][e] = x;
+            const float sx = x * to_f(X0[row * LDD + col]);
+            accKt[i][e] = -sx;
+            st += sx;
+        });
+        rg += row_compact<4, DT>(accKt, lane); pin(rg);
+        st = wave_sum(st);
+        if (lane == 0) misc[16 + NWD + wave] = st;
+        // <h, dh'> over the two staged states (padding is zero), one slot per wave
+        float hd = 0.f;
+        for (int it = tid; it < D * D / 8; it += NTD) {
+            const int row = it / (D / 8), c0 = (it % (D / 8)) * 8;
+            union {
+                uint4 u;
+                u16 x[8];
+            } hx, dx;
+            hx.u = *reinterpret_cast<const uint4 *>(X1 + row * LDD + c0);
+            dx.u = *reinterpret_cast<const uint4 *>(X2 + row * LDD + c0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hd += bf2f(hx.x[e]) * bf2f(dx.x[e]);
+        }
+        hd = wave_sum(hd);
+        if (lane == 0) misc[16 + wave] = hd;
+    }
+    __syncthreads(); // dW^T complete; dh' no longer read
+    // Q, -Kw and U are staged again in P6: requested again here (L2 holds them
+    // from the first request) rather than kept in registers since P1
+    {
+        const size_t qrow = (row0 * H + h) * dk;
+        fq.template fetch<VEC>((const S *)s.q + qrow, (size_t)H * dk, n, dk, tid);
+        if (!add) fn.template fetch<VEC>((const S *)a.NK + cb * C * dk, (size_t)dk, n, dk, tid);
+        fu.template fetch<VEC>((const S *)a.U + cb * C * dv, (size_t)dv, n, dv, tid);
+    }
+    // ---- P5: dOh = dO h^T; dKw = -dW h^T; dP = dO W^T
+    f32x4 accQ[PWD];
+#pragma unroll
+    for (int i = 0; i < PWD; ++i) accQ[i] = zero4();
+    gemm<true, 4, DT, D, false, true, NWD, KUNR>(X3, LDD, X1, LDD, accQ, wave, lane); // dO h^T
+    if (!add) {
+        f32x4 accM[PWM];
+#pragma unroll
+        for (int i = 0; i < PWM; ++i) accM[i] = zero4();
+        gemm<true, DT, 4, D, true, true, NWD, KUNR>(X1, LDD, X5, LDC, accM, wave, lane); // h dW^T
+#pragma unroll
+        for (int i = 0; i < PWM; ++i) accM[i] = -accM[i];
+        store_T<true, DT, 4, NWD>(accM, X2, LDD, wave, lane); // dKw, token rows
+    }
+    {
+        f32x4 accP[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) accP[i] = zero4();
+        gemm<true, 4, 4, D, false, true, NWD, KUNR>(X3, LDD, X4, LDC, accP, wave, lane); // dO W^T
+        f32x4 pp[PWC];
+        for_tiles<4, 4, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+            const float dp = row >= col ? accP[i][e] : 0.f;
+            pp[i][e] = dp * bf2f(X6[col * LDC + row]); // dP o P
+            accP[i][e] = dp * gC[i][e];
+        });
+        xgr += row_compact<4, 4>(pp, lane); pin(xgr);
+        xgc += col_compact(pp); pin(xgc);
+        store_T<true, 4, 4, NWD>(accP, X7, LDC, wave, lane); // (dP o Gam)^T
+    }
+    __syncthreads(); // h, dO, W^T no longer read
+    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw, dQ, dK += (dP o Gam)^T Q
+    ft.stash(X6, LDC, tid);
+    fv.stash(X1, LDD, tid);
+    fq.stash(X1b, LDD, tid);
+    __syncthreads();
+    {
+        f32x4 accV[PWD], accKp[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
+        gemm<true, 4, DT, C, true, false, NWD, KUNR>(X6, LDC, X5, LDC, accV, wave, lane);             // Tm^T dW
+        if (!add) gemm<true, 4, DT, C, true, true, NWD, KUNR>(X6, LDC, X2, LDD, accKp, wave, lane); // Tm^T dKw
+        {
+            f32x4 qq[PWD];
+            for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+                accQ[i][e] *= eg[row];
+                qq[i][e] = accQ[i][e] * to_f(X1b[row * LDD + col]); // e^{gam_i} q_i . dOh_i
+            });
+            rg += row_compact<4, DT>(qq, lane); pin(rg);
+        }
+        gemm<true, 4, DT, C, true, true, NWD, KUNR>(X7, LDC, X0, LDD, accQ, wave, lane);   // + (dP o Gam) K
+        gemm<true, 4, DT, C, false, true, NWD, KUNR>(X7, LDC, X1b, LDD, accKd, wave, lane); // + (dP o Gam)^T Q
+        __syncthreads(); // Tm, dW^T, dKw, Q reads done
+        {
+            f32x4 bb[PWD], gg[PWD];
+            for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+                const float kk = to_f(X0[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
+                bb[i][e] = to_f(X1[row * LDD + col]) * accV[i][e] + eg[row] * kk;
+                gg[i][e] = bet[row] * eg[row] * kk;
+                accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
+            });
+            rb += row_compact<4, DT>(bb, lane); pin(rb);
+            rg += row_compact<4, DT>(gg, lane); pin(rg);
+        }
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
+        store_T<true, 4, DT, NWD>(accV, X3, LDC, wave, lane); // -dV'^T (also the source of dv)
+        if (!add) {
+            store_T<true, 4, DT, NWD>(accKp, X4, LDC, wave, lane); // dK'^T
+            fn.stash(X2, LDD, tid);                               // -Kw again
+            fu.stash(X1b, LDD, tid);                              // U again
+        }
+    }
+    __syncthreads(); // V reads done
+    // ---- P7: dL = (-dV') U^T + dK' (-Kw)^T, dS;  P8: dK += dS K + dS^T K
+    if (!add) {
+        f32x4 accL[PWC], sk[PWC];
+#pragma unroll
+        for (int i = 0; i < PWC; ++i) accL[i] = sk[i] = zero4();
+        gemm<true, 4, 4, D, false, false, NWD, KUNR>(X0, LDD, X0, LDD, sk, wave, lane); // K K^T
+        gemm<true, 4, 4, D, true, false, NWD, KUNR>(X3, LDC, X1b, LDD, accL, wave, lane);
+        gemm<true, 4, 4, D, true, false, NWD, KUNR>(X4, LDC, X2, LDD, accL, wave, lane);
+        f32x4 lb[PWC], lg[PWC];
+        for_tiles<4, 4, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+            const float dl = (row > col) ? accL[i][e] : 0.f;
+            const float kkg = sk[i][e] * gC[i][e]; // (K K^T o Gam), strict lower where dl is used
+            lb[i][e] = dl * kkg;
+            lg[i][e] = dl * bet[row] * kkg; // dL o L
+            accL[i][e] = bet[row] * dl * gC[i][e];
+        });
+        rbc += row_compact<4, 4>(lb, lane); pin(rbc);
+        xgr += row_compact<4, 4>(lg, lane); pin(xgr);
+        xgc += col_compact(lg); pin(xgc);
+        store_T<true, 4, 4, NWD>(accL, X7, LDC, wave, lane); // dS^T
+        __syncthreads();
+        gemm<true, 4, DT, C, true, true, NWD, KUNR>(X7, LDC, X0, LDD, accKd, wave, lane);
+        gemm<true, 4, DT, C, false, true, NWD, KUNR>(X7, LDC, X0, LDD, accKd, wave, lane);
+    }
+    // every fragment is stashed and the products are done: request the next
+    // chunk's first inputs (the current one again after the last, so the loads
+    // never depend on a branch)
+    const Pos nxt = advance(cur);
+    const bool more = nxt.lid < lim;
+    fetch_early(more ? nxt : cur, tid, lane);
+    // dQ and dK leave through LDS as 16-byte rows (V and dW^T were last read
+    // before the barrier that ended P6)
+    store_N<true, 4, DT, NWD>(accQ, X1, LDD, wave, lane);
+    store_N<true, 4, DT, NWD>(accKd, X5, LDD, wave, lane);
+    // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
+    {
+        float *pRbD = (float *)X6, *pRgD = pRbD + C * DT;
+        float *pRbC = pRgD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
+        write_rows<4, 4>(rbc, pRbC, wave, lane);
+        write_rows<4, 4>(xgr, pRgC, wave, lane);
+        write_rows<4, DT>(rb, pRbD, wave, lane);
+        write_rows<4, DT>(rg, pRgD, wave, lane);
+        // column sums [col][slot]: slot j of a column block holds the sum of
+        // wave 4j + tn (slots past the block's waves hold zero)
+        if (lane < 16)
+            for (int j = wave / 4; j < 4; j += NWD / 4)
+                pCgC[(16 * (wave % 4) + lane) * 4 + j] = (j == wave / 4) ? xgc : 0.f;
+        __syncthreads();
+        {
+            S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+            S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+            S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+            constexpr int V = 8, NG = D / V;
+            if (VEC) {
+                for (int it = tid; it < C * NG; it += NTD) {
+                    const int j = it / NG, c0 = (it % NG) * V;
+                    if (j >= n) continue;
+                    if (c0 < dk) {
+                        *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(X1 + j * LDD + c0);
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
+                    }
+                    if (c0 < dv) {
+                        union {
+                            uint4 u;
+                            S x[V];
+                        } pk;
+                        const float nb = -bet[j];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) pk.x[e] = f2bf(nb * bf2f(X3[(c0 + e) * LDC + j]));
+                        *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
+                    }
+                }
+            } else {
+                for (int it = tid; it < C * D; it += NTD) {
+                    const int j = it / D, col = it % D;
+                    if (j >= n) continue;
+                    if (col < dk) {
+                        dq_out[(size_t)j * H * dk + col] = X1[j * LDD + col];
+                        dk_out[(size_t)j * H * dk + col] = X5[j * LDD + col];
+                    }
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = f2bf(-bet[j] * bf2f(X3[col * LDC + j]));
+                }
+            }
+        }
+        if (wave == 0) {
+            const int i = lane;
+            float db = 0.f, dgm = 0.f;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                db += pRbD[i * DT + t];
+                dgm += pRgD[i * DT + t];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                db += pRbC[i * 4 + t];
+                dgm += pRgC[i * 4 + t];
+                dgm -= pCgC[i * 4 + t];
+            }
+            // gam_n enters through e^{gam_n} h and e^{gam_n - gam_j}: its gradient
+            // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row (-s_j to row j
+            // is already in the row sums)
+            float hds = 0.f, stot = 0.f;
+            for (int w = 0; w < NWD; ++w) {
+                hds += misc[16 + w];
+                stot += misc[16 + NWD + w];
+            }
+            if (i == C - 1) dgm += misc[0] * hds + stot;
+            // dlam_r = sum_{i >= r} dgam_i = total - (prefix through r) + dgam_r
+            const float pre = wave_prefix(dgm);
+            const float x = lane_value(pre, 63) - pre + dgm;
+            const float dg = (float)A * x;
+            float p = (lane < n) ? gch[lane] * dg : 0.f;
+            if (lane < n) {
+                const size_t gi = (row0 + lane) * H + h;
+                // with logit inputs, through the sigmoid: d/dx = s (1 - s) d/ds
+                const float gs = gch[lane], bs = bet[lane];
+                a.dg[gi] = s.logits ? dg * gs * (1.f - gs) : dg;
+                a.dbeta[gi] = s.logits ? db * bs * (1.f - bs) : db;
+            }
+            p = wave_sum(p);
+            if (lane == 0) a.dA_part[cb] = p;
+        }
+    }
+    if (!more) break;
+    cur = nxt;
+    __syncthreads(); // outputs read from LDS before the next chunk's stashes
+    } // chunk loop
+}
+
+// Blocks resident at once on the current device for this kernel (compute
+// units x blocks per unit), looked up once per device.
+template <bool VEC> static hipError_t resident128(int &out) {
+    static int cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int &v = cache[dev & 63];
+    if (v <= 0) {
+        int cus = 0, per = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_local128_kernel<VEC>, NTD, 0)) != hipSuccess)
+            return e;
+        v = cus * (per > 0 ? per : 1);
+    }
+    out = v;
+    return hipSuccess;
+}
+
+template <bool VEC> static hipError_t launch128(const BwdLocalArgs &a, hipStream_t st) {
+    const int nch = a.s.B * a.s.H * a.s.NC;
+    int grid = 0;
+    const hipError_t e = resident128<VEC>(grid);
+    if (e != hipSuccess) return e;
+    grid = grid < nch ? grid : nch;
+    hipLaunchKernelGGL((bwd_local128_kernel<VEC>), dim3(grid), dim3(NTD), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_local128(const BwdLocalArgs &a, hipStream_t st) {
+    return vec_ok<true>(a.s) ? launch128<true>(a, st) : launch128<false>(a, st);
+}
+
+} // namespace gdn

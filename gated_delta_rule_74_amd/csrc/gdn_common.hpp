@@ -79,10 +79,11 @@ __device__ __forceinline__ f32x4 mma(const float *a, const float *b, f32x4 acc) 
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Number of 16x16 tiles a wave owns for an MT x NT tile grid.
-template <int MT, int NT> struct Tiles {
+// Number of 16x16 tiles a wave owns for an MT x NT tile grid spread over NW
+// waves (tile t -> wave t % NW).
+template <int MT, int NT, int NW = NWAVE> struct Tiles {
     static constexpr int N = MT * NT;
-    static constexpr int PW = (N + NWAVE - 1) / NWAVE;
+    static constexpr int PW = (N + NW - 1) / NW;
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -124,24 +125,28 @@ __device__ __forceinline__ short4_t operand_tr4(const u16 *X, int ld, int k0, in
 // acc[i] += A * B over K = KD for the tiles of this wave.
 // A is stored [M][K] (ATR = false) or [K][M] (ATR = true); B is stored [N][K]
 // (BTR = false, i.e. B transposed) or [K][N] (BTR = true). Row strides lda, ldb.
-template <bool BF, int MT, int NT, int KD, bool ATR = false, bool BTR = false>
+// KU > 0 limits the unrolling of the K loop (fewer operands in flight, for
+// kernels short of registers); 0 unrolls it fully.
+template <bool BF, int MT, int NT, int KD, bool ATR = false, bool BTR = false, int NW = NWAVE, int KU = 0>
 __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
                                      const typename Op<BF>::S *B, int ldb, f32x4 *acc, int wave,
                                      int lane) {
     using O = Op<BF>;
+    using TL = Tiles<MT, NT, NW>;
     static_assert(KD % O::KSTEP == 0, "contraction length must be a multiple of the MFMA K");
+    constexpr int UNR = KU > 0 ? KU : KD / O::KSTEP;
     const int r = lane & 15, kq = lane >> 4;
-    if constexpr (BF && NWAVE % NT == 0 && Tiles<MT, NT>::N % NWAVE == 0 && Tiles<MT, NT>::PW > 1) {
+    if constexpr (BF && NW % NT == 0 && TL::N % NW == 0 && TL::PW > 1) {
         // all tiles of this wave share the column block tn = wave % NT: read
         // each B operand once per K step and reuse it for every tile
         const int tn = wave % NT;
-#pragma unroll
+#pragma unroll UNR
         for (int k0 = 0; k0 < KD; k0 += O::KSTEP) {
             const bf16x8 bv = BTR ? operand_tr(B, ldb, k0, tn * 16, lane)
                                   : *reinterpret_cast<const bf16x8 *>(B + (tn * 16 + r) * ldb + k0 + kq * 8);
 #pragma unroll
-            for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-                const int tm = (wave + NWAVE * i) / NT;
+            for (int i = 0; i < TL::PW; ++i) {
+                const int tm = (wave + NW * i) / NT;
                 const bf16x8 av = ATR ? operand_tr(A, lda, k0, tm * 16, lane)
                                       : *reinterpret_cast<const bf16x8 *>(A + (tm * 16 + r) * lda + k0 + kq * 8);
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
@@ -150,11 +155,11 @@ __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
         return;
     }
 #pragma unroll
-    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-        const int t = wave + NWAVE * i;
-        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
         const int tm = t / NT, tn = t % NT;
-#pragma unroll
+#pragma unroll UNR
         for (int k0 = 0; k0 < KD; k0 += O::KSTEP) {
             if constexpr (BF) {
                 const bf16x8 av = ATR ? operand_tr(A, lda, k0, tm * 16, lane)
@@ -174,13 +179,14 @@ __device__ __forceinline__ void gemm(const typename Op<BF>::S *A, int lda,
 
 // Visit every element this wave owns in an MT x NT tile grid:
 // f(i, e, row, col) with acc index i and element e in 0..3.
-template <int MT, int NT, class F>
+template <int MT, int NT, int NW = NWAVE, class F>
 __device__ __forceinline__ void for_tiles(int wave, int lane, F &&f) {
+    using TL = Tiles<MT, NT, NW>;
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-        const int t = wave + NWAVE * i;
-        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
         const int tm = t / NT, tn = t % NT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f(i, e, tm * 16 + 4 * kq + e, tn * 16 + r);
@@ -190,14 +196,15 @@ __device__ __forceinline__ void for_tiles(int wave, int lane, F &&f) {
 // Store the tiles of this wave transposed: dst[col][row] (4 consecutive rows
 // per lane become 4 consecutive elements).
 // (optionally scaled per row by rs[row]).
-template <bool BF, int MT, int NT>
+template <bool BF, int MT, int NT, int NW = NWAVE>
 __device__ __forceinline__ void store_T(const f32x4 *acc, typename Op<BF>::S *dst, int ld, int wave,
                                         int lane, const float *rs = nullptr) {
+    using TL = Tiles<MT, NT, NW>;
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-        const int t = wave + NWAVE * i;
-        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
         const int tm = t / NT, tn = t % NT;
         const int row = tm * 16 + 4 * kq, col = tn * 16 + r;
         f32x4 x = acc[i];
@@ -216,10 +223,10 @@ __device__ __forceinline__ void store_T(const f32x4 *acc, typename Op<BF>::S *ds
     }
 }
 
-template <bool BF, int MT, int NT>
+template <bool BF, int MT, int NT, int NW = NWAVE>
 __device__ __forceinline__ void store_N(const f32x4 *acc, typename Op<BF>::S *dst, int ld, int wave,
                                         int lane) {
-    for_tiles<MT, NT>(wave, lane, [&](int i, int e, int row, int col) {
+    for_tiles<MT, NT, NW>(wave, lane, [&](int i, int e, int row, int col) {
         dst[row * ld + col] = from_f<BF>(acc[i][e]);
     });
 }
@@ -554,13 +561,14 @@ __device__ __forceinline__ Decay decay_lane(float g, double A2, int lane) {
 // i): the 16 lanes of a row group are summed inside their row, and lane
 // r == 0 writes part[row * NT + tn]. Every (row, tn) slot has exactly one
 // writer, so a later fixed-order sum over tn is deterministic.
-template <int MT, int NT>
+template <int MT, int NT, int NW = NWAVE>
 __device__ __forceinline__ void row_partials(const f32x4 *x, float *part, int wave, int lane) {
+    using TL = Tiles<MT, NT, NW>;
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-        const int t = wave + NWAVE * i;
-        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
         const int tm = t / NT, tn = t % NT;
         f32x4 s = x[i];
 #pragma unroll
@@ -573,13 +581,14 @@ __device__ __forceinline__ void row_partials(const f32x4 *x, float *part, int wa
 }
 
 // Per-tile column sums: part[col * MT + tm].
-template <int MT, int NT>
+template <int MT, int NT, int NW = NWAVE>
 __device__ __forceinline__ void col_partials(const f32x4 *x, float *part, int wave, int lane) {
+    using TL = Tiles<MT, NT, NW>;
     const int r = lane & 15;
 #pragma unroll
-    for (int i = 0; i < Tiles<MT, NT>::PW; ++i) {
-        const int t = wave + NWAVE * i;
-        if (Tiles<MT, NT>::N % NWAVE != 0 && t >= Tiles<MT, NT>::N) break;
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
         const int tm = t / NT, tn = t % NT;
         float s = (x[i][0] + x[i][1]) + (x[i][2] + x[i][3]);
         s += __shfl_xor(s, 16, 64);

@@ -110,6 +110,8 @@ hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t st);
 hipError_t launch_bwd_local(const BwdLocalArgs &a, bool bf16, int D, hipStream_t st);
+// bf16 heads wider than 64 (padded to 128): the LDS-resident wide kernel
+hipError_t launch_bwd_local128(const BwdLocalArgs &a, hipStream_t st);
 hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int NC, hipStream_t st);
 hipError_t launch_step(const StepArgs &a, bool bf16, hipStream_t st);
 // dst[0..n) = src[0..n), or zeros when src is null
