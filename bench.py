@@ -77,7 +77,7 @@ C = 64
 FLUSH_BYTES = 512 << 20    # larger than the Infinity Cache (256 MB) and the L2s
 
 # Kernels in launch order within one step (forward with context, backward).
-KERNELS = ["fwd_prep", "fwd_chain", "bwd_chain", "bwd_local", "dA_reduce"]
+KERNELS = ["fwd_prep", "fwd_chain", "fwd_scan", "bwd_chain", "bwd_scan", "bwd_local", "dA_reduce"]
 
 
 def kernel_bytes_per_token_head(d):
@@ -92,6 +92,8 @@ def kernel_bytes_per_token_head(d):
         "bwd_chain": 3 * e + 4,         # q, k, do, g
         "bwd_local": 4 * e + 8 + 3 * e + 8,  # q, k, v, do, g, beta -> dq, dk, dv, dg, dbeta
         "dA_reduce": 0,
+        "fwd_scan": 0,
+        "bwd_scan": 0,
     }
 
 
@@ -121,8 +123,9 @@ def kernel_flops(B, T, H, d):
 
 # translation unit of each timed kernel; every kernel also depends on the
 # shared headers and on the launch code of the C ABI
-KERNEL_SOURCE = {"fwd_prep": "gdn_fwd.hip", "fwd_chain": "gdn_fwd.hip", "bwd_chain": "gdn_bwd.hip",
-                 "bwd_local": "gdn_bwd.hip", "dA_reduce": "gdn_bwd.hip"}
+KERNEL_SOURCE = {"fwd_prep": "gdn_fwd.hip", "fwd_chain": "gdn_fwd.hip", "fwd_scan": "gdn_fwd.hip",
+                 "bwd_chain": "gdn_bwd.hip", "bwd_scan": "gdn_fwd.hip", "bwd_local": "gdn_bwd.hip",
+                 "dA_reduce": "gdn_bwd.hip"}
 SHARED_SOURCES = ("gdn_common.hpp", "gdn_launch.hpp", "gdn_api.cpp")
 
 
@@ -155,6 +158,8 @@ def kernel_of(name):
     """Which timed kernel a device kernel's symbol belongs to (None: not ours)."""
     if "gdn::" not in name:
         return None
+    if "gdn::range_scan" in name:  # one kernel serves the scans of both directions
+        return "fwd_scan"
     for k in KERNELS:
         if f"gdn::{k}" in name:  # fwd_chain_ws_kernel and bwd_local_wide_kernel included
             return k

@@ -353,7 +353,7 @@ class LaunchTimer:
         n = min(self.count, len(self.events) // 2)
         return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
 
-    KINDS = ("fwd_prep", "fwd_chain", "bwd_chain", "bwd_local", "dA_reduce", "step")
+    KINDS = ("fwd_prep", "fwd_chain", "bwd_chain", "bwd_local", "dA_reduce", "step", "fwd_scan", "bwd_scan")
 
     def kinds(self):
         """Kernel name of every bracketed launch, in launch order."""

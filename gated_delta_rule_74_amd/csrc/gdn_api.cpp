@@ -131,7 +131,7 @@ thread_local int g_launch = 0;
 constexpr int KIND_LOG = 4096;
 thread_local int8_t g_kinds[KIND_LOG];
 thread_local int g_kind_n = 0; // launches logged by the last bracketing period
-enum Kind { K_FWD_PREP = 0, K_FWD_CHAIN, K_BWD_CHAIN, K_BWD_LOCAL, K_DA_REDUCE, K_STEP };
+enum Kind { K_FWD_PREP = 0, K_FWD_CHAIN, K_BWD_CHAIN, K_BWD_LOCAL, K_DA_REDUCE, K_STEP, K_FWD_SCAN, K_BWD_SCAN };
 
 template <class F> hipError_t timed(Kind kind, F &&launch, hipStream_t st) {
     const int i = g_launch;
@@ -188,15 +188,40 @@ int32_t gdn_time_launches(void *const *events, int32_t n) {
     return done;
 }
 
+} // extern "C"
+
+namespace {
+
 // per-token log2-decay of every chunk (fp32), written by fwd_prep
 size_t gam_bytes(const gdn_shape_t *s) { return (size_t)s->B * s->H * nchunks(s) * 64 * sizeof(float); }
 // one fp32 state per (batch, head): hand-off between chunk ranges
 size_t state32_bytes(const gdn_shape_t *s) { return (size_t)s->B * s->H * s->dk * s->dv * sizeof(float); }
 
+// Segments of the parallel scan over chunk ranges for this shape (1: the
+// serial passes need no scan scratch).
+int scan_segments(const gdn_shape_t *s) {
+    return gdn::fwd_scan_segments(s->dtype == GDN_BF16, pad_of(s), nchunks(s));
+}
+// Scan scratch: the maps [M | R] of all but the last segment, then the
+// state at every segment boundary, fp32, per (batch, head).
+size_t scan_maps_floats(const gdn_shape_t *s) {
+    const int n = scan_segments(s);
+    return n > 1 ? (size_t)s->B * s->H * (n - 1) * s->dk * (s->dk + s->dv) : 0;
+}
+size_t scan_bytes(const gdn_shape_t *s) {
+    const int n = scan_segments(s);
+    if (n <= 1) return 0;
+    return align_up(scan_maps_floats(s) * 4) + align_up((size_t)s->B * s->H * n * s->dk * s->dv * 4);
+}
+
+} // namespace
+
+extern "C" {
+
 size_t gdn_fwd_workspace_size(const gdn_shape_t *s) {
     if (check_shape(s) != GDN_OK) return 0;
     return align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)) + align_up(gam_bytes(s)) +
-           align_up(state32_bytes(s));
+           align_up(state32_bytes(s)) + scan_bytes(s);
 }
 
 size_t gdn_fwd_context_size(const gdn_shape_t *s) {
@@ -211,8 +236,10 @@ size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     const size_t wide = align_up(gdn::bwd_wide_scratch_bytes(s->dtype == GDN_BF16, pad_of(s), nch));
     return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part +
            align_up(gam_bytes(s)) /* forward decay */ + align_up(state32_bytes(s)) /* forward hand-off */ +
-           wide /* local-gradient scratch for wide heads */;
+           wide /* local-gradient scratch for wide heads */ + scan_bytes(s) /* scan scratch */;
 }
+
+} // extern "C"
 
 namespace {
 
@@ -269,8 +296,8 @@ int fwd_segments(const gdn_shape_t *s, bool bf, int D) {
 // no second stream can be had) everything runs on `strm` as a single chunk
 // range; the results are the same bit for bit, only the overlap is lost.
 hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, int D, void *U, void *NK,
-                       void *Tsave, float *gam, float *hs, void *o, float *hT, void *cs, hipStream_t strm,
-                       bool one_stream = false) {
+                       void *Tsave, float *gam, float *hs, float *scan, void *o, float *hT, void *cs,
+                       hipStream_t strm, bool one_stream = false) {
     const int NC = nchunks(s);
     int nseg = one_stream ? 1 : fwd_segments(s, bf, D);
     Aux *x = nullptr;
@@ -292,7 +319,8 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
     fa.gam = gam;
     fa.o = o;
     fa.cs = cs;
-    const int BV = gdn::fwd_vblock(D);
+    const int nscan = scan_segments(s);
+    const int BV = gdn::fwd_vblock(D, nscan > 1);
     fa.NVB = (s->dv + BV - 1) / BV;
     auto seg_lo = [&](int k) { return (int)((long long)k * NC / nseg); };
     hipError_t he;
@@ -305,6 +333,29 @@ hipError_t run_forward(const gdn_shape_t *s, const gdn::SeqArgs &sa, bool bf, in
         fa.c1 = NC;
         fa.h_in = sa.h0;
         fa.hT = hT;
+        if (nscan > 1) {
+            // parallel scan over chunk ranges: the maps of every range but
+            // the last, the start state of every range, then every range
+            // from its start state at once
+            fa.nseg = nscan;
+            fa.mode = 1;
+            fa.maps = scan;
+            he = timed(K_FWD_CHAIN, [&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
+            if (he != hipSuccess) return he;
+            gdn::ScanArgs sc;
+            sc.maps = scan;
+            sc.h0 = sa.h0;
+            sc.seg_h = scan + align_up(scan_maps_floats(s) * 4) / 4;
+            sc.BH = s->B * s->H;
+            sc.nseg = nscan;
+            sc.dk = s->dk;
+            sc.dv = s->dv;
+            he = timed(K_FWD_SCAN, [&] { return gdn::launch_fwd_scan(sc, strm); }, strm);
+            if (he != hipSuccess) return he;
+            fa.mode = 0;
+            fa.maps = nullptr;
+            fa.seg_h = sc.seg_h;
+        }
         return timed(K_FWD_CHAIN, [&] { return gdn::launch_fwd_chain(fa, bf, D, strm); }, strm);
     }
     // fork: the second stream starts after the caller's earlier work
@@ -368,7 +419,7 @@ static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *h0, const void 
     return hip_status(he, "gdn_bwd (empty sequence)");
 }
 
-} // extern "C"
+
 
 namespace gdn {
 
@@ -419,9 +470,10 @@ gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const
     void *Tsave = ctx ? c + cl.t : nullptr;
     float *gam = (float *)(w + align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)));
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
+    float *scan = (float *)((char *)hs + align_up(state32_bytes(s)));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     return hip_status(
-        run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, o, hT, ctx, (hipStream_t)stream, one_stream),
+        run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, scan, o, hT, ctx, (hipStream_t)stream, one_stream),
         "gdn_fwd launch");
 }
 
@@ -493,11 +545,13 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     float *wide = (float *)((char *)hs + align_up(state32_bytes(s)));
     const bool has_wide = gdn::bwd_wide_scratch_bytes(bf, D, s->B * s->H * nchunks(s)) > 0;
+    float *scan = (float *)((char *)wide + align_up(gdn::bwd_wide_scratch_bytes(bf, D, s->B * s->H * nchunks(s))));
     const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
     const CtxLayout cl = ctx_layout(s);
     hipError_t he;
     if (!ctx) {
-        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, hs, nullptr, hT, wctx, strm);
+        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, hs, scan, nullptr, hT, wctx,
+                         strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
         ctx = wctx;
     }
@@ -510,8 +564,33 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     ca.NK = NK;
     ca.dhs = dhs;
     ca.dh0 = dh0;
-    const int BVc = gdn::bwd_chain_vblock(bf, D);
+    const int nscan = scan_segments(s);
+    const int BVc = gdn::bwd_chain_vblock(bf, D, nscan > 1);
     ca.NVB = (s->dv + BVc - 1) / BVc;
+    if (nscan > 1) {
+        // parallel scan, mirror of the forward's: the maps of every range but
+        // the first, the gradient at the end of every range (from dhT
+        // backwards), then every range at once
+        ca.nseg = nscan;
+        ca.mode = 1;
+        ca.maps = scan;
+        he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
+        if (he != hipSuccess) return hip_status(he, "gdn_bwd chain (maps) launch");
+        gdn::ScanArgs sc;
+        sc.maps = scan;
+        sc.h0 = dhT;
+        sc.seg_h = scan + align_up(scan_maps_floats(s) * 4) / 4;
+        sc.BH = s->B * s->H;
+        sc.nseg = nscan;
+        sc.dk = s->dk;
+        sc.dv = s->dv;
+        sc.reverse = 1;
+        he = timed(K_BWD_SCAN, [&] { return gdn::launch_fwd_scan(sc, strm); }, strm);
+        if (he != hipSuccess) return hip_status(he, "gdn_bwd scan launch");
+        ca.mode = 0;
+        ca.maps = nullptr;
+        ca.seg_dh = sc.seg_h;
+    }
     he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd chain launch");
     gdn::BwdLocalArgs la;

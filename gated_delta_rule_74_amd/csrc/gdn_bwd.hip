@@ -77,38 +77,56 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
     const SeqArgs &s = a.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vb = lid % a.NVB, bh = lid / a.NVB;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
+    // workgroup -> (batch-head, segment, value block); with maps the first
+    // NVBM blocks carry dk identity columns (the linear part of the map) and
+    // the segments are 1 .. nseg-1
+    const bool maps = a.mode == 1;
+    const int NVBM = maps ? (dk + BV - 1) / BV : 0;
+    const int nvbe = a.NVB + NVBM, nsl = maps ? a.nseg - 1 : a.nseg;
+    const int vbe = lid % nvbe, seg = (lid / nvbe) % nsl + (maps ? 1 : 0), bh = lid / (nvbe * nsl);
+    const bool mblk = vbe < NVBM;
+    const int v0 = (mblk ? vbe : vbe - NVBM) * BV, nvc = min(BV, (mblk ? dk : dv) - v0);
+    const int c_lo = (int)((long long)seg * NC / a.nseg), c_hi = (int)((long long)(seg + 1) * NC / a.nseg);
     const int b = bh / s.H, h = bh % s.H;
-    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
-    const int v0 = vb * BV, nvc = min(BV, dv - v0);
     const double A2 = -exp((double)s.A_log[h]) * LOG2E;
     const S *q = (const S *)s.q;
     const S *k = (const S *)s.k;
     const S *dO = (const S *)a.dout;
     const S *NK = (const S *)a.NK;
-    S *dhs = (S *)a.dhs;
+    S *dhs = maps ? nullptr : (S *)a.dhs;
 
+    // gradient at the end of the segment: dhT (last segment), the scan's
+    // value, identity columns (maps, linear part) or zero
+    const float *din = maps ? nullptr
+                            : (seg == a.nseg - 1 ? (a.dhT ? a.dhT + (size_t)bh * dk * dv : nullptr)
+                                                 : a.seg_dh + ((size_t)bh * a.nseg + seg) * dk * dv);
     f32x4 accDH[Tiles<DT, VT>::PW];
     for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-        accDH[i][e] = (a.dhT && row < dk && col < nvc) ? a.dhT[((size_t)bh * dk + row) * dv + v0 + col] : 0.f;
+        const bool in = row < dk && col < nvc;
+        accDH[i][e] = mblk ? ((in && row == v0 + col) ? 1.f : 0.f)
+                           : ((din && in) ? din[(size_t)row * dv + v0 + col] : 0.f);
     });
     store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
 
     ChunkFrag<BF, D> fk, fq, fn;
     ChunkFrag<BF, BV> fo;
+    fo.ok = 0; // identity columns take dO as zero: never fetched, stashed as zeros
     float pg = 0.f;
     auto fetch = [&](int c) {
         const int t0 = c * C, n = min(C, T - t0);
         const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
         fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
-        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
-        fo.template fetch<VEC>(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, tid);
+        if (!mblk) {
+            fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+            fo.template fetch<VEC>(dO + (row0 * H + h) * dv + v0, (size_t)H * dv, n, nvc, tid);
+        }
         if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
         pg = load_row_scalar(s.g + row0 * H + h, H, lane, n);
     };
-    fetch(s.NC - 1);
+    if (c_hi > c_lo) fetch(c_hi - 1);
 
-    for (int c = s.NC - 1; c >= 0; --c) {
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int n = min(C, T - c * C);
         wait_vmem();
         // every wave computes the decay of its lane's row: the copy of Q
@@ -120,8 +138,10 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
             if (lane == 0) misc[0] = dc.eglast;
         }
         fk.stash(Ks, LDD, tid);
-        fq.stash(Qs, LDD, tid);
-        fq.stash_scaled(Qe, LDD, tid, dc.eg);
+        if (!mblk) {
+            fq.stash(Qs, LDD, tid);
+            fq.stash_scaled(Qe, LDD, tid, dc.eg);
+        }
         fo.stash(dOs, LDV, tid);
         if (!s.additive) fn.stash(NKs, LDD, tid);
         // stores go out between consuming one prefetch and issuing the next,
@@ -135,8 +155,8 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
                 const int t = wave + NWAVE * i;
                 if (Tiles<DT, VT>::N % NWAVE != 0 && t >= Tiles<DT, VT>::N) break;
                 const int d0 = (t / VT) * 16 + 4 * kq, col = (t % VT) * 16 + r16;
+                if (!dhs || col >= nvc) continue;
                 S *dst = dhs + (((size_t)bh * s.NC + c) * dv + v0 + col) * dk + d0;
-                if (col >= nvc) continue;
                 if (BF && dk % 4 == 0) {
                     if (d0 < dk) {
                         uint2 u;
@@ -151,11 +171,12 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
                 }
             }
         }
-        if (c > 0) fetch(c - 1);
+        if (c > c_lo) fetch(c - 1);
         __syncthreads();
 
-        // P^T and Q^T diag(e^gam) dO: independent of the chain
-        {
+        // P^T and Q^T diag(e^gam) dO: independent of the chain (and zero for
+        // identity columns, whose dO is zero)
+        if (!mblk) {
             f32x4 sq[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq[i] = zero4();
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         f32x4 accQD[Tiles<DT, VT>::PW];
 #pragma unroll
         for (int i = 0; i < Tiles<DT, VT>::PW; ++i) accQD[i] = zero4();
-        gemm<BF, DT, VT, C, true, true>(Qe, LDD, dOs, LDV, accQD, wave, lane);
+        if (!mblk) gemm<BF, DT, VT, C, true, true>(Qe, LDD, dOs, LDV, accQD, wave, lane);
         // dW = diag(e^{gam_n - gam}) K dh' + P^T dO (P^T is read after the barrier)
         f32x4 accW[Tiles<4, VT>::PW];
 #pragma unroll
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         gemm<BF, 4, VT, D>(Ks, LDD, dHT, LDD, accW, wave, lane);
         for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] *= egn[row]; });
         __syncthreads();
-        gemm<BF, 4, VT, C, false, true>(PT, LDC, dOs, LDV, accW, wave, lane);
+        if (!mblk) gemm<BF, 4, VT, C, false, true>(PT, LDC, dOs, LDV, accW, wave, lane);
         store_T<BF, 4, VT>(accW, dWT, LDC, wave, lane);
         __syncthreads();
         // dh = e^{gam_n} dh' + Q^T diag(e^gam) dO - Kw^T dW
@@ -187,7 +208,13 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
         __syncthreads();
         store_T<BF, DT, VT>(accDH, dHT, LDD, wave, lane);
     }
-    if (a.dh0) {
+    if (maps) {
+        // [M | R] of this segment (index seg - 1): identity blocks fill the M columns
+        float *dst = a.maps + ((size_t)bh * (a.nseg - 1) + seg - 1) * dk * (dk + dv) + (mblk ? v0 : dk + v0);
+        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < dk && col < nvc) dst[(size_t)row * (dk + dv) + col] = accDH[i][e];
+        });
+    } else if (a.dh0 && seg == 0) {
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc) a.dh0[((size_t)bh * dk + row) * dv + v0 + col] = accDH[i][e];
         });
@@ -1245,12 +1272,39 @@ __global__ __launch_bounds__(NTHR) void dA_reduce_kernel(const float *__restrict
 // --------------------------------------------------------------- launch
 
 // value columns per workgroup of the reverse serial pass (16 for 128-wide
-// heads: more workgroups share the chain, each carrying half the gradient)
-static int chain_vblock(bool, int D) { return D == 64 ? 32 : 16; }
+// heads: more workgroups share the chain, each carrying half the gradient);
+// segmented launches take the forward's wider blocks
+static int chain_vblock(bool, int D, bool segmented) {
+    if (segmented) return fwd_vblock(D, true);
+    return D == 64 ? 32 : 16;
+}
+
+template <bool BF, int D, int BV> static hipError_t chain_gen(const BwdChainArgs &a, hipStream_t st) {
+    const int nvbe = a.NVB + (a.mode == 1 ? (a.s.dk + BV - 1) / BV : 0);
+    const int nsl = a.mode == 1 ? a.nseg - 1 : a.nseg;
+    const int grid = a.s.B * a.s.H * nsl * nvbe;
+    if (vec_ok<BF>(a.s))
+        hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<BF, D, BV, false>), dim3(grid), dim3(NTHR), 0, st, a);
+    return hipGetLastError();
+}
 
 template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hipStream_t st) {
     constexpr int BV = D == 64 ? 32 : 16;
     const int grid = a.s.B * a.s.H * a.NVB;
+    if (a.nseg < 1 || (a.mode == 1 && a.nseg < 2)) return hipErrorInvalidValue;
+    if (a.nseg > 1) {
+        const int bv = chain_vblock(BF, D, true);
+        if (bv == 16) return chain_gen<BF, D, 16>(a, st);
+        if constexpr (D >= 32)
+            if (bv == 32) return chain_gen<BF, D, 32>(a, st);
+        if constexpr (D >= 64)
+            if (bv == 64) return chain_gen<BF, D, 64>(a, st);
+        if constexpr (D >= 128)
+            if (bv == 128) return chain_gen<BF, D, 128>(a, st);
+        return hipErrorInvalidValue;
+    }
     if constexpr (BF && D <= 64) {
         const dim3 block(64 * (BV / 16 + BWS_HELPERS));
         if (vec_ok<BF>(a.s))
@@ -1267,7 +1321,7 @@ template <bool BF, int D> static hipError_t chain_inst(const BwdChainArgs &a, hi
 }
 
 hipError_t launch_bwd_chain(const BwdChainArgs &a, bool bf16, int D, hipStream_t st) {
-    if (chain_vblock(bf16, D) * a.NVB < a.s.dv) return hipErrorInvalidValue;
+    if (chain_vblock(bf16, D, a.nseg > 1) * a.NVB < a.s.dv) return hipErrorInvalidValue;
     if (bf16) {
         switch (D) {
         case 32: return chain_inst<true, 32>(a, st);
@@ -1357,6 +1411,6 @@ hipError_t launch_dA_reduce(const float *part, float *dA_log, int B, int H, int 
 
 bool bwd_supported(bool bf16, int D) { return bf16 ? (D == 32 || D == 64 || D == 128) : (D == 16 || D == 32 || D == 64); }
 
-int bwd_chain_vblock(bool bf16, int D) { return chain_vblock(bf16, D); }
+int bwd_chain_vblock(bool bf16, int D, bool segmented) { return chain_vblock(bf16, D, segmented); }
 
 } // namespace gdn

@@ -257,36 +257,50 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     const SeqArgs &s = a.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vb = lid % a.NVB, bh = lid / a.NVB;
+    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
+    // workgroup -> (batch-head, segment, value block); with maps the first
+    // NVBM blocks carry dk identity columns (the linear part of the map)
+    const bool maps = a.mode == 1;
+    const int NVBM = maps ? (dk + BV - 1) / BV : 0;
+    const int nvbe = a.NVB + NVBM, nsl = maps ? a.nseg - 1 : a.nseg;
+    const int vbe = lid % nvbe, seg = (lid / nvbe) % nsl, bh = lid / (nvbe * nsl);
+    const bool mblk = vbe < NVBM;
+    const int v0 = (mblk ? vbe : vbe - NVBM) * BV, nvc = min(BV, (mblk ? dk : dv) - v0);
+    const int c_lo = (int)((long long)seg * NC / a.nseg), c_hi = (int)((long long)(seg + 1) * NC / a.nseg);
     const int b = bh / s.H, h = bh % s.H;
-    const int T = s.T, H = s.H, dk = s.dk, dv = s.dv;
-    const int v0 = vb * BV, nvc = min(BV, dv - v0);
     const double A2 = -exp((double)s.A_log[h]) * LOG2E;
     const S *q = (const S *)s.q;
     const S *k = (const S *)s.k;
     const S *U = (const S *)a.U;
     const S *NK = (const S *)a.NK;
-    S *o = (S *)a.o;
-    S *cs = (S *)a.cs;
+    S *o = maps ? nullptr : (S *)a.o;
+    S *cs = maps ? nullptr : (S *)a.cs;
 
-    // state h[D][BV] (fp32) lives in the accumulators of the h-update product
+    // state h[D][BV] (fp32) lives in the accumulators of the h-update product:
+    // the segment's start state, identity columns (maps, linear part) or zero
+    const float *hin = maps ? nullptr
+                            : (seg == 0 ? (a.h_in ? a.h_in + (size_t)bh * dk * dv : nullptr)
+                                        : a.seg_h + ((size_t)bh * a.nseg + seg) * dk * dv);
     f32x4 accH[Tiles<DT, VT>::PW];
     for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-        accH[i][e] = (s.h0 && row < dk && col < nvc) ? s.h0[((size_t)bh * dk + row) * dv + v0 + col] : 0.f;
+        const bool in = row < dk && col < nvc;
+        accH[i][e] = mblk ? ((in && row == v0 + col) ? 1.f : 0.f)
+                          : ((hin && in) ? hin[(size_t)row * dv + v0 + col] : 0.f);
     });
     store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
 
     // inputs of the next chunk are fetched into registers during this one
     ChunkFrag<BF, D> fk, fq, fn;
     ChunkFrag<BF, BV> fu;
+    fu.ok = 0; // identity columns take U as zero: never fetched, stashed as zeros
     float pg = 0.f;
     auto fetch = [&](int c) {
         const int t0 = c * C, n = min(C, T - t0);
         const size_t row0 = (size_t)b * T + t0, cb = (size_t)bh * s.NC + c;
         fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
-        fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+        if (o) fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
         if (!s.additive) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, tid);
-        fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
+        if (!mblk) fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
         pg = gate_of(load_row_scalar(s.g + row0 * H + h, H, lane, n), s.logits);
     };
     // O of a chunk is held in registers and written out during the next
@@ -301,9 +315,9 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
             if (row < n && col < nvc) orow[(size_t)row * H * dv + col] = from_f<BF>(accO[i][e]);
         });
     };
-    fetch(0);
+    fetch(c_lo);
 
-    for (int c = 0; c < s.NC; ++c) {
+    for (int c = c_lo; c < c_hi; ++c) {
         const int t0 = c * C, n = min(C, T - t0);
         wait_vmem();
         if (wave == 0) {
@@ -314,21 +328,21 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
             if (lane == 0) misc[0] = dc.eglast;
         }
         fk.stash(Ks, LDD, tid);
-        fq.stash(Qs, LDD, tid);
+        if (o) fq.stash(Qs, LDD, tid);
         if (!s.additive) fn.stash(NKs, LDD, tid);
         fu.stash(Us, LDV, tid);
-        if (o && c > 0) store_o(c - 1);
+        if (o && c > c_lo) store_o(c - 1);
         if (cs) {
             for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
                 if (row < dk && col < nvc)
                     cs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accH[i][e]);
             });
         }
-        if (c + 1 < s.NC) fetch(c + 1);
+        if (c + 1 < c_hi) fetch(c + 1);
         __syncthreads();
 
-        // P = (Q K^T) o Gam (independent of the state)
-        {
+        // P = (Q K^T) o Gam (independent of the state; only the outputs need it)
+        if (o) {
             f32x4 sq[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq[i] = zero4();
@@ -364,12 +378,92 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         __syncthreads();
         store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
     }
-    if (o) store_o(s.NC - 1);
-    if (a.hT) {
+    if (o && c_hi > c_lo) store_o(c_hi - 1);
+    if (maps) {
+        // [M | R] of this segment: identity blocks fill the M columns
+        float *dst = a.maps + ((size_t)bh * (a.nseg - 1) + seg) * dk * (dk + dv) + (mblk ? v0 : dk + v0);
+        for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+            if (row < dk && col < nvc) dst[(size_t)row * (dk + dv) + col] = accH[i][e];
+        });
+    } else if (a.hT && seg == a.nseg - 1) {
         for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
             if (row < dk && col < nvc) a.hT[((size_t)bh * dk + row) * dv + v0 + col] = accH[i][e];
         });
     }
+}
+
+// Start states of the segments of a segmented pass, one workgroup per
+// (batch-head, 16 value columns): x_0 = h0, x_{s+1} = M_s x_s + R_s with the
+// maps [M | R] of the segments (reverse: from the last segment down), fp32,
+// sums over the key index in order. Columns are independent, so each
+// workgroup carries its own 16. Each step stages M (and the workgroup's R
+// columns) in LDS with 16-byte loads first, so the serial chain of segments
+// waits for memory once per segment.
+__global__ __launch_bounds__(512) void range_scan_kernel(ScanArgs a) {
+    constexpr int DK = 128, LDM = DK + 4, NT = 512, RPT = DK / (NT / 16); // rows per thread
+    __shared__ __attribute__((aligned(16))) float Ms[DK * LDM];
+    __shared__ float Rs[DK * 16];
+    __shared__ __attribute__((aligned(16))) float hc[DK * 16];
+    const int nvb = (a.dv + 15) / 16;
+    const int bh = blockIdx.x / nvb, cb = blockIdx.x % nvb;
+    const int dk = a.dk, dv = a.dv, ld = dk + dv, dk4 = (dk + 3) & ~3;
+    const int tid = threadIdx.x, j = tid % 16, i0 = tid / 16, col = 16 * cb + j;
+    const bool cin = col < dv;
+    // x [k][16] for k < dk4 (rows dk .. dk4-1 stay zero), M rows zero-padded to dk4
+    for (int i = i0; i < DK; i += NT / 16)
+        hc[i * 16 + j] = (a.h0 && cin && i < dk) ? a.h0[((size_t)bh * dk + i) * dv + col] : 0.f;
+    for (int e = tid; e < DK * LDM; e += NT) Ms[e] = 0.f;
+    __syncthreads();
+    for (int it = 0; it < a.nseg; ++it) {
+        // forward: segment sg = it, next map sg; reverse: sg = nseg-1-it, next map sg - 1
+        const int sg = a.reverse ? a.nseg - 1 - it : it;
+        float *out = a.seg_h + ((size_t)bh * a.nseg + sg) * dk * dv;
+        for (int i = i0; i < dk; i += NT / 16)
+            if (cin) out[(size_t)i * dv + col] = hc[i * 16 + j];
+        if (it == a.nseg - 1) break;
+        const float *M = a.maps + ((size_t)bh * (a.nseg - 1) + (a.reverse ? sg - 1 : sg)) * dk * ld;
+        // M rows as 16-byte pieces when the row stride allows, else by element
+        if ((ld & 3) == 0 && (dk & 3) == 0) {
+            for (int e = tid; e < dk * (dk / 4); e += NT) {
+                const int i = e / (dk / 4), k4 = (e % (dk / 4)) * 4;
+                *reinterpret_cast<float4 *>(Ms + i * LDM + k4) = *reinterpret_cast<const float4 *>(M + (size_t)i * ld + k4);
+            }
+        } else {
+            for (int e = tid; e < dk * dk; e += NT) Ms[(e / dk) * LDM + e % dk] = M[(size_t)(e / dk) * ld + e % dk];
+        }
+        for (int i = i0; i < dk; i += NT / 16) Rs[i * 16 + j] = cin ? M[(size_t)i * ld + dk + col] : 0.f;
+        __syncthreads();
+        // rows i0 + 32 r of the new x: every 16-byte read of a row of M
+        // serves four key steps, every read of x four rows
+        float nx[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) nx[r] = 0.f;
+        for (int kk = 0; kk < dk4; kk += 4) {
+            const float x0 = hc[kk * 16 + j], x1 = hc[(kk + 1) * 16 + j];
+            const float x2 = hc[(kk + 2) * 16 + j], x3 = hc[(kk + 3) * 16 + j];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const float4 m = *reinterpret_cast<const float4 *>(Ms + (i0 + (NT / 16) * r) * LDM + kk);
+                nx[r] += m.x * x0;
+                nx[r] += m.y * x1;
+                nx[r] += m.z * x2;
+                nx[r] += m.w * x3;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = i0 + (NT / 16) * r;
+            if (i < dk) hc[i * 16 + j] = Rs[i * 16 + j] + nx[r];
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st) {
+    if (a.dk > 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(range_scan_kernel, dim3(a.BH * ((a.dv + 15) / 16)), dim3(512), 0, st, a);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------- wave-specialised chain
@@ -690,10 +784,29 @@ int pad_dim(int d, bool bf16) {
     return D;
 }
 
-// value columns per workgroup of the generic serial pass; 128-wide heads take
-// 16 so that twice as many workgroups share the chain (each carries half the
-// state), which measured faster on the long-context shape (16 heads)
-int fwd_vblock(int D) { return D == 64 ? 32 : 16; }
+// value columns per workgroup of the generic serial pass. Serial: 128-wide
+// heads take 16 so that more workgroups share the chain (each carries part
+// of the state), which measured faster on the long-context shape (16 heads).
+// Segmented: the segments supply the parallelism, so wider blocks cut the
+// work every block repeats (loading K and -Kw, forming P).
+#ifndef GDN_SEG_BV
+#define GDN_SEG_BV 128
+#endif
+int fwd_vblock(int D, bool segmented) {
+    if (segmented) return D < GDN_SEG_BV ? D : GDN_SEG_BV;
+    return D == 64 ? 32 : 16;
+}
+
+// Segments of the parallel scan: long sequences split into ranges of about
+// SEG_CHUNKS chunks (at most 16 ranges); short ones stay serial.
+#ifndef GDN_SEG_CHUNKS
+#define GDN_SEG_CHUNKS 32
+#endif
+int fwd_scan_segments(bool bf16, int D, int NC) {
+    if (fwd_segmentable(bf16, D)) return 1; // the wave-specialised chain takes chunk ranges instead
+    const int n = NC / GDN_SEG_CHUNKS;
+    return n < 2 ? 1 : (n > 16 ? 16 : n);
+}
 
 bool fwd_segmentable(bool bf16, int D) { return bf16 && (D == 32 || D == 64); }
 
@@ -716,14 +829,28 @@ template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a, hipStrea
     return hipGetLastError();
 }
 
-template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
-    constexpr int BV = D == 64 ? 32 : 16;
-    const int grid = a.s.B * a.s.H * a.NVB;
+template <bool BF, int D, int BV> static hipError_t chain_bv(const FwdChainArgs &a, hipStream_t st) {
+    const int nvbe = a.NVB + (a.mode == 1 ? (a.s.dk + BV - 1) / BV : 0);
+    const int nsl = a.mode == 1 ? a.nseg - 1 : a.nseg;
+    const int grid = a.s.B * a.s.H * nsl * nvbe;
     if (vec_ok<BF>(a.s))
         hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, true>), dim3(grid), dim3(NTHR), 0, st, a);
     else
         hipLaunchKernelGGL((fwd_chain_kernel<BF, D, BV, false>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
+}
+
+template <bool BF, int D> static hipError_t chain_inst(const FwdChainArgs &a, hipStream_t st) {
+    const int bv = fwd_vblock(D, a.nseg > 1);
+    if (a.nseg < 1 || (a.mode == 1 && a.nseg < 2)) return hipErrorInvalidValue;
+    if (bv == 16) return chain_bv<BF, D, 16>(a, st);
+    if constexpr (D >= 32)
+        if (bv == 32) return chain_bv<BF, D, 32>(a, st);
+    if constexpr (D >= 64)
+        if (bv == 64) return chain_bv<BF, D, 64>(a, st);
+    if constexpr (D >= 128)
+        if (bv == 128) return chain_bv<BF, D, 128>(a, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st) {
@@ -744,7 +871,7 @@ hipError_t launch_fwd_prep(const PrepArgs &a, bool bf16, int D, hipStream_t st) 
 }
 
 hipError_t launch_fwd_chain(const FwdChainArgs &a, bool bf16, int D, hipStream_t st) {
-    if (fwd_vblock(D) * a.NVB < a.s.dv) return hipErrorInvalidValue;
+    if (fwd_vblock(D, a.nseg > 1) * a.NVB < a.s.dv) return hipErrorInvalidValue;
     if (bf16) {
         switch (D) {
         case 32: return chain_ws_inst<32>(a, st);

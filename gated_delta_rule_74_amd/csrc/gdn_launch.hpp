@@ -53,6 +53,30 @@ struct FwdChainArgs {
     // chain kernel supports only the whole range with h_in == s.h0.
     int c0, c1;
     const float *h_in;
+    // Segmented launches of the general chain kernel (the parallel scan over
+    // chunk ranges): the chunks are split into nseg equal segments and the
+    // grid covers (batch-head, segment, value block). mode 0: every segment
+    // runs from its start state (h_in for segment 0, seg_h for the others),
+    // writes o and cs for its chunks, and the last segment writes hT. mode 1
+    // (maps): segments 0 .. nseg-2 run from a zero start over dk identity
+    // columns (U taken as zero) and the value columns; their final states are
+    // the segment's affine map [M | R] (h_end = M h_start + R), written to
+    // maps [B*H][nseg-1][dk][dk+dv] fp32; nothing else is written.
+    int nseg = 1, mode = 0;
+    const float *seg_h = nullptr; // [B*H][nseg][dk][dv] fp32
+    float *maps = nullptr;
+};
+
+// Start state of every segment from the segment maps: h_0 = h0 (zero when
+// null), h_{s+1} = M_s h_s + R_s; seg_h [B*H][nseg][dk][dv] fp32.
+// With reverse set, the backward's mirror: x_{nseg-1} = h0 (there: dhT),
+// x_{s-1} = M_{s-1} x_s + R_{s-1} with the map of segment s at index s - 1.
+struct ScanArgs {
+    const float *maps; // [B*H][nseg-1][dk][dk+dv]
+    const float *h0;   // [B*H][dk][dv] or null
+    float *seg_h;
+    int BH, nseg, dk, dv;
+    int reverse = 0;
 };
 
 struct BwdChainArgs {
@@ -63,6 +87,17 @@ struct BwdChainArgs {
     void *dhs;        // [B,H,NC,dv,dk]: gradient wrt the state after each chunk, transposed
     float *dh0;       // may be null
     int NVB;
+    // Segmented launches of the general reverse chain (mirror of the
+    // forward's): mode 0: segment s runs backwards from the gradient at its
+    // end (dhT for the last segment, seg_dh for the others), writes dhs for
+    // its chunks, and segment 0 writes dh0. mode 1 (maps): segments
+    // 1 .. nseg-1 run from a zero end gradient over dk identity columns (dO
+    // taken as zero) and the value columns; their final gradients are the
+    // segment's map [M | R] (dh_start = M dh_end + R), written to maps
+    // [B*H][nseg-1][dk][dk+dv] fp32 (segment s at index s - 1).
+    int nseg = 1, mode = 0;
+    const float *seg_dh = nullptr; // [B*H][nseg][dk][dv] fp32: gradient at the end of each segment
+    float *maps = nullptr;
 };
 
 struct BwdLocalArgs {
@@ -98,9 +133,12 @@ template <bool BF> inline bool vec_ok(const SeqArgs &s) {
 
 // Padded head dimension the kernels are instantiated for.
 int pad_dim(int d, bool bf16);
-int fwd_vblock(int D);
+int fwd_vblock(int D, bool segmented);
+// segments of the parallel scan the general forward chain uses (1: serial)
+int fwd_scan_segments(bool bf16, int D, int NC);
+hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st);
 bool fwd_segmentable(bool bf16, int D); // chain launch accepts a chunk range
-int bwd_chain_vblock(bool bf16, int D);
+int bwd_chain_vblock(bool bf16, int D, bool segmented);
 bool bwd_supported(bool bf16, int D);
 // Scratch bytes the local-gradient pass needs for this padded head dim (0
 // when the LDS-resident kernel covers it).

@@ -208,9 +208,12 @@ int32_t gdn_time_launches(void *const *events, int32_t n);
 /* Which kernel the i-th bracketed launch of the current (or, once switched
  * off, the last) bracketing period was: 0 forward prep, 1 forward serial
  * pass, 2 backward serial pass, 3 backward local gradients, 4 dA_log
- * reduction, 5 decode step; -1 when i is out of range. A forward call may launch its two kernels several times
- * each, over consecutive chunk ranges (prep of the next range runs on a
- * second stream while the serial pass works on the current one). */
+ * reduction, 5 decode step, 6 forward scan over chunk ranges, 7 backward
+ * scan; -1 when i is out of range. A forward call may launch its two kernels
+ * several times each, over consecutive chunk ranges (prep of the next range
+ * runs on a second stream while the serial pass works on the current one),
+ * and a serial pass run as a parallel scan launches twice (the ranges' maps,
+ * then every range from its start). */
 int32_t gdn_launch_kind(int32_t i);
 
 const char *gdn_status_string(gdn_status_t st);

@@ -205,3 +205,17 @@ def test_fwd_noalloc_validation(L):
     bad[7] = args[0]  # o aliases q
     assert L.gdn_fwd_noalloc(ctypes.byref(small), *bad) == EINVAL
     assert L.gdn_fwd_noalloc(ctypes.byref(gdn.Shape(1, 8, 2, 16, 16, 1, 32, 0)), *args) == EUNSUPPORTED
+
+
+def test_exports_only_declared_c_symbols():
+    """The library's exported C-linkage functions are exactly the ones
+    include/gdn.h declares (internal helpers stay out of the ABI)."""
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    c_syms = {x for x in syms if not x.startswith("_Z") and not x.startswith("_")}
+    assert c_syms == set(header_functions())

@@ -373,3 +373,24 @@ def test_caller_stream():
     for name, t in ref.items():
         if t is not None:
             assert torch.equal(got[name], t), name
+
+
+@pytest.mark.parametrize("dtype,d,T,decay", [("f32", 32, 4100, "weak"), ("f32", 16, 8192, "zero"),
+                                             ("bf16", 128, 4160, "weak"), ("bf16", 72, 6000, "normal")])
+def test_scan_over_chunk_ranges(dtype, d, T, decay):
+    """The reverse pass as a parallel scan over chunk ranges (mirror of the
+    forward's): every gradient, dh0 and dA_log against the oracle, with a
+    nonzero upstream dhT; the recomputing path equals the saved-context path
+    bit for bit."""
+    say(f"bwd scan over chunk ranges {dtype} d{d} T{T} decay={decay}")
+    x = with_dhT(gi.gen_seq(1, T, 2, d, d, dtype, seed=7920 + d, h0="randn", with_do=True, decay=decay), 15)
+    check_bwd(x, dtype)
+    a = run_bwd(x, use_saved=True)
+    b = run_bwd(x, use_saved=False)
+    for name in GRADS + ["dA_log"]:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_scan_additive_bwd():
+    x = with_dhT(gi.gen_seq(1, 4096, 2, 32, 32, "f32", seed=7930, h0="randn", with_do=True, decay="weak"), 16)
+    check_bwd(x, "f32", additive=True)

@@ -195,3 +195,35 @@ def test_state_only_forward(dtype, T, d):
     _, rh = _oracle().fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["g"]), f64(x["beta"]),
                           f64(x["A_log"]), f64(x["h0"]))
     assert_close("hT", host(hT2), rh, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,d,T,decay", [("f32", 32, 4100, "weak"), ("f32", 16, 8192, "zero"),
+                                             ("f32", 64, 4096, "normal"), ("bf16", 128, 4160, "weak"),
+                                             ("bf16", 100, 6000, "zero")])
+def test_scan_over_chunk_ranges(dtype, d, T, decay):
+    """Sequences of 64 chunks or more on the general serial pass (fp32 heads,
+    bf16 heads past 64) run as a parallel scan over chunk ranges: each
+    range's affine map from a zero start, the start states composed from
+    them, every range rerun from its start. Outputs, final state and the
+    saved chunk states against the oracle (weak and zero decay carry the
+    state across every range boundary)."""
+    say(f"fwd scan over chunk ranges {dtype} d{d} T{T} decay={decay}")
+    x = gi.gen_seq(1, T, 2, d, d, dtype, seed=7900 + d, h0="randn", decay=decay)
+    check_fwd(x, dtype)
+    o, _, ctx = run_fwd(x)
+    cs = host(gdn.context_states(ctx, dev(x["q"]), dev(x["v"])))
+    c = 40  # a chunk inside the second range
+    _, ref = _oracle().fwd(f64(x["q"])[:, :64 * c], f64(x["k"])[:, :64 * c], f64(x["v"])[:, :64 * c],
+                           f64(x["g"])[:, :64 * c], f64(x["beta"])[:, :64 * c], f64(x["A_log"]),
+                           f64(x["h0"]))
+    assert_close(f"chunk state {c}", cs[:, :, c], ref, TOL[dtype])
+
+
+def test_scan_additive_and_bitwise():
+    """The scan in the additive form, and twice the same call bit for bit."""
+    x = gi.gen_seq(2, 4096, 2, 32, 32, "f32", seed=7910, h0="randn", decay="weak")
+    check_fwd(x, "f32", additive=True)
+    a = run_fwd(x)
+    b = run_fwd(x)
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
