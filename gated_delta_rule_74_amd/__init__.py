@@ -10,8 +10,12 @@ calls raise.
     grads      = bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, context=ctx)
     o, h      = step(q, k, v, g, beta, A_log, h_in, h_out=None)
     o, h      = step_tokens(q, k, v, g, beta, A_log, h_in)     # [N, S, H, *] tokens
-    o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0, additive, gate_logits)
+    o, hT     = GatedDeltaRule.apply(q, k, v, g, beta, A_log, h0, additive, gate_logits, norm_k, D)
     o, hT, ctx = fwd_noalloc(q, k, v, g, beta, A_log, h0, o=o)   # no device allocation
+
+Layer edges (fused into the kernels, off by default): norm_k=True
+L2-normalises every key row where it is loaded (dk comes back with respect to
+the raw keys); D [H] fp32 adds the skip term o_t += D[h] v_t (bwd returns dD).
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ GDN_F32, GDN_BF16 = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 GDN_FLAG_ADDITIVE = 1
 GDN_FLAG_GATE_LOGITS = 2
+GDN_FLAG_L2NORM_K = 4
 _lib = None
 
 
@@ -60,11 +65,11 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, S, Z = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_size_t
         I32, U32 = ctypes.c_int32, ctypes.c_uint32
-        L.gdn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, Z, P]
-        L.gdn_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P]
-        L.gdn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
-        L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
-        L.gdn_step_tokens.argtypes = [I32, I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P]
+        L.gdn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.gdn_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.gdn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.gdn_step.argtypes = [I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P, P]
+        L.gdn_step_tokens.argtypes = [I32, I32, I32, I32, I32, I32, U32, P, P, P, P, P, P, P, P, P, P, P]
         for f in (L.gdn_fwd, L.gdn_fwd_noalloc, L.gdn_bwd, L.gdn_step, L.gdn_step_tokens):
             f.restype = ctypes.c_int
         for f in (L.gdn_fwd_workspace_size, L.gdn_bwd_workspace_size, L.gdn_fwd_context_size):
@@ -120,16 +125,17 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _flags(additive, gate_logits):
-    return (GDN_FLAG_ADDITIVE if additive else 0) | (GDN_FLAG_GATE_LOGITS if gate_logits else 0)
+def _flags(additive, gate_logits, norm_k=False):
+    return ((GDN_FLAG_ADDITIVE if additive else 0) | (GDN_FLAG_GATE_LOGITS if gate_logits else 0)
+            | (GDN_FLAG_L2NORM_K if norm_k else 0))
 
 
-def _shape(q, v, additive, gate_logits=False):
+def _shape(q, v, additive, gate_logits=False, norm_k=False):
     B, T, H, dk = q.shape
-    return Shape(B, T, H, dk, v.shape[-1], _dtype_code(q), 64, _flags(additive, gate_logits))
+    return Shape(B, T, H, dk, v.shape[-1], _dtype_code(q), 64, _flags(additive, gate_logits, norm_k))
 
 
-def _check_seq(q, k, v, g, beta, A_log, h0=None):
+def _check_seq(q, k, v, g, beta, A_log, h0=None, D=None):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -142,6 +148,7 @@ def _check_seq(q, k, v, g, beta, A_log, h0=None):
     _need(beta, "beta", torch.float32, (B, T, H), dev)
     _need(A_log, "A_log", torch.float32, (H,), dev)
     _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
+    _need(D, "D", torch.float32, (H,), dev)
     return B, T, H, dk, dv
 
 
@@ -175,14 +182,15 @@ def bwd_workspace_size(q, v, additive=False):
     return int(lib().gdn_bwd_workspace_size(ctypes.byref(s)))
 
 
-def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, save_context=False,
-        want_hT=True, want_o=True, o=None, hT=None, context=None, workspace=None):
+def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, norm_k=False, D=None,
+        save_context=False, want_hT=True, want_o=True, o=None, hT=None, context=None, workspace=None):
     """Chunked forward. Returns (o or None, hT or None, context or None); the
     context (a byte tensor) lets bwd() skip recomputing the forward.
     gate_logits: g and beta are logits (the kernels apply the sigmoid).
+    norm_k: keys L2-normalised per token; D [H]: skip term o += D[h] v.
     want_o=False: a state-only pass (e.g. a prefill for decoding)."""
-    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
-    s = _shape(q, v, additive, gate_logits)
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0, D)
+    s = _shape(q, v, additive, gate_logits, norm_k)
     dev = q.device
     if o is None and want_o:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
@@ -199,20 +207,20 @@ def fwd(q, k, v, g, beta, A_log, h0=None, *, additive=False, gate_logits=False, 
     need = int(L.gdn_fwd_workspace_size(ctypes.byref(s)))
     if workspace is None or workspace.numel() < need:
         workspace = _bytes(need, dev)
-    st = L.gdn_fwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0), _p(o),
-                   _p(hT), _p(context), _p(workspace), workspace.numel(), _stream(dev))
+    st = L.gdn_fwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(D), _p(h0),
+                   _p(o), _p(hT), _p(context), _p(workspace), workspace.numel(), _stream(dev))
     _check("gdn_fwd", st)
     return o, hT, context
 
 
 def fwd_noalloc(q, k, v, g, beta, A_log, h0=None, *, o, hT=None, context=None, additive=False,
-                gate_logits=False):
+                gate_logits=False, norm_k=False, D=None):
     """The forward through gdn_fwd_noalloc: the library takes its workspace
     from a static device array, so the call allocates nothing. Every output
     is the caller's (o may be None only for a state-only pass, given
     explicitly as o=None). Returns (o, hT, context)."""
-    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
-    s = _shape(q, v, additive, gate_logits)
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0, D)
+    s = _shape(q, v, additive, gate_logits, norm_k)
     dev = q.device
     _need(o, "o", q.dtype, (B, T, H, dv), dev)
     _need(hT, "hT", torch.float32, (B, H, dk, dv), dev)
@@ -220,23 +228,26 @@ def fwd_noalloc(q, k, v, g, beta, A_log, h0=None, *, o, hT=None, context=None, a
     L = lib()
     if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
         raise ValueError("context is smaller than gdn_fwd_context_size()")
-    st = L.gdn_fwd_noalloc(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0),
-                           _p(o), _p(hT), _p(context), _stream(dev))
+    st = L.gdn_fwd_noalloc(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(D),
+                           _p(h0), _p(o), _p(hT), _p(context), _stream(dev))
     _check("gdn_fwd_noalloc", st)
     return o, hT, context
 
 
 def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additive=False,
-        gate_logits=False, want_dh0=True, want_hT=False, workspace=None, out=None):
+        gate_logits=False, norm_k=False, D=None, want_dD=None, want_dh0=True, want_hT=False, workspace=None,
+        out=None):
     """Backward of sum(do * o) + sum(dhT * hT). Returns a dict with dq, dk,
-    dv, dg, dbeta, dA_log, dh0 (or None) and hT (when want_hT); with
-    gate_logits, dg and dbeta are with respect to the logits."""
-    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0)
+    dv, dg, dbeta, dA_log, dD (when want_dD, by default when D is given),
+    dh0 (or None) and hT (when want_hT); with gate_logits, dg and dbeta are
+    with respect to the logits; with norm_k, dk is with respect to the raw
+    keys. norm_k and D must be those of the forward."""
+    B, T, H, dk, dv = _check_seq(q, k, v, g, beta, A_log, h0, D)
     dev = q.device
     _need(do, "do", q.dtype, (B, T, H, dv), dev)
     _need(dhT, "dhT", torch.float32, (B, H, dk, dv), dev)
     _need(context, "context", torch.uint8, None, dev)
-    s = _shape(q, v, additive, gate_logits)
+    s = _shape(q, v, additive, gate_logits, norm_k)
     L = lib()
     if context is not None and context.numel() < L.gdn_fwd_context_size(ctypes.byref(s)):
         raise ValueError("context is smaller than gdn_fwd_context_size()")
@@ -250,6 +261,12 @@ def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additiv
     r.setdefault("dg", torch.empty_like(g))
     r.setdefault("dbeta", torch.empty_like(beta))
     r.setdefault("dA_log", torch.empty_like(A_log))
+    if want_dD is None:
+        want_dD = D is not None
+    if want_dD:
+        r.setdefault("dD", torch.empty((H,), dtype=torch.float32, device=dev))
+    else:
+        r["dD"] = None
     if want_dh0:
         r.setdefault("dh0", torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
     else:
@@ -258,15 +275,16 @@ def bwd(q, k, v, g, beta, A_log, do, h0=None, dhT=None, *, context=None, additiv
         r.setdefault("hT", torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
     else:
         r["hT"] = None
-    st = L.gdn_bwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h0),
+    st = L.gdn_bwd(ctypes.byref(s), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(D), _p(h0),
                    _p(context), _p(do), _p(dhT), _p(r["dq"]), _p(r["dk"]), _p(r["dv"]),
-                   _p(r["dg"]), _p(r["dbeta"]), _p(r["dA_log"]), _p(r["dh0"]), _p(r["hT"]),
+                   _p(r["dg"]), _p(r["dbeta"]), _p(r["dA_log"]), _p(r["dD"]), _p(r["dh0"]), _p(r["hT"]),
                    _p(workspace), workspace.numel(), _stream(dev))
     _check("gdn_bwd", st)
     return r
 
 
-def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate_logits=False, o=None):
+def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate_logits=False, norm_k=False,
+         D=None, o=None):
     """One decode token per sequence. q, k [N,H,dk]; v [N,H,dv]; g, beta
     [N,H]; h_in [N,H,dk,dv] fp32 or None. h_out may be h_in (in place).
     Returns (o, h_out)."""
@@ -282,21 +300,22 @@ def step(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate
     _need(beta, "beta", torch.float32, (N, H), dev)
     _need(A_log, "A_log", torch.float32, (H,), dev)
     _need(h_in, "h_in", torch.float32, (N, H, dk, dv), dev)
+    _need(D, "D", torch.float32, (H,), dev)
     if h_out is None:
         h_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _need(h_out, "h_out", torch.float32, (N, H, dk, dv), dev)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (N, H, dv), dev)
-    st = lib().gdn_step(N, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits), _p(q),
-                        _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out), _p(o),
+    st = lib().gdn_step(N, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits, norm_k), _p(q),
+                        _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(D), _p(h_in), _p(h_out), _p(o),
                         _stream(dev))
     _check("gdn_step", st)
     return o, h_out
 
 
 def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=False, gate_logits=False,
-                o=None):
+                norm_k=False, D=None, o=None):
     """S consecutive decode tokens per sequence from a carried state (e.g. the
     draft tokens of a multi-token prediction). q, k [N,S,H,dk]; v [N,S,H,dv];
     g, beta [N,S,H]; h_in [N,H,dk,dv] fp32 or None; h_out may be h_in.
@@ -313,15 +332,16 @@ def step_tokens(q, k, v, g, beta, A_log, h_in=None, h_out=None, *, additive=Fals
     _need(beta, "beta", torch.float32, (N, S, H), dev)
     _need(A_log, "A_log", torch.float32, (H,), dev)
     _need(h_in, "h_in", torch.float32, (N, H, dk, dv), dev)
+    _need(D, "D", torch.float32, (H,), dev)
     if h_out is None:
         h_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _need(h_out, "h_out", torch.float32, (N, H, dk, dv), dev)
     if o is None:
         o = torch.empty((N, S, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (N, S, H, dv), dev)
-    st = lib().gdn_step_tokens(N, S, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits),
-                               _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(h_in), _p(h_out),
-                               _p(o), _stream(dev))
+    st = lib().gdn_step_tokens(N, S, H, dk, dv, _dtype_code(q), _flags(additive, gate_logits, norm_k),
+                               _p(q), _p(k), _p(v), _p(g), _p(beta), _p(A_log), _p(D), _p(h_in),
+                               _p(h_out), _p(o), _stream(dev))
     _check("gdn_step_tokens", st)
     return o, h_out
 
@@ -366,20 +386,23 @@ class GatedDeltaRule(torch.autograd.Function):
     per-chunk key blocks), backward reads it instead of recomputing."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False, gate_logits=False):
-        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, gate_logits=gate_logits,
-                        save_context=True)
-        ctx.save_for_backward(q, k, v, g, beta, A_log, h0, cs)
+    def forward(ctx, q, k, v, g, beta, A_log, h0=None, additive=False, gate_logits=False, norm_k=False, D=None):
+        o, hT, cs = fwd(q, k, v, g, beta, A_log, h0, additive=additive, gate_logits=gate_logits, norm_k=norm_k,
+                        D=D, save_context=True)
+        ctx.save_for_backward(q, k, v, g, beta, A_log, h0, cs, D)
         ctx.additive = additive
         ctx.gate_logits = gate_logits
+        ctx.norm_k = norm_k
         return o, hT
 
     @staticmethod
     def backward(ctx, do, dhT):
-        q, k, v, g, beta, A_log, h0, cs = ctx.saved_tensors
+        q, k, v, g, beta, A_log, h0, cs, D = ctx.saved_tensors
         if do is None:
             do = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
         r = bwd(q, k, v, g, beta, A_log, do.contiguous(), h0,
                 None if dhT is None else dhT.contiguous(), context=cs,
-                additive=ctx.additive, gate_logits=ctx.gate_logits, want_dh0=h0 is not None)
-        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None, None
+                additive=ctx.additive, gate_logits=ctx.gate_logits, norm_k=ctx.norm_k, D=D,
+                want_dD=D is not None and ctx.needs_input_grad[10], want_dh0=h0 is not None)
+        return (r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"], r["dh0"], None, None, None,
+                r["dD"])

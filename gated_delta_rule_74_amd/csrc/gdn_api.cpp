@@ -57,6 +57,8 @@ gdn_status_t check_aliasing(const Range *in, int nin, const Range *out, int nout
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+constexpr uint32_t KNOWN_FLAGS = GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS | GDN_FLAG_L2NORM_K;
+
 gdn_status_t check_shape(const gdn_shape_t *s) {
     if (!s) return fail(GDN_EINVAL, "shape is NULL");
     if (s->B < 1 || s->T < 0 || s->H < 1) return fail(GDN_EINVAL, "B and H must be >= 1, T >= 0");
@@ -64,8 +66,7 @@ gdn_status_t check_shape(const gdn_shape_t *s) {
         return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", s->dtype);
     if (s->chunk != 0 && s->chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 0 or 64");
-    if (s->flags & ~(GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS))
-        return fail(GDN_EINVAL, "unknown flag bits 0x%x", s->flags);
+    if (s->flags & ~KNOWN_FLAGS) return fail(GDN_EINVAL, "unknown flag bits 0x%x", s->flags);
     if (s->dtype == GDN_F32 && (s->dk > 64 || s->dv > 64))
         return fail(GDN_EUNSUPPORTED, "fp32 supports dk, dv <= 64");
     const double elems = (double)s->B * s->T * s->H * (s->dk > s->dv ? s->dk : s->dv);
@@ -100,7 +101,7 @@ CtxLayout ctx_layout(const gdn_shape_t *s) {
 size_t ctx_bytes(const gdn_shape_t *s) { return ctx_layout(s).total; }
 
 gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                 const float *beta, const float *A_log, const float *h0) {
+                 const float *beta, const float *A_log, const float *D, const float *h0) {
     gdn::SeqArgs a;
     a.q = q;
     a.k = k;
@@ -117,6 +118,8 @@ gdn::SeqArgs seq(const gdn_shape_t *s, const void *q, const void *k, const void 
     a.NC = nchunks(s);
     a.additive = (s->flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
     a.logits = (s->flags & GDN_FLAG_GATE_LOGITS) ? 1 : 0;
+    a.l2k = (s->flags & GDN_FLAG_L2NORM_K) ? 1 : 0;
+    a.D = D;
     return a;
 }
 
@@ -208,6 +211,10 @@ size_t scan_maps_floats(const gdn_shape_t *s) {
     const int n = scan_segments(s);
     return n > 1 ? (size_t)s->B * s->H * (n - 1) * s->dk * (s->dk + s->dv) : 0;
 }
+// per-chunk partial sums of do * v for dD, one slot per wave
+size_t dD_part_bytes(const gdn_shape_t *s) {
+    return align_up((size_t)s->B * s->H * nchunks(s) * gdn::DD_SLOTS * sizeof(float));
+}
 size_t scan_bytes(const gdn_shape_t *s) {
     const int n = scan_segments(s);
     if (n <= 1) return 0;
@@ -236,7 +243,8 @@ size_t gdn_bwd_workspace_size(const gdn_shape_t *s) {
     const size_t wide = align_up(gdn::bwd_wide_scratch_bytes(s->dtype == GDN_BF16, pad_of(s), nch));
     return ctx_bytes(s) /* recomputed forward context */ + align_up(states_bytes(s)) /* dh per chunk */ + part +
            align_up(gam_bytes(s)) /* forward decay */ + align_up(state32_bytes(s)) /* forward hand-off */ +
-           wide /* local-gradient scratch for wide heads */ + scan_bytes(s) /* scan scratch */;
+           wide /* local-gradient scratch for wide heads */ + scan_bytes(s) /* scan scratch */ +
+           dD_part_bytes(s) /* skip-term partial sums */;
 }
 
 } // extern "C"
@@ -401,19 +409,22 @@ static gdn_status_t fwd_empty(const gdn_shape_t *s, const float *h0, float *hT, 
     return hip_status(gdn::launch_copy_or_zero(hT, h0, sb / 4, st), "gdn_fwd (empty sequence)");
 }
 
-static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *h0, const void *ctx, const float *dhT,
-                              float *dA_log, float *dh0, float *hT, hipStream_t st) {
+static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *D, const float *h0, const void *ctx,
+                              const float *dhT, float *dA_log, float *dD, float *dh0, float *hT, hipStream_t st) {
     if (!dA_log) return fail(GDN_EINVAL, "a required pointer is NULL");
     if (ctx && hT) return fail(GDN_EINVAL, "hT can only be recomputed when ctx is NULL");
-    const float *f32[] = {h0, dhT, dA_log, dh0, hT};
+    const float *f32[] = {D, h0, dhT, dA_log, dD, dh0, hT};
     for (const float *p : f32)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
     const size_t sb = state32_bytes(s);
-    const Range in[] = {{h0, h0 ? sb : 0, "h0"}, {dhT, dhT ? sb : 0, "dhT"}};
-    const Range out[] = {{dA_log, (size_t)s->H * 4, "dA_log"}, {dh0, dh0 ? sb : 0, "dh0"}, {hT, hT ? sb : 0, "hT"}};
-    gdn_status_t e = check_aliasing(in, 2, out, 3);
+    const size_t hb = (size_t)s->H * 4;
+    const Range in[] = {{h0, h0 ? sb : 0, "h0"}, {dhT, dhT ? sb : 0, "dhT"}, {D, D ? hb : 0, "D"}};
+    const Range out[] = {{dA_log, hb, "dA_log"}, {dD, dD ? hb : 0, "dD"}, {dh0, dh0 ? sb : 0, "dh0"},
+                         {hT, hT ? sb : 0, "hT"}};
+    gdn_status_t e = check_aliasing(in, 3, out, 4);
     if (e != GDN_OK) return e;
     hipError_t he = gdn::launch_copy_or_zero(dA_log, nullptr, (size_t)s->H, st);
+    if (he == hipSuccess && dD) he = gdn::launch_copy_or_zero(dD, nullptr, (size_t)s->H, st);
     if (he == hipSuccess && dh0) he = gdn::launch_copy_or_zero(dh0, dhT, sb / 4, st);
     if (he == hipSuccess && hT) he = gdn::launch_copy_or_zero(hT, h0, sb / 4, st);
     return hip_status(he, "gdn_bwd (empty sequence)");
@@ -424,7 +435,8 @@ static gdn_status_t bwd_empty(const gdn_shape_t *s, const float *h0, const void 
 namespace gdn {
 
 gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                       const float *beta, const float *A_log, const float *D, const float *h0, void *o, float *hT,
+                       void *ctx,
                        void *ws, size_t ws_bytes, void *stream, bool one_stream,
                        gdn_status_t (*ws_lookup)(void *&ws)) {
     gdn_status_t st = check_shape(s);
@@ -435,7 +447,7 @@ gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const
     const void *vec[] = {q, k, v, o};
     for (const void *p : vec)
         if (!aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, o must be 16-byte aligned");
-    const void *f32[] = {g, beta, A_log, h0, hT};
+    const void *f32[] = {g, beta, A_log, D, h0, hT};
     for (const void *p : f32)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
     if (ctx && !aligned(ctx, 256)) return fail(GDN_EINVAL, "ctx must be 256-byte aligned");
@@ -451,18 +463,18 @@ gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const
     const size_t sb = (size_t)s->B * s->H * s->dk * s->dv * 4;
     const Range in[] = {{q, BTH * s->dk * e, "q"},     {k, BTH * s->dk * e, "k"}, {v, BTH * s->dv * e, "v"},
                         {g, BTH * 4, "g"},             {beta, BTH * 4, "beta"},   {A_log, (size_t)s->H * 4, "A_log"},
-                        {h0, h0 ? sb : 0, "h0"}};
+                        {h0, h0 ? sb : 0, "h0"},       {D, D ? (size_t)s->H * 4 : 0, "D"}};
     const Range out[] = {{o, BTH * s->dv * e, "o"},
                          {hT, hT ? sb : 0, "hT"},
                          {ctx, ctx ? ctx_bytes(s) : 0, "ctx"},
                          {ws, ws_lookup ? 0 : need, "workspace"}};
-    st = check_aliasing(in, 7, out, 4);
+    st = check_aliasing(in, 8, out, 4);
     if (st != GDN_OK) return st;
     // a workspace the library owns is looked up only once the call is known
     // to be valid (its lookup is the first device call)
     if (ws_lookup && (st = ws_lookup(ws)) != GDN_OK) return st;
     const bool bf = s->dtype == GDN_BF16;
-    const int D = pad_of(s);
+    const int Dp = pad_of(s);
     char *w = (char *)ws, *c = (char *)ctx;
     const CtxLayout cl = ctx_layout(s);
     void *U = ctx ? c + cl.u : w;
@@ -471,9 +483,9 @@ gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const
     float *gam = (float *)(w + align_up(blocks_bytes(s, s->dv)) + align_up(blocks_bytes(s, s->dk)));
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     float *scan = (float *)((char *)hs + align_up(state32_bytes(s)));
-    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
+    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, D, h0);
     return hip_status(
-        run_forward(s, sa, bf, D, U, NK, Tsave, gam, hs, scan, o, hT, ctx, (hipStream_t)stream, one_stream),
+        run_forward(s, sa, bf, Dp, U, NK, Tsave, gam, hs, scan, o, hT, ctx, (hipStream_t)stream, one_stream),
         "gdn_fwd launch");
 }
 
@@ -484,31 +496,31 @@ gdn_status_t fail_detail(gdn_status_t st, const char *text) { return fail(st, "%
 extern "C" {
 
 gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
-                     void *ws, size_t ws_bytes, void *stream) {
-    return gdn::fwd_entry(s, q, k, v, g, beta, A_log, h0, o, hT, ctx, ws, ws_bytes, stream, false, nullptr);
+                     const float *beta, const float *A_log, const float *D, const float *h0, void *o, float *hT,
+                     void *ctx, void *ws, size_t ws_bytes, void *stream) {
+    return gdn::fwd_entry(s, q, k, v, g, beta, A_log, D, h0, o, hT, ctx, ws, ws_bytes, stream, false, nullptr);
 }
 
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *A_log, const float *h0, const void *ctx,
+                     const float *beta, const float *A_log, const float *D, const float *h0, const void *ctx,
                      const void *dout, const float *dhT, void *dq, void *dk, void *dv, float *dg,
-                     float *dbeta, float *dA_log, float *dh0, float *hT, void *ws, size_t ws_bytes,
+                     float *dbeta, float *dA_log, float *dD, float *dh0, float *hT, void *ws, size_t ws_bytes,
                      void *stream) {
     gdn_status_t st = check_shape(s);
     if (st != GDN_OK) return st;
-    if (s->T == 0) return bwd_empty(s, h0, ctx, dhT, dA_log, dh0, hT, (hipStream_t)stream);
+    if (s->T == 0) return bwd_empty(s, D, h0, ctx, dhT, dA_log, dD, dh0, hT, (hipStream_t)stream);
     if (!q || !k || !v || !g || !beta || !A_log || !dout || !dq || !dk || !dv || !dg || !dbeta || !dA_log)
         return fail(GDN_EINVAL, "a required pointer is NULL");
     if (ctx && hT) return fail(GDN_EINVAL, "hT can only be recomputed when ctx is NULL");
     const bool bf = s->dtype == GDN_BF16;
-    const int D = pad_of(s);
-    if (!gdn::bwd_supported(bf, D))
+    const int Dp = pad_of(s);
+    if (!gdn::bwd_supported(bf, Dp))
         return fail(GDN_EUNSUPPORTED, "backward not built for %s with head dim %d", bf ? "bf16" : "fp32",
                     s->dk > s->dv ? s->dk : s->dv);
     const void *vec[] = {q, k, v, dout, dq, dk, dv};
     for (const void *p : vec)
         if (!aligned(p, 16)) return fail(GDN_EINVAL, "q, k, v, do, dq, dk, dv must be 16-byte aligned");
-    const void *f32[] = {g, beta, A_log, h0, dhT, dg, dbeta, dA_log, dh0, hT};
+    const void *f32[] = {g, beta, A_log, D, h0, dhT, dg, dbeta, dA_log, dD, dh0, hT};
     for (const void *p : f32)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "fp32 arrays must be 4-byte aligned");
     if (ctx && !aligned(ctx, 256)) return fail(GDN_EINVAL, "ctx must be 256-byte aligned");
@@ -528,12 +540,14 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
                         {ctx, ctx ? ctx_bytes(s) : 0, "ctx"},
                         {dout, BTH * s->dv * e, "do"},
                         {dhT, dhT ? sb : 0, "dhT"},
+                        {D, D ? (size_t)s->H * 4 : 0, "D"},
                         {ws, need, "workspace"}};
     const Range out[] = {{dq, BTH * s->dk * e, "dq"},       {dk, BTH * s->dk * e, "dk"},
                          {dv, BTH * s->dv * e, "dv"},       {dg, BTH * 4, "dg"},
                          {dbeta, BTH * 4, "dbeta"},         {dA_log, (size_t)s->H * 4, "dA_log"},
-                         {dh0, dh0 ? sb : 0, "dh0"},        {hT, hT ? sb : 0, "hT"}};
-    st = check_aliasing(in, 11, out, 8);
+                         {dh0, dh0 ? sb : 0, "dh0"},        {hT, hT ? sb : 0, "hT"},
+                         {dD, dD ? (size_t)s->H * 4 : 0, "dD"}};
+    st = check_aliasing(in, 12, out, 9);
     if (st != GDN_OK) return st;
 
     hipStream_t strm = (hipStream_t)stream;
@@ -544,13 +558,14 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     float *gam = (float *)((char *)part + align_up((size_t)s->B * s->H * nchunks(s) * sizeof(float)));
     float *hs = (float *)((char *)gam + align_up(gam_bytes(s)));
     float *wide = (float *)((char *)hs + align_up(state32_bytes(s)));
-    const bool has_wide = gdn::bwd_wide_scratch_bytes(bf, D, s->B * s->H * nchunks(s)) > 0;
-    float *scan = (float *)((char *)wide + align_up(gdn::bwd_wide_scratch_bytes(bf, D, s->B * s->H * nchunks(s))));
-    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, h0);
+    const bool has_wide = gdn::bwd_wide_scratch_bytes(bf, Dp, s->B * s->H * nchunks(s)) > 0;
+    float *scan = (float *)((char *)wide + align_up(gdn::bwd_wide_scratch_bytes(bf, Dp, s->B * s->H * nchunks(s))));
+    float *dD_part = (float *)((char *)scan + scan_bytes(s));
+    const gdn::SeqArgs sa = seq(s, q, k, v, g, beta, A_log, D, h0);
     const CtxLayout cl = ctx_layout(s);
     hipError_t he;
     if (!ctx) {
-        he = run_forward(s, sa, bf, D, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, hs, scan, nullptr, hT, wctx,
+        he = run_forward(s, sa, bf, Dp, wctx + cl.u, wctx + cl.nk, wctx + cl.t, gam, hs, scan, nullptr, hT, wctx,
                          strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd forward recompute launch");
         ctx = wctx;
@@ -565,7 +580,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     ca.dhs = dhs;
     ca.dh0 = dh0;
     const int nscan = scan_segments(s);
-    const int BVc = gdn::bwd_chain_vblock(bf, D, nscan > 1);
+    const int BVc = gdn::bwd_chain_vblock(bf, Dp, nscan > 1);
     ca.NVB = (s->dv + BVc - 1) / BVc;
     if (nscan > 1) {
         // parallel scan, mirror of the forward's: the maps of every range but
@@ -574,7 +589,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
         ca.nseg = nscan;
         ca.mode = 1;
         ca.maps = scan;
-        he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
+        he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, Dp, strm); }, strm);
         if (he != hipSuccess) return hip_status(he, "gdn_bwd chain (maps) launch");
         gdn::ScanArgs sc;
         sc.maps = scan;
@@ -591,7 +606,7 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
         ca.maps = nullptr;
         ca.seg_dh = sc.seg_h;
     }
-    he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, D, strm); }, strm);
+    he = timed(K_BWD_CHAIN, [&] { return gdn::launch_bwd_chain(ca, bf, Dp, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd chain launch");
     gdn::BwdLocalArgs la;
     la.s = sa;
@@ -607,11 +622,17 @@ gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const v
     la.dg = dg;
     la.dbeta = dbeta;
     la.dA_part = part;
+    la.dD_part = dD ? dD_part : nullptr;
     la.wide = has_wide ? wide : nullptr;
-    he = timed(K_BWD_LOCAL, [&] { return gdn::launch_bwd_local(la, bf, D, strm); }, strm);
+    he = timed(K_BWD_LOCAL, [&] { return gdn::launch_bwd_local(la, bf, Dp, strm); }, strm);
     if (he != hipSuccess) return hip_status(he, "gdn_bwd local launch");
     he = timed(K_DA_REDUCE, [&] { return gdn::launch_dA_reduce(part, dA_log, s->B, s->H, nchunks(s), strm); }, strm);
-    return hip_status(he, "gdn_bwd dA_log launch");
+    if (he != hipSuccess || !dD) return hip_status(he, "gdn_bwd dA_log launch");
+    // dD[h]: the [B][H][NC][DD_SLOTS] partial sums read as NC * DD_SLOTS
+    // terms per (batch, head), the layout the dA_log reduction walks
+    he = timed(K_DA_REDUCE,
+               [&] { return gdn::launch_dA_reduce(dD_part, dD, s->B, s->H, nchunks(s) * gdn::DD_SLOTS, strm); }, strm);
+    return hip_status(he, "gdn_bwd dD launch");
 }
 
 // S = 0: no token, so the state is carried over unchanged (h_out = h_in,
@@ -629,27 +650,28 @@ static gdn_status_t step_empty(int32_t N, int32_t H, int32_t dk, int32_t dv, con
 
 gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
                              uint32_t flags, const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, const float *A_log, const float *h_in, float *h_out, void *o,
-                             void *stream) {
+                             const float *beta, const float *A_log, const float *D, const float *h_in,
+                             float *h_out, void *o, void *stream) {
     if (N < 0 || H < 1 || S < 0) return fail(GDN_EINVAL, "N, S must be >= 0 and H >= 1");
     if (dk < 1 || dv < 1 || dk > 128 || dv > 128) return fail(GDN_EINVAL, "dk and dv must be in [1, 128]");
     if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EINVAL, "unknown dtype %d", dtype);
-    if (flags & ~(GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS)) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
+    if (flags & ~KNOWN_FLAGS) return fail(GDN_EINVAL, "unknown flag bits 0x%x", flags);
     if ((double)N * H * dk * dv >= 2147483648.0 || (double)N * S * H * (dk > dv ? dk : dv) >= 2147483648.0)
         return fail(GDN_EINVAL, "state or tokens too large");
     if (N == 0) return GDN_OK; // no sequence: nothing to read or write
     if (S == 0) return step_empty(N, H, dk, dv, h_in, h_out, (hipStream_t)stream);
     if (!q || !k || !v || !g || !beta || !A_log || !h_out || !o)
         return fail(GDN_EINVAL, "a required pointer is NULL");
-    const void *all[] = {q, k, v, o, g, beta, A_log, h_in, h_out};
+    const void *all[] = {q, k, v, o, g, beta, A_log, D, h_in, h_out};
     for (const void *p : all)
         if (p && !aligned(p, 4)) return fail(GDN_EINVAL, "pointers must be 4-byte aligned");
     const size_t e = esize(dtype), NSH = (size_t)N * S * H, sb = (size_t)N * H * dk * dv * 4;
     const Range in[] = {{q, NSH * dk * e, "q"},        {k, NSH * dk * e, "k"},     {v, NSH * dv * e, "v"},
                         {g, NSH * 4, "g"},             {beta, NSH * 4, "beta"},    {A_log, (size_t)H * 4, "A_log"},
-                        {h_in == h_out ? nullptr : h_in, sb, "h_in"}};
+                        {h_in == h_out ? nullptr : h_in, sb, "h_in"},
+                        {D, D ? (size_t)H * 4 : 0, "D"}};
     const Range out[] = {{h_out, sb, "h_out"}, {o, NSH * dv * e, "o"}};
-    gdn_status_t st = check_aliasing(in, 7, out, 2);
+    gdn_status_t st = check_aliasing(in, 8, out, 2);
     if (st != GDN_OK) return st;
     if (h_in && h_in != h_out && overlap(Range{h_in, sb, "h_in"}, Range{h_out, sb, "h_out"}))
         return fail(GDN_EINVAL, "h_in and h_out overlap without being equal");
@@ -669,6 +691,8 @@ gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_
     a.dv = dv;
     a.additive = (flags & GDN_FLAG_ADDITIVE) ? 1 : 0;
     a.logits = (flags & GDN_FLAG_GATE_LOGITS) ? 1 : 0;
+    a.l2k = (flags & GDN_FLAG_L2NORM_K) ? 1 : 0;
+    a.D = D;
     a.S = S;
     return hip_status(timed(K_STEP, [&] { return gdn::launch_step(a, dtype == GDN_BF16, (hipStream_t)stream); }, (hipStream_t)stream),
                       "gdn_step launch");
@@ -676,8 +700,9 @@ gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_
 
 gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
                       const void *q, const void *k, const void *v, const float *g, const float *beta,
-                      const float *A_log, const float *h_in, float *h_out, void *o, void *stream) {
-    return gdn_step_tokens(N, 1, H, dk, dv, dtype, flags, q, k, v, g, beta, A_log, h_in, h_out, o, stream);
+                      const float *A_log, const float *D, const float *h_in, float *h_out, void *o,
+                      void *stream) {
+    return gdn_step_tokens(N, 1, H, dk, dv, dtype, flags, q, k, v, g, beta, A_log, D, h_in, h_out, o, stream);
 }
 
 } // extern "C"

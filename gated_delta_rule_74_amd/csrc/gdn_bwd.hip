@@ -137,6 +137,7 @@ __global__ __launch_bounds__(NTHR) void bwd_chain_kernel(BwdChainArgs a) {
             egn[lane] = dc.egn;
             if (lane == 0) misc[0] = dc.eglast;
         }
+        if (s.l2k) fk.normalize_rows(nullptr, tid);
         fk.stash(Ks, LDD, tid);
         if (!mblk) {
             fq.stash(Qs, LDD, tid);
@@ -332,6 +333,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
             egn_of(i3)[lane] = dc.egn;
             if (lane == 0) el_of(i3)[0] = dc.eglast;
         }
+        if (s.l2k) fk.normalize_rows(nullptr, gtid);
         fk.stash(kbuf(i3), LDD, gtid);
         if (!add) fn.stash(nbuf(i3), LDD, gtid);
         fq.stash(qbuf(i2), LDD, gtid);
@@ -554,6 +556,9 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
 //   RQ Q (whole chunk)                RP (dP o Gam)^T (P5-6) -> dQ (P9)
 // Inputs needed in two phases stay in registers between their stashes.
 
+// every wave of a local-gradient workgroup writes one skip-term slot per chunk
+static_assert(NWAVE == DD_SLOTS, "skip-term slots");
+
 template <bool BF, int D> struct LocalSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
@@ -580,7 +585,8 @@ template <bool BF, int D> struct LocalSmem {
     static constexpr int oBet = oEgn + C * 4;
     static constexpr int oGch = oBet + C * 4;
     static constexpr int oMisc = oGch + C * 4;
-    static constexpr int SIZE = oMisc + (16 + NWAVE) * 4;
+    static constexpr int oRinv = oMisc + (16 + NWAVE) * 4; // 1/|k| per row (normalised keys)
+    static constexpr int SIZE = oRinv + C * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -609,6 +615,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     float *bet = (float *)(smem + L::oBet);
     float *gch = (float *)(smem + L::oGch);
     float *misc = (float *)(smem + L::oMisc);
+    float *rinvK = (float *)(smem + L::oRinv);
 
     const SeqArgs &s = a.s;
     const int tid0 = threadIdx.x;
@@ -693,6 +700,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
 
     // ---- P1: gates, decay, K K^T and Q K^T; W = U - Kw h
+    if (s.l2k) fk.normalize_rows(rinvK, tid);
     fk.stash(Ks, LDD, tid);
     fq.stash(RQ, LDD, tid);
     fh.stash(R1, LDD, tid);
@@ -887,43 +895,95 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         col_partials<4, 4>(xgC, pCgC, wave, lane);
         __syncthreads();
         // dq, dk, dv rows of the chunk: 16-byte stores (dv = -beta * (-dV'), from
-        // the transposed -dV't)
+        // the transposed -dV't). Edges: with normalised keys dk goes back
+        // through the normalisation, dk = (dk_hat - k_hat (k_hat . dk_hat)) / |k|
+        // (row dots over the lanes that hold a row); with the skip term dv
+        // gains D_h do, and the chunk's share of dD_h (sum of do * v) goes to
+        // one slot per wave.
         {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+            const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
+            const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
+            const float Dh = s.D ? s.D[h] : 0.f;
+            const bool edge_v = s.D || a.dD_part; // do (and v) rows are needed
+            float dsum = 0.f;
             constexpr int V = O::VEC, NG = D / V;
+            union Pk {
+                uint4 u;
+                S x[V];
+            };
             if (VEC) {
                 for (int it = tid; it < C * NG; it += NTHR) {
                     const int j = it / NG, c0 = (it % NG) * V;
+                    Pk kd;
+                    kd.u = *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                    if (s.l2k) {
+                        Pk kh;
+                        kh.u = *reinterpret_cast<const uint4 *>(Ks + j * LDD + c0);
+                        float dot = 0.f;
+#pragma unroll
+                        for (int e = 0; e < V; ++e) dot += to_f(kh.x[e]) * to_f(kd.x[e]);
+#pragma unroll
+                        for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                        const float ri = rinvK[j];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) kd.x[e] = from_f<BF>((to_f(kd.x[e]) - to_f(kh.x[e]) * dot) * ri);
+                    }
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
                             *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
-                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
-                            *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
                     }
                     if (c0 < dv) {
-                        union {
-                            uint4 u;
-                            S x[V];
-                        } pk;
+                        Pk pk, dov, vv;
                         const float nb = -bet[j];
+                        if (edge_v) {
+                            dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
+                            vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
+                        }
 #pragma unroll
-                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(R4[(c0 + e) * LDC + j]));
+                        for (int e = 0; e < V; ++e) {
+                            float x = nb * to_f(R4[(c0 + e) * LDC + j]);
+                            if (s.D) x += Dh * to_f(dov.x[e]);
+                            if (a.dD_part) dsum += to_f(dov.x[e]) * to_f(vv.x[e]);
+                            pk.x[e] = from_f<BF>(x);
+                        }
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
             } else {
                 for (int it = tid; it < C * D; it += NTHR) {
                     const int j = it / D, col = it % D;
+                    float kdv = to_f(R5[j * LDD + col]);
+                    if (s.l2k) {
+                        const float khv = to_f(Ks[j * LDD + col]);
+                        float dot = khv * kdv;
+#pragma unroll
+                        for (int off = D / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                        kdv = (kdv - khv * dot) * rinvK[j];
+                    }
                     if (j >= n) continue;
                     if (col < dk) {
                         dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
-                        dk_out[(size_t)j * H * dk + col] = R5[j * LDD + col];
+                        dk_out[(size_t)j * H * dk + col] = from_f<BF>(kdv);
                     }
-                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(R4[col * LDC + j]));
+                    if (col < dv) {
+                        float x = -bet[j] * to_f(R4[col * LDC + j]);
+                        if (edge_v) {
+                            const float dd = to_f(do_in[(size_t)j * H * dv + col]);
+                            if (s.D) x += Dh * dd;
+                            if (a.dD_part) dsum += dd * to_f(v_in[(size_t)j * H * dv + col]);
+                        }
+                        dv_out[(size_t)j * H * dv + col] = from_f<BF>(x);
+                    }
                 }
+            }
+            if (a.dD_part) {
+                dsum = wave_sum(dsum);
+                if (lane == 0) a.dD_part[cb * DD_SLOTS + wave] = dsum;
             }
         }
         if (wave == 0) {
@@ -1038,7 +1098,7 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
     __shared__ float As[C * WIDE_LDA];
     __shared__ float Bs[WIDE_KS * WIDE_LDB];
     __shared__ double gam[C];
-    __shared__ float eg[C], egn[C], bet[C], gch[C], red[NTHR];
+    __shared__ float eg[C], egn[C], bet[C], gch[C], rk[C], red[NTHR];
     const SeqArgs &s = a.s;
     const int tid0 = threadIdx.x;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC;
@@ -1069,7 +1129,8 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
         const S *tc = (const S *)a.Tm + cb * C * C;
         const size_t sq = (size_t)H * dk, sv = (size_t)H * dv;
         auto Q = [&](int i, int d) { return i < n ? to_f(qb[i * sq + d]) : 0.f; };
-        auto K = [&](int i, int d) { return i < n ? to_f(kb[i * sq + d]) : 0.f; };
+        // keys as the recurrence sees them (rk: 1 / |k| per row when normalised)
+        auto K = [&](int i, int d) { return i < n ? to_f(kb[i * sq + d]) * rk[i] : 0.f; };
         auto V = [&](int i, int e) { return i < n ? to_f(vb[i * sv + e]) : 0.f; };
         auto dO = [&](int i, int e) { return i < n ? to_f(ob[i * sv + e]) : 0.f; };
         auto Hm = [&](int d, int e) { return to_f(hc[(size_t)e * dk + d]); };
@@ -1092,6 +1153,19 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
             bet[lane] = lane < n ? gate_of(br, s.logits) : 0.f;
             gch[lane] = gl;
             if (lane == 0) red[0] = dcy.eglast;
+        }
+        {
+            // 1 / sqrt(|k|^2 + KEY_EPS) per row: eight lanes per row
+            const int i = tid >> 3, gq = tid & 7;
+            float ss = 0.f;
+            if (s.l2k && i < n)
+                for (int d = gq; d < dk; d += 8) {
+                    const float x = to_f(kb[i * sq + d]);
+                    ss += x * x;
+                }
+#pragma unroll
+            for (int off = 4; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            if (gq == 0) rk[i] = s.l2k ? 1.f / sqrtf(ss + KEY_EPS) : 1.f;
         }
         __syncthreads();
         const float eglast = red[0];
@@ -1167,16 +1241,45 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void bwd_local_wide_kernel
         wide_mm(C, dk, C, [&](int i, int j) { return sdP[j * C + i] * Gm(j, i); }, Q, As, Bs, tid, acc);
         wide_mm(C, dk, C, [&](int i, int j) { return sT[i * C + j]; }, K, As, Bs, tid, acc2);
         S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
-        each(C, dk, [&](int i, int d, int x, int y) {
+        if (!s.l2k) {
+            each(C, dk, [&](int i, int d, int x, int y) {
+                if (i < n)
+                    dk_out[i * sq + d] = from_f<BF>(acc[x][y] + acc2[x][y] + egn[i] * sdKt[i * WIDE_LD + d] +
+                                                    bet[i] * eg[i] * sdKp[i * WIDE_LD + d]);
+            });
+        } else {
+            // gradient wrt the normalised keys into the free dKw scratch, then
+            // back through the normalisation, dk = (dk_hat - k_hat (k_hat .
+            // dk_hat)) / |k|, eight lanes per row
+            each(C, dk, [&](int i, int d, int x, int y) {
+                sdKw[i * WIDE_LD + d] = acc[x][y] + acc2[x][y] + egn[i] * sdKt[i * WIDE_LD + d] +
+                                        bet[i] * eg[i] * sdKp[i * WIDE_LD + d];
+            });
+            __syncthreads();
+            const int i = tid >> 3, gq = tid & 7;
+            float dot = 0.f;
+            for (int d = gq; d < dk; d += 8) dot += K(i, d) * sdKw[i * WIDE_LD + d];
+#pragma unroll
+            for (int off = 4; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
             if (i < n)
-                dk_out[i * sq + d] = from_f<BF>(acc[x][y] + acc2[x][y] + egn[i] * sdKt[i * WIDE_LD + d] +
-                                                bet[i] * eg[i] * sdKp[i * WIDE_LD + d]);
-        });
-        // ---- dV = diag(beta) dV'
+                for (int d = gq; d < dk; d += 8)
+                    dk_out[i * sq + d] = from_f<BF>((sdKw[i * WIDE_LD + d] - K(i, d) * dot) * rk[i]);
+        }
+        // ---- dV = diag(beta) dV' (+ D_h dO with the skip term, whose dD_h
+        // share, the sum of dO * V, goes to one slot per wave)
         S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+        const float Dh = s.D ? s.D[h] : 0.f;
+        float dsum = 0.f;
         for (int e = tid; e < n * dv; e += NTHR) {
             const int i = e / dv, f = e % dv;
-            dv_out[i * sv + f] = from_f<BF>(bet[i] * sdVp[i * WIDE_LD + f]);
+            float x = bet[i] * sdVp[i * WIDE_LD + f];
+            if (s.D) x += Dh * dO(i, f);
+            if (a.dD_part) dsum += dO(i, f) * V(i, f);
+            dv_out[i * sv + f] = from_f<BF>(x);
+        }
+        if (a.dD_part) {
+            dsum = wave_sum(dsum);
+            if (lane == 0) a.dD_part[cb * DD_SLOTS + wave] = dsum;
         }
         // ---- <h, dh'> in a fixed order
         float hd = 0.f;

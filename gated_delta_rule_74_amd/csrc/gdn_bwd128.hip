@@ -41,6 +41,7 @@ namespace {
 #endif
 constexpr int NWD = GDN_W128;
 constexpr int NTD = 64 * NWD; // threads per workgroup
+static_assert(NWD == DD_SLOTS, "one skip-term slot per wave");
 constexpr int DW = 128;       // padded head dim
 constexpr int KUNR = 2;       // K steps unrolled per product (register budget)
 
@@ -51,7 +52,7 @@ struct Wide128 {
     static constexpr int sDD = DW * LDD * 2;
     static constexpr int sDC = DW * LDC * 2;
     static constexpr int sCC = C * LDC * 2;
-    static constexpr int sPart = (2 * C * (DW / 16) + 3 * C * 4) * 4;
+    static constexpr int sPart = (3 * C * (DW / 16) + 3 * C * 4) * 4;
     static constexpr int x0 = 0;
     static constexpr int x1 = x0 + sCD;
     static constexpr int x2 = x1 + sDD;
@@ -65,7 +66,9 @@ struct Wide128 {
     static constexpr int oBet = oEgn + C * 4;
     static constexpr int oGch = oBet + C * 4;
     static constexpr int oMisc = oGch + C * 4;
-    static constexpr int SIZE = oMisc + (16 + 2 * NWD) * 4;
+    static constexpr int oRinv = oMisc + (16 + NWD) * 4; // 1/|k| per row (normalised keys)
+    static constexpr int oRdot = oRinv + C * 4;              // k_hat . dk_hat per row
+    static constexpr int SIZE = oRdot + C * 4;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 
     static_assert(sCD <= sDC && 2 * sCD == sDD, "region sharing");
@@ -138,6 +141,7 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     float *bet = (float *)(smem + L::oBet);
     float *gch = (float *)(smem + L::oGch);
     float *misc = (float *)(smem + L::oMisc);
+    float *rinvK = (float *)(smem + L::oRinv), *rdot = (float *)(smem + L::oRdot);
 
     const SeqArgs &s = a.s;
     const int tid0 = threadIdx.x;
@@ -208,10 +212,13 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     // dbeta / dgam contributions, row-summed per tile as they are formed
     // (row_compact / col_compact): rb, rg over [C][D] grids (dbeta, dgam; the
     // s_j terms of dgam enter rg with their sign, their total a per-wave
-    // slot); rbc row sums, xgr row sums and xgc column sums over [C][C]
-    float rb = 0.f, rg = 0.f, rbc = 0.f, xgr = 0.f, xgc = 0.f;
+    // slot); rbc row sums, xgr row sums and xgc column sums over [C][C]; rs
+    // row sums of s_j (kept apart so that row j's -s_j and the last row's
+    // total are made of the very same per-row values)
+    float rb = 0.f, rg = 0.f, rbc = 0.f, xgr = 0.f, xgc = 0.f, rs = 0.f;
 
     // ---- P1: K K^T, Q K^T, decay; W = U - Kw h
+    if (s.l2k) fk.normalize_rows(rinvK, tid);
     fk.stash(X0, LDD, tid);
     fq.stash(X3, LDD, tid);
     fh.stash(X1, LDD, tid);
@@ -275,17 +282,12 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         gemm<true, 4, DT, D, true, true, NWD, KUNR>(X4, LDC, X2, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
         // enters dgam_j with a minus sign and the last row with its total
-        float st = 0.f;
         for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];
             accKd[i][e] = x;
-            const float sx = x * to_f(X0[row * LDD + col]);
-            accKt[i][e] = -sx;
-            st += sx;
+            accKt[i][e] = x * to_f(X0[row * LDD + col]);
         });
-        rg += row_compact<4, DT>(accKt, lane); pin(rg);
-        st = wave_sum(st);
-        if (lane == 0) misc[16 + NWD + wave] = st;
+        rs += row_compact<4, DT>(accKt, lane); pin(rs);
         // <h, dh'> over the two staged states (padding is zero), one slot per wave
         float hd = 0.f;
         for (int it = tid; it < D * D / 8; it += NTD) {
@@ -421,8 +423,9 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
     {
         float *pRbD = (float *)X6, *pRgD = pRbD + C * DT;
-        float *pRbC = pRgD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
+        float *pRbC = pRgD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4, *pRsD = pCgC + C * 4;
         write_rows<4, 4>(rbc, pRbC, wave, lane);
+        write_rows<4, DT>(rs, pRsD, wave, lane);
         write_rows<4, 4>(xgr, pRgC, wave, lane);
         write_rows<4, DT>(rb, pRbD, wave, lane);
         write_rows<4, DT>(rg, pRgD, wave, lane);
@@ -432,29 +435,72 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
             for (int j = wave / 4; j < 4; j += NWD / 4)
                 pCgC[(16 * (wave % 4) + lane) * 4 + j] = (j == wave / 4) ? xgc : 0.f;
         __syncthreads();
+        // Edges: with normalised keys dk goes back through the normalisation,
+        // dk = (dk_hat - k_hat (k_hat . dk_hat)) / |k|; with the skip term dv
+        // gains D_h do and the chunk's share of dD_h (sum of do * v) goes to
+        // one slot per wave.
+        if (s.l2k && !VEC) {
+            // row dots first (a row spans more lanes than a wave here)
+            constexpr int PARTS = NTD / C, CPP = D / PARTS;
+            const int j = tid / PARTS, p0 = (tid % PARTS) * CPP;
+            float dot = 0.f;
+            for (int c = p0; c < p0 + CPP; ++c) dot += bf2f(X0[j * LDD + c]) * bf2f(X5[j * LDD + c]);
+#pragma unroll
+            for (int off = PARTS / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+            if (tid % PARTS == 0) rdot[j] = dot;
+            __syncthreads();
+        }
         {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+            const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
+            const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
+            const float Dh = s.D ? s.D[h] : 0.f;
+            const bool edge_v = s.D || a.dD_part; // do (and v) rows are needed
+            float dsum = 0.f;
             constexpr int V = 8, NG = D / V;
+            union Pk {
+                uint4 u;
+                S x[V];
+            };
             if (VEC) {
                 for (int it = tid; it < C * NG; it += NTD) {
                     const int j = it / NG, c0 = (it % NG) * V;
+                    Pk kd;
+                    kd.u = *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
+                    if (s.l2k) {
+                        Pk kh;
+                        kh.u = *reinterpret_cast<const uint4 *>(X0 + j * LDD + c0);
+                        float dot = 0.f;
+#pragma unroll
+                        for (int e = 0; e < V; ++e) dot += bf2f(kh.x[e]) * bf2f(kd.x[e]);
+#pragma unroll
+                        for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                        const float ri = rinvK[j];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) kd.x[e] = f2bf((bf2f(kd.x[e]) - bf2f(kh.x[e]) * dot) * ri);
+                    }
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
                             *reinterpret_cast<const uint4 *>(X1 + j * LDD + c0);
-                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
-                            *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
                     }
                     if (c0 < dv) {
-                        union {
-                            uint4 u;
-                            S x[V];
-                        } pk;
+                        Pk pk, dov, vv;
                         const float nb = -bet[j];
+                        if (edge_v) {
+                            dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
+                            vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
+                        }
 #pragma unroll
-                        for (int e = 0; e < V; ++e) pk.x[e] = f2bf(nb * bf2f(X3[(c0 + e) * LDC + j]));
+                        for (int e = 0; e < V; ++e) {
+                            float x = nb * bf2f(X3[(c0 + e) * LDC + j]);
+                            if (s.D) x += Dh * bf2f(dov.x[e]);
+                            if (a.dD_part) dsum += bf2f(dov.x[e]) * bf2f(vv.x[e]);
+                            pk.x[e] = f2bf(x);
+                        }
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
@@ -464,19 +510,34 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
                     if (j >= n) continue;
                     if (col < dk) {
                         dq_out[(size_t)j * H * dk + col] = X1[j * LDD + col];
-                        dk_out[(size_t)j * H * dk + col] = X5[j * LDD + col];
+                        float kdv = bf2f(X5[j * LDD + col]);
+                        if (s.l2k) kdv = (kdv - bf2f(X0[j * LDD + col]) * rdot[j]) * rinvK[j];
+                        dk_out[(size_t)j * H * dk + col] = f2bf(kdv);
                     }
-                    if (col < dv) dv_out[(size_t)j * H * dv + col] = f2bf(-bet[j] * bf2f(X3[col * LDC + j]));
+                    if (col < dv) {
+                        float x = -bet[j] * bf2f(X3[col * LDC + j]);
+                        if (edge_v) {
+                            const float dd = bf2f(do_in[(size_t)j * H * dv + col]);
+                            if (s.D) x += Dh * dd;
+                            if (a.dD_part) dsum += dd * bf2f(v_in[(size_t)j * H * dv + col]);
+                        }
+                        dv_out[(size_t)j * H * dv + col] = f2bf(x);
+                    }
                 }
+            }
+            if (a.dD_part) {
+                dsum = wave_sum(dsum);
+                if (lane == 0) a.dD_part[cb * DD_SLOTS + wave] = dsum;
             }
         }
         if (wave == 0) {
             const int i = lane;
-            float db = 0.f, dgm = 0.f;
+            float db = 0.f, dgm = 0.f, sj = 0.f;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 db += pRbD[i * DT + t];
                 dgm += pRgD[i * DT + t];
+                sj += pRsD[i * DT + t];
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -485,13 +546,13 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
                 dgm -= pCgC[i * 4 + t];
             }
             // gam_n enters through e^{gam_n} h and e^{gam_n - gam_j}: its gradient
-            // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row (-s_j to row j
-            // is already in the row sums)
-            float hds = 0.f, stot = 0.f;
-            for (int w = 0; w < NWD; ++w) {
-                hds += misc[16 + w];
-                stot += misc[16 + NWD + w];
-            }
+            // e^{gam_n} <h, dh'> + sum_j s_j goes to the last row, -s_j to row j
+            // (with a decay that vanishes inside the chunk the two cancel
+            // exactly, so no gradient leaks to the tokens before it)
+            float hds = 0.f;
+            for (int w = 0; w < NWD; ++w) hds += misc[16 + w];
+            const float stot = wave_sum(sj);
+            dgm -= sj;
             if (i == C - 1) dgm += misc[0] * hds + stot;
             // dlam_r = sum_{i >= r} dgam_i = total - (prefix through r) + dgam_r
             const float pre = wave_prefix(dgm);

@@ -24,6 +24,8 @@ namespace gdn {
 constexpr int C = 64;
 constexpr int NTHR = 512;
 constexpr int NWAVE = 8;
+// epsilon under the root of the per-token key normalisation
+constexpr float KEY_EPS = 1e-6f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -296,6 +298,33 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
 
     __device__ __forceinline__ uint4 item(int m) const {
         return ((ok >> m) & 1u) ? r[m].u : uint4{0u, 0u, 0u, 0u};
+    }
+
+    // Per-row L2 normalisation, k_hat = k / sqrt(|k|^2 + KEY_EPS): the NG
+    // consecutive lanes that hold a row sum its squares with xor shuffles
+    // (every lane takes part, items outside the tile count as zero), then
+    // every item is rescaled and rounded back to the operand type. The lane
+    // holding column group 0 of a row writes 1 / sqrt(|k|^2 + KEY_EPS) to
+    // rinv[row] when rinv is given.
+    __device__ __forceinline__ void normalize_rows(float *rinv, int tid) {
+        static_assert(NT % 64 == 0 && 64 % NG == 0, "a row's lanes lie in one wave");
+#pragma unroll
+        for (int m = 0; m < NIT; ++m) {
+            U x;
+            x.u = item(m);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) ss += to_f(x.s[e]) * to_f(x.s[e]);
+#pragma unroll
+            for (int off = NG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            const float inv = 1.f / sqrtf(ss + KEY_EPS);
+#pragma unroll
+            for (int e = 0; e < V; ++e) x.s[e] = from_f<BF>(to_f(x.s[e]) * inv);
+            r[m].u = x.u;
+            int j, cg;
+            pos(tid + m * NT, j, cg);
+            if (rinv && cg == 0 && (FULL || j < NR)) rinv[j] = inv;
+        }
     }
 
     // Straight copy to dst [NR][ldd].

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(NTHR, 8) void fwd_prep_kernel(PrepArgs a) {
         if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
         bet[lane] = be;
     }
+    if (s.l2k) fk.normalize_rows(nullptr, tid);
     fk.stash(Ks, LDD, tid);
     __syncthreads();
 
@@ -308,11 +309,17 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
     // between consuming one prefetch and issuing the next, so waiting for
     // the inputs never waits for a store to complete
     f32x4 accO[Tiles<4, VT>::PW];
+    const float Dh = s.D ? s.D[h] : 0.f; // skip term o_t += D_h v_t
     auto store_o = [&](int c) {
         const int n = min(C, T - c * C);
-        S *orow = o + (((size_t)b * T + c * C) * H + h) * dv + v0;
+        const size_t off = (((size_t)b * T + c * C) * H + h) * dv + v0;
+        S *orow = o + off;
+        const S *vrow = (const S *)s.v + off;
         for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < n && col < nvc) orow[(size_t)row * H * dv + col] = from_f<BF>(accO[i][e]);
+            if (row < n && col < nvc) {
+                const size_t x = (size_t)row * H * dv + col;
+                orow[x] = from_f<BF>(s.D ? accO[i][e] + Dh * to_f(vrow[x]) : accO[i][e]);
+            }
         });
     };
     fetch(c_lo);
@@ -327,6 +334,7 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
             egn[lane] = dc.egn;
             if (lane == 0) misc[0] = dc.eglast;
         }
+        if (s.l2k) fk.normalize_rows(nullptr, tid);
         fk.stash(Ks, LDD, tid);
         if (o) fq.stash(Qs, LDD, tid);
         if (!s.additive) fn.stash(NKs, LDD, tid);
@@ -569,6 +577,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         const int st = c & 1;
         wait_vmem();
         fq.stash(stage(st, 0), LDD, htid);
+        if (s.l2k) fk.normalize_rows(nullptr, htid);
         fk.stash(stage(st, 1), LDD, htid);
         if (!add) fn.stash(stage(st, 2), LDD, htid);
         fu.stash(stage(st, 3), LDD, htid);
@@ -583,19 +592,40 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
 
     // rows 16*bi.. and value blocks vb..vb+VH-1 of O of chunk cc, from LDS
     // (16 rows of LDO elements) to global
+    // skip term o_t += D_h v_t, added to the rounded O rows as they leave
+    const float Dh = s.D ? s.D[h] : 0.f;
     auto store_o = [&](int cc, int bi, int vb, const u16 *Os) {
         const int n = min(C, T - cc * C);
         const int nr = min(16, n - 16 * bi), vlo = 16 * vb, nvc = min(16 * VH, dv - vlo);
-        u16 *orow = o + (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
+        const size_t off = (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
+        u16 *orow = o + off;
+        const u16 *vrow = (const u16 *)s.v + off;
         if (VEC) {
             for (int it = lane; it < 16 * 2 * VH; it += 64) {
                 const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
-                if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
+                if (i < nr && v < nvc) {
+                    uint4 x = *(const uint4 *)(Os + i * LDO + v);
+                    if (s.D) {
+                        const uint4 y = *(const uint4 *)(vrow + (size_t)i * H * dv + v);
+                        const uint32_t *xo = (const uint32_t *)&x, *yv = (const uint32_t *)&y;
+                        uint4 z;
+                        uint32_t *zo = (uint32_t *)&z;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            zo[e] = f2bf2(bf2f((u16)(xo[e] & 0xFFFF)) + Dh * bf2f((u16)(yv[e] & 0xFFFF)),
+                                          bf2f((u16)(xo[e] >> 16)) + Dh * bf2f((u16)(yv[e] >> 16)));
+                        x = z;
+                    }
+                    *(uint4 *)(orow + (size_t)i * H * dv + v) = x;
+                }
             }
         } else {
             for (int it = lane; it < 16 * 16 * VH; it += 64) {
                 const int i = it / (16 * VH), v = it % (16 * VH);
-                if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
+                if (i < nr && v < nvc) {
+                    const size_t x = (size_t)i * H * dv + v;
+                    orow[x] = s.D ? f2bf(bf2f(Os[i * LDO + v]) + Dh * bf2f(vrow[x])) : Os[i * LDO + v];
+                }
             }
         }
     };

@@ -15,7 +15,8 @@ namespace gdn {
 // supplies the workspace (ws_bytes long, library-owned, so it aliases no
 // argument).
 gdn_status_t fwd_entry(const gdn_shape_t *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const float *A_log, const float *h0, void *o, float *hT, void *ctx,
+                       const float *beta, const float *A_log, const float *D, const float *h0, void *o, float *hT,
+                       void *ctx,
                        void *ws, size_t ws_bytes, void *stream, bool one_stream,
                        gdn_status_t (*ws_lookup)(void *&ws));
 // Sets the text gdn_last_error_detail() returns and passes st through.
@@ -27,6 +28,8 @@ struct SeqArgs {
     int B, T, H, dk, dv, NC;
     int additive;
     int logits; // g and beta are logits (sigmoid applied where they are used)
+    int l2k;    // keys are L2-normalised per token where they are loaded
+    const float *D; // [H] skip weights (o_t += D_h v_t), or null
 };
 
 // Per-chunk products that do not depend on the state:
@@ -111,8 +114,13 @@ struct BwdLocalArgs {
     void *dq, *dk, *dv;
     float *dg, *dbeta;
     float *dA_part;  // [B*H*NC]
+    float *dD_part;  // [B*H*NC][DD_SLOTS] partial sums of do * v (skip term), or null
     float *wide;     // scratch of the wide-head kernel (null for the others)
 };
+
+// Slots per chunk of the skip term's partial sums (one per wave of the local
+// gradient kernels), reduced in a fixed order.
+constexpr int DD_SLOTS = 8;
 
 struct StepArgs {
     const void *q, *k, *v;
@@ -122,6 +130,8 @@ struct StepArgs {
     int N, H, dk, dv, additive;
     int S; // tokens per sequence; q, k, v, o, g, beta are [N, S, H, *]
     int logits;
+    int l2k;        // keys L2-normalised per token
+    const float *D; // [H] skip weights, or null
 };
 
 // 16-byte vector loads are possible when every row of q/k/v (and of the

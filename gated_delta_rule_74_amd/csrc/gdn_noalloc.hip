@@ -53,8 +53,8 @@ gdn_status_t scratch_of_current(void *&out) {
 } // namespace
 
 extern "C" gdn_status_t gdn_fwd_noalloc(const gdn_shape_t *s, const void *q, const void *k, const void *v,
-                                        const float *g, const float *beta, const float *A_log, const float *h0,
-                                        void *o, float *hT, void *ctx, void *stream) {
+                                        const float *g, const float *beta, const float *A_log, const float *D,
+                                        const float *h0, void *o, float *hT, void *ctx, void *stream) {
     const size_t need = gdn_fwd_workspace_size(s);
     if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) {
         char msg[200];
@@ -65,6 +65,6 @@ extern "C" gdn_status_t gdn_fwd_noalloc(const gdn_shape_t *s, const void *q, con
         return gdn::fail_detail(GDN_EWORKSPACE, msg);
     }
     // an invalid shape (need == 0) is reported by the forward's own checks
-    return gdn::fwd_entry(s, q, k, v, g, beta, A_log, h0, o, hT, ctx, nullptr, (size_t)GDN_NOALLOC_SCRATCH_BYTES,
-                          stream, true, scratch_of_current);
+    return gdn::fwd_entry(s, q, k, v, g, beta, A_log, D, h0, o, hT, ctx, nullptr,
+                          (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream, true, scratch_of_current);
 }

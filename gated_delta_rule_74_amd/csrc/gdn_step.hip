@@ -85,9 +85,18 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
         const float *src = t == 0 ? hin : hout; // state before this token (not KEEP)
 
         const float alpha = expf(gate_of(a.g[tok], a.logits) * A), beta = gate_of(a.beta[tok], a.logits);
-        const float qa = lane < dk ? to_f(q[lane]) : 0.f, ka = lane < dk ? to_f(k[lane]) : 0.f;
+        const float qa = lane < dk ? to_f(q[lane]) : 0.f;
         const float qb = lane + 64 < dk ? to_f(q[lane + 64]) : 0.f;
-        const float kb = lane + 64 < dk ? to_f(k[lane + 64]) : 0.f;
+        float ka = lane < dk ? to_f(k[lane]) : 0.f, kb = lane + 64 < dk ? to_f(k[lane + 64]) : 0.f;
+        if (a.l2k) {
+            // per-token key normalisation, k / sqrt(|k|^2 + KEY_EPS), in fp32
+            float ss = ka * ka + kb * kb;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            const float inv = 1.f / sqrtf(ss + KEY_EPS);
+            ka *= inv;
+            kb *= inv;
+        }
         // s = k . q, butterfly sum (same value and order on every lane)
         float sk = qa * ka + qb * kb;
 #pragma unroll
@@ -171,6 +180,7 @@ __global__ __launch_bounds__(NTHR) void step_kernel(StepArgs a) {
                 oj = alpha * (r[c] - beta * sk * u[c]) + beta * sk * vj;
                 w[c] = beta * (vj - alpha * u[c]);
             }
+            if (a.D) oj += a.D[h] * vj; // skip term
             if (ok[c]) o[col[c]] = from_f<BF>(oj);
         }
         if (KEEP) {
@@ -249,7 +259,14 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepA
             gg[t] = a.g[tok];
             bb[t] = a.beta[tok];
             qs[t][lane] = lane < dk ? to_f(((const S *)a.q)[tok * dk + lane]) : 0.f;
-            ks[t][lane] = lane < dk ? to_f(((const S *)a.k)[tok * dk + lane]) : 0.f;
+            float kl = lane < dk ? to_f(((const S *)a.k)[tok * dk + lane]) : 0.f;
+            if (a.l2k) {
+                float ss = kl * kl;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                kl *= 1.f / sqrtf(ss + KEY_EPS);
+            }
+            ks[t][lane] = kl;
             vv[t] = ok ? to_f(((const S *)a.v)[tok * dv + lane]) : 0.f;
         }
     }
@@ -304,6 +321,7 @@ template <bool BF> __global__ __launch_bounds__(NTHR) void step_pre_kernel(StepA
                 oj = alpha * (r - beta * sk * u) + beta * sk * vj;
                 w = beta * (vj - alpha * u);
             }
+            if (a.D) oj += a.D[h] * vj; // skip term
             if (ok) ((S *)a.o)[tok * dv + lane] = from_f<BF>(oj);
 #pragma unroll
             for (int i = 0; i < 64; i += 4) {

@@ -11,6 +11,9 @@ Recipe (numpy ``Generator(PCG64(seed))``; normals drawn in float64):
   weak-decay variant: A_log ~ U(ln 1e-3, ln 1e-1) and seed + 100
   g-zero variant: g == 0 exactly (no decay)
   h0 = 0.1 * N(0, 1) when requested (float32)
+  layer-edge variants, drawn after everything above so the other draws stay
+  the same: raw keys (key_spread) = the unit rows times a per-row length
+  drawn U(0.25, 4); skip weights (with_D) D ~ N(0, 1) per head (float32)
   q, k, v, do are then rounded to the workload dtype (bf16: RNE).
 
 The decode workload draws its per-step tokens in blocks of steps, each block
@@ -111,10 +114,12 @@ CONFIGS = {
 }
 
 
-def gen_seq(B, T, H, dk, dv, dtype="bf16", seed=0, h0="none", with_do=False, decay="normal"):
+def gen_seq(B, T, H, dk, dv, dtype="bf16", seed=0, h0="none", with_do=False, decay="normal",
+            key_spread=False, with_D=False):
     """Inputs for one sequence workload. decay: 'normal' | 'weak' | 'zero'.
-    Returns a dict: q, k, v, do (Tensor or None); g, beta, A_log, h0 (float32
-    numpy or None)."""
+    Returns a dict: q, k, v, do (Tensor or None); g, beta, A_log, h0, D
+    (float32 numpy or None). key_spread: keys of per-row lengths in
+    [0.25, 4] instead of unit rows (inputs for the fused key normalisation)."""
     if decay == "weak":
         seed = seed + 100
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -136,8 +141,11 @@ def gen_seq(B, T, H, dk, dv, dtype="bf16", seed=0, h0="none", with_do=False, dec
     else:
         h0a = None
     do = _cast(rng.standard_normal((B, T, H, dv)), dtype) if with_do else None
+    if key_spread:
+        k = k * rng.uniform(0.25, 4.0, (B, T, H, 1))
+    D = rng.standard_normal(H).astype(np.float32) if with_D else None
     return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), g=g, beta=beta,
-                A_log=A_log, h0=h0a, do=do)
+                A_log=A_log, h0=h0a, do=do, D=D)
 
 
 def gen_config(name, decay="normal", **override):

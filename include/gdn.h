@@ -29,8 +29,17 @@
  *   h0, hT, dhT, dh0    [B, H, dk, dv]  fp32 (row i = key index)
  *   decode (gdn_step):  q,k [N,H,dk], v,o [N,H,dv], g,beta [N,H],
  *                       states [N,H,dk,dv]; gdn_step_tokens: [N,S,H,*]
+ *   D, dD               [H]             fp32 (skip term, optional)
  * bf16 outputs are rounded to nearest even. The library applies no scaling
- * to q and no normalisation to k.
+ * to q; k is used as given unless GDN_FLAG_L2NORM_K asks for its per-token
+ * normalisation.
+ *
+ * Layer edges. Two steps that sit on either side of the recurrence in the
+ * GDN layer are fused into the kernels when asked for: the per-token L2
+ * normalisation of the keys (GDN_FLAG_L2NORM_K) and the per-head skip term
+ * o_t += D[h] v_t (a non-NULL D argument; "HyMo-434M documentation portal",
+ * Architecture: the recurrence carries A_log, dt_bias and D). Both default
+ * to off, which gives the recurrence above unchanged.
  *
  * Ownership. The caller allocates every buffer, including the workspaces
  * sized by the *_workspace_size queries; the library never allocates, frees
@@ -50,8 +59,8 @@
  * pointers 16-byte aligned, B*H < 2^31, tensors below 2^31 elements.
  *
  * Empty sequences (T = 0) run no step: gdn_fwd sets hT = h0 (zeros when h0
- * is NULL); gdn_bwd sets dh0 = dhT (zeros when dhT is NULL), dA_log = 0 and,
- * when asked, hT = h0. Pointers to arrays with a factor T in their extent may
+ * is NULL); gdn_bwd sets dh0 = dhT (zeros when dhT is NULL), dA_log = 0,
+ * dD = 0 when given and, when asked, hT = h0. Pointers to arrays with a factor T in their extent may
  * then be NULL, and no workspace or context is used.
  */
 #ifndef GDN_H
@@ -85,12 +94,21 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
  * values). Without the flag g and beta are the gate values themselves. */
 #define GDN_FLAG_GATE_LOGITS 2u
 
+/* Keys are L2-normalised per token where the kernels load them: the
+ * recurrence runs on k_hat = k / sqrt(sum_j k_j^2 + 1e-6), the unit-length
+ * erase/write key of "GDN & MLA Mechanism Deep-Dive", Step 3 and Step 4 (the
+ * epsilon under the root keeps a zero key finite). gdn_bwd then returns dk
+ * with respect to the raw keys, dk = (dk_hat - k_hat (k_hat . dk_hat)) /
+ * sqrt(sum_j k_j^2 + 1e-6). The raw keys are what the caller passes and
+ * keeps; nothing normalised is written back. */
+#define GDN_FLAG_L2NORM_K 4u
+
 typedef struct {
     int32_t B, T, H; /* batch, tokens, heads */
     int32_t dk, dv;  /* key and value head dimensions */
     int32_t dtype;   /* gdn_dtype_t of q, k, v, o, do, dq, dk, dv */
     int32_t chunk;   /* 0 or 64 */
-    uint32_t flags;  /* GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS, or 0 */
+    uint32_t flags;  /* GDN_FLAG_ADDITIVE | GDN_FLAG_GATE_LOGITS | GDN_FLAG_L2NORM_K, or 0 */
 } gdn_shape_t;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this shape. Return 0
@@ -108,6 +126,7 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s);
 /* Forward pass over a whole sequence ("GDN & MLA Mechanism Deep-Dive",
  * Step 4 and Step 5).
  *   q, k, v, g, beta, A_log  inputs (layouts above)
+ *   D             [H] skip weights (o_t += D[h] v_t) or NULL (no skip term)
  *   h0            initial state or NULL (zero state)
  *   o             output [B,T,H,dv], or NULL: a state-only pass (e.g. the
  *                 prefill of a decode state), which writes hT and/or ctx
@@ -118,8 +137,9 @@ size_t gdn_fwd_context_size(const gdn_shape_t *s);
  *   ws, ws_bytes  workspace of gdn_fwd_workspace_size() bytes, 256-byte
  *                 aligned; its contents are scratch */
 gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
-                     const float *g, const float *beta, const float *A_log, const float *h0,
-                     void *o, float *hT, void *ctx, void *ws, size_t ws_bytes, void *stream);
+                     const float *g, const float *beta, const float *A_log, const float *D,
+                     const float *h0, void *o, float *hT, void *ctx, void *ws, size_t ws_bytes,
+                     void *stream);
 
 /* Bytes of the static device scratch gdn_fwd_noalloc uses as its workspace
  * (64 MiB per GPU, held until the process ends). */
@@ -137,18 +157,21 @@ gdn_status_t gdn_fwd(const gdn_shape_t *s, const void *q, const void *k, const v
  * with GDN_EWORKSPACE before anything is enqueued (at d = 56 in bf16 the
  * scratch holds about 290,000 token-heads, e.g. B*T = 18,000 at H = 16). */
 gdn_status_t gdn_fwd_noalloc(const gdn_shape_t *s, const void *q, const void *k, const void *v,
-                             const float *g, const float *beta, const float *A_log, const float *h0,
-                             void *o, float *hT, void *ctx, void *stream);
+                             const float *g, const float *beta, const float *A_log, const float *D,
+                             const float *h0, void *o, float *hT, void *ctx, void *stream);
 
 /* Backward pass: gradients of sum(do * o) + sum(dhT * hT) with respect to q,
- * k, v, g, beta, A_log and h0, by the reverse-chunk derivative of the chunked
- * forward. Inputs are those of the gdn_fwd call; do is the upstream gradient of
- * o, dhT that of the final state (NULL = zero).
+ * k, v, g, beta, A_log, D and h0, by the reverse-chunk derivative of the
+ * chunked forward. Inputs are those of the gdn_fwd call (same flags, same D);
+ * do is the upstream gradient of o, dhT that of the final state (NULL = zero).
  *   ctx           NULL (the forward is recomputed in the workspace) or the
  *                 context gdn_fwd saved for the same inputs
  *   dq, dk, dv    [B,T,H,*] in the call's dtype
  *   dg, dbeta     [B,T,H] fp32
  *   dA_log        [H] fp32, overwritten (sum over the batch)
+ *   dD            [H] fp32 or NULL: overwritten with the sum over batch,
+ *                 tokens and value columns of do * v, the gradient of the
+ *                 skip weights (also when D is NULL: the gradient at D = 0)
  *   dh0           [B,H,dk,dv] fp32 or NULL
  *   hT            NULL, or receives the recomputed final state; only allowed
  *                 when ctx is NULL
@@ -159,21 +182,22 @@ gdn_status_t gdn_fwd_noalloc(const gdn_shape_t *s, const void *q, const void *k,
  * a kernel that keeps its intermediates in the workspace; the workspace size
  * query includes that scratch. */
 gdn_status_t gdn_bwd(const gdn_shape_t *s, const void *q, const void *k, const void *v,
-                     const float *g, const float *beta, const float *A_log, const float *h0,
-                     const void *ctx, const void *dout, const float *dhT, void *dq, void *dk,
-                     void *dv, float *dg, float *dbeta, float *dA_log, float *dh0, float *hT,
-                     void *ws, size_t ws_bytes, void *stream);
+                     const float *g, const float *beta, const float *A_log, const float *D,
+                     const float *h0, const void *ctx, const void *dout, const float *dhT,
+                     void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dA_log,
+                     float *dD, float *dh0, float *hT, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode token for each of N independent sequences: one step of the
  * recurrence from a carried state (the O(1)-state read/write of "GDN & MLA
  * Mechanism Deep-Dive", Intuition). h_in may be NULL (zero state) and may
  * equal h_out (in-place update); no other aliasing is allowed. `dtype` is the
- * gdn_dtype_t of q, k, v and o; `flags` is GDN_FLAG_ADDITIVE and/or
- * GDN_FLAG_GATE_LOGITS, or 0. */
+ * gdn_dtype_t of q, k, v and o; `flags` is any of GDN_FLAG_ADDITIVE,
+ * GDN_FLAG_GATE_LOGITS and GDN_FLAG_L2NORM_K, or 0; D is the [H] skip
+ * weights or NULL, as in gdn_fwd. */
 gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype, uint32_t flags,
                       const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, const float *A_log, const float *h_in, float *h_out,
-                      void *o, void *stream);
+                      const float *beta, const float *A_log, const float *D, const float *h_in,
+                      float *h_out, void *o, void *stream);
 
 /* S consecutive decode tokens for each of N independent sequences from a
  * carried state: the recurrence applied token after token (the serial
@@ -193,7 +217,7 @@ gdn_status_t gdn_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtyp
  * and the [N,H,*] layouts. */
 gdn_status_t gdn_step_tokens(int32_t N, int32_t S, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
                              uint32_t flags, const void *q, const void *k, const void *v,
-                             const float *g, const float *beta, const float *A_log,
+                             const float *g, const float *beta, const float *A_log, const float *D,
                              const float *h_in, float *h_out, void *o, void *stream);
 
 /* Timing aid for benchmarks (no effect on results). While `events` is
@@ -207,8 +231,8 @@ int32_t gdn_time_launches(void *const *events, int32_t n);
 
 /* Which kernel the i-th bracketed launch of the current (or, once switched
  * off, the last) bracketing period was: 0 forward prep, 1 forward serial
- * pass, 2 backward serial pass, 3 backward local gradients, 4 dA_log
- * reduction, 5 decode step, 6 forward scan over chunk ranges, 7 backward
+ * pass, 2 backward serial pass, 3 backward local gradients, 4 dA_log (or
+ * dD) reduction, 5 decode step, 6 forward scan over chunk ranges, 7 backward
  * scan; -1 when i is out of range. A forward call may launch its two kernels
  * several times each, over consecutive chunk ranges (prep of the next range
  * runs on a second stream while the serial pass works on the current one),
