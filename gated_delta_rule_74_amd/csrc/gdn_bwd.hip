@@ -590,7 +590,9 @@ template <bool BF, int D> struct LocalSmem {
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-template <bool BF, int D, bool VEC>
+// EDGE: the layer edges (key normalisation, skip term, dD) are compiled in;
+// the plain instantiation carries none of their code or registers
+template <bool BF, int D, bool VEC, bool EDGE>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -700,7 +702,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
     for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
 
     // ---- P1: gates, decay, K K^T and Q K^T; W = U - Kw h
-    if (s.l2k) fk.normalize_rows(rinvK, tid);
+    if constexpr (EDGE) {
+        if (s.l2k) fk.normalize_rows(rinvK, tid);
+    }
     fk.stash(Ks, LDD, tid);
     fq.stash(RQ, LDD, tid);
     fh.stash(R1, LDD, tid);
@@ -900,90 +904,132 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         // (row dots over the lanes that hold a row); with the skip term dv
         // gains D_h do, and the chunk's share of dD_h (sum of do * v) goes to
         // one slot per wave.
-        {
+        if constexpr (!EDGE) {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
-            const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
-            const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
-            const float Dh = s.D ? s.D[h] : 0.f;
-            const bool edge_v = s.D || a.dD_part; // do (and v) rows are needed
-            float dsum = 0.f;
             constexpr int V = O::VEC, NG = D / V;
-            union Pk {
-                uint4 u;
-                S x[V];
-            };
             if (VEC) {
                 for (int it = tid; it < C * NG; it += NTHR) {
                     const int j = it / NG, c0 = (it % NG) * V;
-                    Pk kd;
-                    kd.u = *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
-                    if (s.l2k) {
-                        Pk kh;
-                        kh.u = *reinterpret_cast<const uint4 *>(Ks + j * LDD + c0);
-                        float dot = 0.f;
-#pragma unroll
-                        for (int e = 0; e < V; ++e) dot += to_f(kh.x[e]) * to_f(kd.x[e]);
-#pragma unroll
-                        for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-                        const float ri = rinvK[j];
-#pragma unroll
-                        for (int e = 0; e < V; ++e) kd.x[e] = from_f<BF>((to_f(kd.x[e]) - to_f(kh.x[e]) * dot) * ri);
-                    }
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
                             *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
-                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
                     }
                     if (c0 < dv) {
-                        Pk pk, dov, vv;
+                        union {
+                            uint4 u;
+                            S x[V];
+                        } pk;
                         const float nb = -bet[j];
-                        if (edge_v) {
-                            dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
-                            vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
-                        }
 #pragma unroll
-                        for (int e = 0; e < V; ++e) {
-                            float x = nb * to_f(R4[(c0 + e) * LDC + j]);
-                            if (s.D) x += Dh * to_f(dov.x[e]);
-                            if (a.dD_part) dsum += to_f(dov.x[e]) * to_f(vv.x[e]);
-                            pk.x[e] = from_f<BF>(x);
-                        }
+                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(R4[(c0 + e) * LDC + j]));
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
             } else {
                 for (int it = tid; it < C * D; it += NTHR) {
                     const int j = it / D, col = it % D;
-                    float kdv = to_f(R5[j * LDD + col]);
-                    if (s.l2k) {
-                        const float khv = to_f(Ks[j * LDD + col]);
-                        float dot = khv * kdv;
-#pragma unroll
-                        for (int off = D / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-                        kdv = (kdv - khv * dot) * rinvK[j];
-                    }
                     if (j >= n) continue;
                     if (col < dk) {
                         dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
-                        dk_out[(size_t)j * H * dk + col] = from_f<BF>(kdv);
+                        dk_out[(size_t)j * H * dk + col] = R5[j * LDD + col];
                     }
-                    if (col < dv) {
-                        float x = -bet[j] * to_f(R4[col * LDC + j]);
-                        if (edge_v) {
-                            const float dd = to_f(do_in[(size_t)j * H * dv + col]);
-                            if (s.D) x += Dh * dd;
-                            if (a.dD_part) dsum += dd * to_f(v_in[(size_t)j * H * dv + col]);
-                        }
-                        dv_out[(size_t)j * H * dv + col] = from_f<BF>(x);
-                    }
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(R4[col * LDC + j]));
                 }
             }
-            if (a.dD_part) {
-                dsum = wave_sum(dsum);
-                if (lane == 0) a.dD_part[cb * DD_SLOTS + wave] = dsum;
+        } else {
+            {
+                S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+                S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+                S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+                const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
+                const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
+                const bool l2k = EDGE && s.l2k;
+                const float *Dp = EDGE ? s.D : nullptr;
+                float *dDp = EDGE ? a.dD_part : nullptr;
+                const float Dh = Dp ? Dp[h] : 0.f;
+                const bool edge_v = Dp || dDp; // do (and v) rows are needed
+                float dsum = 0.f;
+                constexpr int V = O::VEC, NG = D / V;
+                union Pk {
+                    uint4 u;
+                    S x[V];
+                };
+                if (VEC) {
+                    for (int it = tid; it < C * NG; it += NTHR) {
+                        const int j = it / NG, c0 = (it % NG) * V;
+                        Pk kd;
+                        kd.u = *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                        if (l2k) {
+                            Pk kh;
+                            kh.u = *reinterpret_cast<const uint4 *>(Ks + j * LDD + c0);
+                            float dot = 0.f;
+#pragma unroll
+                            for (int e = 0; e < V; ++e) dot += to_f(kh.x[e]) * to_f(kd.x[e]);
+#pragma unroll
+                            for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                            const float ri = rinvK[j];
+#pragma unroll
+                            for (int e = 0; e < V; ++e) kd.x[e] = from_f<BF>((to_f(kd.x[e]) - to_f(kh.x[e]) * dot) * ri);
+                        }
+                        if (j >= n) continue;
+                        if (c0 < dk) {
+                            *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
+                                *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
+                            *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
+                        }
+                        if (c0 < dv) {
+                            Pk pk, dov, vv;
+                            const float nb = -bet[j];
+                            if (edge_v) {
+                                dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
+                                vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
+                            }
+#pragma unroll
+                            for (int e = 0; e < V; ++e) {
+                                float x = nb * to_f(R4[(c0 + e) * LDC + j]);
+                                if (Dp) x += Dh * to_f(dov.x[e]);
+                                if (dDp) dsum += to_f(dov.x[e]) * to_f(vv.x[e]);
+                                pk.x[e] = from_f<BF>(x);
+                            }
+                            *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
+                        }
+                    }
+                } else {
+                    for (int it = tid; it < C * D; it += NTHR) {
+                        const int j = it / D, col = it % D;
+                        float kdv = to_f(R5[j * LDD + col]);
+                        if (l2k) {
+                            const float khv = to_f(Ks[j * LDD + col]);
+                            float dot = khv * kdv;
+#pragma unroll
+                            for (int off = D / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                            kdv = (kdv - khv * dot) * rinvK[j];
+                        }
+                        if (j >= n) continue;
+                        if (col < dk) {
+                            dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
+                            dk_out[(size_t)j * H * dk + col] = from_f<BF>(kdv);
+                        }
+                        if (col < dv) {
+                            float x = -bet[j] * to_f(R4[col * LDC + j]);
+                            if (edge_v) {
+                                const float dd = to_f(do_in[(size_t)j * H * dv + col]);
+                                if (Dp) x += Dh * dd;
+                                if (dDp) dsum += dd * to_f(v_in[(size_t)j * H * dv + col]);
+                            }
+                            dv_out[(size_t)j * H * dv + col] = from_f<BF>(x);
+                        }
+                    }
+                }
+                if (dDp) {
+                    dsum = wave_sum(dsum);
+                    if (lane == 0) dDp[cb * DD_SLOTS + wave] = dsum;
+                }
             }
         }
         if (wave == 0) {
@@ -1463,18 +1509,20 @@ template <auto KERNEL> static hipError_t resident_blocks(int &out) {
     return hipSuccess;
 }
 
-template <bool BF, int D, bool VEC> static hipError_t local_launch(const BwdLocalArgs &a, hipStream_t st) {
+template <bool BF, int D, bool VEC, bool EDGE> static hipError_t local_launch(const BwdLocalArgs &a, hipStream_t st) {
     const int nch = a.s.B * a.s.H * a.s.NC;
     int grid = 0;
-    const hipError_t e = resident_blocks<bwd_local_kernel<BF, D, VEC>>(grid);
+    const hipError_t e = resident_blocks<bwd_local_kernel<BF, D, VEC, EDGE>>(grid);
     if (e != hipSuccess) return e;
     grid = grid < nch ? grid : nch;
-    hipLaunchKernelGGL((bwd_local_kernel<BF, D, VEC>), dim3(grid), dim3(NTHR), 0, st, a);
+    hipLaunchKernelGGL((bwd_local_kernel<BF, D, VEC, EDGE>), dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 
 template <bool BF, int D> static hipError_t local_inst(const BwdLocalArgs &a, hipStream_t st) {
-    return vec_ok<BF>(a.s) ? local_launch<BF, D, true>(a, st) : local_launch<BF, D, false>(a, st);
+    const bool vec = vec_ok<BF>(a.s), edge = a.s.l2k || a.s.D || a.dD_part;
+    if (edge) return vec ? local_launch<BF, D, true, true>(a, st) : local_launch<BF, D, false, true>(a, st);
+    return vec ? local_launch<BF, D, true, false>(a, st) : local_launch<BF, D, false, false>(a, st);
 }
 
 template <bool BF> static hipError_t wide_inst(const BwdLocalArgs &a, hipStream_t st) {

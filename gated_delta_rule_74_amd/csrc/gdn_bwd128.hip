@@ -123,7 +123,9 @@ template <int MT, int NT> __device__ __forceinline__ void write_rows(float v, fl
 
 } // namespace
 
-template <bool VEC>
+// EDGE: the layer edges (key normalisation, skip term, dD) are compiled in;
+// the plain instantiation carries none of their code or registers
+template <bool VEC, bool EDGE>
 __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     using L = Wide128;
     using S = u16;
@@ -218,7 +220,9 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     float rb = 0.f, rg = 0.f, rbc = 0.f, xgr = 0.f, xgc = 0.f, rs = 0.f;
 
     // ---- P1: K K^T, Q K^T, decay; W = U - Kw h
-    if (s.l2k) fk.normalize_rows(rinvK, tid);
+    if constexpr (EDGE) {
+        if (s.l2k) fk.normalize_rows(rinvK, tid);
+    }
     fk.stash(X0, LDD, tid);
     fq.stash(X3, LDD, tid);
     fh.stash(X1, LDD, tid);
@@ -439,68 +443,29 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         // dk = (dk_hat - k_hat (k_hat . dk_hat)) / |k|; with the skip term dv
         // gains D_h do and the chunk's share of dD_h (sum of do * v) goes to
         // one slot per wave.
-        if (s.l2k && !VEC) {
-            // row dots first (a row spans more lanes than a wave here)
-            constexpr int PARTS = NTD / C, CPP = D / PARTS;
-            const int j = tid / PARTS, p0 = (tid % PARTS) * CPP;
-            float dot = 0.f;
-            for (int c = p0; c < p0 + CPP; ++c) dot += bf2f(X0[j * LDD + c]) * bf2f(X5[j * LDD + c]);
-#pragma unroll
-            for (int off = PARTS / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-            if (tid % PARTS == 0) rdot[j] = dot;
-            __syncthreads();
-        }
-        {
+        if constexpr (!EDGE) {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
-            const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
-            const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
-            const float Dh = s.D ? s.D[h] : 0.f;
-            const bool edge_v = s.D || a.dD_part; // do (and v) rows are needed
-            float dsum = 0.f;
             constexpr int V = 8, NG = D / V;
-            union Pk {
-                uint4 u;
-                S x[V];
-            };
             if (VEC) {
                 for (int it = tid; it < C * NG; it += NTD) {
                     const int j = it / NG, c0 = (it % NG) * V;
-                    Pk kd;
-                    kd.u = *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
-                    if (s.l2k) {
-                        Pk kh;
-                        kh.u = *reinterpret_cast<const uint4 *>(X0 + j * LDD + c0);
-                        float dot = 0.f;
-#pragma unroll
-                        for (int e = 0; e < V; ++e) dot += bf2f(kh.x[e]) * bf2f(kd.x[e]);
-#pragma unroll
-                        for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-                        const float ri = rinvK[j];
-#pragma unroll
-                        for (int e = 0; e < V; ++e) kd.x[e] = f2bf((bf2f(kd.x[e]) - bf2f(kh.x[e]) * dot) * ri);
-                    }
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
                             *reinterpret_cast<const uint4 *>(X1 + j * LDD + c0);
-                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
+                        *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
+                            *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
                     }
                     if (c0 < dv) {
-                        Pk pk, dov, vv;
+                        union {
+                            uint4 u;
+                            S x[V];
+                        } pk;
                         const float nb = -bet[j];
-                        if (edge_v) {
-                            dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
-                            vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
-                        }
 #pragma unroll
-                        for (int e = 0; e < V; ++e) {
-                            float x = nb * bf2f(X3[(c0 + e) * LDC + j]);
-                            if (s.D) x += Dh * bf2f(dov.x[e]);
-                            if (a.dD_part) dsum += bf2f(dov.x[e]) * bf2f(vv.x[e]);
-                            pk.x[e] = f2bf(x);
-                        }
+                        for (int e = 0; e < V; ++e) pk.x[e] = f2bf(nb * bf2f(X3[(c0 + e) * LDC + j]));
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
@@ -510,24 +475,105 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
                     if (j >= n) continue;
                     if (col < dk) {
                         dq_out[(size_t)j * H * dk + col] = X1[j * LDD + col];
-                        float kdv = bf2f(X5[j * LDD + col]);
-                        if (s.l2k) kdv = (kdv - bf2f(X0[j * LDD + col]) * rdot[j]) * rinvK[j];
-                        dk_out[(size_t)j * H * dk + col] = f2bf(kdv);
+                        dk_out[(size_t)j * H * dk + col] = X5[j * LDD + col];
                     }
-                    if (col < dv) {
-                        float x = -bet[j] * bf2f(X3[col * LDC + j]);
-                        if (edge_v) {
-                            const float dd = bf2f(do_in[(size_t)j * H * dv + col]);
-                            if (s.D) x += Dh * dd;
-                            if (a.dD_part) dsum += dd * bf2f(v_in[(size_t)j * H * dv + col]);
-                        }
-                        dv_out[(size_t)j * H * dv + col] = f2bf(x);
-                    }
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = f2bf(-bet[j] * bf2f(X3[col * LDC + j]));
                 }
             }
-            if (a.dD_part) {
-                dsum = wave_sum(dsum);
-                if (lane == 0) a.dD_part[cb * DD_SLOTS + wave] = dsum;
+        } else {
+            const bool l2k = EDGE && s.l2k;
+            const float *Dp = EDGE ? s.D : nullptr;
+            float *dDp = EDGE ? a.dD_part : nullptr;
+            if (l2k && !VEC) {
+                // row dots first (a row spans more lanes than a wave here)
+                constexpr int PARTS = NTD / C, CPP = D / PARTS;
+                const int j = tid / PARTS, p0 = (tid % PARTS) * CPP;
+                float dot = 0.f;
+                for (int c = p0; c < p0 + CPP; ++c) dot += bf2f(X0[j * LDD + c]) * bf2f(X5[j * LDD + c]);
+#pragma unroll
+                for (int off = PARTS / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                if (tid % PARTS == 0) rdot[j] = dot;
+                __syncthreads();
+            }
+            {
+                S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
+                S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
+                S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
+                const S *do_in = (const S *)a.dout + (row0 * H + h) * dv;
+                const S *v_in = (const S *)s.v + (row0 * H + h) * dv;
+                const float Dh = Dp ? Dp[h] : 0.f;
+                const bool edge_v = Dp || dDp; // do (and v) rows are needed
+                float dsum = 0.f;
+                constexpr int V = 8, NG = D / V;
+                union Pk {
+                    uint4 u;
+                    S x[V];
+                };
+                if (VEC) {
+                    for (int it = tid; it < C * NG; it += NTD) {
+                        const int j = it / NG, c0 = (it % NG) * V;
+                        Pk kd;
+                        kd.u = *reinterpret_cast<const uint4 *>(X5 + j * LDD + c0);
+                        if (l2k) {
+                            Pk kh;
+                            kh.u = *reinterpret_cast<const uint4 *>(X0 + j * LDD + c0);
+                            float dot = 0.f;
+#pragma unroll
+                            for (int e = 0; e < V; ++e) dot += bf2f(kh.x[e]) * bf2f(kd.x[e]);
+#pragma unroll
+                            for (int off = NG / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                            const float ri = rinvK[j];
+#pragma unroll
+                            for (int e = 0; e < V; ++e) kd.x[e] = f2bf((bf2f(kd.x[e]) - bf2f(kh.x[e]) * dot) * ri);
+                        }
+                        if (j >= n) continue;
+                        if (c0 < dk) {
+                            *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
+                                *reinterpret_cast<const uint4 *>(X1 + j * LDD + c0);
+                            *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
+                        }
+                        if (c0 < dv) {
+                            Pk pk, dov, vv;
+                            const float nb = -bet[j];
+                            if (edge_v) {
+                                dov.u = *reinterpret_cast<const uint4 *>(do_in + (size_t)j * H * dv + c0);
+                                vv.u = *reinterpret_cast<const uint4 *>(v_in + (size_t)j * H * dv + c0);
+                            }
+#pragma unroll
+                            for (int e = 0; e < V; ++e) {
+                                float x = nb * bf2f(X3[(c0 + e) * LDC + j]);
+                                if (Dp) x += Dh * bf2f(dov.x[e]);
+                                if (dDp) dsum += bf2f(dov.x[e]) * bf2f(vv.x[e]);
+                                pk.x[e] = f2bf(x);
+                            }
+                            *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
+                        }
+                    }
+                } else {
+                    for (int it = tid; it < C * D; it += NTD) {
+                        const int j = it / D, col = it % D;
+                        if (j >= n) continue;
+                        if (col < dk) {
+                            dq_out[(size_t)j * H * dk + col] = X1[j * LDD + col];
+                            float kdv = bf2f(X5[j * LDD + col]);
+                            if (l2k) kdv = (kdv - bf2f(X0[j * LDD + col]) * rdot[j]) * rinvK[j];
+                            dk_out[(size_t)j * H * dk + col] = f2bf(kdv);
+                        }
+                        if (col < dv) {
+                            float x = -bet[j] * bf2f(X3[col * LDC + j]);
+                            if (edge_v) {
+                                const float dd = bf2f(do_in[(size_t)j * H * dv + col]);
+                                if (Dp) x += Dh * dd;
+                                if (dDp) dsum += dd * bf2f(v_in[(size_t)j * H * dv + col]);
+                            }
+                            dv_out[(size_t)j * H * dv + col] = f2bf(x);
+                        }
+                    }
+                }
+                if (dDp) {
+                    dsum = wave_sum(dsum);
+                    if (lane == 0) dDp[cb * DD_SLOTS + wave] = dsum;
+                }
             }
         }
         if (wave == 0) {
@@ -578,7 +624,7 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
 
 // Blocks resident at once on the current device for this kernel (compute
 // units x blocks per unit), looked up once per device.
-template <bool VEC> static hipError_t resident128(int &out) {
+template <bool VEC, bool EDGE> static hipError_t resident128(int &out) {
     static int cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -587,7 +633,7 @@ template <bool VEC> static hipError_t resident128(int &out) {
     if (v <= 0) {
         int cus = 0, per = 0;
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_local128_kernel<VEC>, NTD, 0)) != hipSuccess)
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_local128_kernel<VEC, EDGE>, NTD, 0)) != hipSuccess)
             return e;
         v = cus * (per > 0 ? per : 1);
     }
@@ -595,18 +641,20 @@ template <bool VEC> static hipError_t resident128(int &out) {
     return hipSuccess;
 }
 
-template <bool VEC> static hipError_t launch128(const BwdLocalArgs &a, hipStream_t st) {
+template <bool VEC, bool EDGE> static hipError_t launch128(const BwdLocalArgs &a, hipStream_t st) {
     const int nch = a.s.B * a.s.H * a.s.NC;
     int grid = 0;
-    const hipError_t e = resident128<VEC>(grid);
+    const hipError_t e = resident128<VEC, EDGE>(grid);
     if (e != hipSuccess) return e;
     grid = grid < nch ? grid : nch;
-    hipLaunchKernelGGL((bwd_local128_kernel<VEC>), dim3(grid), dim3(NTD), 0, st, a);
+    hipLaunchKernelGGL((bwd_local128_kernel<VEC, EDGE>), dim3(grid), dim3(NTD), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_local128(const BwdLocalArgs &a, hipStream_t st) {
-    return vec_ok<true>(a.s) ? launch128<true>(a, st) : launch128<false>(a, st);
+    const bool vec = vec_ok<true>(a.s), edge = a.s.l2k || a.s.D || a.dD_part;
+    if (edge) return vec ? launch128<true, true>(a, st) : launch128<false, true>(a, st);
+    return vec ? launch128<true, false>(a, st) : launch128<false, false>(a, st);
 }
 
 } // namespace gdn

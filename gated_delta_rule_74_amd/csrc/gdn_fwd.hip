@@ -70,7 +70,8 @@ __device__ __forceinline__ void store_global(const f32x4 *acc, typename Op<BF>::
     });
 }
 
-template <bool BF, int D, bool VEC>
+// EDGE: keys normalised where they are loaded (compiled in only then)
+template <bool BF, int D, bool VEC, bool EDGE>
 __global__ __launch_bounds__(NTHR, 8) void fwd_prep_kernel(PrepArgs a) {
     using O = Op<BF>;
     using S = typename O::S;
@@ -117,7 +118,9 @@ __global__ __launch_bounds__(NTHR, 8) void fwd_prep_kernel(PrepArgs a) {
         if (a.gam) a.gam[((size_t)bh * s.NC + c) * C + lane] = (float)dc.gam2;
         bet[lane] = be;
     }
-    if (s.l2k) fk.normalize_rows(nullptr, tid);
+    if constexpr (EDGE) {
+        if (s.l2k) fk.normalize_rows(nullptr, tid);
+    }
     fk.stash(Ks, LDD, tid);
     __syncthreads();
 
@@ -522,7 +525,18 @@ template <int D> struct WsSmem {
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool VEC>
+// x + c y on eight packed bf16 values (fp32 arithmetic, one rounding)
+__device__ __forceinline__ uint4 add_scaled_bf16x8(uint4 x, uint4 y, float c) {
+    auto two = [&](uint32_t a, uint32_t b) {
+        return f2bf2(bf2f((u16)(a & 0xFFFF)) + c * bf2f((u16)(b & 0xFFFF)), bf2f((u16)(a >> 16)) + c * bf2f((u16)(b >> 16)));
+    };
+    return uint4{two(x.x, y.x), two(x.y, y.y), two(x.z, y.z), two(x.w, y.w)};
+}
+
+// EDGE: the layer edges (key normalisation, skip term) are compiled in; the
+// plain instantiation carries none of their code, so its schedule is that of
+// the recurrence alone
+template <int D, bool VEC, bool EDGE>
 __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
     constexpr int DT = D / 16, KS = D / 32;
     constexpr int NLT = 64 * 4; // loading helper threads (helpers 0..3)
@@ -577,7 +591,9 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         const int st = c & 1;
         wait_vmem();
         fq.stash(stage(st, 0), LDD, htid);
-        if (s.l2k) fk.normalize_rows(nullptr, htid);
+        if constexpr (EDGE) {
+            if (s.l2k) fk.normalize_rows(nullptr, htid);
+        }
         fk.stash(stage(st, 1), LDD, htid);
         if (!add) fn.stash(stage(st, 2), LDD, htid);
         fu.stash(stage(st, 3), LDD, htid);
@@ -592,39 +608,45 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
 
     // rows 16*bi.. and value blocks vb..vb+VH-1 of O of chunk cc, from LDS
     // (16 rows of LDO elements) to global
-    // skip term o_t += D_h v_t, added to the rounded O rows as they leave
-    const float Dh = s.D ? s.D[h] : 0.f;
+    // (with EDGE, the skip term o_t += D_h v_t is added to the rounded O rows
+    // as they leave)
     auto store_o = [&](int cc, int bi, int vb, const u16 *Os) {
         const int n = min(C, T - cc * C);
         const int nr = min(16, n - 16 * bi), vlo = 16 * vb, nvc = min(16 * VH, dv - vlo);
-        const size_t off = (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
-        u16 *orow = o + off;
-        const u16 *vrow = (const u16 *)s.v + off;
-        if (VEC) {
-            for (int it = lane; it < 16 * 2 * VH; it += 64) {
-                const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
-                if (i < nr && v < nvc) {
-                    uint4 x = *(const uint4 *)(Os + i * LDO + v);
-                    if (s.D) {
-                        const uint4 y = *(const uint4 *)(vrow + (size_t)i * H * dv + v);
-                        const uint32_t *xo = (const uint32_t *)&x, *yv = (const uint32_t *)&y;
-                        uint4 z;
-                        uint32_t *zo = (uint32_t *)&z;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            zo[e] = f2bf2(bf2f((u16)(xo[e] & 0xFFFF)) + Dh * bf2f((u16)(yv[e] & 0xFFFF)),
-                                          bf2f((u16)(xo[e] >> 16)) + Dh * bf2f((u16)(yv[e] >> 16)));
-                        x = z;
-                    }
-                    *(uint4 *)(orow + (size_t)i * H * dv + v) = x;
+        u16 *orow = o + (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
+        if constexpr (!EDGE) {
+            if (VEC) {
+                for (int it = lane; it < 16 * 2 * VH; it += 64) {
+                    const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
+                    if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
+                }
+            } else {
+                for (int it = lane; it < 16 * 16 * VH; it += 64) {
+                    const int i = it / (16 * VH), v = it % (16 * VH);
+                    if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
                 }
             }
         } else {
-            for (int it = lane; it < 16 * 16 * VH; it += 64) {
-                const int i = it / (16 * VH), v = it % (16 * VH);
-                if (i < nr && v < nvc) {
-                    const size_t x = (size_t)i * H * dv + v;
-                    orow[x] = s.D ? f2bf(bf2f(Os[i * LDO + v]) + Dh * bf2f(vrow[x])) : Os[i * LDO + v];
+            const u16 *vrow = (const u16 *)s.v + (orow - o);
+            const float Dh = s.D ? s.D[h] : 0.f;
+            if (VEC) {
+                for (int it = lane; it < 16 * 2 * VH; it += 64) {
+                    const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
+                    if (i < nr && v < nvc) {
+                        uint4 x = *(const uint4 *)(Os + i * LDO + v);
+                        if (s.D) x = add_scaled_bf16x8(x, *(const uint4 *)(vrow + (size_t)i * H * dv + v), Dh);
+                        *(uint4 *)(orow + (size_t)i * H * dv + v) = x;
+                    }
+                }
+            } else {
+                for (int it = lane; it < 16 * 16 * VH; it += 64) {
+                    const int i = it / (16 * VH), v = it % (16 * VH);
+                    if (i < nr && v < nvc) {
+                        const size_t x = (size_t)i * H * dv + v;
+                        u16 val = Os[i * LDO + v];
+                        if (s.D) val = f2bf(bf2f(val) + Dh * bf2f(vrow[x]));
+                        orow[x] = val;
+                    }
                 }
             }
         }
@@ -842,20 +864,28 @@ bool fwd_segmentable(bool bf16, int D) { return bf16 && (D == 32 || D == 64); }
 
 template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStream_t st) {
     const int grid = a.s.B * a.s.H * a.ncs;
-    if (vec_ok<BF>(a.s))
-        hipLaunchKernelGGL((fwd_prep_kernel<BF, D, true>), dim3(grid), dim3(NTHR), 0, st, a);
+    const bool vec = vec_ok<BF>(a.s);
+    if (a.s.l2k)
+        hipLaunchKernelGGL((vec ? fwd_prep_kernel<BF, D, true, true> : fwd_prep_kernel<BF, D, false, true>), dim3(grid),
+                           dim3(NTHR), 0, st, a);
     else
-        hipLaunchKernelGGL((fwd_prep_kernel<BF, D, false>), dim3(grid), dim3(NTHR), 0, st, a);
+        hipLaunchKernelGGL((vec ? fwd_prep_kernel<BF, D, true, false> : fwd_prep_kernel<BF, D, false, false>),
+                           dim3(grid), dim3(NTHR), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a, hipStream_t st) {
     const int grid = a.s.B * a.s.H;
     const int block = 64 * (D / 16 + WS_HELPERS);
-    if (vec_ok<true>(a.s))
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true>), dim3(grid), dim3(block), 0, st, a);
+    const bool vec = vec_ok<true>(a.s), edge = a.s.l2k || a.s.D;
+    if (vec && !edge)
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true, false>), dim3(grid), dim3(block), 0, st, a);
+    else if (vec)
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true, true>), dim3(grid), dim3(block), 0, st, a);
+    else if (!edge)
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false, false>), dim3(grid), dim3(block), 0, st, a);
     else
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false>), dim3(grid), dim3(block), 0, st, a);
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false, true>), dim3(grid), dim3(block), 0, st, a);
     return hipGetLastError();
 }
 
