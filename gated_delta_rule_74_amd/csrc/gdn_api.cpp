@@ -292,10 +292,13 @@ hipError_t aux_of_current(Aux *&out, hipStream_t strm) {
 
 // Number of chunk ranges the forward is split into (one when the serial
 // kernel cannot take a range, or the sequence is short).
+#ifndef GDN_FWD_RANGES
+#define GDN_FWD_RANGES 4
+#endif
 int fwd_segments(const gdn_shape_t *s, bool bf, int D) {
     if (!gdn::fwd_segmentable(bf, D)) return 1;
     const int n = nchunks(s) / 16;
-    return n < 1 ? 1 : (n > 4 ? 4 : n);
+    return n < 1 ? 1 : (n > GDN_FWD_RANGES ? GDN_FWD_RANGES : n);
 }
 
 // Forward pass into caller-provided buffers: U, NK (and Tm, γ) of every

@@ -408,8 +408,7 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
 // maps [M | R] of the segments (reverse: from the last segment down), fp32,
 // sums over the key index in order. Columns are independent, so each
 // workgroup carries its own 16. Each step stages M (and the workgroup's R
-// columns) in LDS with 16-byte loads first, so the serial chain of segments
-// waits for memory once per segment.
+// columns) in LDS from registers loaded two steps earlier.
 __global__ __launch_bounds__(512) void range_scan_kernel(ScanArgs a) {
     constexpr int DK = 128, LDM = DK + 4, NT = 512, RPT = DK / (NT / 16); // rows per thread
     __shared__ __attribute__((aligned(16))) float Ms[DK * LDM];
@@ -425,25 +424,54 @@ __global__ __launch_bounds__(512) void range_scan_kernel(ScanArgs a) {
         hc[i * 16 + j] = (a.h0 && cin && i < dk) ? a.h0[((size_t)bh * dk + i) * dv + col] : 0.f;
     for (int e = tid; e < DK * LDM; e += NT) Ms[e] = 0.f;
     __syncthreads();
-    for (int it = 0; it < a.nseg; ++it) {
-        // forward: segment sg = it, next map sg; reverse: sg = nseg-1-it, next map sg - 1
+    // map of step it: forward the map of segment it, reverse that of segment
+    // nseg-1-it (stored at index nseg-2-it)
+    auto map_of = [&](int it) {
+        return a.maps + ((size_t)bh * (a.nseg - 1) + (a.reverse ? a.nseg - 2 - it : it)) * dk * ld;
+    };
+    // M rows go through registers as 16-byte pieces when the row stride
+    // allows, requested two steps ahead (two register sets taking turns), so
+    // the serial chain of segments does not wait for memory
+    const bool vec = (ld & 3) == 0 && (dk & 3) == 0;
+    constexpr int PM = DK * (DK / 4) / NT; // 16-byte pieces of M per thread
+    float4 pmA[PM], pmB[PM];
+    float prA[RPT], prB[RPT];
+    auto load_map = [&](int it, auto &pm, auto &pr) {
+        const float *M = map_of(it);
+#pragma unroll
+        for (int r = 0; r < PM; ++r) {
+            const int e = tid + NT * r, i = e / (dk / 4), k4 = (e % (dk / 4)) * 4;
+            pm[r] = i < dk ? *reinterpret_cast<const float4 *>(M + (size_t)i * ld + k4) : float4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = i0 + (NT / 16) * r;
+            pr[r] = (cin && i < dk) ? M[(size_t)i * ld + dk + col] : 0.f;
+        }
+    };
+    // one step of the scan with the map staged from (pm, pr); returns true
+    // after the last segment's start state is written
+    auto step = [&](int it, auto &pm, auto &pr) {
         const int sg = a.reverse ? a.nseg - 1 - it : it;
         float *out = a.seg_h + ((size_t)bh * a.nseg + sg) * dk * dv;
         for (int i = i0; i < dk; i += NT / 16)
             if (cin) out[(size_t)i * dv + col] = hc[i * 16 + j];
-        if (it == a.nseg - 1) break;
-        const float *M = a.maps + ((size_t)bh * (a.nseg - 1) + (a.reverse ? sg - 1 : sg)) * dk * ld;
-        // M rows as 16-byte pieces when the row stride allows, else by element
-        if ((ld & 3) == 0 && (dk & 3) == 0) {
-            for (int e = tid; e < dk * (dk / 4); e += NT) {
-                const int i = e / (dk / 4), k4 = (e % (dk / 4)) * 4;
-                *reinterpret_cast<float4 *>(Ms + i * LDM + k4) = *reinterpret_cast<const float4 *>(M + (size_t)i * ld + k4);
+        if (it == a.nseg - 1) return true;
+        if (vec) {
+#pragma unroll
+            for (int r = 0; r < PM; ++r) {
+                const int e = tid + NT * r, i = e / (dk / 4), k4 = (e % (dk / 4)) * 4;
+                if (i < dk) *reinterpret_cast<float4 *>(Ms + i * LDM + k4) = pm[r];
             }
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) Rs[(i0 + (NT / 16) * r) * 16 + j] = pr[r];
         } else {
+            const float *M = map_of(it);
             for (int e = tid; e < dk * dk; e += NT) Ms[(e / dk) * LDM + e % dk] = M[(size_t)(e / dk) * ld + e % dk];
+            for (int i = i0; i < dk; i += NT / 16) Rs[i * 16 + j] = cin ? M[(size_t)i * ld + dk + col] : 0.f;
         }
-        for (int i = i0; i < dk; i += NT / 16) Rs[i * 16 + j] = cin ? M[(size_t)i * ld + dk + col] : 0.f;
         __syncthreads();
+        if (vec && it + 2 < a.nseg - 1) load_map(it + 2, pm, pr);
         // rows i0 + 32 r of the new x: every 16-byte read of a row of M
         // serves four key steps, every read of x four rows
         float nx[RPT];
@@ -468,6 +496,13 @@ __global__ __launch_bounds__(512) void range_scan_kernel(ScanArgs a) {
             if (i < dk) hc[i * 16 + j] = Rs[i * 16 + j] + nx[r];
         }
         __syncthreads();
+        return false;
+    };
+    if (vec && a.nseg > 1) load_map(0, pmA, prA);
+    if (vec && a.nseg > 2) load_map(1, pmB, prB);
+    for (int it = 0;; it += 2) {
+        if (step(it, pmA, prA)) break;
+        if (step(it + 1, pmB, prB)) break;
     }
 }
 
