@@ -215,6 +215,24 @@ __global__ __launch_bounds__(NTHR, 8) void fwd_prep_kernel(PrepArgs a) {
 
 // ----------------------------------------------------------------- chain
 
+// x + c y on eight packed bf16 values (fp32 arithmetic, one rounding)
+__device__ __forceinline__ uint4 add_scaled_bf16x8(uint4 x, uint4 y, float c) {
+    auto two = [&](uint32_t a, uint32_t b) {
+        return f2bf2(bf2f((u16)(a & 0xFFFF)) + c * bf2f((u16)(b & 0xFFFF)), bf2f((u16)(a >> 16)) + c * bf2f((u16)(b >> 16)));
+    };
+    return uint4{two(x.x, y.x), two(x.y, y.y), two(x.z, y.z), two(x.w, y.w)};
+}
+
+// x + c y on one 16-byte vector of the operand type
+template <bool BF> __device__ __forceinline__ uint4 add_scaled_vec(uint4 x, uint4 y, float c) {
+    if constexpr (BF) {
+        return add_scaled_bf16x8(x, y, c);
+    } else {
+        const float4 a = __builtin_bit_cast(float4, x), b = __builtin_bit_cast(float4, y);
+        return __builtin_bit_cast(uint4, float4{a.x + c * b.x, a.y + c * b.y, a.z + c * b.z, a.w + c * b.w});
+    }
+}
+
 template <bool BF, int D, int BV> struct FwdChainSmem {
     using S = typename Op<BF>::S;
     static constexpr int LDD = D + Op<BF>::PAD;
@@ -235,6 +253,9 @@ template <bool BF, int D, int BV> struct FwdChainSmem {
     static constexpr int oMisc = oEgn + C * 4;
     static constexpr int SIZE = oMisc + 16;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
+    // O of a chunk [C][LDV] is staged over WT and WTd, which are free from the
+    // end of one chunk's products to the W product of the next
+    static_assert(C * LDV <= 2 * BV * LDC, "O staging fits the W area");
 };
 
 template <bool BF, int D, int BV, bool VEC>
@@ -307,23 +328,39 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         if (!mblk) fu.template fetch<VEC>(U + cb * C * dv + v0, (size_t)dv, n, nvc, tid);
         pg = gate_of(load_row_scalar(s.g + row0 * H + h, H, lane, n), s.logits);
     };
-    // O of a chunk is held in registers and written out during the next
-    // chunk, after that chunk's inputs have arrived: stores are issued only
-    // between consuming one prefetch and issuing the next, so waiting for
-    // the inputs never waits for a store to complete
+    // O of a chunk is written out during the next chunk, after that chunk's
+    // inputs have arrived: stores are issued only between consuming one
+    // prefetch and issuing the next, so waiting for the inputs never waits
+    // for a store to complete. With 16-byte rows (VEC) O goes through LDS:
+    // staged in tile layout once the chunk's products are done, then stored
+    // as row pieces after the next chunk's first barrier; otherwise it is
+    // held in registers and stored element by element.
     f32x4 accO[Tiles<4, VT>::PW];
+    S *Os = WT; // [C][LDV]
     const float Dh = s.D ? s.D[h] : 0.f; // skip term o_t += D_h v_t
     auto store_o = [&](int c) {
         const int n = min(C, T - c * C);
         const size_t off = (((size_t)b * T + c * C) * H + h) * dv + v0;
         S *orow = o + off;
         const S *vrow = (const S *)s.v + off;
-        for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
-            if (row < n && col < nvc) {
-                const size_t x = (size_t)row * H * dv + col;
-                orow[x] = from_f<BF>(s.D ? accO[i][e] + Dh * to_f(vrow[x]) : accO[i][e]);
+        if constexpr (VEC) {
+            constexpr int V = O::VEC, NG = BV / V;
+            for (int it = tid; it < C * NG; it += NTHR) {
+                const int j = it / NG, c0 = (it % NG) * V;
+                if (j >= n || c0 >= nvc) continue;
+                const size_t x = (size_t)j * H * dv + c0;
+                uint4 val = *reinterpret_cast<const uint4 *>(Os + j * LDV + c0);
+                if (s.D) val = add_scaled_vec<BF>(val, *reinterpret_cast<const uint4 *>(vrow + x), Dh);
+                *reinterpret_cast<uint4 *>(orow + x) = val;
             }
-        });
+        } else {
+            for_tiles<4, VT>(wave, lane, [&](int i, int e, int row, int col) {
+                if (row < n && col < nvc) {
+                    const size_t x = (size_t)row * H * dv + col;
+                    orow[x] = from_f<BF>(s.D ? accO[i][e] + Dh * to_f(vrow[x]) : accO[i][e]);
+                }
+            });
+        }
     };
     fetch(c_lo);
 
@@ -342,15 +379,42 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         if (o) fq.stash(Qs, LDD, tid);
         if (!s.additive) fn.stash(NKs, LDD, tid);
         fu.stash(Us, LDV, tid);
-        if (o && c > c_lo) store_o(c - 1);
+        if (!VEC && o && c > c_lo) store_o(c - 1);
         if (cs) {
-            for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
-                if (row < dk && col < nvc)
-                    cs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accH[i][e]);
-            });
+            // chunk-start state, transposed [dv][dk]: a lane's 4 consecutive
+            // key rows of one value column are contiguous (dk % 4 == 0 with
+            // VEC): one 8-byte (bf16) or 16-byte (fp32) store
+            if constexpr (VEC) {
+                using TL = Tiles<DT, VT>;
+                const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+                for (int i = 0; i < TL::PW; ++i) {
+                    const int t = wave + NWAVE * i;
+                    if (TL::N % NWAVE != 0 && t >= TL::N) break;
+                    const int row = (t / VT) * 16 + 4 * kq, col = (t % VT) * 16 + r;
+                    if (row < dk && col < nvc) {
+                        S *dst = cs + (((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row;
+                        if constexpr (BF)
+                            *reinterpret_cast<short4_t *>(dst) = pack4(accH[i]);
+                        else
+                            *reinterpret_cast<f32x4 *>(dst) = accH[i];
+                    }
+                }
+            } else {
+                for_tiles<DT, VT>(wave, lane, [&](int i, int e, int row, int col) {
+                    if (row < dk && col < nvc)
+                        cs[(((size_t)bh * s.NC + c) * dv + v0 + col) * dk + row] = from_f<BF>(accH[i][e]);
+                });
+            }
         }
         if (c + 1 < c_hi) fetch(c + 1);
         __syncthreads();
+        if (VEC && o && c > c_lo) {
+            // O rows of the previous chunk out of the W area, which this
+            // chunk's W product overwrites after the next barrier
+            store_o(c - 1);
+            __syncthreads();
+        }
 
         // P = (Q K^T) o Gam (independent of the state; only the outputs need it)
         if (o) {
@@ -388,8 +452,12 @@ __global__ __launch_bounds__(NTHR) void fwd_chain_kernel(FwdChainArgs a) {
         }
         __syncthreads();
         store_T<BF, DT, VT>(accH, hTs, LDD, wave, lane);
+        if (VEC && o) store_N<BF, 4, VT>(accO, Os, LDV, wave, lane); // O staged for the next chunk
     }
-    if (o && c_hi > c_lo) store_o(c_hi - 1);
+    if (o && c_hi > c_lo) {
+        if (VEC) __syncthreads(); // staged O rows complete
+        store_o(c_hi - 1);
+    }
     if (maps) {
         // [M | R] of this segment: identity blocks fill the M columns
         float *dst = a.maps + ((size_t)bh * (a.nseg - 1) + seg) * dk * (dk + dv) + (mblk ? v0 : dk + v0);
@@ -559,14 +627,6 @@ template <int D> struct WsSmem {
     static constexpr int SIZE = oDec + 2 * szDec;
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
-
-// x + c y on eight packed bf16 values (fp32 arithmetic, one rounding)
-__device__ __forceinline__ uint4 add_scaled_bf16x8(uint4 x, uint4 y, float c) {
-    auto two = [&](uint32_t a, uint32_t b) {
-        return f2bf2(bf2f((u16)(a & 0xFFFF)) + c * bf2f((u16)(b & 0xFFFF)), bf2f((u16)(a >> 16)) + c * bf2f((u16)(b >> 16)));
-    };
-    return uint4{two(x.x, y.x), two(x.y, y.y), two(x.z, y.z), two(x.w, y.w)};
-}
 
 // EDGE: the layer edges (key normalisation, skip term) are compiled in; the
 // plain instantiation carries none of their code, so its schedule is that of
