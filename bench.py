@@ -53,6 +53,10 @@ Profiling aids (the counter runs behind the committed summaries):
     python bench.py --mfma-summary DIR [--workload W]
                                          per-kernel MFMA busy % and flops from
                                          one --pmc run of MFMA_COUNTERS
+    python bench.py --counter-summary DIR1 DIR2 [--workload W]
+                                         per-kernel LDS busy and bank-conflict
+                                         share, waits and instruction mix from
+                                         one --pmc run per COUNTER_PASSES entry
     python bench.py --trace-summary KT_DIR KT_LOG BENCH_LOG [--workload W]
                                          kernel-trace table from one rocprofv3
                                          --kernel-trace --stats run of bench.py
@@ -716,6 +720,75 @@ def mfma_summary(counter_dir, workload):
     print("\n".join(lines))
 
 
+# Counter passes behind profiles/counters_<workload>.txt (each within one
+# rocprofv3 run's limits: at most 8 SQ counters and the GRBM clock).
+COUNTER_PASSES = [
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_WAVE_CYCLES SQ_WAIT_ANY "
+    "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_WAVES "
+    "GRBM_GUI_ACTIVE",
+]
+CU_NUM = 256
+
+
+def counter_summary(dirs, workload):
+    """Per-kernel LDS use, waits and instruction mix from the rocprofv3 --pmc
+    runs of COUNTER_PASSES (one directory each) over `bench.py --profile-run
+    N`, averaged over launches: LDS busy % = SQ_LDS_IDX_ACTIVE / (active
+    cycles of one XCD x CUs), bank-conflict share of that time, wave-cycles
+    spent waiting, and instructions per wave by kind."""
+    import collections
+    import csv
+    import glob
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    name = {}
+    for i, d in enumerate(dirs):
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (i, r["Dispatch_Id"])
+                    per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                    name[key] = r["Kernel_Name"]
+    wl = "" if workload == HEADLINE else f" --workload {workload}"
+    lines = [f"# LDS, waits and instruction mix per launch, workload {workload} ({_workload_text(workload)}),"
+             " one MI355X", "#", "# commands (from /tmp on the GPU host, TMPDIR=/tmp), one run per pass:"]
+    for i, cs in enumerate(COUNTER_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {cs} --output-format csv -d <dir{i + 1}> -o p -- "
+                     f"python3 <repo>/bench.py --profile-run 2{wl}")
+    lines += [f"#   python3 <repo>/bench.py --counter-summary <dir1> <dir2>{wl}   (writes this file)", "#",
+              f"# cycles = GRBM_GUI_ACTIVE / {XCD_NUM} (one XCD's active cycles); LDS busy % ="
+              f" SQ_LDS_IDX_ACTIVE / (cycles x {CU_NUM} CUs);",
+              "# conflict % = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; wait % = SQ_WAIT_ANY / SQ_WAVE_CYCLES"
+              " (wave-cycles",
+              "# waiting on any dependency or barrier); instructions per wave = SQ_INSTS_* / SQ_WAVES.",
+              f"# source_hash {source_hash()}", "",
+              f"{'kernel':12s} {'us@clk':>8s} {'LDS busy%':>9s} {'conflict%':>9s} {'wait%':>6s} "
+              f"{'VALU/wave':>9s} {'MFMA/wave':>9s} {'LDS/wave':>8s} {'SALU/wave':>9s} {'VMEM/wave':>9s}"]
+    for k in KERNELS:
+        res = {}
+        for i in range(len(dirs)):
+            ds = [x for x in per if x[0] == i and kernel_of(name[x]) == k]
+            for c in set().union(*[per[x].keys() for x in ds]) if ds else ():
+                res[(i, c)] = sum(per[x][c] for x in ds) / len(ds)
+        if not res:
+            continue
+        g = lambda c: next((v for (i, cc), v in res.items() if cc == c), float("nan"))
+        cyc = res.get((0, "GRBM_GUI_ACTIVE"), g("GRBM_GUI_ACTIVE")) / XCD_NUM
+        lds = g("SQ_LDS_IDX_ACTIVE")
+        waves = g("SQ_WAVES")
+        per_wave = lambda c: g(c) / waves if waves and waves == waves else float("nan")
+        lines.append(f"{k:12s} {cyc / 2.4e3:8.1f} {100 * lds / (cyc * CU_NUM):9.1f} "
+                     f"{100 * g('SQ_LDS_BANK_CONFLICT') / lds if lds else float('nan'):9.1f} "
+                     f"{100 * g('SQ_WAIT_ANY') / g('SQ_WAVE_CYCLES'):6.1f} {per_wave('SQ_INSTS_VALU'):9.0f} "
+                     f"{per_wave('SQ_INSTS_MFMA'):9.0f} {per_wave('SQ_INSTS_LDS'):8.0f} {per_wave('SQ_INSTS_SALU'):9.0f} "
+                     f"{per_wave('SQ_INSTS_VMEM_RD') + per_wave('SQ_INSTS_VMEM_WR'):9.0f}")
+    lines += ["", "# us@clk: one XCD's active cycles at 2.4 GHz (the counters' own view of the launch length)."]
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------ CPU oracle
 
 def _f64_inputs(x):
@@ -843,6 +916,7 @@ def main():
     ap.add_argument("--profile-run", type=int, default=0, metavar="N")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-summary", metavar="COUNTER_DIR")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PASS_DIR")
     ap.add_argument("--trace-summary", nargs=3, metavar=("KT_DIR", "KT_LOG", "BENCH_LOG"))
     args = ap.parse_args()
     if args.trace_summary:
@@ -853,6 +927,9 @@ def main():
         return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, args.workload)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.workload)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the gated delta rule path here is built and timed "
