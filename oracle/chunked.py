@@ -3,12 +3,12 @@
 A self-check of the serial oracle only: the tests require this and the serial
 loop in ``gdn_oracle.c`` to agree. Nothing on the product path imports it.
 
-"GDN & MLA Mechanism Deep-Dive", Step 5 (chunked recurrence) says: split the
-sequence into chunks of 64, solve each chunk in closed form with a
-chunk x chunk matrix, and carry the state h serially between chunks. The
-closed form used here is the WY/UT representation of the cited Gated Delta
-Net paper (Yang et al. 2024), written out for one chunk of n rows with start
-state h:
+What it follows: the chunked evaluation of "GDN & MLA Mechanism Deep-Dive",
+Math derivation Step 5 (fixed-length chunks of 64 tokens, the inside of a
+chunk solved at once through a small square matrix, the state handed from
+one chunk to the next). The pages leave the in-chunk solution unspecified;
+the one written out here is the WY/UT form of the Gated Delta Net paper that
+page cites (Yang et al. 2024), for one chunk of n rows with start state h:
 
     lam_r   = g_r * A                       (A = -exp(A_log))
     gam_i   = sum_{r <= i} lam_r            (restarted at every chunk)
