@@ -184,7 +184,10 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         const size_t row0 = (size_t)b * T + c * C, cb = ((size_t)b * H + h) * s.NC + c;
         fk.template fetch<VEC>((const S *)s.k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
         fq.template fetch<VEC>((const S *)s.q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
-        fh.template fetch<VEC>((const S *)a.cs + cb * dk * dv, (size_t)dk, dv, dk, tid);
+        // the chunk-start state by element loads: with 16-byte loads here the
+        // register allocator kept ~56 registers of the prefetch in scratch
+        // (spill stores and reloads through the memory system every chunk)
+        fh.template fetch<false>((const S *)a.cs + cb * dk * dv, (size_t)dk, dv, dk, tid);
         fu.template fetch<VEC>((const S *)a.U + cb * C * dv, (size_t)dv, n, dv, tid);
         if (!add) fn.template fetch<VEC>((const S *)a.NK + cb * C * dk, (size_t)dk, n, dk, tid);
         alr = s.A_log[h];

@@ -946,13 +946,16 @@ int fwd_vblock(int D, bool segmented) {
 
 // Segments of the parallel scan: long sequences split into ranges of about
 // SEG_CHUNKS chunks (at most 16 ranges); short ones stay serial.
+#ifndef GDN_SEG_MAX
+#define GDN_SEG_MAX 16
+#endif
 #ifndef GDN_SEG_CHUNKS
 #define GDN_SEG_CHUNKS 32
 #endif
 int fwd_scan_segments(bool bf16, int D, int NC) {
     if (fwd_segmentable(bf16, D)) return 1; // the wave-specialised chain takes chunk ranges instead
     const int n = NC / GDN_SEG_CHUNKS;
-    return n < 2 ? 1 : (n > 16 ? 16 : n);
+    return n < 2 ? 1 : (n > GDN_SEG_MAX ? GDN_SEG_MAX : n);
 }
 
 bool fwd_segmentable(bool bf16, int D) { return bf16 && (D == 32 || D == 64); }
