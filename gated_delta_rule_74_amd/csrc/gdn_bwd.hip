@@ -898,8 +898,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
         row_partials<4, DT>(rsD, pRsD, wave, lane);
         col_partials<4, 4>(xgC, pCgC, wave, lane);
         __syncthreads();
-        // dq, dk, dv rows of the chunk: 16-byte stores (dv = -beta * (-dV'), from
-        // the transposed -dV't). Edges: with normalised keys dk goes back
+        // dq, dk, dv rows of the chunk, written by waves 1.. while wave 0 forms
+        // dbeta and dg: 16-byte stores (dv = -beta * (-dV'), from the
+        // transposed -dV't). Edges: with normalised keys dk goes back
         // through the normalisation, dk = (dk_hat - k_hat (k_hat . dk_hat)) / |k|
         // (row dots over the lanes that hold a row); with the skip term dv
         // gains D_h do, and the chunk's share of dD_h (sum of do * v) goes to
@@ -909,8 +910,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
             constexpr int V = O::VEC, NG = D / V;
-            if (VEC) {
-                for (int it = tid; it < C * NG; it += NTHR) {
+            if (wave == 0) {
+            } else if (VEC) {
+                for (int it = tid - 64; it < C * NG; it += NTHR - 64) {
                     const int j = it / NG, c0 = (it % NG) * V;
                     if (j >= n) continue;
                     if (c0 < dk) {
@@ -931,7 +933,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                     }
                 }
             } else {
-                for (int it = tid; it < C * D; it += NTHR) {
+                for (int it = tid - 64; it < C * D; it += NTHR - 64) {
                     const int j = it / D, col = it % D;
                     if (j >= n) continue;
                     if (col < dk) {
@@ -959,8 +961,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                     uint4 u;
                     S x[V];
                 };
-                if (VEC) {
-                    for (int it = tid; it < C * NG; it += NTHR) {
+                if (wave == 0) {
+                } else if (VEC) {
+                    for (int it = tid - 64; it < C * NG; it += NTHR - 64) {
                         const int j = it / NG, c0 = (it % NG) * V;
                         Pk kd;
                         kd.u = *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(BwdLocalArgs a) {
                         }
                     }
                 } else {
-                    for (int it = tid; it < C * D; it += NTHR) {
+                    for (int it = tid - 64; it < C * D; it += NTHR - 64) {
                         const int j = it / D, col = it % D;
                         float kdv = to_f(R5[j * LDD + col]);
                         if (l2k) {

@@ -81,16 +81,13 @@ struct Wide128 {
 // i = (r % 4PW) / 4, row 4g + r % 4 (the other lanes hold copies).
 template <int MT, int NT> __device__ __forceinline__ float row_compact(const f32x4 *x, int lane) {
     constexpr int PW = Tiles<MT, NT, NWD>::PW;
-    const int r = lane & 15;
-    float out = 0.f;
+    static_assert((MT * NT) % NWD == 0 && (PW == 2 || PW == 4), "whole tiles per wave");
+    float xs[4 * PW];
 #pragma unroll
     for (int i = 0; i < PW; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float sm = sum16(x[i][e]);
-            out = (r % (4 * PW) == 4 * i + e) ? sm : out;
-        }
-    return out;
+        for (int e = 0; e < 4; ++e) xs[4 * i + e] = x[i][e];
+    return rsum16<4 * PW>(xs, lane & 15);
 }
 
 // Column sums over the rows of this wave's tiles of a [C][C] grid (all in

@@ -533,6 +533,59 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// One reduce-scatter step over a 16-lane row: the lanes whose selecting bit
+// is set keep the upper half of the N values they carry, the others the lower
+// half, and each adds the partner lane's copy of the half it keeps (CTRL names
+// a partner with the other selecting bit). With N == 1 the step is a plain add.
+template <int CTRL, int N> __device__ __forceinline__ void rs_step(float *v, bool hi) {
+    if constexpr (N == 1) {
+        v[0] += dpp_f<CTRL>(v[0]);
+    } else {
+        constexpr int h = N / 2;
+#pragma unroll
+        for (int j = 0; j < h; ++j) {
+            const float keep = hi ? v[j + h] : v[j], send = hi ? v[j] : v[j + h];
+            v[j] = keep + dpp_f<CTRL>(send);
+        }
+    }
+}
+
+// Row sums of N values at once (N = 2, 4, 8 or 16; x[v] is this lane's
+// value v): lane r of every 16-lane row ends with the sum over the row's
+// lanes of value r % N. The bits of r that pick the value are settled from
+// the highest down, each by a partner that differs in that bit and agrees in
+// the bits already settled (lane 15 - r, r ^ 7, r ^ 2, r ^ 1); the remaining
+// steps add lanes that hold the same value (rotations by 8 and 4). Costs
+// 3(N - 1) + (4 - log2 N) instructions against 4N for N calls of sum16.
+template <int N> __device__ __forceinline__ float rsum16(const float *x, int r) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "2, 4, 8 or 16 values");
+    float v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = x[j];
+    if constexpr (N == 16) {
+        rs_step<0x140, 16>(v, r & 8); // row_mirror
+        rs_step<0x141, 8>(v, r & 4);  // row_half_mirror
+        rs_step<0x4E, 4>(v, r & 2);   // quad_perm [2,3,0,1]
+        rs_step<0xB1, 2>(v, r & 1);   // quad_perm [1,0,3,2]
+    } else if constexpr (N == 8) {
+        rs_step<0x141, 8>(v, r & 4);
+        rs_step<0x4E, 4>(v, r & 2);
+        rs_step<0xB1, 2>(v, r & 1);
+        rs_step<0x128, 1>(v, false); // row_ror:8
+    } else if constexpr (N == 4) {
+        rs_step<0x4E, 4>(v, r & 2);
+        rs_step<0xB1, 2>(v, r & 1);
+        rs_step<0x124, 1>(v, false); // row_ror:4
+        rs_step<0x128, 1>(v, false);
+    } else {
+        rs_step<0xB1, 2>(v, r & 1);
+        rs_step<0x4E, 1>(v, false);
+        rs_step<0x124, 1>(v, false);
+        rs_step<0x128, 1>(v, false);
+    }
+    return v[0];
+}
+
 // Sum over the 64 lanes (fixed order: row sums, then rows 0+1 and 2+3);
 // the same value in every lane.
 __device__ __forceinline__ float wave_sum(float x) {
@@ -587,13 +640,29 @@ __device__ __forceinline__ Decay decay_lane(float g, double A2, int lane) {
 }
 
 // Per-tile row sums of x (x[i][e] is this lane's value at (row, col) of tile
-// i): the 16 lanes of a row group are summed inside their row, and lane
-// r == 0 writes part[row * NT + tn]. Every (row, tn) slot has exactly one
-// writer, so a later fixed-order sum over tn is deterministic.
+// i): the 16 lanes of a row group are summed inside their row, and one lane
+// writes part[row * NT + tn]. Every (row, tn) slot has exactly one writer, so
+// a later fixed-order sum over tn is deterministic. When every wave holds
+// 1, 2 or 4 tiles, all of its values are reduced together (rsum16): lane r < 4PW
+// then holds tile r / 4, row 4 kq + r % 4.
 template <int MT, int NT, int NW = NWAVE>
 __device__ __forceinline__ void row_partials(const f32x4 *x, float *part, int wave, int lane) {
     using TL = Tiles<MT, NT, NW>;
     const int r = lane & 15, kq = lane >> 4;
+    if constexpr (TL::N % NW == 0 && (TL::PW == 1 || TL::PW == 2 || TL::PW == 4)) {
+        constexpr int NV = 4 * TL::PW;
+        float xs[NV];
+#pragma unroll
+        for (int i = 0; i < TL::PW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xs[4 * i + e] = x[i][e];
+        const float s = rsum16<NV>(xs, r);
+        if (r < NV) {
+            const int t = wave + NW * (r >> 2);
+            part[((t / NT) * 16 + 4 * kq + (r & 3)) * NT + t % NT] = s;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TL::PW; ++i) {
         const int t = wave + NW * i;
