@@ -546,15 +546,19 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
 // X[row][col]). Each product reads an operand straight or through the
 // transposing LDS read, whichever its storage needs (gemm<..., ATR, BTR>).
 // U and Tm come from the forward context, so no triangular solve runs here.
-// Eight LDS regions are reused phase by phase (Pn = phase n):
-//   R0 K                              R4 dh'^T (P4-5) -> -dV't (P6-7)
-//   R1 h^T (P1-5) -> V (P6) -> dSt (P7-8)
-//   R2 Pt (P1-4) -> Tm (P6) -> -Kw (P7)
-//   R3 U (P1) -> dO (P4-5) -> partial sums (P9)
-//   R5 Wt (P1-5) -> dK (P9)           R6 dWt (P4-6) -> dK't (P6-7)
-//   R7 -Kw (P1) -> dKw (P5-6) -> U (P7)
-//   RQ Q (whole chunk)                RP (dP o Gam)^T (P5-6) -> dQ (P9)
-// Inputs needed in two phases stay in registers between their stashes.
+// Thirteen LDS regions, some reused once a value is dead (Pn = phase n; the
+// workgroup barrier that ends a phase separates the last read of a value
+// from the first write of its successor):
+//   RK K, RQ Q, RH h^T (P1-5), RU U (P1, P7), RN -Kw (P1, P7)
+//   RPt Pt (P1-4) -> V (stashed in P5, read in P6) -> dSt (P7-8)
+//   RWt Wt (P1-5) -> -dV't (P6-9)     RdO dO (stashed in P1, P4-5) -> dK't (P6-7)
+//   Rdh dh'^T (stashed in P1, P4-5) -> partial sums (P9)
+//   RdW dWt (P4-6)                    RdKw dKw (P5-6)
+//   RdPG (dP o Gam)^T (P5-6) -> dQ (P9)
+//   RTm Tm (stashed in P5, P6) -> dK (P9)
+// Every input is stashed once; dO and dh' (requested at the top of the
+// chunk) are stashed at the end of P1, V and Tm at the end of P5, so each
+// rides on a barrier that is there anyway.
 
 
 template <bool BF, int D, int NW> struct LocalSmem {
@@ -567,17 +571,20 @@ template <bool BF, int D, int NW> struct LocalSmem {
     static constexpr int sDD = D * LDD * (int)sizeof(S); // state [D][D]
     static constexpr int sCC = C * LDC * (int)sizeof(S); // [C][C]
     static constexpr int sPart = (3 * C * (D / 16) + 3 * C * 4) * 4;
-    static constexpr int o0 = 0;
-    static constexpr int o1 = o0 + sCD;
-    static constexpr int o2 = o1 + mx(mx(sCD, sDD), sCC);
-    static constexpr int o3 = o2 + mx(sCC, sCD);
-    static constexpr int o4 = o3 + mx(sCD, sPart);
-    static constexpr int o5 = o4 + mx(sDD, sDC);
-    static constexpr int o6 = o5 + mx(sDC, sCD);
-    static constexpr int o7 = o6 + sDC;
-    static constexpr int oQ = o7 + mx(sCD, sCC);           // RQ: Q (whole chunk)
-    static constexpr int oP = oQ + sCD;                      // RP: dPGt (P5-6) -> dQ
-    static constexpr int oGam = oP + mx(sCC, sCD);
+    static constexpr int oK = 0;
+    static constexpr int oQ = oK + sCD;
+    static constexpr int oH = oQ + sCD;
+    static constexpr int oU = oH + sDD;
+    static constexpr int oN = oU + sCD;
+    static constexpr int oPt = oN + sCD;
+    static constexpr int oWt = oPt + mx(sCC, sCD);
+    static constexpr int odO = oWt + sDC;
+    static constexpr int odh = odO + mx(sCD, sDC);
+    static constexpr int odW = odh + mx(sDD, sPart);
+    static constexpr int odKw = odW + sDC;
+    static constexpr int odPG = odKw + sCD;
+    static constexpr int oTm = odPG + mx(sCC, sCD);
+    static constexpr int oGam = oTm + mx(sCC, sCD);
     static constexpr int oEg = oGam + NW * C * 8; // gam: one copy per wave
     static constexpr int oEgn = oEg + C * 4;
     static constexpr int oBet = oEgn + C * 4;
@@ -600,17 +607,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     constexpr int LDD = L::LDD, LDC = L::LDC, DT = D / 16;
     constexpr int PWC = Tiles<4, 4, NW>::PW, PWD = Tiles<4, DT, NW>::PW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
-    S *R0 = (S *)(smem + L::o0);
-    S *R1 = (S *)(smem + L::o1);
-    S *R2 = (S *)(smem + L::o2);
-    S *R3 = (S *)(smem + L::o3);
-    S *R4 = (S *)(smem + L::o4);
-    S *R5 = (S *)(smem + L::o5);
-    S *R6 = (S *)(smem + L::o6);
-    S *R7 = (S *)(smem + L::o7);
+    S *Ks = (S *)(smem + L::oK);
     S *RQ = (S *)(smem + L::oQ);
-    S *RP = (S *)(smem + L::oP);
-    S *Ks = R0;
+    S *RH = (S *)(smem + L::oH);
+    S *RU = (S *)(smem + L::oU);
+    S *RN = (S *)(smem + L::oN);
+    S *RPt = (S *)(smem + L::oPt);
+    S *RWt = (S *)(smem + L::oWt);
+    S *RdO = (S *)(smem + L::odO);
+    S *Rdh = (S *)(smem + L::odh);
+    S *RdW = (S *)(smem + L::odW);
+    S *RdKw = (S *)(smem + L::odKw);
+    S *RdPG = (S *)(smem + L::odPG);
+    S *RTm = (S *)(smem + L::oTm);
     double *gam = (double *)(smem + L::oGam);
     float *eg = (float *)(smem + L::oEg);
     float *egn = (float *)(smem + L::oEgn);
@@ -707,9 +716,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     }
     fk.stash(Ks, LDD, tid);
     fq.stash(RQ, LDD, tid);
-    fh.stash(R1, LDD, tid);
-    fu.stash(R3, LDD, tid);
-    if (!add) fn.stash(R7, LDD, tid);
+    fh.stash(RH, LDD, tid);
+    fu.stash(RU, LDD, tid);
+    if (!add) fn.stash(RN, LDD, tid);
     __syncthreads();
     // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
     f32x4 gC[PWC], kkg[PWC], pC[PWC];
@@ -738,50 +747,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
             kkg[i][e] = (row > col) ? sk[i][e] * G : 0.f;
             pC[i][e] = sq[i][e] * G;
         });
-        store_T<BF, 4, 4, NW>(pC, R2, LDC, wave, lane); // Pt
+        store_T<BF, 4, 4, NW>(pC, RPt, LDC, wave, lane); // Pt
     }
     {
         f32x4 accW[PWD];
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(R3[row * LDD + col]); });
-        if (!add) gemm<BF, 4, DT, D, false, false, NW>(R7, LDD, R1, LDD, accW, wave, lane); // + (-Kw) h
-        store_T<BF, 4, DT, NW>(accW, R5, LDC, wave, lane);                               // Wt
+        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(RU[row * LDD + col]); });
+        if (!add) gemm<BF, 4, DT, D, false, false, NW>(RN, LDD, RH, LDD, accW, wave, lane); // + (-Kw) h
+        store_T<BF, 4, DT, NW>(accW, RWt, LDC, wave, lane);                               // Wt
     }
-    __syncthreads(); // Pt and Wt complete; U reads done
-    // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
-    fo.stash(R3, LDD, tid);
-    fd.stash(R4, LDD, tid);
-    __syncthreads();
+    // dO and dh' into their own regions, and <h, dh'> from the register
+    // fragments while both are held (one butterfly, one slot per wave)
+    fo.stash(RdO, LDD, tid);
+    fd.stash(Rdh, LDD, tid);
     {
-        f32x4 accdW[PWD], accX[PWD];
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
-        gemm<BF, 4, DT, C, false, true, NW>(R2, LDC, R3, LDD, accdW, wave, lane); // P^T dO
-        gemm<BF, 4, DT, D, false, false, NW>(Ks, LDD, R4, LDD, accX, wave, lane); // K dh'
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
-        store_T<BF, 4, DT, NW>(accdW, R6, LDC, wave, lane); // dWt
-    }
-    __syncthreads();
-    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, <h, dh'>, dP
-    f32x4 accQ[PWD], accKd[PWD];
-#pragma unroll
-    for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
-    gemm<BF, 4, DT, D, false, true, NW>(R3, LDD, R1, LDD, accQ, wave, lane); // dO h^T
-    {
-        f32x4 accM[Tiles<DT, 4, NW>::PW];
-#pragma unroll
-        for (int i = 0; i < Tiles<DT, 4, NW>::PW; ++i) accM[i] = zero4();
-        if (!add) gemm<BF, DT, 4, D, true, true, NW>(R1, LDD, R6, LDC, accM, wave, lane); // h dW^T
-        f32x4 accKt[PWD];
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
-        gemm<BF, 4, DT, D, true, true, NW>(R5, LDC, R4, LDD, accKt, wave, lane); // W dh'^T
-        // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
-            const float x = egn[row] * accKt[i][e];
-            accKd[i][e] = x;
-            rsD[i][e] = x * to_f(Ks[row * LDD + col]);
-        });
-        // <h, dh'> from the register fragments: one butterfly, one slot per wave
         float hd = 0.f;
 #pragma unroll
         for (int m = 0; m < fh.NIT; ++m) {
@@ -793,78 +771,106 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         }
         hd = wave_sum(hd);
         if (lane == 0) misc[16 + wave] = hd;
-        // dP = dO W^T (lower incl. diagonal), dP o Gam -> RP
+    }
+    __syncthreads(); // Pt, Wt, dO and dh' complete
+    // ---- P4: dW = P^T dO + diag(e^{gam_n - gam}) K dh'
+    {
+        f32x4 accdW[PWD], accX[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accdW[i] = accX[i] = zero4();
+        gemm<BF, 4, DT, C, false, true, NW>(RPt, LDC, RdO, LDD, accdW, wave, lane); // P^T dO
+        gemm<BF, 4, DT, D, false, false, NW>(Ks, LDD, Rdh, LDD, accX, wave, lane);  // K dh'
+        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { accdW[i][e] += egn[row] * accX[i][e]; });
+        store_T<BF, 4, DT, NW>(accdW, RdW, LDC, wave, lane); // dWt
+    }
+    __syncthreads();
+    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, dP
+    f32x4 accQ[PWD], accKd[PWD];
+#pragma unroll
+    for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
+    gemm<BF, 4, DT, D, false, true, NW>(RdO, LDD, RH, LDD, accQ, wave, lane); // dO h^T
+    {
+        f32x4 accM[Tiles<DT, 4, NW>::PW];
+#pragma unroll
+        for (int i = 0; i < Tiles<DT, 4, NW>::PW; ++i) accM[i] = zero4();
+        if (!add) gemm<BF, DT, 4, D, true, true, NW>(RH, LDD, RdW, LDC, accM, wave, lane); // h dW^T
+        f32x4 accKt[PWD];
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
+        gemm<BF, 4, DT, D, true, true, NW>(RWt, LDC, Rdh, LDD, accKt, wave, lane); // W dh'^T
+        // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
+        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
+            const float x = egn[row] * accKt[i][e];
+            accKd[i][e] = x;
+            rsD[i][e] = x * to_f(Ks[row * LDD + col]);
+        });
+        // dP = dO W^T (lower incl. diagonal), dP o Gam -> RdPG
         {
             f32x4 accP[PWC];
 #pragma unroll
             for (int i = 0; i < PWC; ++i) accP[i] = zero4();
-            gemm<BF, 4, 4, D, false, true, NW>(R3, LDD, R5, LDC, accP, wave, lane);
+            gemm<BF, 4, 4, D, false, true, NW>(RdO, LDD, RWt, LDC, accP, wave, lane);
             for_tiles<4, 4, NW>(wave, lane, [&](int i, int e, int row, int col) {
                 const float dp = row >= col ? accP[i][e] : 0.f;
                 xgC[i][e] += dp * pC[i][e]; // dP o P
                 accP[i][e] = dp * gC[i][e];
             });
-            store_T<BF, 4, 4, NW>(accP, RP, LDC, wave, lane); // dPGt
+            store_T<BF, 4, 4, NW>(accP, RdPG, LDC, wave, lane); // dPGt
         }
-        // R7 (-Kw) and R2 (Pt) are free: dKw (token rows) and Tm go there
         if (!add) {
 #pragma unroll
             for (int i = 0; i < Tiles<DT, 4, NW>::PW; ++i) accM[i] = -accM[i];
-            store_T<BF, DT, 4, NW>(accM, R7, LDD, wave, lane); // dKw, token rows [C][D]
+            store_T<BF, DT, 4, NW>(accM, RdKw, LDD, wave, lane); // dKw, token rows [C][D]
         }
-        ft.stash(R2, LDC, tid);
+        // Tm, and V where Pt was (last read in P4)
+        ft.stash(RTm, LDC, tid);
+        fv.stash(RPt, LDD, tid);
     }
-    __syncthreads(); // h, dh' no longer read
+    __syncthreads(); // dWt, dKw, dPGt, Tm and V complete; h, dO, Wt, dh' no longer read
     // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw, dQ, dK += (dP o Gam)^T Q
-    fv.stash(R1, LDD, tid);
     {
         f32x4 accV[PWD], accKp[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
-        gemm<BF, 4, DT, C, true, false, NW>(R2, LDC, R6, LDC, accV, wave, lane);
-        if (!add) gemm<BF, 4, DT, C, true, true, NW>(R2, LDC, R7, LDD, accKp, wave, lane);
+        gemm<BF, 4, DT, C, true, false, NW>(RTm, LDC, RdW, LDC, accV, wave, lane);
+        if (!add) gemm<BF, 4, DT, C, true, true, NW>(RTm, LDC, RdKw, LDD, accKp, wave, lane);
         // dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
         for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
             accQ[i][e] *= eg[row];
             rgD[i][e] += accQ[i][e] * to_f(RQ[row * LDD + col]); // e^{gam_i} q_i . dOh_i
         });
-        gemm<BF, 4, DT, C, true, true, NW>(RP, LDC, Ks, LDD, accQ, wave, lane);
-        gemm<BF, 4, DT, C, false, true, NW>(RP, LDC, RQ, LDD, accKd, wave, lane);
-        __syncthreads(); // V visible; Tm, dWt, dKw reads done
+        gemm<BF, 4, DT, C, true, true, NW>(RdPG, LDC, Ks, LDD, accQ, wave, lane);
+        gemm<BF, 4, DT, C, false, true, NW>(RdPG, LDC, RQ, LDD, accKd, wave, lane);
         for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
             const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
-            rbD[i][e] += to_f(R1[row * LDD + col]) * accV[i][e] + eg[row] * kk;
+            rbD[i][e] += to_f(RPt[row * LDD + col]) * accV[i][e] + eg[row] * kk;
             rgD[i][e] += bet[row] * eg[row] * kk;
             accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
         });
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-        store_T<BF, 4, DT, NW>(accV, R4, LDC, wave, lane); // -dV't (also the source of dv)
-        if (!add) {
-            store_T<BF, 4, DT, NW>(accKp, R6, LDC, wave, lane); // dK't
-            fn.stash(R2, LDD, tid);                         // -Kw again
-            fu.stash(R7, LDD, tid);                         // U again
-        }
+        store_T<BF, 4, DT, NW>(accV, RWt, LDC, wave, lane);               // -dV't (also the source of dv)
+        if (!add) store_T<BF, 4, DT, NW>(accKp, RdO, LDC, wave, lane); // dK't
     }
-    __syncthreads(); // V reads done
+    __syncthreads(); // -dV't and dK't complete; V, Tm, dWt, dKw, dPGt no longer read
     // ---- P7: dL = -(dV' U^T + dK' Kw^T) = (-dV') U^T + dK' (-Kw)^T, dS
     if (!add) {
         f32x4 accL[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accL[i] = zero4();
-        gemm<BF, 4, 4, D, true, false, NW>(R4, LDC, R7, LDD, accL, wave, lane);
-        gemm<BF, 4, 4, D, true, false, NW>(R6, LDC, R2, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, false, NW>(RWt, LDC, RU, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, false, NW>(RdO, LDC, RN, LDD, accL, wave, lane);
         for_tiles<4, 4, NW>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
             rbC[i][e] += dl * kkg[i][e];
             xgC[i][e] += dl * bet[row] * kkg[i][e]; // dL o L
             accL[i][e] = bet[row] * dl * gC[i][e];
         });
-        store_T<BF, 4, 4, NW>(accL, R1, LDC, wave, lane); // dSt
+        store_T<BF, 4, 4, NW>(accL, RPt, LDC, wave, lane); // dSt
         __syncthreads();
         // ---- P8: dK += dS K + dS^T K
-        gemm<BF, 4, DT, C, true, true, NW>(R1, LDC, Ks, LDD, accKd, wave, lane);
-        gemm<BF, 4, DT, C, false, true, NW>(R1, LDC, Ks, LDD, accKd, wave, lane);
+        gemm<BF, 4, DT, C, true, true, NW>(RPt, LDC, Ks, LDD, accKd, wave, lane);
+        gemm<BF, 4, DT, C, false, true, NW>(RPt, LDC, Ks, LDD, accKd, wave, lane);
     }
     // every fragment is stashed and the products are done: request the first
     // inputs of the next chunk (the current one again after the last, so the
@@ -872,14 +878,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     const Pos nxt = advance(cur);
     const bool more = nxt.lid < lim;
     fetch_early(more ? nxt : cur, tid, lane);
-    // dQ and dK leave through LDS as 16-byte rows: RP was last read before the
-    // middle barrier of P6, R5 (Wt) in P5
-    store_N<BF, 4, DT, NW>(accQ, RP, LDD, wave, lane);
-    store_N<BF, 4, DT, NW>(accKd, R5, LDD, wave, lane);
+    // dQ and dK leave through LDS as 16-byte rows (dPGt and Tm were last read
+    // in P6)
+    store_N<BF, 4, DT, NW>(accQ, RdPG, LDD, wave, lane);
+    store_N<BF, 4, DT, NW>(accKd, RTm, LDD, wave, lane);
     // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
     {
-        // R3 (dO) was last read in P5
-        float *pRbD = (float *)R3, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
+        // dh' was last read in P5
+        float *pRbD = (float *)Rdh, *pRgD = pRbD + C * DT, *pRsD = pRgD + C * DT;
         float *pRbC = pRsD + C * DT, *pRgC = pRbC + C * 4, *pCgC = pRgC + C * 4;
         if constexpr (DT == 4) {
             // [C][D] and [C][C] tiles sit at the same places: add the row
@@ -917,9 +923,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                     if (j >= n) continue;
                     if (c0 < dk) {
                         *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
-                            *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
+                            *reinterpret_cast<const uint4 *>(RdPG + j * LDD + c0);
                         *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) =
-                            *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                            *reinterpret_cast<const uint4 *>(RTm + j * LDD + c0);
                     }
                     if (c0 < dv) {
                         union {
@@ -928,7 +934,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                         } pk;
                         const float nb = -bet[j];
 #pragma unroll
-                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(R4[(c0 + e) * LDC + j]));
+                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(RWt[(c0 + e) * LDC + j]));
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
@@ -937,10 +943,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                     const int j = it / D, col = it % D;
                     if (j >= n) continue;
                     if (col < dk) {
-                        dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
-                        dk_out[(size_t)j * H * dk + col] = R5[j * LDD + col];
+                        dq_out[(size_t)j * H * dk + col] = RdPG[j * LDD + col];
+                        dk_out[(size_t)j * H * dk + col] = RTm[j * LDD + col];
                     }
-                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(R4[col * LDC + j]));
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(RWt[col * LDC + j]));
                 }
             }
         } else {
@@ -966,7 +972,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                     for (int it = tid - 64; it < C * NG; it += NTL - 64) {
                         const int j = it / NG, c0 = (it % NG) * V;
                         Pk kd;
-                        kd.u = *reinterpret_cast<const uint4 *>(R5 + j * LDD + c0);
+                        kd.u = *reinterpret_cast<const uint4 *>(RTm + j * LDD + c0);
                         if (l2k) {
                             Pk kh;
                             kh.u = *reinterpret_cast<const uint4 *>(Ks + j * LDD + c0);
@@ -982,7 +988,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                         if (j >= n) continue;
                         if (c0 < dk) {
                             *reinterpret_cast<uint4 *>(dq_out + (size_t)j * H * dk + c0) =
-                                *reinterpret_cast<const uint4 *>(RP + j * LDD + c0);
+                                *reinterpret_cast<const uint4 *>(RdPG + j * LDD + c0);
                             *reinterpret_cast<uint4 *>(dk_out + (size_t)j * H * dk + c0) = kd.u;
                         }
                         if (c0 < dv) {
@@ -994,7 +1000,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                             }
 #pragma unroll
                             for (int e = 0; e < V; ++e) {
-                                float x = nb * to_f(R4[(c0 + e) * LDC + j]);
+                                float x = nb * to_f(RWt[(c0 + e) * LDC + j]);
                                 if (Dp) x += Dh * to_f(dov.x[e]);
                                 if (dDp) dsum += to_f(dov.x[e]) * to_f(vv.x[e]);
                                 pk.x[e] = from_f<BF>(x);
@@ -1005,7 +1011,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                 } else {
                     for (int it = tid - 64; it < C * D; it += NTL - 64) {
                         const int j = it / D, col = it % D;
-                        float kdv = to_f(R5[j * LDD + col]);
+                        float kdv = to_f(RTm[j * LDD + col]);
                         if (l2k) {
                             const float khv = to_f(Ks[j * LDD + col]);
                             float dot = khv * kdv;
@@ -1015,11 +1021,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                         }
                         if (j >= n) continue;
                         if (col < dk) {
-                            dq_out[(size_t)j * H * dk + col] = RP[j * LDD + col];
+                            dq_out[(size_t)j * H * dk + col] = RdPG[j * LDD + col];
                             dk_out[(size_t)j * H * dk + col] = from_f<BF>(kdv);
                         }
                         if (col < dv) {
-                            float x = -bet[j] * to_f(R4[col * LDC + j]);
+                            float x = -bet[j] * to_f(RWt[col * LDC + j]);
                             if (edge_v) {
                                 const float dd = to_f(do_in[(size_t)j * H * dv + col]);
                                 if (Dp) x += Dh * dd;
