@@ -683,6 +683,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     if (first >= lim) return;
     Pos cur{first, first % H, (first / H) % s.NC, first / (H * s.NC)};
     fetch_early(cur, tid0, tid0 & 63);
+    // a chunk's first inputs (K, Q, h, U, -Kw) go to LDS as soon as their
+    // regions are free: before the loop for the first chunk, right after the
+    // previous chunk's output stores for the others
+    auto stash_inputs = [&](int tid) {
+        if constexpr (EDGE) {
+            if (s.l2k) fk.normalize_rows(rinvK, tid);
+        }
+        fk.stash(Ks, LDD, tid);
+        fq.stash(RQ, LDD, tid);
+        fh.stash(RH, LDD, tid);
+        fu.stash(RU, LDD, tid);
+        if (!add) fn.stash(RN, LDD, tid);
+    };
+    stash_inputs(tid0);
     for (;;) {
     // the thread index is hidden from the optimiser at the top of every
     // chunk, so per-lane addresses are formed where they are used instead of
@@ -711,15 +725,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     for (int i = 0; i < PWC; ++i) rbC[i] = xgC[i] = zero4();
 
     // ---- P1: gates, decay, K K^T and Q K^T; W = U - Kw h
-    if constexpr (EDGE) {
-        if (s.l2k) fk.normalize_rows(rinvK, tid);
-    }
-    fk.stash(Ks, LDD, tid);
-    fq.stash(RQ, LDD, tid);
-    fh.stash(RH, LDD, tid);
-    fu.stash(RU, LDD, tid);
-    if (!add) fn.stash(RN, LDD, tid);
-    __syncthreads();
+    __syncthreads(); // K, Q, h, U, -Kw stashed
     // Gam, K K^T o Gam and P stay in registers at this lane's [C][C] positions
     f32x4 gC[PWC], kkg[PWC], pC[PWC];
     {
@@ -1083,7 +1089,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     }
     if (!more) break;
     cur = nxt;
-    __syncthreads(); // outputs read from LDS before the next chunk's stashes
+    // the next chunk's first inputs: K was last read in P8, Q, h, U and -Kw
+    // earlier, all before the partial-sum barrier; only the outputs with
+    // normalised keys still read K and 1/|k|
+    if constexpr (EDGE) __syncthreads();
+    stash_inputs(tid);
     } // chunk loop
 }
 
