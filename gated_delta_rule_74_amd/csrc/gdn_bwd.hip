@@ -12,6 +12,9 @@
 //   dQ  = diag(e^gam) dO h^T + (dP o Gam) K,   dP = dO W^T
 //   dKw = -dW h^T,  dV' = Tm^T dW,  dK' = Tm^T dKw,  dV = diag(beta) dV'
 //   dL  = -(dV' U^T + dK' Kw^T) (strictly lower part)
+// and, by associativity, dK' = -(Tm^T dW) h^T = -dV' h^T and
+//   dL  = -dV' U^T + dV' (Kw h)^T = -dV' W^T,
+// the forms the per-chunk kernel for heads up to 64 wide uses.
 //   dK  = (dP o Gam)^T Q + diag(e^{gam_n - gam}) W dh'^T + diag(beta e^gam) dK'
 //         + dS K + dS^T K,  dS = diag(beta)(dL o Gam)
 //   dbeta_i = v_i . dV'_i + e^{gam_i} k_i . dK'_i + sum_j dL_ij (K K^T o Gam)_ij
@@ -546,14 +549,14 @@ __global__ __launch_bounds__(64 * (BV / 16 + BWS_HELPERS)) void bwd_chain_ws_ker
 // X[row][col]). Each product reads an operand straight or through the
 // transposing LDS read, whichever its storage needs (gemm<..., ATR, BTR>).
 // U and Tm come from the forward context, so no triangular solve runs here.
-// Thirteen LDS regions, some reused once a value is dead (Pn = phase n; the
+// Twelve LDS regions, some reused once a value is dead (Pn = phase n; the
 // workgroup barrier that ends a phase separates the last read of a value
 // from the first write of its successor):
-//   RK K, RQ Q, RH h^T (P1-5), RU U (P1, P7), RN -Kw (P1, P7)
+//   RK K, RQ Q, RH h^T (P1-7), RU U (P1), RN -Kw (P1)
 //   RPt Pt (P1-4) -> V (stashed in P5, read in P6) -> dSt (P7-8)
-//   RWt Wt (P1-5) -> -dV't (P6-9)     RdO dO (stashed in P1, P4-5) -> dK't (P6-7)
+//   RWt Wt (P1-7)                     RdO dO (stashed in P1, P4-5) -> -dV't (P6-9)
 //   Rdh dh'^T (stashed in P1, P4-5) -> partial sums (P9)
-//   RdW dWt (P4-6)                    RdKw dKw (P5-6)
+//   RdW dWt (P4-6)
 //   RdPG (dP o Gam)^T (P5-6) -> dQ (P9)
 //   RTm Tm (stashed in P5, P6) -> dK (P9)
 // Every input is stashed once; dO and dh' (requested at the top of the
@@ -581,8 +584,7 @@ template <bool BF, int D, int NW> struct LocalSmem {
     static constexpr int odO = oWt + sDC;
     static constexpr int odh = odO + mx(sCD, sDC);
     static constexpr int odW = odh + mx(sDD, sPart);
-    static constexpr int odKw = odW + sDC;
-    static constexpr int odPG = odKw + sCD;
+    static constexpr int odPG = odW + sDC;
     static constexpr int oTm = odPG + mx(sCC, sCD);
     static constexpr int oGam = oTm + mx(sCC, sCD);
     static constexpr int oEg = oGam + NW * C * 8; // gam: one copy per wave
@@ -617,7 +619,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     S *RdO = (S *)(smem + L::odO);
     S *Rdh = (S *)(smem + L::odh);
     S *RdW = (S *)(smem + L::odW);
-    S *RdKw = (S *)(smem + L::odKw);
     S *RdPG = (S *)(smem + L::odPG);
     S *RTm = (S *)(smem + L::oTm);
     double *gam = (double *)(smem + L::oGam);
@@ -790,16 +791,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         store_T<BF, 4, DT, NW>(accdW, RdW, LDC, wave, lane); // dWt
     }
     __syncthreads();
-    // ---- P5: dOh = dO h^T, dKw^T = -h dW^T, dKt = W dh'^T, dP
+    // ---- P5: dOh = dO h^T, dKt = W dh'^T, dP
     f32x4 accQ[PWD], accKd[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = accKd[i] = zero4();
     gemm<BF, 4, DT, D, false, true, NW>(RdO, LDD, RH, LDD, accQ, wave, lane); // dO h^T
     {
-        f32x4 accM[Tiles<DT, 4, NW>::PW];
-#pragma unroll
-        for (int i = 0; i < Tiles<DT, 4, NW>::PW; ++i) accM[i] = zero4();
-        if (!add) gemm<BF, DT, 4, D, true, true, NW>(RH, LDD, RdW, LDC, accM, wave, lane); // h dW^T
         f32x4 accKt[PWD];
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
@@ -823,23 +820,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
             });
             store_T<BF, 4, 4, NW>(accP, RdPG, LDC, wave, lane); // dPGt
         }
-        if (!add) {
-#pragma unroll
-            for (int i = 0; i < Tiles<DT, 4, NW>::PW; ++i) accM[i] = -accM[i];
-            store_T<BF, DT, 4, NW>(accM, RdKw, LDD, wave, lane); // dKw, token rows [C][D]
-        }
         // Tm, and V where Pt was (last read in P4)
         ft.stash(RTm, LDC, tid);
         fv.stash(RPt, LDD, tid);
     }
-    __syncthreads(); // dWt, dKw, dPGt, Tm and V complete; h, dO, Wt, dh' no longer read
-    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw, dQ, dK += (dP o Gam)^T Q
+    __syncthreads(); // dWt, dPGt, Tm and V complete; dO and dh' no longer read
+    // ---- P6: dV' = Tm^T dW, dQ, dK += (dP o Gam)^T Q
     {
-        f32x4 accV[PWD], accKp[PWD];
+        f32x4 accV[PWD];
 #pragma unroll
-        for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
+        for (int i = 0; i < PWD; ++i) accV[i] = zero4();
         gemm<BF, 4, DT, C, true, false, NW>(RTm, LDC, RdW, LDC, accV, wave, lane);
-        if (!add) gemm<BF, 4, DT, C, true, true, NW>(RTm, LDC, RdKw, LDD, accKp, wave, lane);
         // dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
         for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
             accQ[i][e] *= eg[row];
@@ -848,24 +839,31 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         gemm<BF, 4, DT, C, true, true, NW>(RdPG, LDC, Ks, LDD, accQ, wave, lane);
         gemm<BF, 4, DT, C, false, true, NW>(RdPG, LDC, RQ, LDD, accKd, wave, lane);
         for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
-            const float kk = to_f(Ks[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
-            rbD[i][e] += to_f(RPt[row * LDD + col]) * accV[i][e] + eg[row] * kk;
-            rgD[i][e] += bet[row] * eg[row] * kk;
-            accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
+            rbD[i][e] += to_f(RPt[row * LDD + col]) * accV[i][e]; // v_i . dV'_i
         });
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-        store_T<BF, 4, DT, NW>(accV, RWt, LDC, wave, lane);               // -dV't (also the source of dv)
-        if (!add) store_T<BF, 4, DT, NW>(accKp, RdO, LDC, wave, lane); // dK't
+        store_T<BF, 4, DT, NW>(accV, RdO, LDC, wave, lane); // -dV't (also the source of dv)
     }
-    __syncthreads(); // -dV't and dK't complete; V, Tm, dWt, dKw, dPGt no longer read
-    // ---- P7: dL = -(dV' U^T + dK' Kw^T) = (-dV') U^T + dK' (-Kw)^T, dS
+    __syncthreads(); // -dV't complete; V, Tm, dWt, dPGt no longer read
+    // ---- P7: dK' = (-dV') h^T and its terms, dL = (-dV') W^T, dS
     if (!add) {
+        {
+            f32x4 accKp[PWD];
+#pragma unroll
+            for (int i = 0; i < PWD; ++i) accKp[i] = zero4();
+            gemm<BF, 4, DT, D, true, true, NW>(RdO, LDC, RH, LDD, accKp, wave, lane);
+            for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
+                const float kk = eg[row] * to_f(Ks[row * LDD + col]) * accKp[i][e]; // e^{gam_i} k_i . dK'_i
+                rbD[i][e] += kk;
+                rgD[i][e] += bet[row] * kk;
+                accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
+            });
+        }
         f32x4 accL[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accL[i] = zero4();
-        gemm<BF, 4, 4, D, true, false, NW>(RWt, LDC, RU, LDD, accL, wave, lane);
-        gemm<BF, 4, 4, D, true, false, NW>(RdO, LDC, RN, LDD, accL, wave, lane);
+        gemm<BF, 4, 4, D, true, true, NW>(RdO, LDC, RWt, LDC, accL, wave, lane);
         for_tiles<4, 4, NW>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
             rbC[i][e] += dl * kkg[i][e];
@@ -940,7 +938,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                         } pk;
                         const float nb = -bet[j];
 #pragma unroll
-                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(RWt[(c0 + e) * LDC + j]));
+                        for (int e = 0; e < V; ++e) pk.x[e] = from_f<BF>(nb * to_f(RdO[(c0 + e) * LDC + j]));
                         *reinterpret_cast<uint4 *>(dv_out + (size_t)j * H * dv + c0) = pk.u;
                     }
                 }
@@ -952,7 +950,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                         dq_out[(size_t)j * H * dk + col] = RdPG[j * LDD + col];
                         dk_out[(size_t)j * H * dk + col] = RTm[j * LDD + col];
                     }
-                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(RWt[col * LDC + j]));
+                    if (col < dv) dv_out[(size_t)j * H * dv + col] = from_f<BF>(-bet[j] * to_f(RdO[col * LDC + j]));
                 }
             }
         } else {
@@ -1006,7 +1004,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                             }
 #pragma unroll
                             for (int e = 0; e < V; ++e) {
-                                float x = nb * to_f(RWt[(c0 + e) * LDC + j]);
+                                float x = nb * to_f(RdO[(c0 + e) * LDC + j]);
                                 if (Dp) x += Dh * to_f(dov.x[e]);
                                 if (dDp) dsum += to_f(dov.x[e]) * to_f(vv.x[e]);
                                 pk.x[e] = from_f<BF>(x);
@@ -1031,7 +1029,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
                             dk_out[(size_t)j * H * dk + col] = from_f<BF>(kdv);
                         }
                         if (col < dv) {
-                            float x = -bet[j] * to_f(RWt[col * LDC + j]);
+                            float x = -bet[j] * to_f(RdO[col * LDC + j]);
                             if (edge_v) {
                                 const float dd = to_f(do_in[(size_t)j * H * dv + col]);
                                 if (Dp) x += Dh * dd;
