@@ -7,7 +7,8 @@
 // with respect to the chunk-end state, the saved U, -Kw and Tm,
 //   W   = U - Kw h,  P = (Q K^T) o Gam,  dW = P^T dO + diag(e^{gam_n-gam}) K dh'
 //   dQ  = diag(e^gam) dO h^T + (dP o Gam) K,       dP = dO W^T (lower)
-//   dKw = -dW h^T,  dV' = Tm^T dW,  dK' = Tm^T dKw,  dL = -(dV' U^T + dK' Kw^T)
+//   dV' = Tm^T dW,  dK' = Tm^T dKw = -dV' h^T  (dKw = -dW h^T),
+//   dL  = -(dV' U^T + dK' Kw^T) = -dV' W^T,
 //   dK  = (dP o Gam)^T Q + diag(e^{gam_n-gam}) W dh'^T + diag(beta e^gam) dK'
 //         + dS K + dS^T K,  dS = diag(beta)(dL o Gam),  dV = diag(beta) dV'
 // plus the dbeta / dgam row sums. Every intermediate stays on chip: one
@@ -20,10 +21,10 @@
 //
 // Regions (bf16 unless noted; rows padded by 16 bytes):
 //   X0 K [64][136]                    whole chunk
-//   X1 h^T [128][136] (P1-P5) -> V | Q, then U (P6-P7) -> dq rows (P9)
-//   X2 -Kw | U (P1) -> dh'^T [128][136] (P4) -> dKw rows (P5-P6) -> -Kw (P7)
+//   X1 h^T [128][136] (P1-P7) -> dq rows (P9)
+//   X2 -Kw | U (P1) -> dh'^T [128][136] (P4) -> V | Q (P6)
 //   X3 Q (P1) -> dO (P4-P5) -> -dV'^T [128][72] (P6-P9)
-//   X4 W^T [128][72] (P1-P5) -> dK'^T (P6-P7)
+//   X4 W^T [128][72] (P1-P7)
 //   X5 dW^T [128][72] (P4-P6) -> dk rows (P9)
 //   X6 P^T [64][72] (P1-P4) -> Tm (P6) -> row/column partial sums (P9, fp32)
 //   X7 (dP o Gam)^T [64][72] (P5-P6) -> dS^T (P7-P8)
@@ -129,7 +130,6 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     constexpr int D = DW, DT = D / 16, LDD = L::LDD, LDC = L::LDC;
     constexpr int PWC = Tiles<4, 4, NWD>::PW;  // [C][C] tiles per wave
     constexpr int PWD = Tiles<4, DT, NWD>::PW; // [C][D] tiles per wave
-    constexpr int PWM = Tiles<DT, 4, NWD>::PW; // [D][C] tiles per wave
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     S *X0 = (S *)(smem + L::x0), *X1 = (S *)(smem + L::x1), *X2 = (S *)(smem + L::x2);
     S *X3 = (S *)(smem + L::x3), *X4 = (S *)(smem + L::x4), *X5 = (S *)(smem + L::x5);
@@ -309,28 +309,14 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         if (lane == 0) misc[16 + wave] = hd;
     }
     __syncthreads(); // dW^T complete; dh' no longer read
-    // Q, -Kw and U are staged again in P6: requested again here (L2 holds them
-    // from the first request) rather than kept in registers since P1
-    {
-        const size_t qrow = (row0 * H + h) * dk;
-        fq.template fetch<VEC>((const S *)s.q + qrow, (size_t)H * dk, n, dk, tid);
-        if (!add) fn.template fetch<VEC>((const S *)a.NK + cb * C * dk, (size_t)dk, n, dk, tid);
-        fu.template fetch<VEC>((const S *)a.U + cb * C * dv, (size_t)dv, n, dv, tid);
-    }
-    // ---- P5: dOh = dO h^T; dKw = -dW h^T; dP = dO W^T
+    // Q is staged again in P6: requested again here (L2 holds it from the
+    // first request) rather than kept in registers since P1
+    fq.template fetch<VEC>((const S *)s.q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, tid);
+    // ---- P5: dOh = dO h^T; dP = dO W^T
     f32x4 accQ[PWD];
 #pragma unroll
     for (int i = 0; i < PWD; ++i) accQ[i] = zero4();
     gemm<true, 4, DT, D, false, true, NWD, KUNR>(X3, LDD, X1, LDD, accQ, wave, lane); // dO h^T
-    if (!add) {
-        f32x4 accM[PWM];
-#pragma unroll
-        for (int i = 0; i < PWM; ++i) accM[i] = zero4();
-        gemm<true, DT, 4, D, true, true, NWD, KUNR>(X1, LDD, X5, LDC, accM, wave, lane); // h dW^T
-#pragma unroll
-        for (int i = 0; i < PWM; ++i) accM[i] = -accM[i];
-        store_T<true, DT, 4, NWD>(accM, X2, LDD, wave, lane); // dKw, token rows
-    }
     {
         f32x4 accP[PWC];
 #pragma unroll
@@ -346,58 +332,62 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         xgc += col_compact(pp); pin(xgc);
         store_T<true, 4, 4, NWD>(accP, X7, LDC, wave, lane); // (dP o Gam)^T
     }
-    __syncthreads(); // h, dO, W^T no longer read
-    // ---- P6: dV' = Tm^T dW, dK' = Tm^T dKw, dQ, dK += (dP o Gam)^T Q
+    __syncthreads(); // dO no longer read; dh' since P4
+    // ---- P6: dV' = Tm^T dW, dQ, dK += (dP o Gam)^T Q
     ft.stash(X6, LDC, tid);
-    fv.stash(X1, LDD, tid);
-    fq.stash(X1b, LDD, tid);
+    fv.stash(X2, LDD, tid);
+    fq.stash(X2b, LDD, tid);
     __syncthreads();
     {
-        f32x4 accV[PWD], accKp[PWD];
+        f32x4 accV[PWD];
 #pragma unroll
-        for (int i = 0; i < PWD; ++i) accV[i] = accKp[i] = zero4();
-        gemm<true, 4, DT, C, true, false, NWD, KUNR>(X6, LDC, X5, LDC, accV, wave, lane);             // Tm^T dW
-        if (!add) gemm<true, 4, DT, C, true, true, NWD, KUNR>(X6, LDC, X2, LDD, accKp, wave, lane); // Tm^T dKw
+        for (int i = 0; i < PWD; ++i) accV[i] = zero4();
+        gemm<true, 4, DT, C, true, false, NWD, KUNR>(X6, LDC, X5, LDC, accV, wave, lane); // Tm^T dW
         {
             f32x4 qq[PWD];
             for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
                 accQ[i][e] *= eg[row];
-                qq[i][e] = accQ[i][e] * to_f(X1b[row * LDD + col]); // e^{gam_i} q_i . dOh_i
+                qq[i][e] = accQ[i][e] * to_f(X2b[row * LDD + col]); // e^{gam_i} q_i . dOh_i
             });
             rg += row_compact<4, DT>(qq, lane); pin(rg);
         }
         gemm<true, 4, DT, C, true, true, NWD, KUNR>(X7, LDC, X0, LDD, accQ, wave, lane);   // + (dP o Gam) K
-        gemm<true, 4, DT, C, false, true, NWD, KUNR>(X7, LDC, X1b, LDD, accKd, wave, lane); // + (dP o Gam)^T Q
-        __syncthreads(); // Tm, dW^T, dKw, Q reads done
+        gemm<true, 4, DT, C, false, true, NWD, KUNR>(X7, LDC, X2b, LDD, accKd, wave, lane); // + (dP o Gam)^T Q
         {
+            f32x4 bb[PWD];
+            for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+                bb[i][e] = to_f(X2[row * LDD + col]) * accV[i][e]; // v_i . dV'_i
+            });
+            rb += row_compact<4, DT>(bb, lane); pin(rb);
+        }
+#pragma unroll
+        for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
+        store_T<true, 4, DT, NWD>(accV, X3, LDC, wave, lane); // -dV'^T (also the source of dv)
+    }
+    __syncthreads(); // -dV'^T complete; V, Q, Tm, dW^T no longer read
+    // ---- P7: dK' = (-dV') h^T and its terms, dL = (-dV') W^T, dS;
+    //      P8: dK += dS K + dS^T K
+    if (!add) {
+        {
+            f32x4 accKp[PWD];
+#pragma unroll
+            for (int i = 0; i < PWD; ++i) accKp[i] = zero4();
+            gemm<true, 4, DT, D, true, true, NWD, KUNR>(X3, LDC, X1, LDD, accKp, wave, lane); // (-dV') h^T
             f32x4 bb[PWD], gg[PWD];
             for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
-                const float kk = to_f(X0[row * LDD + col]) * accKp[i][e]; // k_i . dK'_i term
-                bb[i][e] = to_f(X1[row * LDD + col]) * accV[i][e] + eg[row] * kk;
-                gg[i][e] = bet[row] * eg[row] * kk;
+                const float kk = eg[row] * to_f(X0[row * LDD + col]) * accKp[i][e]; // e^{gam_i} k_i . dK'_i
+                bb[i][e] = kk;
+                gg[i][e] = bet[row] * kk;
                 accKd[i][e] += bet[row] * eg[row] * accKp[i][e];
             });
             rb += row_compact<4, DT>(bb, lane); pin(rb);
             rg += row_compact<4, DT>(gg, lane); pin(rg);
         }
-#pragma unroll
-        for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
-        store_T<true, 4, DT, NWD>(accV, X3, LDC, wave, lane); // -dV'^T (also the source of dv)
-        if (!add) {
-            store_T<true, 4, DT, NWD>(accKp, X4, LDC, wave, lane); // dK'^T
-            fn.stash(X2, LDD, tid);                               // -Kw again
-            fu.stash(X1b, LDD, tid);                              // U again
-        }
-    }
-    __syncthreads(); // V reads done
-    // ---- P7: dL = (-dV') U^T + dK' (-Kw)^T, dS;  P8: dK += dS K + dS^T K
-    if (!add) {
         f32x4 accL[PWC], sk[PWC];
 #pragma unroll
         for (int i = 0; i < PWC; ++i) accL[i] = sk[i] = zero4();
         gemm<true, 4, 4, D, false, false, NWD, KUNR>(X0, LDD, X0, LDD, sk, wave, lane); // K K^T
-        gemm<true, 4, 4, D, true, false, NWD, KUNR>(X3, LDC, X1b, LDD, accL, wave, lane);
-        gemm<true, 4, 4, D, true, false, NWD, KUNR>(X4, LDC, X2, LDD, accL, wave, lane);
+        gemm<true, 4, 4, D, true, true, NWD, KUNR>(X3, LDC, X4, LDC, accL, wave, lane); // (-dV') W^T
         f32x4 lb[PWC], lg[PWC];
         for_tiles<4, 4, NWD>(wave, lane, [&](int i, int e, int row, int col) {
             const float dl = (row > col) ? accL[i][e] : 0.f;
@@ -420,8 +410,8 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     const Pos nxt = advance(cur);
     const bool more = nxt.lid < lim;
     fetch_early(more ? nxt : cur, tid, lane);
-    // dQ and dK leave through LDS as 16-byte rows (V and dW^T were last read
-    // before the barrier that ended P6)
+    // dQ and dK leave through LDS as 16-byte rows (h was last read in P7, dW^T
+    // in P6, each before a workgroup barrier)
     store_N<true, 4, DT, NWD>(accQ, X1, LDD, wave, lane);
     store_N<true, 4, DT, NWD>(accKd, X5, LDD, wave, lane);
     // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
