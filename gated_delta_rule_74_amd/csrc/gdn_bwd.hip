@@ -882,10 +882,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     const Pos nxt = advance(cur);
     const bool more = nxt.lid < lim;
     fetch_early(more ? nxt : cur, tid, lane);
-    // dQ and dK leave through LDS as 16-byte rows (dPGt and Tm were last read
-    // in P6)
-    store_N<BF, 4, DT, NW>(accQ, RdPG, LDD, wave, lane);
-    store_N<BF, 4, DT, NW>(accKd, RTm, LDD, wave, lane);
+    // dQ and dK leave through LDS (dPGt and Tm were last read in P6): bf16
+    // with 16-byte rows transposed, [D][C] like -dV't, so that one
+    // transposing read hands a lane 16 bytes of an output row; otherwise
+    // (and with the layer edges, whose key normalisation sums over rows) as
+    // 16-byte rows
+    constexpr bool TOUT = BF && VEC && !EDGE;
+    if constexpr (TOUT) {
+        store_T<BF, 4, DT, NW>(accQ, RdPG, LDC, wave, lane);
+        store_T<BF, 4, DT, NW>(accKd, RTm, LDC, wave, lane);
+    } else {
+        store_N<BF, 4, DT, NW>(accQ, RdPG, LDD, wave, lane);
+        store_N<BF, 4, DT, NW>(accKd, RTm, LDD, wave, lane);
+    }
     // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
     {
         // dh' was last read in P5
@@ -915,7 +924,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         // (row dots over the lanes that hold a row); with the skip term dv
         // gains D_h do, and the chunk's share of dD_h (sum of do * v) goes to
         // one slot per wave.
-        if constexpr (!EDGE) {
+        if constexpr (TOUT) {
+            // units of 16 rows x 32 columns of dq, dk or dv, spread over
+            // waves 1..: lane (g, r) stores row 16 mb + r, columns
+            // 32 kb + 8 g .. + 7 (dv = -beta * (-dV'))
+            constexpr int UPM = 4 * (D / 32);
+            const int r16 = lane & 15, g4 = lane >> 4;
+            if (wave > 0) {
+                for (int u = wave - 1; u < 3 * UPM; u += NW - 1) {
+                    const int mtx = u / UPM, mb = (u % UPM) & 3, kb = (u % UPM) >> 2;
+                    const u16 *X = mtx == 0 ? (const u16 *)RdPG : (mtx == 1 ? (const u16 *)RTm : (const u16 *)RdO);
+                    union {
+                        bf16x8 b;
+                        uint4 u;
+                        u16 x[8];
+                    } w;
+                    w.b = operand_tr(X, LDC, 32 * kb, 16 * mb, lane);
+                    const int j = 16 * mb + r16, c0 = 32 * kb + 8 * g4, dd = mtx == 2 ? dv : dk;
+                    if (j < n && c0 < dd) {
+                        if (mtx == 2) {
+                            const float nb = -bet[j];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) w.x[e] = f2bf(nb * bf2f(w.x[e]));
+                        }
+                        S *dst = (S *)(mtx == 0 ? a.dq : (mtx == 1 ? a.dk : a.dv)) + (row0 * H + h) * dd;
+                        *reinterpret_cast<uint4 *>(dst + (size_t)j * H * dd + c0) = w.u;
+                    }
+                }
+            }
+        } else if constexpr (!EDGE) {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
