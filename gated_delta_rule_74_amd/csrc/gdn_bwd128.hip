@@ -410,10 +410,19 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     const Pos nxt = advance(cur);
     const bool more = nxt.lid < lim;
     fetch_early(more ? nxt : cur, tid, lane);
-    // dQ and dK leave through LDS as 16-byte rows (h was last read in P7, dW^T
-    // in P6, each before a workgroup barrier)
-    store_N<true, 4, DT, NWD>(accQ, X1, LDD, wave, lane);
-    store_N<true, 4, DT, NWD>(accKd, X5, LDD, wave, lane);
+    // dQ and dK leave through LDS (h was last read in P7, dW^T in P6, each
+    // before a workgroup barrier): transposed, [D][C] like -dV'^T, so that
+    // one transposing read hands a lane 16 bytes of an output row; with the
+    // layer edges (whose key normalisation sums over rows), or without
+    // 16-byte access, as 16-byte rows
+    constexpr bool TOUT = VEC && !EDGE;
+    if constexpr (TOUT) {
+        store_T<true, 4, DT, NWD>(accQ, X1, LDC, wave, lane);
+        store_T<true, 4, DT, NWD>(accKd, X5, LDC, wave, lane);
+    } else {
+        store_N<true, 4, DT, NWD>(accQ, X1, LDD, wave, lane);
+        store_N<true, 4, DT, NWD>(accKd, X5, LDD, wave, lane);
+    }
     // ---- P9: one fixed-order reduction of every dbeta / dgam contribution
     {
         float *pRbD = (float *)X6, *pRgD = pRbD + C * DT;
@@ -433,7 +442,33 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         // dk = (dk_hat - k_hat (k_hat . dk_hat)) / |k|; with the skip term dv
         // gains D_h do and the chunk's share of dD_h (sum of do * v) goes to
         // one slot per wave.
-        if constexpr (!EDGE) {
+        if constexpr (TOUT) {
+            // units of 16 rows x 32 columns of dq, dk or dv over the waves:
+            // lane (g, r) stores row 16 mb + r, columns 32 kb + 8 g .. + 7
+            // (dv = -beta * (-dV'))
+            constexpr int UPM = 4 * (D / 32);
+            const int g4 = lane >> 4;
+            for (int u = wave; u < 3 * UPM; u += NWD) {
+                const int mtx = u / UPM, mb = (u % UPM) & 3, kb = (u % UPM) >> 2;
+                const u16 *X = mtx == 0 ? (const u16 *)X1 : (mtx == 1 ? (const u16 *)X5 : (const u16 *)X3);
+                union {
+                    bf16x8 b;
+                    uint4 u;
+                    u16 x[8];
+                } w;
+                w.b = operand_tr(X, LDC, 32 * kb, 16 * mb, lane);
+                const int j = 16 * mb + r16, c0 = 32 * kb + 8 * g4, dd = mtx == 2 ? dv : dk;
+                if (j < n && c0 < dd) {
+                    if (mtx == 2) {
+                        const float nb = -bet[j];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w.x[e] = f2bf(nb * bf2f(w.x[e]));
+                    }
+                    S *dst = (S *)(mtx == 0 ? a.dq : (mtx == 1 ? a.dk : a.dv)) + (row0 * H + h) * dd;
+                    *reinterpret_cast<uint4 *>(dst + (size_t)j * H * dd + c0) = w.u;
+                }
+            }
+        } else if constexpr (!EDGE) {
             S *dq_out = (S *)a.dq + (row0 * H + h) * dk;
             S *dk_out = (S *)a.dk + (row0 * H + h) * dk;
             S *dv_out = (S *)a.dv + (row0 * H + h) * dv;
