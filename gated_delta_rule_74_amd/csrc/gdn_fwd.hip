@@ -610,6 +610,11 @@ template <int D> struct WsSmem {
     static constexpr int LDC = C + 8;  // W^T [D][LDC]
     static constexpr int LDP = 16 + 8; // P^T of one 16-row block [C][LDP]
     static constexpr int LDO = 16 * VH + 8;
+    // heads 64 wide: each helper's O block (16 rows x 32 columns) is kept
+    // transposed, [32][LDOT], in the same bytes as [16][LDO]
+    static constexpr bool OT = VH == 2;
+    static constexpr int LDOT = 16 + 4;
+    static_assert(!OT || 32 * LDOT == 16 * LDO, "transposed O block fits its buffer");
     static constexpr int szCD = C * LDD * 2;
     static constexpr int szStage = 4 * szCD; // Q, K, -Kw, U
     static constexpr int szHX = D * LDD * 2;
@@ -636,7 +641,8 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     constexpr int DT = D / 16, KS = D / 32;
     constexpr int NLT = 64 * 4; // loading helper threads (helpers 0..3)
     using L = WsSmem<D>;
-    constexpr int LDD = L::LDD, LDC = L::LDC, LDP = L::LDP, LDO = L::LDO, VH = L::VH;
+    constexpr int LDD = L::LDD, LDC = L::LDC, LDP = L::LDP, LDO = L::LDO, VH = L::VH, LDOT = L::LDOT;
+    constexpr bool OT = L::OT;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
     auto stage = [&](int st, int m) { return (u16 *)(smem + L::oStage + st * L::szStage + m * L::szCD); };
     auto hx = [&](int i) { return (u16 *)(smem + L::oHX + i * L::szHX); };
@@ -710,7 +716,12 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         const int nr = min(16, n - 16 * bi), vlo = 16 * vb, nvc = min(16 * VH, dv - vlo);
         u16 *orow = o + (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
         if constexpr (!EDGE) {
-            if (VEC) {
+            if (OT && VEC) {
+                // one transposing read: row r, columns 8g .. 8g + 7
+                const int i = lane & 15, v = 8 * (lane >> 4);
+                const bf16x8 x = operand_tr(Os, LDOT, 0, 0, lane);
+                if (i < nr && v < nvc) *(bf16x8 *)(orow + (size_t)i * H * dv + v) = x;
+            } else if (VEC) {
                 for (int it = lane; it < 16 * 2 * VH; it += 64) {
                     const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
                     if (i < nr && v < nvc) *(uint4 *)(orow + (size_t)i * H * dv + v) = *(const uint4 *)(Os + i * LDO + v);
@@ -718,7 +729,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
             } else {
                 for (int it = lane; it < 16 * 16 * VH; it += 64) {
                     const int i = it / (16 * VH), v = it % (16 * VH);
-                    if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = Os[i * LDO + v];
+                    if (i < nr && v < nvc) orow[(size_t)i * H * dv + v] = OT ? Os[v * LDOT + i] : Os[i * LDO + v];
                 }
             }
         } else {
@@ -726,9 +737,13 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
             const float Dh = s.D ? s.D[h] : 0.f;
             if (VEC) {
                 for (int it = lane; it < 16 * 2 * VH; it += 64) {
-                    const int i = it / (2 * VH), v = (it % (2 * VH)) * 8;
+                    const int i = OT ? (lane & 15) : it / (2 * VH), v = OT ? 8 * (lane >> 4) : (it % (2 * VH)) * 8;
+                    uint4 x;
+                    if (OT)
+                        x = __builtin_bit_cast(uint4, operand_tr(Os, LDOT, 0, 0, lane));
+                    else
+                        x = *(const uint4 *)(Os + i * LDO + v);
                     if (i < nr && v < nvc) {
-                        uint4 x = *(const uint4 *)(Os + i * LDO + v);
                         if (s.D) x = add_scaled_bf16x8(x, *(const uint4 *)(vrow + (size_t)i * H * dv + v), Dh);
                         *(uint4 *)(orow + (size_t)i * H * dv + v) = x;
                     }
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                     const int i = it / (16 * VH), v = it % (16 * VH);
                     if (i < nr && v < nvc) {
                         const size_t x = (size_t)i * H * dv + v;
-                        u16 val = Os[i * LDO + v];
+                        u16 val = OT ? Os[v * LDOT + i] : Os[i * LDO + v];
                         if (s.D) val = f2bf(bf2f(val) + Dh * bf2f(vrow[x]));
                         orow[x] = val;
                     }
@@ -861,9 +876,15 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                 // pieces; helpers 0..3 leave it for helpers 4..7
                 u16 *Os = loader ? obufA(c - 1, hw) : obuf(hw);
 #pragma unroll
-                for (int x = 0; x < VH; ++x)
+                for (int x = 0; x < VH; ++x) {
+                    if constexpr (OT) {
+                        // four consecutive rows of one column: one 8-byte store
+                        *(short4_t *)(Os + (16 * x + r) * LDOT + 4 * g) = pack4(accO[x]);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Os[(4 * g + e) * LDO + 16 * x + r] = f2bf(accO[x][e]);
+                        for (int e = 0; e < 4; ++e) Os[(4 * g + e) * LDO + 16 * x + r] = f2bf(accO[x][e]);
+                    }
+                }
                 if (!loader) store_o(c - 1, ib, vb0, Os);
             }
             // P (this helper's half of the columns) and diag(e^gam) Q h
