@@ -705,6 +705,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     int tid = tid0;
     asm volatile("" : "+v"(tid));
     const int wave = tid >> 6, lane = tid & 63;
+    // this wave's [C][D] tiles of an LDS matrix with rows of LDD elements, in
+    // the accumulator layout (bf16: one transposing read per tile)
+    auto tiles_cd = [&](const S *X, f32x4 *out) {
+        if constexpr (BF)
+            load_tiles<4, DT, NW>(X, LDD, out, wave, lane);
+        else
+            for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { out[i][e] = to_f(X[row * LDD + col]); });
+    };
     const int h = cur.h, c = cur.c, b = cur.b;
     const int bh = b * H + h;
     const int t0 = c * C, n = min(C, T - t0);
@@ -758,7 +766,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
     }
     {
         f32x4 accW[PWD];
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(RU[row * LDD + col]); });
+        tiles_cd(RU, accW);
         if (!add) gemm<BF, 4, DT, D, false, false, NW>(RN, LDD, RH, LDD, accW, wave, lane); // + (-Kw) h
         store_T<BF, 4, DT, NW>(accW, RWt, LDC, wave, lane);                               // Wt
     }
@@ -802,10 +810,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWD; ++i) accKt[i] = zero4();
         gemm<BF, 4, DT, D, true, true, NW>(RWt, LDC, Rdh, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
+        f32x4 kt[PWD];
+        tiles_cd(Ks, kt);
         for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
             const float x = egn[row] * accKt[i][e];
             accKd[i][e] = x;
-            rsD[i][e] = x * to_f(Ks[row * LDD + col]);
+            rsD[i][e] = x * kt[i][e];
         });
         // dP = dO W^T (lower incl. diagonal), dP o Gam -> RdPG
         {
@@ -832,15 +842,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWD; ++i) accV[i] = zero4();
         gemm<BF, 4, DT, C, true, false, NW>(RTm, LDC, RdW, LDC, accV, wave, lane);
         // dQ = diag(e^gam) dO h^T + (dP o Gam) K, dK += (dP o Gam)^T Q
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
-            accQ[i][e] *= eg[row];
-            rgD[i][e] += accQ[i][e] * to_f(RQ[row * LDD + col]); // e^{gam_i} q_i . dOh_i
-        });
+        {
+            f32x4 qt[PWD];
+            tiles_cd(RQ, qt);
+            for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
+                accQ[i][e] *= eg[row];
+                rgD[i][e] += accQ[i][e] * qt[i][e]; // e^{gam_i} q_i . dOh_i
+            });
+        }
         gemm<BF, 4, DT, C, true, true, NW>(RdPG, LDC, Ks, LDD, accQ, wave, lane);
         gemm<BF, 4, DT, C, false, true, NW>(RdPG, LDC, RQ, LDD, accKd, wave, lane);
-        for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
-            rbD[i][e] += to_f(RPt[row * LDD + col]) * accV[i][e]; // v_i . dV'_i
-        });
+        {
+            f32x4 vt[PWD];
+            tiles_cd(RPt, vt);
+            for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
+                rbD[i][e] += vt[i][e] * accV[i][e]; // v_i . dV'_i
+            });
+        }
 #pragma unroll
         for (int i = 0; i < PWD; ++i) accV[i] = -accV[i];
         store_T<BF, 4, DT, NW>(accV, RdO, LDC, wave, lane); // -dV't (also the source of dv)
@@ -853,8 +871,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_local_kernel(BwdLocalArgs a) {
 #pragma unroll
             for (int i = 0; i < PWD; ++i) accKp[i] = zero4();
             gemm<BF, 4, DT, D, true, true, NW>(RdO, LDC, RH, LDD, accKp, wave, lane);
+            f32x4 kt[PWD];
+            tiles_cd(Ks, kt);
             for_tiles<4, DT, NW>(wave, lane, [&](int i, int e, int row, int col) {
-                const float kk = eg[row] * to_f(Ks[row * LDD + col]) * accKp[i][e]; // e^{gam_i} k_i . dK'_i
+                const float kk = eg[row] * kt[i][e] * accKp[i][e]; // e^{gam_i} k_i . dK'_i
                 rbD[i][e] += kk;
                 rgD[i][e] += bet[row] * kk;
                 accKd[i][e] += bet[row] * eg[row] * accKp[i][e];

@@ -195,6 +195,22 @@ __device__ __forceinline__ void for_tiles(int wave, int lane, F &&f) {
     }
 }
 
+// This wave's tiles of a bf16 [rows][cols] LDS matrix X (row stride ld) in
+// the accumulator layout: lane 16g + r gets rows 16 tm + 4g .. + 3 of column
+// 16 tn + r, one transposing 64-bit read per tile (X read as the [K][M]
+// operand of a 16x16x16 product).
+template <int MT, int NT, int NW = NWAVE>
+__device__ __forceinline__ void load_tiles(const u16 *X, int ld, f32x4 *out, int wave, int lane) {
+    using TL = Tiles<MT, NT, NW>;
+#pragma unroll
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
+        const short4_t v = operand_tr4(X, ld, 16 * (t / NT), 16 * (t % NT), lane);
+        out[i] = f32x4{bf2f((u16)v[0]), bf2f((u16)v[1]), bf2f((u16)v[2]), bf2f((u16)v[3])};
+    }
+}
+
 // Store the tiles of this wave transposed: dst[col][row] (4 consecutive rows
 // per lane become 4 consecutive elements).
 // (optionally scaled per row by rs[row]).
