@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
     }
     {
         f32x4 accW[PWD];
-        for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) { accW[i][e] = to_f(X2b[row * LDD + col]); });
+        load_tiles<4, DT, NWD>(X2b, LDD, accW, wave, lane);
         if (!add) gemm<true, 4, DT, D, false, false, NWD, KUNR>(X2, LDD, X1, LDD, accW, wave, lane); // + (-Kw) h
         store_T<true, 4, DT, NWD>(accW, X4, LDC, wave, lane);                              // W^T
     }
@@ -286,11 +286,15 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         gemm<true, 4, DT, D, true, true, NWD, KUNR>(X4, LDC, X2, LDD, accKt, wave, lane); // W dh'^T
         // dK += diag(e^{gam_n - gam}) dKt ; s_j = e^{gam_n - gam_j} k_j . dKt_j
         // enters dgam_j with a minus sign and the last row with its total
-        for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
-            const float x = egn[row] * accKt[i][e];
-            accKd[i][e] = x;
-            accKt[i][e] = x * to_f(X0[row * LDD + col]);
-        });
+        {
+            f32x4 kt[PWD];
+            load_tiles<4, DT, NWD>(X0, LDD, kt, wave, lane);
+            for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
+                const float x = egn[row] * accKt[i][e];
+                accKd[i][e] = x;
+                accKt[i][e] = x * kt[i][e];
+            });
+        }
         rs += row_compact<4, DT>(accKt, lane); pin(rs);
         // <h, dh'> over the two staged states (padding is zero), one slot per wave
         float hd = 0.f;
@@ -323,9 +327,10 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         for (int i = 0; i < PWC; ++i) accP[i] = zero4();
         gemm<true, 4, 4, D, false, true, NWD, KUNR>(X3, LDD, X4, LDC, accP, wave, lane); // dO W^T
         f32x4 pp[PWC];
+        load_tiles_t<4, 4, NWD>(X6, LDC, pp, wave, lane); // P (held transposed)
         for_tiles<4, 4, NWD>(wave, lane, [&](int i, int e, int row, int col) {
             const float dp = row >= col ? accP[i][e] : 0.f;
-            pp[i][e] = dp * bf2f(X6[col * LDC + row]); // dP o P
+            pp[i][e] = dp * pp[i][e]; // dP o P
             accP[i][e] = dp * gC[i][e];
         });
         xgr += row_compact<4, 4>(pp, lane); pin(xgr);
@@ -345,9 +350,10 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         gemm<true, 4, DT, C, true, false, NWD, KUNR>(X6, LDC, X5, LDC, accV, wave, lane); // Tm^T dW
         {
             f32x4 qq[PWD];
+            load_tiles<4, DT, NWD>(X2b, LDD, qq, wave, lane); // Q
             for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
                 accQ[i][e] *= eg[row];
-                qq[i][e] = accQ[i][e] * to_f(X2b[row * LDD + col]); // e^{gam_i} q_i . dOh_i
+                qq[i][e] = accQ[i][e] * qq[i][e]; // e^{gam_i} q_i . dOh_i
             });
             rg += row_compact<4, DT>(qq, lane); pin(rg);
         }
@@ -355,9 +361,9 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
         gemm<true, 4, DT, C, false, true, NWD, KUNR>(X7, LDC, X2b, LDD, accKd, wave, lane); // + (dP o Gam)^T Q
         {
             f32x4 bb[PWD];
-            for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
-                bb[i][e] = to_f(X2[row * LDD + col]) * accV[i][e]; // v_i . dV'_i
-            });
+            load_tiles<4, DT, NWD>(X2, LDD, bb, wave, lane); // V
+#pragma unroll
+            for (int i = 0; i < PWD; ++i) bb[i] = bb[i] * accV[i]; // v_i . dV'_i
             rb += row_compact<4, DT>(bb, lane); pin(rb);
         }
 #pragma unroll
@@ -374,8 +380,9 @@ __global__ __launch_bounds__(NTD) void bwd_local128_kernel(BwdLocalArgs a) {
             for (int i = 0; i < PWD; ++i) accKp[i] = zero4();
             gemm<true, 4, DT, D, true, true, NWD, KUNR>(X3, LDC, X1, LDD, accKp, wave, lane); // (-dV') h^T
             f32x4 bb[PWD], gg[PWD];
+            load_tiles<4, DT, NWD>(X0, LDD, bb, wave, lane); // K
             for_tiles<4, DT, NWD>(wave, lane, [&](int i, int e, int row, int col) {
-                const float kk = eg[row] * to_f(X0[row * LDD + col]) * accKp[i][e]; // e^{gam_i} k_i . dK'_i
+                const float kk = eg[row] * bb[i][e] * accKp[i][e]; // e^{gam_i} k_i . dK'_i
                 bb[i][e] = kk;
                 gg[i][e] = bet[row] * kk;
                 accKd[i][e] += bet[row] * eg[row] * accKp[i][e];

@@ -211,6 +211,21 @@ __device__ __forceinline__ void load_tiles(const u16 *X, int ld, f32x4 *out, int
     }
 }
 
+// The same tiles of a matrix held transposed, Xt[col][row]: the four rows
+// a lane owns are adjacent, one 64-bit read per tile.
+template <int MT, int NT, int NW = NWAVE>
+__device__ __forceinline__ void load_tiles_t(const u16 *Xt, int ld, f32x4 *out, int wave, int lane) {
+    using TL = Tiles<MT, NT, NW>;
+#pragma unroll
+    for (int i = 0; i < TL::PW; ++i) {
+        const int t = wave + NW * i;
+        if (TL::N % NW != 0 && t >= TL::N) break;
+        const short4_t v = *reinterpret_cast<const short4_t *>(Xt + (16 * (t % NT) + (lane & 15)) * ld +
+                                                               16 * (t / NT) + 4 * (lane >> 4));
+        out[i] = f32x4{bf2f((u16)v[0]), bf2f((u16)v[1]), bf2f((u16)v[2]), bf2f((u16)v[3])};
+    }
+}
+
 // Store the tiles of this wave transposed: dst[col][row] (4 consecutive rows
 // per lane become 4 consecutive elements).
 // (optionally scaled per row by rs[row]).
