@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -290,13 +291,33 @@ hipError_t aux_of_current(Aux *&out, hipStream_t strm) {
     return hipSuccess;
 }
 
-// Number of chunk ranges the forward is split into (one when the serial
-// kernel cannot take a range, or the sequence is short).
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int v = cache[dev & 63].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev & 63].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Number of chunk ranges the forward is split into, so that the prep of one
+// range runs beside the serial pass of the previous one. One range when the
+// serial kernel cannot take a range, when the sequence is short, or when the
+// serial pass alone takes more than half of the compute units: a serial
+// workgroup holds most of a unit's LDS, so the prep then finds no room beside
+// it and the ranges only add launches (at B8 H16 T4096 d56, 256 serial
+// workgroups: 0.224 ms for the forward as one range, 0.25 as four).
 #ifndef GDN_FWD_RANGES
 #define GDN_FWD_RANGES 4
 #endif
 int fwd_segments(const gdn_shape_t *s, bool bf, int D) {
     if (!gdn::fwd_segmentable(bf, D)) return 1;
+    const long long wgs = (long long)s->B * s->H * gdn::fwd_ws_blocks(D, s->dv);
+    if (2 * wgs > device_cus()) return 1;
     const int n = nchunks(s) / 16;
     return n < 1 ? 1 : (n > GDN_FWD_RANGES ? GDN_FWD_RANGES : n);
 }

@@ -116,6 +116,20 @@ __device__ __forceinline__ short4_t pack4(f32x4 x) {
     return __builtin_bit_cast(short4_t, u);
 }
 
+// A lane's two 16x16x16 operand pieces (4 values each, from K blocks k0 and
+// k1) as its 8 values of one 16x16x32 operand. A product sums over K in any
+// order, so when both operands are joined the same way, one K = 32 step
+// covering both blocks gives the sum of the two K = 16 steps, in half the
+// instructions (gfx950 runs a K = 32 step in the time of a K = 16 one).
+__device__ __forceinline__ bf16x8 join8(short4_t lo, short4_t hi) {
+    uint4 u;
+    u.x = __builtin_bit_cast(uint2, lo).x;
+    u.y = __builtin_bit_cast(uint2, lo).y;
+    u.z = __builtin_bit_cast(uint2, hi).x;
+    u.w = __builtin_bit_cast(uint2, hi).y;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 // One 16x16x16 operand from an LDS matrix stored with K as its row index,
 // X[k][m]: lane 16g + j receives X[k0 + 4g + e][m0 + j], e = 0..3.
 __device__ __forceinline__ short4_t operand_tr4(const u16 *X, int ld, int k0, int m0, int lane) {
@@ -388,20 +402,20 @@ template <bool BF, int DP, int NR = C, int NT = NTHR> struct ChunkFrag {
     }
 };
 
-// A per-lane scalar of a chunk (g or beta of row `lane`), loaded from a
-// clamped in-range address without a branch. The caller masks rows >= n
-// where it uses the value, so the load can stay in flight until then.
+// A gate from its input: the logistic sigmoid of a logit when the inputs are
+// logits, else the input itself.
+__device__ __forceinline__ float gate_of(float x, bool logit) { return logit ? 1.f / (1.f + expf(-x)) : x; }
+
 // Wait until every vector memory access this wave issued has completed
 // (s_waitcnt with vmcnt = 0 and the other counters left free). Placed where
 // all prefetched registers are needed anyway, it also tells the compiler's
 // wait tracking that no load into them is still outstanding, so later loads
 // into the same registers are not held back behind stores.
-// A gate from its input: the logistic sigmoid of a logit when the inputs are
-// logits, else the input itself.
-__device__ __forceinline__ float gate_of(float x, bool logit) { return logit ? 1.f / (1.f + expf(-x)) : x; }
-
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A per-lane scalar of a chunk (g or beta of row `lane`), loaded from a
+// clamped in-range address without a branch. The caller masks rows >= n
+// where it uses the value, so the load can stay in flight until then.
 __device__ __forceinline__ float load_row_scalar(const float *__restrict__ p, size_t stride, int lane,
                                                  int n) {
     return p[(size_t)min(lane, n - 1) * stride];

@@ -582,9 +582,12 @@ hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st) {
 
 // ------------------------------------------------- wave-specialised chain
 //
-// bf16 path for head dims up to 64. One workgroup per (batch, head).
-// Waves 0..DT-1 ("chain waves", DT = D/16) each carry 16 value columns of
-// the state h [D][16] in MFMA accumulators and run only the recurrence
+// bf16 path for head dims up to 64. One workgroup per (batch, head, block
+// of BV value columns): the state's value columns evolve independently, so
+// a block needs only its own columns of U, h, W and O (every block loads Q,
+// K and -Kw and forms P). Waves 0..BV/16-1 ("chain waves") each carry 16
+// value columns of the state h [D][16] in MFMA accumulators and run only
+// the recurrence
 //   W = U + NK h,   h <- e^{gam_n} h + K^T diag(e^{gam_n - gam}) W.
 // With 16x16x16 products an accumulator tile (rows 4*(lane/16)+e, column
 // lane%16) is already the B operand of a product over the same rows, so W
@@ -593,7 +596,8 @@ hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st) {
 // follow split the rest: they stage the next chunk's inputs into LDS, form
 // P = (Q K^T) o Gam and diag(e^gam) Q h for the current chunk, and finish
 // O = ... + P W one chunk behind the chain (W arrives through LDS). Helper w
-// owns chunk rows 16*(w%4).. and half of the value columns. One barrier per
+// owns chunk rows 16*(w%4).. and half of the block's value columns (and
+// half of P's column blocks). One barrier per
 // chunk hands the double-buffered LDS over. Helpers 0..3 issue every global
 // load and helpers 4..7 store O (their own rows, and the rows helpers 0..3
 // leave in LDS one chunk earlier), so the wait of a loading wave for its
@@ -604,21 +608,21 @@ hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st) {
 
 constexpr int WS_HELPERS = 8;
 
-template <int D> struct WsSmem {
-    static constexpr int VH = D / 32;  // value blocks per helper
-    static constexpr int LDD = D + 8;  // token rows [C][LDD]; h^T [D][LDD]
-    static constexpr int LDC = C + 8;  // W^T [D][LDC]
+template <int D, int BV> struct WsSmem {
+    static constexpr int VH = BV / 32; // value blocks per helper
+    static constexpr int LDD = D + 8;  // token rows [C][LDD]; h^T [BV][LDD]
+    static constexpr int LDC = C + 8;  // W^T [BV][LDC]
     static constexpr int LDP = 16 + 8; // P^T of one 16-row block [C][LDP]
     static constexpr int LDO = 16 * VH + 8;
-    // heads 64 wide: each helper's O block (16 rows x 32 columns) is kept
+    // 64-column blocks: each helper's O block (16 rows x 32 columns) is kept
     // transposed, [32][LDOT], in the same bytes as [16][LDO]
     static constexpr bool OT = VH == 2;
     static constexpr int LDOT = 16 + 4;
     static_assert(!OT || 32 * LDOT == 16 * LDO, "transposed O block fits its buffer");
     static constexpr int szCD = C * LDD * 2;
     static constexpr int szStage = 4 * szCD; // Q, K, -Kw, U
-    static constexpr int szHX = D * LDD * 2;
-    static constexpr int szWX = D * LDC * 2;
+    static constexpr int szHX = BV * LDD * 2;
+    static constexpr int szWX = BV * LDC * 2;
     static constexpr int szP = C * LDP * 2;
     static constexpr int szO = 16 * LDO * 2;
     static constexpr int szDec = 3 * C * 4 + 16; // gam (log2), e^gam, e^{gam_n-gam}, e^{gam_n}
@@ -636,11 +640,11 @@ template <int D> struct WsSmem {
 // EDGE: the layer edges (key normalisation, skip term) are compiled in; the
 // plain instantiation carries none of their code, so its schedule is that of
 // the recurrence alone
-template <int D, bool VEC, bool EDGE>
-__global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
-    constexpr int DT = D / 16, KS = D / 32;
+template <int D, int BV, bool VEC, bool EDGE>
+__global__ __launch_bounds__(64 * (BV / 16 + WS_HELPERS)) void fwd_chain_ws_kernel(FwdChainArgs a) {
+    constexpr int DT = D / 16, KS = D / 32, VT = BV / 16;
     constexpr int NLT = 64 * 4; // loading helper threads (helpers 0..3)
-    using L = WsSmem<D>;
+    using L = WsSmem<D, BV>;
     constexpr int LDD = L::LDD, LDC = L::LDC, LDP = L::LDP, LDO = L::LDO, VH = L::VH, LDOT = L::LDOT;
     constexpr bool OT = L::OT;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::SIZE];
@@ -658,21 +662,27 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     const SeqArgs &s = a.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, r = lane & 15;
-    const int bh = xcd_remap(blockIdx.x, gridDim.x);
+    // workgroup -> (batch-head, value block): the value blocks of one head
+    // are neighbours, so they run on one XCD and share its cache for the
+    // rows every block loads (q, k, -Kw)
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = lid / a.NVB, V0 = (lid % a.NVB) * BV;
     const int b = bh / s.H, h = bh % s.H;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC, c0 = a.c0, c1 = a.c1;
-    const bool chain = wave < DT;
+    const int nvc = min(BV, dv - V0); // value columns of this block
+    const bool chain = wave < VT;
     const bool add = s.additive != 0;
 
-    // ---- chain-wave state
+    // ---- chain-wave state: value columns V0 + v0 .. + 15 (block-local v0)
     const int v0 = 16 * wave;
     f32x4 hacc[DT];
     short4_t hb[DT];
     // ---- helper-wave state: rows 16*ib.., value blocks vb0..vb0+VH-1
-    const int hw = wave - DT, htid = tid - 64 * DT;
+    const int hw = wave - VT, htid = tid - 64 * VT;
     const int ib = hw & 3, half = hw >> 2, vb0 = half * VH;
     const bool loader = !chain && hw < 4;
-    ChunkFrag<true, D, C, NLT> fq, fk, fn, fu;
+    ChunkFrag<true, D, C, NLT> fq, fk, fn;
+    ChunkFrag<true, BV, C, NLT> fu;
     float pg = 0.f;
     f32x4 accO[VH];
     const u16 *q = (const u16 *)s.q, *k = (const u16 *)s.k;
@@ -685,7 +695,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
         fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
         if (!add) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, htid);
-        fu.template fetch<VEC>(U + cb * C * dv, (size_t)dv, n, dv, htid);
+        fu.template fetch<VEC>(U + cb * C * dv + V0, (size_t)dv, n, nvc, htid);
         pg = a.gam[cb * C + lane];
     };
     auto stash = [&](int c) {
@@ -713,7 +723,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
     // as they leave)
     auto store_o = [&](int cc, int bi, int vb, const u16 *Os) {
         const int n = min(C, T - cc * C);
-        const int nr = min(16, n - 16 * bi), vlo = 16 * vb, nvc = min(16 * VH, dv - vlo);
+        const int nr = min(16, n - 16 * bi), vlo = V0 + 16 * vb, nvc = min(16 * VH, dv - vlo);
         u16 *orow = o + (((size_t)b * T + cc * C + 16 * bi) * H + h) * dv + vlo;
         if constexpr (!EDGE) {
             if (OT && VEC) {
@@ -768,7 +778,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         for (int kb = 0; kb < DT; ++kb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int d = 16 * kb + 4 * g + e, v = v0 + r;
+                const int d = 16 * kb + 4 * g + e, v = V0 + v0 + r;
                 hacc[kb][e] = (a.h_in && d < dk && v < dv) ? a.h_in[((size_t)bh * dk + d) * dv + v] : 0.f;
             }
             hb[kb] = pack4(hacc[kb]);
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
                 // lane (one 8-byte store when dk % 8 == 0, else per element)
                 if (cs) {
                     u16 *dst = cs + ((size_t)bh * NC + c) * dv * dk;
-                    const int v = v0 + r;
+                    const int v = V0 + v0 + r;
 #pragma unroll
                     for (int kb = 0; kb < DT; ++kb) {
                         const int d = 16 * kb + 4 * g;
@@ -937,7 +947,7 @@ __global__ __launch_bounds__(64 * (D / 16 + WS_HELPERS)) void fwd_chain_ws_kerne
         for (int kb = 0; kb < DT; ++kb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int d = 16 * kb + 4 * g + e, v = v0 + r;
+                const int d = 16 * kb + 4 * g + e, v = V0 + v0 + r;
                 if (d < dk && v < dv) a.hT[((size_t)bh * dk + d) * dv + v] = hacc[kb][e];
             }
         }
@@ -993,18 +1003,37 @@ template <bool BF, int D> static hipError_t prep_inst(const PrepArgs &a, hipStre
     return hipGetLastError();
 }
 
-template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a, hipStream_t st) {
-    const int grid = a.s.B * a.s.H;
-    const int block = 64 * (D / 16 + WS_HELPERS);
+// Value columns per workgroup of the wave-specialised serial pass. Heads 64
+// wide are split into two 32-column blocks: each workgroup then stages,
+// multiplies and stores half of U, Qh and O (Q, K, -Kw and P are formed by
+// both), which shortens the helpers' share of a chunk step, and the pass
+// fills twice the compute units. At B8 H16 T4096 d56 the pass took 0.133 ms
+// against 0.152 with one 64-column block (each run alone).
+#ifndef GDN_WS_BV64
+#define GDN_WS_BV64 32
+#endif
+constexpr int ws_vblock(int D) { return D == 64 ? GDN_WS_BV64 : D; }
+
+int fwd_ws_blocks(int D, int dv) {
+    const int bv = ws_vblock(D);
+    return (dv + bv - 1) / bv;
+}
+
+template <int D> static hipError_t chain_ws_inst(const FwdChainArgs &a0, hipStream_t st) {
+    constexpr int BV = ws_vblock(D);
+    FwdChainArgs a = a0;
+    a.NVB = (a.s.dv + BV - 1) / BV;
+    const int grid = a.s.B * a.s.H * a.NVB;
+    const int block = 64 * (BV / 16 + WS_HELPERS);
     const bool vec = vec_ok<true>(a.s), edge = a.s.l2k || a.s.D;
     if (vec && !edge)
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true, false>), dim3(grid), dim3(block), 0, st, a);
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, BV, true, false>), dim3(grid), dim3(block), 0, st, a);
     else if (vec)
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, true, true>), dim3(grid), dim3(block), 0, st, a);
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, BV, true, true>), dim3(grid), dim3(block), 0, st, a);
     else if (!edge)
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false, false>), dim3(grid), dim3(block), 0, st, a);
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, BV, false, false>), dim3(grid), dim3(block), 0, st, a);
     else
-        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, false, true>), dim3(grid), dim3(block), 0, st, a);
+        hipLaunchKernelGGL((fwd_chain_ws_kernel<D, BV, false, true>), dim3(grid), dim3(block), 0, st, a);
     return hipGetLastError();
 }
 

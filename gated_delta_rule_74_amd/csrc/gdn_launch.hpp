@@ -148,6 +148,8 @@ int fwd_vblock(int D, bool segmented);
 int fwd_scan_segments(bool bf16, int D, int NC);
 hipError_t launch_fwd_scan(const ScanArgs &a, hipStream_t st);
 bool fwd_segmentable(bool bf16, int D); // chain launch accepts a chunk range
+// workgroups per (batch, head) of the wave-specialised serial pass
+int fwd_ws_blocks(int D, int dv);
 int bwd_chain_vblock(bool bf16, int D, bool segmented);
 bool bwd_supported(bool bf16, int D);
 // Scratch bytes the local-gradient pass needs for this padded head dim (0

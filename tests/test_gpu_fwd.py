@@ -79,8 +79,12 @@ def test_ragged_lengths_bf16(T):
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (100, 100), (128, 128), (64, 40),
-                                   (24, 72), (5, 9)])
+                                   (24, 72), (5, 9), (64, 16), (40, 56)])
 def test_head_dims_bf16(dk, dv):
+    """Head widths of every forward kernel; heads up to 64 wide run the
+    serial pass in 32-column value blocks, including a single narrow block
+    (64, 16), a partial second block (64, 40) and keys narrower than the
+    values (40, 56)."""
     say(f"fwd bf16 dk={dk} dv={dv}")
     x = gi.gen_seq(1, 130, 2, dk, dv, "bf16", seed=700 + dk + dv, h0="randn", decay="weak")
     check_fwd(x, "bf16")
