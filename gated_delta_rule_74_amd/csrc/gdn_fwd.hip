@@ -897,7 +897,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + WS_HELPERS)) void fwd_chain_ws_kern
                 }
                 if (!loader) store_o(c - 1, ib, vb0, Os);
             }
-            // P (this helper's half of the columns) and diag(e^gam) Q h
+            // P's row block ib (storing helpers) and diag(e^gam) Q h
             if (o && c < c1) {
                 const int st = c & 1;
                 const u16 *Qs = stage(st, 0), *Ks = stage(st, 1), *HT = hx(st);
@@ -909,9 +909,20 @@ __global__ __launch_bounds__(64 * (BV / 16 + WS_HELPERS)) void fwd_chain_ws_kern
                 u16 *Pt = pbuf(st, ib);
                 const float4 gi = *(const float4 *)(gam + 16 * ib + 4 * g);
                 const float gil[4] = {gi.x, gi.y, gi.z, gi.w};
+                // P is lower triangular over the chunk: of row block ib only
+                // the column blocks 0..ib hold values. The storing helper of
+                // the row block forms them and writes zeros for the others;
+                // the loading helper, which also stages and requests the
+                // chunks, forms none. (Handing the diagonal block of row
+                // blocks 2 and 3 to the loading helpers, so that no helper
+                // forms more than three, measured slower.)
 #pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    const int jb = 2 * half + y;
+                for (int jb = 0; jb < 4; ++jb) {
+                    if (loader) break;
+                    if (jb > ib) {
+                        *(short4_t *)(Pt + (16 * jb + r) * LDP + 4 * g) = short4_t{0, 0, 0, 0};
+                        continue;
+                    }
                     f32x4 p = zero4();
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
