@@ -669,7 +669,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + WS_HELPERS)) void fwd_chain_ws_kern
     const int bh = lid / a.NVB, V0 = (lid % a.NVB) * BV;
     const int b = bh / s.H, h = bh % s.H;
     const int T = s.T, H = s.H, dk = s.dk, dv = s.dv, NC = s.NC, c0 = a.c0, c1 = a.c1;
-    const int nvc = min(BV, dv - V0); // value columns of this block
+    const int bcols = min(BV, dv - V0); // value columns of this block
     const bool chain = wave < VT;
     const bool add = s.additive != 0;
 
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + WS_HELPERS)) void fwd_chain_ws_kern
         fq.template fetch<VEC>(q + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
         fk.template fetch<VEC>(k + (row0 * H + h) * dk, (size_t)H * dk, n, dk, htid);
         if (!add) fn.template fetch<VEC>(NK + cb * C * dk, (size_t)dk, n, dk, htid);
-        fu.template fetch<VEC>(U + cb * C * dv + V0, (size_t)dv, n, nvc, htid);
+        fu.template fetch<VEC>(U + cb * C * dv + V0, (size_t)dv, n, bcols, htid);
         pg = a.gam[cb * C + lane];
     };
     auto stash = [&](int c) {
