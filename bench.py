@@ -33,6 +33,8 @@ Objects on the line besides the headline:
                  HBM: the HBM roofline) and "hot" (one 51 MB state set that
                  the Infinity Cache holds: cache-resident rate, no HBM
                  fraction); "mtp3_*" three tokens per call
+  "stream_copy"  a plain 1 GiB device-to-device copy: the HBM rate the box
+                 reaches on a streaming kernel (context, not a denominator)
   "cpu_baseline" the fp64 oracle, fwd+bwd of the headline workload, and
   "oracle_times" its per-configuration timings (fwd, fwd+bwd, the 1024-step
                  decode chain, a one-thread forward)
@@ -903,6 +905,33 @@ def oracle_times(x_decode, budget_s=3.0):
 
 # ------------------------------------------------------------------ main
 
+def copy_bench(dev, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy (torch's copy kernel) of 1 GiB, read and
+    write bytes both counted: the HBM rate this machine reaches on the simplest
+    streaming kernel. Context for the roofline fractions, never their
+    denominator (that is the 8 TB/s peak)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"bytes_per_copy": 2 * nbytes, "ms": round(ms, 4), "GB_s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "torch device-to-device copy of 1 GiB (read + write counted), mean of 10 back to back; "
+                    "context, not a roofline denominator"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -993,6 +1022,8 @@ def main():
     }
     out["forward"] = forward_bench(dev, args.steps, args.warmup, flush)
     print(f"forward: {out['forward']['ms']} ms", file=sys.stderr, flush=True)
+    out["stream_copy"] = copy_bench(dev)
+    print(f"stream copy: {out['stream_copy']['GB_s']} GB/s", file=sys.stderr, flush=True)
     if not args.no_long_ctx:
         lc, _, _ = fwdbwd_measure("long_ctx", dev, max(3, args.steps // 2), 2, flush)
         out["long_ctx"] = lc
